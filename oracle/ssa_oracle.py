@@ -1,0 +1,337 @@
+"""Plain, slow fp64 CPU oracle for causal block-sparse attention as used by SSA.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call
+this module: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers, tables or pre/post-processing).
+
+Sources (titles of the web pages the method is described on):
+  [SSA-summary]  "Resumen Tecnico: SSA (Sparse Sparse Attention)", gist.science 2511.20102
+  [SSA-guide]    "SSA: Guida a Sparse Sparse Attention per LLM", mauroscia.it
+  [DashAttn]     "Resumen Tecnico: DashAttention", gist.science 2605.18753
+  [S2O]          "Resumen Tecnico: S2O - Parada Temprana para Atencion Escasa ...", gist.science 2602.22575
+
+What is computed (all arithmetic in float64 unless a step says it rounds):
+  1. block means of K (and of the queries of each query block)      [SSA-guide] "Block-sparse attention e Receptive Field";
+                                                                     [DashAttn] "Etapa 0" (zero-initialised learned
+                                                                     query == uniform average over the chunk)
+  2. coarse block scores  s = scale * qbar . kbar  for causal blocks [SSA-guide] same section; [DashAttn] "Etapa 1"
+  3. top-k block selection per query block, diagonal always kept    [SSA-guide] same section; [DashAttn] "Etapa 2"
+                                                                     (separate branch for near-diagonal chunks)
+  4. softmax attention restricted to the selected blocks            [SSA-summary] 2 "Mecanismo Central" (SA stream)
+  5. full causal softmax attention (the counterpart output)         [SSA-summary] "Alineacion Bidireccional"
+  6. dropped attention mass: full-softmax probability on keys the
+     sparse pattern leaves out                                      [SSA-summary] 1 "Planteamiento del Problema",
+                                                                     "Alineacion Bidireccional" (delta(t))
+
+Readings where the pages leave a step open (each also listed in the design doc):
+  * selection is per query block (block-mean query), per query head; the
+    budget ``topk`` counts the forced diagonal block;
+  * summaries are held in fp32 and scores are rounded to fp32 before the
+    top-k decision (the decision is taken in the precision the scores are
+    stored in, on both sides);
+  * ties order by lower block index first; a NaN score ranks below -inf;
+  * with fewer than ``topk`` causal blocks, all of them are selected;
+  * softmax scale 1/sqrt(d) unless given; logs are natural logs;
+  * query row r (0-based within the query tensor) sits at absolute position
+    ``q_offset + r`` and sees keys c <= q_offset + r; query block i holds rows
+    [i*B, (i+1)*B) and its diagonal key block is (q_offset + i*B) // B.
+    Decode is the case seq_q == 1, q_offset == L-1.
+
+Arrays: Q [b, Hq, seq_q, d], K/V [b, Hkv, seq_kv, d] (any float dtype whose
+values are exactly the bf16 inputs), query head h uses KV head h // (Hq/Hkv).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------- helpers
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def round_f32(x) -> np.ndarray:
+    """Round float64 values to the nearest float32 (ties to even) and return
+    them as float64 again."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def n_blocks(n: int, block: int) -> int:
+    return -(-n // block)
+
+
+def diag_block(i: int, q_offset: int, block: int) -> int:
+    """Key block holding the first row of query block i."""
+    return (q_offset + i * block) // block
+
+
+def _check_geometry(seq_q: int, seq_kv: int, q_offset: int, block: int):
+    if seq_kv != q_offset + seq_q:
+        raise ValueError("causal layout requires seq_kv == q_offset + seq_q")
+    if seq_q > 1 and q_offset % block != 0:
+        raise ValueError("a multi-row query chunk must start on a block boundary")
+
+
+# --------------------------------------------------------------------------- step 1: summaries
+
+def block_means(x, block: int) -> np.ndarray:
+    """Mean of the rows of each contiguous block of ``block`` rows (the last,
+    possibly partial, block averages the rows it has).
+
+    x: [..., n, d]  ->  [..., ceil(n/block), d], float64 (exact sums, one division).
+    [SSA-guide] "Block-sparse attention e Receptive Field": the sequence is cut
+    into contiguous blocks and each is represented by its mean."""
+    x = _f64(x)
+    n = x.shape[-2]
+    nb = n_blocks(n, block)
+    out = np.empty(x.shape[:-2] + (nb, x.shape[-1]), dtype=np.float64)
+    for j in range(nb):
+        rows = x[..., j * block: min((j + 1) * block, n), :]
+        out[..., j, :] = rows.sum(axis=-2) / rows.shape[-2]
+    return out
+
+
+def key_summaries(k, block: int) -> np.ndarray:
+    """Stored key-block summaries: block means rounded to fp32 (float64 array)."""
+    return round_f32(block_means(k, block))
+
+
+def query_summaries(q, block: int) -> np.ndarray:
+    """Query-block summaries: block means of the query rows, rounded to fp32."""
+    return round_f32(block_means(q, block))
+
+
+# --------------------------------------------------------------------------- step 2: scores
+
+def block_scores(q, k, block: int, scale: Optional[float] = None, q_offset: int = 0,
+                 k_summary=None) -> np.ndarray:
+    """Coarse block scores s[b,h,i,j] = fp32(scale * qbar[b,h,i] . kbar[b,g(h),j])
+    for key blocks j up to the diagonal block of query block i, -inf beyond it.
+
+    [SSA-guide] "Block-sparse attention e Receptive Field" (query vs block mean
+    representations); [DashAttn] "Etapa 1" (logits of each query against the
+    chunk summaries).  ``k_summary`` (fp32 values) replaces the pooled K when
+    summaries were cached once their block completed ([DashAttn] "Etapa 0")."""
+    q = _f64(q)
+    b, hq, seq_q, d = q.shape
+    if k_summary is None:
+        kbar = key_summaries(k, block)
+        seq_kv = _f64(k).shape[-2]
+    else:
+        kbar = round_f32(k_summary)
+        seq_kv = q_offset + seq_q
+    hkv = kbar.shape[1]
+    group = hq // hkv
+    _check_geometry(seq_q, seq_kv, q_offset, block)
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    qbar = query_summaries(q, block)
+    nqb, nkb = qbar.shape[2], kbar.shape[2]
+    s = np.full((b, hq, nqb, nkb), -np.inf, dtype=np.float64)
+    for bi in range(b):
+        for h in range(hq):
+            g = h // group
+            dots = qbar[bi, h] @ kbar[bi, g].T           # [nqb, nkb]
+            for i in range(nqb):
+                jd = diag_block(i, q_offset, block)
+                s[bi, h, i, : jd + 1] = round_f32(scale * dots[i, : jd + 1])
+    return s
+
+
+# --------------------------------------------------------------------------- step 3: selection
+
+def _rank_key(score: float, j: int):
+    """Sort key: larger score first, then smaller block index; NaN below -inf."""
+    if math.isnan(score):
+        return (1, 0.0, j)
+    return (0, -score, j)
+
+
+def select_blocks(scores, topk: int, block: int, q_offset: int = 0) -> np.ndarray:
+    """Selected key blocks per (b, h, query block): the diagonal block plus the
+    ``topk - 1`` best-scoring earlier blocks (all causal blocks when there are
+    at most ``topk``), listed in ascending order and padded with -1.
+
+    [SSA-guide] "Block-sparse attention e Receptive Field" (keep only the top-k
+    most relevant blocks); [DashAttn] "Etapa 2" (near-diagonal chunks handled
+    by their own branch).  Returns int64 [b, Hq, nqb, topk]."""
+    scores = _f64(scores)
+    b, hq, nqb, _ = scores.shape
+    out = np.full((b, hq, nqb, topk), -1, dtype=np.int64)
+    for bi in range(b):
+        for h in range(hq):
+            for i in range(nqb):
+                jd = diag_block(i, q_offset, block)
+                if jd + 1 <= topk:
+                    chosen = list(range(jd + 1))
+                else:
+                    ranked = sorted(range(jd), key=lambda j: _rank_key(scores[bi, h, i, j], j))
+                    chosen = sorted(ranked[: topk - 1] + [jd])
+                out[bi, h, i, : len(chosen)] = chosen
+    return out
+
+
+# --------------------------------------------------------------------------- steps 4-6: attention
+
+def _row_attention(qrow, keys, vals, scale):
+    """Softmax attention of one query row over the given keys (float64).
+    Returns (output [d], lse, logits [n])."""
+    logits = scale * (keys @ qrow)
+    m = logits.max()
+    w = np.exp(logits - m)
+    z = w.sum()
+    return (w @ vals) / z, m + math.log(z), logits
+
+
+def _allowed_keys(sel_row, pos: int, block: int, seq_kv: int) -> np.ndarray:
+    """Key positions c <= pos whose block is in the selected list."""
+    cols = []
+    for j in sel_row:
+        if j < 0:
+            continue
+        lo, hi = j * block, min((j + 1) * block, seq_kv, pos + 1)
+        if lo < hi:
+            cols.append(np.arange(lo, hi))
+    return np.concatenate(cols) if cols else np.zeros(0, dtype=np.int64)
+
+
+def sparse_attention(q, k, v, sel, block: int, scale: Optional[float] = None, q_offset: int = 0,
+                     rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Block-sparse attention: row r of query block i attends to keys c <= its
+    position whose block is selected for (b, h, i).
+    [SSA-summary] 2 "Mecanismo Central" (SA stream); [SSA-guide]
+    "Block-sparse attention e Receptive Field" (attention only over the tokens
+    inside the chosen blocks).
+
+    Returns (O [b,Hq,seq_q,d], LSE [b,Hq,seq_q]) or, when ``rows`` lists
+    (b, h, r) triples, (O [n,d], LSE [n]) for just those rows."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    b, hq, seq_q, d = q.shape
+    hkv, seq_kv = k.shape[1], k.shape[2]
+    group = hq // hkv
+    _check_geometry(seq_q, seq_kv, q_offset, block)
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+
+    def one(bi, h, r):
+        g = h // group
+        cols = _allowed_keys(sel[bi, h, r // block], q_offset + r, block, seq_kv)
+        o, lse, _ = _row_attention(q[bi, h, r], k[bi, g, cols], v[bi, g, cols], scale)
+        return o, lse
+
+    if rows is not None:
+        res = [one(*t) for t in rows]
+        return np.stack([o for o, _ in res]), np.array([l for _, l in res])
+    out = np.empty((b, hq, seq_q, d))
+    lse = np.empty((b, hq, seq_q))
+    for bi in range(b):
+        for h in range(hq):
+            g = h // group
+            for i in range(n_blocks(seq_q, block)):
+                r0, r1 = i * block, min((i + 1) * block, seq_q)
+                # key columns of the selected blocks, up to the last row's position
+                cols = _allowed_keys(sel[bi, h, i], q_offset + r1 - 1, block, seq_kv)
+                logits = scale * (q[bi, h, r0:r1] @ k[bi, g, cols].T)
+                pos = q_offset + np.arange(r0, r1)
+                logits[cols[None, :] > pos[:, None]] = -np.inf          # causal
+                m = logits.max(axis=1, keepdims=True)
+                w = np.exp(logits - m)
+                z = w.sum(axis=1, keepdims=True)
+                out[bi, h, r0:r1] = (w @ v[bi, g, cols]) / z
+                lse[bi, h, r0:r1] = (m + np.log(z))[:, 0]
+    return out, lse
+
+
+def full_attention_dropped_mass(q, k, v, sel, block: int, scale: Optional[float] = None,
+                                q_offset: int = 0, row_range: Optional[Tuple[int, int]] = None,
+                                rows: Optional[Sequence[Tuple[int, int, int]]] = None):
+    """Full causal attention (the counterpart output) and the dropped mass
+        delta_r = sum over keys c <= pos(r) whose block is NOT selected for r's
+                  query block of  exp(logit_rc - LSE_full[r]),
+    i.e. the full-softmax probability that the sparse pattern leaves out,
+    summed directly.
+    [SSA-summary] "Alineacion Bidireccional" (auxiliary output in the opposite
+    mode; delta(t)) and 1 "Planteamiento del Problema" (approximation error
+    linear in the attention weight on unselected tokens).
+
+    ``row_range`` = (lo, hi) restricts to query rows [lo, hi) (lo, hi multiples
+    of the block size or hi == seq_q).  Returns (O, LSE, delta) over those rows,
+    or per listed (b, h, r) triple when ``rows`` is given."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    b, hq, seq_q, d = q.shape
+    hkv, seq_kv = k.shape[1], k.shape[2]
+    group = hq // hkv
+    _check_geometry(seq_q, seq_kv, q_offset, block)
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+
+    def one(bi, h, r):
+        g = h // group
+        pos = q_offset + r
+        o, lse, logits = _row_attention(q[bi, h, r], k[bi, g, : pos + 1], v[bi, g, : pos + 1], scale)
+        keep = np.zeros(pos + 1, dtype=bool)
+        keep[_allowed_keys(sel[bi, h, r // block], pos, block, seq_kv)] = True
+        delta = np.exp(logits[~keep] - lse).sum()
+        return o, lse, delta
+
+    if rows is not None:
+        res = [one(*t) for t in rows]
+        return (np.stack([t[0] for t in res]), np.array([t[1] for t in res]),
+                np.array([t[2] for t in res]))
+    lo, hi = (0, seq_q) if row_range is None else row_range
+    out = np.empty((b, hq, hi - lo, d))
+    lse = np.empty((b, hq, hi - lo))
+    delta = np.empty((b, hq, hi - lo))
+    for bi in range(b):
+        for h in range(hq):
+            g = h // group
+            for i in range(lo // block, n_blocks(hi, block)):
+                r0, r1 = max(i * block, lo), min((i + 1) * block, hi)
+                last = q_offset + r1 - 1
+                logits = scale * (q[bi, h, r0:r1] @ k[bi, g, : last + 1].T)
+                pos = q_offset + np.arange(r0, r1)
+                cols = np.arange(last + 1)
+                future = cols[None, :] > pos[:, None]
+                logits[future] = -np.inf
+                m = logits.max(axis=1, keepdims=True)
+                w = np.exp(logits - m)
+                z = w.sum(axis=1, keepdims=True)
+                out[bi, h, r0 - lo:r1 - lo] = (w @ v[bi, g, : last + 1]) / z
+                row_lse = m + np.log(z)
+                lse[bi, h, r0 - lo:r1 - lo] = row_lse[:, 0]
+                selected = np.zeros(last + 1, dtype=bool)
+                selected[_allowed_keys(sel[bi, h, i], last, block, seq_kv)] = True
+                dropped = (~selected)[None, :] & ~future
+                delta[bi, h, r0 - lo:r1 - lo] = np.where(dropped, np.exp(logits - row_lse), 0.0).sum(axis=1)
+    return out, lse, delta
+
+
+# --------------------------------------------------------------------------- the whole path
+
+def hot_path(q, k, v, block: int, topk: int, scale: Optional[float] = None, q_offset: int = 0,
+             k_summary=None, full_row_range: Optional[Tuple[int, int]] = None, with_full: bool = True):
+    """Summaries -> scores -> selection -> sparse attention -> full attention and
+    dropped mass, as one dict of float64 / int64 arrays."""
+    res = {}
+    if k_summary is None:
+        res["k_summary"] = key_summaries(k, block)
+    res["scores"] = block_scores(q, k, block, scale, q_offset, k_summary=k_summary)
+    res["idx"] = select_blocks(res["scores"], topk, block, q_offset)
+    res["o_sparse"], res["lse_sparse"] = sparse_attention(q, k, v, res["idx"], block, scale, q_offset)
+    if with_full:
+        res["o_full"], res["lse_full"], res["dropped"] = full_attention_dropped_mass(
+            q, k, v, res["idx"], block, scale, q_offset, row_range=full_row_range)
+    return res
+

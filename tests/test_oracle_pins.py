@@ -1,0 +1,400 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is checked against things other than itself: a hand-worked
+example, closed forms, PyTorch library routines (SDPA, logsumexp, avg_pool1d,
+matmul), brute-force enumeration on tiny inputs, and identities the
+mathematics fixes.  Each ``check_*`` takes the oracle module so the mutation
+tests at the bottom can show that a planted mistake in the oracle fails at
+least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ssa_oracle
+from tests import torch_reference as tr
+
+RNG = np.random.default_rng(20261203)
+
+
+def bf16_values(shape, rng=RNG, scale=1.0):
+    x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * scale)
+    return x.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def rand_qkv(b, hq, hkv, n, d, rng=RNG):
+    return bf16_values((b, hq, n, d), rng), bf16_values((b, hkv, n, d), rng), bf16_values((b, hkv, n, d), rng)
+
+
+# ----------------------------------------------------------------------------- checks
+
+def check_hand_example(O, golden_dir):
+    with open(os.path.join(golden_dir, "hand_example.json")) as f:
+        g = json.load(f)
+    B, k, sc = g["block"], g["topk"], g["scale"]
+    q = np.array(g["q"], float)[None, None]
+    kk = np.array(g["k"], float)[None, None]
+    v = np.array(g["v"], float)[None, None]
+    ks = O.key_summaries(kk, B)
+    assert np.array_equal(ks[0, 0], np.array(g["k_summary"], float))
+    s = O.block_scores(q, kk, B, scale=sc)
+    exp_s = np.array([[np.inf * -1 if x is None else x for x in row] for row in g["scores"]])
+    assert np.array_equal(s[0, 0], exp_s)
+    idx = O.select_blocks(s, k, B)
+    assert np.array_equal(idx[0, 0], np.array(g["idx"]))
+    o_sp, lse_sp = O.sparse_attention(q, kk, v, idx, B, scale=sc)
+    o_f, lse_f, dm = O.full_attention_dropped_mass(q, kk, v, idx, B, scale=sc)
+    r5 = g["row5"]
+    w = np.exp(np.array(r5["sparse_logits"]))
+    vs = v[0, 0, r5["sparse_keys"]]
+    np.testing.assert_allclose(o_sp[0, 0, 5], (w[:, None] * vs).sum(0) / w.sum(), rtol=1e-14)
+    np.testing.assert_allclose(lse_sp[0, 0, 5], math.log(w.sum()), rtol=1e-14)
+    wf = np.exp(np.array(r5["full_logits"]))
+    vf = v[0, 0, r5["full_keys"]]
+    np.testing.assert_allclose(o_f[0, 0, 5], (wf[:, None] * vf).sum(0) / wf.sum(), rtol=1e-14)
+    dropped = [r5["full_keys"].index(c) for c in r5["dropped_keys"]]
+    np.testing.assert_allclose(dm[0, 0, 5], wf[dropped].sum() / wf.sum(), rtol=1e-14)
+
+
+def check_block_means(O):
+    # library: avg_pool1d (ceil mode averages the rows a partial window has)
+    for n, B in [(256, 64), (200, 64), (37, 8), (5, 5), (1, 64)]:
+        x = bf16_values((2, 3, n, 4))
+        np.testing.assert_allclose(O.block_means(x, B), tr.avg_pool_blocks(x, B), rtol=1e-14, atol=0)
+    # closed form: row c holds the value c  ->  block j mean = midpoint of its rows
+    n, B = 13, 4
+    x = np.repeat(np.arange(n, dtype=float)[:, None], 3, axis=1)[None, None]
+    got = O.block_means(x, B)[0, 0, :, 0]
+    want = [(j * B + min((j + 1) * B, n) - 1) / 2 for j in range(-(-n // B))]
+    assert np.array_equal(got, np.array(want))
+    # a constant block is its own mean, exactly
+    row = bf16_values((1, 1, 1, 64))
+    assert np.array_equal(O.block_means(np.repeat(row, 64, axis=2), 64), row)
+
+
+def check_scores_token_level(O):
+    # block size 1: block scores are the token logits fp32(scale * q_r . k_c) for c <= r
+    b, hq, hkv, n, d = 1, 4, 2, 24, 16
+    q, k, _ = rand_qkv(b, hq, hkv, n, d)
+    sc = 0.3
+    s = O.block_scores(q, k, 1, scale=sc)
+    kk = torch.from_numpy(k).double().repeat_interleave(hq // hkv, dim=1)
+    logits = (torch.matmul(torch.from_numpy(q).double(), kk.transpose(-1, -2)) * float(np.float32(sc)))
+    want = logits.to(torch.float32).double().numpy()
+    want = np.where(np.tril(np.ones((n, n), bool))[None, None], want, -np.inf)
+    assert np.array_equal(s, want)
+
+
+def check_scores_gqa_and_causal(O):
+    # KV head g holds rows (g+1)*e0; every query row is e0  ->  s = scale*(g(h)+1) on causal blocks
+    b, hq, hkv, n, d, B = 2, 6, 3, 48, 8, 16
+    q = np.zeros((b, hq, n, d)); q[..., 0] = 1
+    k = np.zeros((b, hkv, n, d))
+    for g in range(hkv):
+        k[:, g, :, 0] = g + 1
+    s = O.block_scores(q, k, B, scale=0.5)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        for i in range(n // B):
+            assert np.all(s[:, h, i, : i + 1] == 0.5 * (g + 1))
+            assert np.all(np.isneginf(s[:, h, i, i + 1:]))
+
+
+def _brute_top(scores_row, cands, m):
+    """The unique m-subset T of cands such that every member outranks every
+    non-member under (higher score, then lower index); NaN ranks lowest."""
+    def beats(a, c):
+        sa, sb = scores_row[a], scores_row[c]
+        if math.isnan(sb) and not math.isnan(sa):
+            return True
+        if math.isnan(sa):
+            return math.isnan(sb) and a < c
+        return sa > sb or (sa == sb and a < c)
+    found = [set(T) for T in itertools.combinations(cands, m)
+             if all(beats(t, u) for t in T for u in cands if u not in T)]
+    assert len(found) == 1
+    return found[0]
+
+
+def check_select_brute_force(O):
+    rng = np.random.default_rng(7)
+    nqb, k, B = 9, 4, 4
+    for trial in range(40):
+        s = np.round(rng.standard_normal((1, 2, nqb, nqb)), 1)  # coarse values force exact ties
+        if trial % 5 == 0:
+            s[0, 0, 6, 2] = np.nan
+        idx = O.select_blocks(s, k, B)
+        for h in range(2):
+            for i in range(nqb):
+                if i + 1 <= k:
+                    want = set(range(i + 1))
+                else:
+                    want = _brute_top(s[0, h, i], list(range(i)), k - 1) | {i}
+                got = [j for j in idx[0, h, i] if j >= 0]
+                assert got == sorted(want)
+                assert list(idx[0, h, i, len(got):]) == [-1] * (k - len(got))
+
+
+def check_select_ties_and_decode(O):
+    # all scores equal -> blocks 0..k-2 plus the diagonal
+    s = np.zeros((1, 1, 10, 10))
+    idx = O.select_blocks(s, 4, 64)
+    assert list(idx[0, 0, 9]) == [0, 1, 2, 9]
+    # decode: one query row at position L-1; the forced block is the one holding it
+    L, B = 1000, 64
+    row = np.linspace(-1, 1, 16)[None, None, None, :]
+    idx = O.select_blocks(row, 5, B, q_offset=L - 1)
+    assert (L - 1) // B == 15
+    assert list(idx[0, 0, 0]) == [11, 12, 13, 14, 15]
+
+
+def check_sparse_vs_sdpa(O):
+    for (b, hq, hkv, n, d, B, k, q_off) in [(2, 4, 2, 160, 16, 16, 4, 0),   # ragged: 160 = 10 blocks
+                                           (1, 3, 1, 100, 8, 16, 3, 0),      # ragged tail block
+                                           (1, 2, 2, 64, 8, 8, 2, 0)]:
+        q, kk, v = rand_qkv(b, hq, hkv, n, d)
+        sc = float(np.float32(1.0 / math.sqrt(d)))   # the scale argument is an fp32 value
+        s = O.block_scores(q, kk, B)
+        idx = O.select_blocks(s, k, B)
+        o, lse = O.sparse_attention(q, kk, v, idx, B)
+        mask = tr.block_mask_from_idx(idx, n, n, B, 0)
+        o_ref, lse_ref = tr.sdpa(q, kk, v, mask, sc)
+        np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+        # per-row evaluation agrees with the blocked evaluation
+        rows = [(0, hq - 1, n - 1), (b - 1, 0, 5), (0, 1 % hq, n // 2)]
+        o_r, lse_r = O.sparse_attention(q, kk, v, idx, B, rows=rows)
+        for t, (bi, h, r) in enumerate(rows):
+            np.testing.assert_allclose(o_r[t], o[bi, h, r], rtol=1e-12, atol=1e-13)
+
+
+def check_sparse_special_cases(O):
+    b, hq, hkv, n, d, B = 1, 4, 2, 128, 16, 16
+    q, kk, v = rand_qkv(b, hq, hkv, n, d)
+    sc = 0.25
+    causal = tr.causal_mask(n, n, 0)
+    full_ref = tr.sdpa(q, kk, v, causal, sc)
+    # k >= number of blocks: sparse == full causal attention, dropped mass == 0
+    idx = O.select_blocks(O.block_scores(q, kk, B, scale=sc), n // B, B)
+    o, lse = O.sparse_attention(q, kk, v, idx, B, scale=sc)
+    np.testing.assert_allclose(o, full_ref[0], rtol=1e-11, atol=1e-12)
+    _, _, dm = O.full_attention_dropped_mass(q, kk, v, idx, B, scale=sc)
+    assert np.all(dm == 0)
+    # B == N: one block, always the diagonal -> full causal attention
+    idx1 = O.select_blocks(O.block_scores(q, kk, n, scale=sc), 1, n)
+    o1, _ = O.sparse_attention(q, kk, v, idx1, n, scale=sc)
+    np.testing.assert_allclose(o1, full_ref[0], rtol=1e-11, atol=1e-12)
+    # k == 1: block-diagonal causal attention
+    idxd = O.select_blocks(O.block_scores(q, kk, B, scale=sc), 1, B)
+    od, _ = O.sparse_attention(q, kk, v, idxd, B, scale=sc)
+    blockdiag = torch.block_diag(*[torch.ones(B, B, dtype=torch.bool)] * (n // B)) & causal
+    np.testing.assert_allclose(od, tr.sdpa(q, kk, v, blockdiag, sc)[0], rtol=1e-11, atol=1e-12)
+
+
+def check_sparse_brute_force_loops(O):
+    # pure-Python loops over a tiny problem, straight from the definition
+    n, d, B, k = 10, 3, 3, 2
+    rng = np.random.default_rng(3)
+    q, kk, v = rand_qkv(1, 2, 1, n, d, rng)
+    sc = 0.7
+    idx = O.select_blocks(O.block_scores(q, kk, B, scale=sc), k, B)
+    o, lse = O.sparse_attention(q, kk, v, idx, B, scale=sc)
+    of, lsef, dm = O.full_attention_dropped_mass(q, kk, v, idx, B, scale=sc)
+    scf = float(np.float32(sc))
+    for h in range(2):
+        for r in range(n):
+            sel = [j for j in idx[0, h, r // B] if j >= 0]
+            num = [0.0] * d
+            den = 0.0
+            numf = [0.0] * d
+            denf = 0.0
+            drop = 0.0
+            for c in range(r + 1):
+                logit = scf * sum(float(q[0, h, r, t]) * float(kk[0, 0, c, t]) for t in range(d))
+                e = math.exp(logit)
+                denf += e
+                for t in range(d):
+                    numf[t] += e * float(v[0, 0, c, t])
+                if c // B in sel:
+                    den += e
+                    for t in range(d):
+                        num[t] += e * float(v[0, 0, c, t])
+                else:
+                    drop += e
+            np.testing.assert_allclose(o[0, h, r], np.array(num) / den, rtol=1e-12)
+            np.testing.assert_allclose(lse[0, h, r], math.log(den), rtol=1e-12)
+            np.testing.assert_allclose(of[0, h, r], np.array(numf) / denf, rtol=1e-12)
+            np.testing.assert_allclose(dm[0, h, r], drop / denf, rtol=1e-12, atol=1e-15)
+
+
+def check_full_and_dropped_identities(O):
+    b, hq, hkv, n, d, B, k = 2, 4, 2, 192, 16, 16, 3
+    q, kk, v = rand_qkv(b, hq, hkv, n, d)
+    sc = 1 / 4
+    idx = O.select_blocks(O.block_scores(q, kk, B), k, B)
+    o_sp, lse_sp = O.sparse_attention(q, kk, v, idx, B)
+    o_f, lse_f, dm = O.full_attention_dropped_mass(q, kk, v, idx, B)
+    ref_o, ref_lse = tr.sdpa(q, kk, v, tr.causal_mask(n, n, 0), sc)
+    np.testing.assert_allclose(o_f, ref_o, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse_f, ref_lse, rtol=1e-12, atol=1e-12)
+    # (i) rows of the first k blocks keep every causal key
+    assert np.all(dm[:, :, : k * B] == 0)
+    # (iv) 0 <= delta < 1
+    assert np.all(dm >= 0) and np.all(dm < 1)
+    # (ii) delta = 1 - exp(LSE_sparse - LSE_full)
+    np.testing.assert_allclose(dm, 1 - np.exp(lse_sp - lse_f), rtol=1e-9, atol=1e-12)
+    # (iii) O_full - O_sparse = delta * (O_dropped - O_sparse), O_dropped from SDPA on the complement
+    keep = tr.block_mask_from_idx(idx, n, n, B, 0)
+    comp = tr.causal_mask(n, n, 0) & ~keep
+    rows_with_drop = comp.any(-1)
+    comp_safe = comp | ~rows_with_drop[..., None]     # rows without dropped keys: any valid mask
+    o_drop = tr.sdpa(q, kk, v, comp_safe, sc)[0]
+    lhs = o_f - o_sp
+    rhs = dm[..., None] * (o_drop - o_sp)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-8, atol=1e-12)
+    # the row-range slice equals the matching rows of the whole
+    o_s, lse_s, dm_s = O.full_attention_dropped_mass(q, kk, v, idx, B, row_range=(64, 192))
+    np.testing.assert_allclose(o_s, o_f[:, :, 64:], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dm_s, dm[:, :, 64:], rtol=1e-12, atol=1e-15)
+
+
+def check_tie_closed_form(O):
+    # every K row identical -> all logits of a row equal -> uniform softmax
+    b, hq, hkv, n, d, B, k = 1, 2, 1, 160, 8, 16, 3
+    q, kk, v = rand_qkv(b, hq, hkv, n, d)
+    kk = np.repeat(kk[:, :, :1], n, axis=2)
+    s = O.block_scores(q, kk, B)
+    idx = O.select_blocks(s, k, B)
+    o_sp, _ = O.sparse_attention(q, kk, v, idx, B)
+    o_f, _, dm = O.full_attention_dropped_mass(q, kk, v, idx, B)
+    for i in range(n // B):
+        want = list(range(i + 1)) if i + 1 <= k else list(range(k - 1)) + [i]
+        assert [j for j in idx[0, 0, i] if j >= 0] == want
+    for r in range(n):
+        i = r // B
+        kept = (r + 1) if i < k else (k - 1) * B + (r - i * B + 1)
+        np.testing.assert_allclose(dm[0, 0, r], 1 - kept / (r + 1), rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(o_f[0, 0, r], v[0, 0, : r + 1].mean(0), rtol=1e-11, atol=1e-13)
+        cols = [c for c in range(r + 1) if (c // B) in [j for j in idx[0, 0, i] if j >= 0]]
+        np.testing.assert_allclose(o_sp[0, 0, r], v[0, 0, cols].mean(0), rtol=1e-11, atol=1e-13)
+
+
+def check_decode(O):
+    # one query token per (seq, head) at position L-1 against a cache of L keys
+    b, hq, hkv, L, d, B, k = 2, 4, 2, 300, 8, 32, 4
+    rng = np.random.default_rng(11)
+    q = bf16_values((b, hq, 1, d), rng)
+    kk, v = bf16_values((b, hkv, L, d), rng), bf16_values((b, hkv, L, d), rng)
+    ksum = O.key_summaries(kk, B)
+    s = O.block_scores(q, kk, B, q_offset=L - 1)
+    s2 = O.block_scores(q, None, B, q_offset=L - 1, k_summary=ksum)
+    assert np.array_equal(s, s2)
+    jd = (L - 1) // B
+    idx = O.select_blocks(s, k, B, q_offset=L - 1)
+    o, lse = O.sparse_attention(q, kk, v, idx, B, q_offset=L - 1)
+    sc = float(np.float32(1 / math.sqrt(d)))
+    for bi in range(b):
+        for h in range(hq):
+            g = h // 2
+            # scores straight from avg_pool1d summaries and a dot product
+            kb = tr.avg_pool_blocks(kk[bi, g][None, None], B)[0, 0].astype(np.float32).astype(np.float64)
+            logits = (kb @ q[bi, h, 0].astype(np.float64)) * float(np.float32(sc))
+            sf = logits.astype(np.float32).astype(np.float64)
+            assert np.array_equal(s[bi, h, 0, : jd + 1], sf[: jd + 1])
+            want = sorted(_brute_top(sf, list(range(jd)), k - 1) | {jd})
+            assert list(idx[bi, h, 0]) == want
+    mask = tr.block_mask_from_idx(idx, 1, L, B, L - 1)
+    o_ref, lse_ref = tr.sdpa(q, kk, v, mask, sc)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_causal,
+              check_select_brute_force, check_select_ties_and_decode, check_sparse_vs_sdpa,
+              check_sparse_special_cases, check_sparse_brute_force_loops,
+              check_full_and_dropped_identities, check_tie_closed_form, check_decode]
+
+
+# ----------------------------------------------------------------------------- the pins
+
+def test_hand_example(golden_dir):
+    check_hand_example(ssa_oracle, golden_dir)
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_pin(check):
+    check(ssa_oracle)
+
+
+def test_geometry_rejected():
+    q = np.zeros((1, 1, 3, 4))
+    k = np.zeros((1, 1, 5, 4))
+    with pytest.raises(ValueError):
+        ssa_oracle.block_scores(q, k, 2, q_offset=0)        # seq_kv != q_offset + seq_q
+    with pytest.raises(ValueError):
+        ssa_oracle.block_scores(q, k, 4, q_offset=2)        # chunk not on a block boundary
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+# Each mutant plants one plausible mistake in the oracle (on the CPU); at least
+# one pin must fail for it.
+
+def _fails(check, *args):
+    try:
+        check(ssa_oracle, *args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _any_pin_fails(golden_dir):
+    if _fails(check_hand_example, golden_dir):
+        return True
+    return any(_fails(c) for c in ALL_CHECKS)
+
+
+MUTANTS = {
+    "tie_break_higher_index_first": ("_rank_key", lambda s, j: (1, 0.0, -j) if math.isnan(s) else (0, -s, -j)),
+    "nan_ranks_highest": ("_rank_key", lambda s, j: (-1, 0.0, j) if math.isnan(s) else (0, -s, j)),
+    "diagonal_off_by_one": ("diag_block", lambda i, q_offset, block: max(0, (q_offset + i * block) // block - 1)),
+    "partial_block_divides_by_block": ("block_means", None),
+    "scale_one_over_d": ("default_scale", lambda d: 1.0 / d),
+    "no_fp32_rounding": ("round_f32", lambda x: np.asarray(x, dtype=np.float64)),
+    "drops_last_selected_block": ("_allowed_keys", None),
+}
+
+
+def _mutant_block_means(x, block):
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-2]
+    nb = -(-n // block)
+    out = np.empty(x.shape[:-2] + (nb, x.shape[-1]))
+    for j in range(nb):
+        out[..., j, :] = x[..., j * block: (j + 1) * block, :].sum(axis=-2) / block
+    return out
+
+
+_orig_allowed = ssa_oracle._allowed_keys
+
+
+def _mutant_allowed(sel_row, pos, block, seq_kv):
+    kept = [j for j in sel_row if j >= 0]
+    return _orig_allowed(kept[:-1] if len(kept) > 1 else kept, pos, block, seq_kv)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch, golden_dir):
+    attr, fn = MUTANTS[name]
+    if name == "partial_block_divides_by_block":
+        fn = _mutant_block_means
+    if name == "drops_last_selected_block":
+        fn = _mutant_allowed
+    monkeypatch.setattr(ssa_oracle, attr, fn)
+    assert _any_pin_fails(golden_dir), f"no pin catches mutant {name}"
