@@ -1,0 +1,246 @@
+// C-ABI host layer of libssa: argument validation, geometry, kernel launch.
+// All validation happens before anything touches the HIP runtime, so invalid
+// calls fail the same way on machines without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ssa.h"
+#include "ssa_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ssa_status_t fail(ssa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ssa_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(SSA_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validate the shape and fill the kernel geometry.  `want_empty` is set when
+// there is nothing to compute.
+ssa_status_t make_geometry(const ssa_shape_t* s, ssa::Geometry* g, bool* empty, const char* fn) {
+  if (!s) return fail(SSA_ERR_INVALID_ARG, "%s: shape is NULL", fn);
+  if (s->batch < 0 || s->seq_q < 0 || s->seq_kv < 0 || s->q_offset < 0)
+    return fail(SSA_ERR_INVALID_ARG, "%s: negative batch/seq_q/seq_kv/q_offset", fn);
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads != 0)
+    return fail(SSA_ERR_INVALID_ARG, "%s: n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                fn, s->n_q_heads, s->n_kv_heads);
+  if (s->head_dim < 1 || s->block < 1 || s->topk < 1)
+    return fail(SSA_ERR_INVALID_ARG, "%s: head_dim, block and topk must be >= 1", fn);
+  if ((int64_t)s->q_offset + s->seq_q != s->seq_kv)
+    return fail(SSA_ERR_INVALID_ARG, "%s: seq_kv (%d) must equal q_offset (%d) + seq_q (%d)", fn,
+                s->seq_kv, s->q_offset, s->seq_q);
+  if (s->seq_q > 1 && s->q_offset % s->block != 0)
+    return fail(SSA_ERR_INVALID_ARG, "%s: a multi-row query chunk must start on a block boundary", fn);
+  if (!isfinite(s->scale)) return fail(SSA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (s->causal != 1) return fail(SSA_ERR_UNSUPPORTED, "%s: only causal attention is implemented", fn);
+  if (s->head_dim != ssa::kHeadDim)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: head_dim %d (this build: %d)", fn, s->head_dim, ssa::kHeadDim);
+  if (s->block != ssa::kBlock)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: block %d (this build: %d)", fn, s->block, ssa::kBlock);
+  if (s->topk > ssa::kMaxTopk)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: topk %d (this build: <= %d)", fn, s->topk, ssa::kMaxTopk);
+  const int64_t rows_q = (int64_t)s->batch * s->n_q_heads * s->seq_q * s->head_dim;
+  const int64_t rows_kv = (int64_t)s->batch * s->n_kv_heads * s->seq_kv * s->head_dim;
+  const int64_t nkb = (s->seq_kv + s->block - 1) / s->block;
+  const int64_t nqb = (s->seq_q + s->block - 1) / s->block;
+  const int64_t nscores = (int64_t)s->batch * s->n_q_heads * nqb * nkb;
+  const int64_t limit = (int64_t)1 << 40;
+  if (rows_q > limit || rows_kv > limit || nscores > limit || s->batch * (int64_t)s->n_q_heads * nqb > INT32_MAX)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  g->batch = s->batch;
+  g->hq = s->n_q_heads;
+  g->hkv = s->n_kv_heads;
+  g->group = s->n_q_heads / s->n_kv_heads;
+  g->seq_q = s->seq_q;
+  g->seq_kv = s->seq_kv;
+  g->q_offset = s->q_offset;
+  g->topk = s->topk;
+  g->nqb = (int)nqb;
+  g->nkb = (int)nkb;
+  const double scale = s->scale != 0.f ? (double)s->scale : 1.0 / sqrt((double)s->head_dim);
+  g->scale = (float)scale;
+  g->scale_log2 = (float)((double)g->scale * 1.4426950408889634);
+  *empty = (s->batch == 0 || s->seq_q == 0);
+  g_last_error[0] = '\0';
+  return SSA_OK;
+}
+
+#define CHECK_PTR(p, align, fn)                                                              \
+  do {                                                                                       \
+    if (!(p)) return fail(SSA_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);                    \
+    if (!aligned((p), (align))) return fail(SSA_ERR_INVALID_ARG, "%s: %s is not %d-byte aligned", fn, #p, (int)(align)); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+ssa_status_t ssa_block_summaries(const ssa_shape_t* shape, const void* k, float* k_summary,
+                                 hipStream_t stream) {
+  const char* fn = "ssa_block_summaries";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (g.batch == 0 || g.seq_kv == 0) return SSA_OK;
+  CHECK_PTR(k, 16, fn);
+  CHECK_PTR(k_summary, 16, fn);
+  hipError_t e = ssa::launch_block_summaries((const uint16_t*)k, k_summary, g, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
+ssa_status_t ssa_block_scores(const ssa_shape_t* shape, const void* q, const void* k, float* k_summary,
+                              int summary_is_input, float* scores, hipStream_t stream) {
+  const char* fn = "ssa_block_scores";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (empty) return SSA_OK;
+  CHECK_PTR(q, 16, fn);
+  CHECK_PTR(k_summary, 16, fn);
+  CHECK_PTR(scores, 4, fn);
+  if (!summary_is_input) CHECK_PTR(k, 16, fn);
+  if (g.seq_q == 1 && g.group > 64)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: decode with more than 64 query heads per KV head", fn);
+  hipError_t e = hipSuccess;
+  if (!summary_is_input) e = ssa::launch_block_summaries((const uint16_t*)k, k_summary, g, stream);
+  if (e == hipSuccess) {
+    if (g.seq_q == 1)
+      e = ssa::launch_decode_scores((const uint16_t*)q, k_summary, scores, g, stream);
+    else
+      e = ssa::launch_prefill_scores((const uint16_t*)q, k_summary, scores, g, stream);
+  }
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
+ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
+                             hipStream_t stream) {
+  const char* fn = "ssa_select_topk";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (empty) return SSA_OK;
+  CHECK_PTR(scores, 4, fn);
+  CHECK_PTR(block_idx, 4, fn);
+  hipError_t e = ssa::launch_select_topk(scores, block_idx, g, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
+ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, const void* k,
+                                       const void* v, const int32_t* block_idx, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "ssa_block_sparse_attn_fwd";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (empty) return SSA_OK;
+  CHECK_PTR(q, 16, fn);
+  CHECK_PTR(k, 16, fn);
+  CHECK_PTR(v, 16, fn);
+  CHECK_PTR(block_idx, 4, fn);
+  CHECK_PTR(out, 16, fn);
+  CHECK_PTR(lse, 4, fn);
+  ssa::AttnArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.idx = block_idx;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.qb_begin = 0;
+  a.qb_count = g.nqb;
+  a.rows_out = g.seq_q;
+  hipError_t e;
+  if (g.seq_q == 1) {
+    if (g.group > 32)
+      return fail(SSA_ERR_UNSUPPORTED, "%s: decode with more than 32 query heads per KV head", fn);
+    const size_t need = ssa::decode_workspace_bytes(g.batch, g.hq, g.nkb);
+    if (workspace_bytes < need)
+      return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+    CHECK_PTR(workspace, 16, fn);
+    e = ssa::launch_attn_decode(a, (float*)workspace, g, stream);
+  } else {
+    e = ssa::launch_attn_prefill(a, false, g, stream);
+  }
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
+ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void* q, const void* k,
+                                            const void* v, const int32_t* block_idx, int32_t q_block_begin,
+                                            int32_t q_block_count, void* out_full, float* lse_full,
+                                            float* dropped_mass, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const char* fn = "ssa_full_attn_fwd_dropped_mass";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (q_block_begin < 0 || q_block_count < 0 || (int64_t)q_block_begin + q_block_count > g.nqb)
+    return fail(SSA_ERR_INVALID_ARG, "%s: query block range [%d, %d) outside [0, %d)", fn, q_block_begin,
+                q_block_begin + q_block_count, g.nqb);
+  if (empty || q_block_count == 0) return SSA_OK;
+  CHECK_PTR(q, 16, fn);
+  CHECK_PTR(k, 16, fn);
+  CHECK_PTR(v, 16, fn);
+  CHECK_PTR(block_idx, 4, fn);
+  CHECK_PTR(out_full, 16, fn);
+  CHECK_PTR(lse_full, 4, fn);
+  CHECK_PTR(dropped_mass, 4, fn);
+  ssa::AttnArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.idx = block_idx;
+  a.out = (uint16_t*)out_full;
+  a.lse = lse_full;
+  a.dropped = dropped_mass;
+  a.qb_begin = q_block_begin;
+  a.qb_count = q_block_count;
+  const int64_t end_row = (int64_t)(q_block_begin + q_block_count) * ssa::kBlock;
+  a.rows_out = (int)((end_row < g.seq_q ? end_row : g.seq_q) - (int64_t)q_block_begin * ssa::kBlock);
+  hipError_t e = ssa::launch_attn_prefill(a, true, g, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
+size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {
+  ssa::Geometry g;
+  bool empty;
+  if (make_geometry(shape, &g, &empty, "ssa_workspace_bytes") != SSA_OK) return SIZE_MAX;
+  if (empty) return 0;
+  if (op == SSA_OP_SPARSE_FWD && g.seq_q == 1) return ssa::decode_workspace_bytes(g.batch, g.hq, g.nkb);
+  return 0;
+}
+
+const char* ssa_status_string(ssa_status_t status) {
+  switch (status) {
+    case SSA_OK: return "ok";
+    case SSA_ERR_INVALID_ARG: return "invalid argument";
+    case SSA_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case SSA_ERR_HIP: return "HIP runtime error";
+    case SSA_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* ssa_last_error(void) { return g_last_error; }
+
+int32_t ssa_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssa {
+
+constexpr int kHeadDim = 64;  // d supported by this build
+constexpr int kBlock = 64;    // B supported by this build (one 64-key tile per block)
+constexpr int kMaxTopk = 256;
+
+struct Geometry {
+  int batch, hq, hkv, group;
+  int seq_q, seq_kv, q_offset;
+  int topk;
+  int nqb, nkb;
+  float scale;       // softmax / score scale
+  float scale_log2;  // scale * log2(e)
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  uint16_t* out;
+  float* lse;
+  float* dropped;    // full mode only
+  int qb_begin;      // first query block handled
+  int qb_count;      // number of query blocks handled
+  int rows_out;      // rows per (b, h) in the output tensors
+};
+
+// Decode split: key blocks of one (batch, KV head) group are cut into chunks
+// of kDecodeChunk blocks; each chunk writes one partial (m, l, o[64]) per query
+// head, merged afterwards.
+constexpr int kDecodeChunk = 32;
+constexpr int kPartialFloats = 2 + 64;
+
+inline int decode_chunks(int nkb) { return (nkb + kDecodeChunk - 1) / kDecodeChunk; }
+inline size_t decode_workspace_bytes(int batch, int hq, int nkb) {
+  return (size_t)batch * hq * decode_chunks(nkb) * kPartialFloats * sizeof(float);
+}
+
+hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geometry& g,
+                                  hipStream_t stream);
+hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, float* scores,
+                                 const Geometry& g, hipStream_t stream);
+hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float* scores,
+                                const Geometry& g, hipStream_t stream);
+hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g,
+                              hipStream_t stream);
+hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream);
+hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometry& g,
+                              hipStream_t stream);
+
+}  // namespace ssa

@@ -1,0 +1,210 @@
+// Block summaries and coarse block scores (gfx950).
+//
+// Summaries: the mean of each 64-row key block, summed exactly in fp64 and
+// rounded once to fp32.  Scores: fp32 rounding of scale * qbar . kbar, with
+// the dot product accumulated in fp64 from the fp32 summaries, so the top-k
+// decision downstream is taken on correctly rounded fp32 scores.
+// Method: SSA guide (mauroscia.it), "Block-sparse attention e Receptive Field";
+// DashAttention summary, "Etapa 0" (mean summary, cached once complete) and
+// "Etapa 1" (query-vs-summary routing logits).
+#include "ssa_common.hpp"
+#include "ssa_internal.hpp"
+
+namespace ssa {
+namespace {
+
+// Sum the rows [0, nrows) of a 64-wide bf16 block in fp64.  Lane layout: lane
+// covers columns 8*(lane%8) .. +8 of rows lane/8, lane/8 + 8, ...; the eight
+// row groups are then folded together, so lanes 0..7 end with the column sums.
+__device__ __forceinline__ void pool_rows_f64(const uint16_t* __restrict__ base, int nrows,
+                                              int lane, double acc[8]) {
+  const int c8 = lane & 7, rg = lane >> 3;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int r = rg; r < nrows; r += 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (size_t)r * kHeadDim + c8 * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)bf16_to_f32((uint16_t)(v[e] & 0xffffu));
+      acc[2 * e + 1] += (double)bf16_to_f32((uint16_t)(v[e] >> 16));
+    }
+  }
+#pragma unroll
+  for (int o = 8; o <= 32; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  }
+}
+
+__global__ __launch_bounds__(64) void block_summaries_kernel(const uint16_t* __restrict__ k,
+                                                             float* __restrict__ ksum, int seq_kv,
+                                                             int nkb) {
+  const int lane = threadIdx.x;
+  const size_t bgj = blockIdx.x;
+  const size_t bg = bgj / (size_t)nkb;
+  const int j = (int)(bgj - bg * (size_t)nkb);
+  const int r0 = j * kBlock;
+  const int nrows = min(kBlock, seq_kv - r0);
+  double acc[8];
+  pool_rows_f64(k + (bg * (size_t)seq_kv + r0) * kHeadDim, nrows, lane, acc);
+  if (lane < 8) {
+    float4 lo, hi;
+    lo.x = (float)(acc[0] / nrows); lo.y = (float)(acc[1] / nrows);
+    lo.z = (float)(acc[2] / nrows); lo.w = (float)(acc[3] / nrows);
+    hi.x = (float)(acc[4] / nrows); hi.y = (float)(acc[5] / nrows);
+    hi.z = (float)(acc[6] / nrows); hi.w = (float)(acc[7] / nrows);
+    float4* dst = reinterpret_cast<float4*>(ksum + bgj * kHeadDim + lane * 8);
+    dst[0] = lo;
+    dst[1] = hi;
+  }
+}
+
+constexpr int kScoreQTile = 16;   // query blocks per workgroup (prefill)
+constexpr int kScoreKTile = 64;   // key blocks staged per pass
+constexpr int kKbStride = 65;     // padded LDS row (floats) -> conflict-free row-per-lane reads
+
+// One workgroup: (b, h) x kScoreQTile query blocks.  Pools its query blocks
+// (Q is read exactly once overall), then sweeps the key summaries in passes of
+// kScoreKTile blocks staged through LDS.
+__global__ __launch_bounds__(256) void prefill_scores_kernel(const uint16_t* __restrict__ q,
+                                                             const float* __restrict__ ksum,
+                                                             float* __restrict__ scores,
+                                                             Geometry geo) {
+  __shared__ double sQ[kScoreQTile][kHeadDim];
+  __shared__ float sKb[kScoreKTile * kKbStride];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ntile = (geo.nqb + kScoreQTile - 1) / kScoreQTile;
+  const int bh = blockIdx.x / ntile;
+  const int i0 = (blockIdx.x - bh * ntile) * kScoreQTile;
+  const int b = bh / geo.hq, h = bh - b * geo.hq, g = h / geo.group;
+  const int nq = min(kScoreQTile, geo.nqb - i0);
+
+  for (int qi = wave; qi < nq; qi += 4) {
+    const int r0 = (i0 + qi) * kBlock;
+    const int nrows = min(kBlock, geo.seq_q - r0);
+    double acc[8];
+    pool_rows_f64(q + ((size_t)bh * geo.seq_q + r0) * kHeadDim, nrows, lane, acc);
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sQ[qi][lane * 8 + e] = (double)(float)(acc[e] / nrows);
+    }
+  }
+  __syncthreads();
+
+  const float* kb = ksum + (size_t)(b * geo.hkv + g) * geo.nkb * kHeadDim;
+  float* srow = scores + (size_t)bh * geo.nqb * geo.nkb;
+  const int jd0 = geo.q_offset / kBlock + i0;  // diagonal block of the first query block
+  const int jd_last = jd0 + nq - 1;
+  const double scale = (double)geo.scale;
+  for (int jc = 0; jc < geo.nkb; jc += kScoreKTile) {
+    const int nj = min(kScoreKTile, geo.nkb - jc);
+    if (jc > jd_last) {
+      for (int e = tid; e < nq * nj; e += 256) {
+        const int qi = e / nj, jj = e - qi * nj;
+        srow[(size_t)(i0 + qi) * geo.nkb + jc + jj] = -__builtin_inff();
+      }
+      continue;
+    }
+    __syncthreads();
+    for (int e = tid; e < nj * 16; e += 256) {
+      const int jj = e >> 4, c4 = e & 15;
+      const float4 v = reinterpret_cast<const float4*>(kb + (size_t)(jc + jj) * kHeadDim)[c4];
+      float* d = &sKb[jj * kKbStride + c4 * 4];
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+    const int jj = tid & 63;
+    for (int qi = wave; qi < nq; qi += 4) {
+      if (jj >= nj) continue;
+      const int j = jc + jj, jd = jd0 + qi;
+      float out;
+      if (j > jd) {
+        out = -__builtin_inff();
+      } else {
+        double acc = 0.0;
+#pragma unroll 16
+        for (int d = 0; d < kHeadDim; ++d) acc = fma(sQ[qi][d], (double)sKb[jj * kKbStride + d], acc);
+        out = (float)(scale * acc);
+      }
+      srow[(size_t)(i0 + qi) * geo.nkb + j] = out;
+    }
+  }
+}
+
+// Decode (one query row per (b, h)): one workgroup per (b, KV head, pass of
+// kScoreKTile key blocks) scores every query head of the group against the
+// staged summaries, so each summary is read from HBM once.
+constexpr int kMaxGroupScores = 64;
+__global__ __launch_bounds__(256) void decode_scores_kernel(const uint16_t* __restrict__ q,
+                                                            const float* __restrict__ ksum,
+                                                            float* __restrict__ scores,
+                                                            Geometry geo) {
+  __shared__ double sQ[kMaxGroupScores][kHeadDim];
+  __shared__ float sKb[kScoreKTile * kKbStride];
+  const int tid = threadIdx.x;
+  const int npass = (geo.nkb + kScoreKTile - 1) / kScoreKTile;
+  const int bg = blockIdx.x / npass;
+  const int jc = (blockIdx.x - bg * npass) * kScoreKTile;
+  const int b = bg / geo.hkv, g = bg - b * geo.hkv;
+  const int G = geo.group;
+  const int nj = min(kScoreKTile, geo.nkb - jc);
+  const uint16_t* qg = q + (size_t)(b * geo.hq + g * G) * kHeadDim;  // seq_q == 1
+  for (int e = tid; e < G * kHeadDim; e += 256) sQ[e >> 6][e & 63] = (double)bf16_to_f32(qg[e]);
+  const float* kb = ksum + ((size_t)bg * geo.nkb + jc) * kHeadDim;
+  for (int e = tid; e < nj * 16; e += 256) {
+    const int jj = e >> 4, c4 = e & 15;
+    const float4 v = reinterpret_cast<const float4*>(kb + (size_t)jj * kHeadDim)[c4];
+    float* d = &sKb[jj * kKbStride + c4 * 4];
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  }
+  __syncthreads();
+  const int jd = geo.q_offset / kBlock;
+  const double scale = (double)geo.scale;
+  for (int e = tid; e < G * kScoreKTile; e += 256) {
+    const int hh = e >> 6, jj = e & 63;
+    if (jj >= nj) continue;
+    const int j = jc + jj;
+    float out;
+    if (j > jd) {
+      out = -__builtin_inff();
+    } else {
+      double acc = 0.0;
+#pragma unroll 16
+      for (int d = 0; d < kHeadDim; ++d) acc = fma(sQ[hh][d], (double)sKb[jj * kKbStride + d], acc);
+      out = (float)(scale * acc);
+    }
+    scores[(size_t)(b * geo.hq + g * G + hh) * geo.nkb + j] = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geometry& g,
+                                  hipStream_t stream) {
+  const size_t nblk = (size_t)g.batch * g.hkv * g.nkb;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(block_summaries_kernel, dim3((unsigned)nblk), dim3(64), 0, stream, k,
+                     k_summary, g.seq_kv, g.nkb);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, float* scores,
+                                 const Geometry& g, hipStream_t stream) {
+  const size_t nwg = (size_t)g.batch * g.hq * ((g.nqb + kScoreQTile - 1) / kScoreQTile);
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_scores_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, q,
+                     k_summary, scores, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float* scores,
+                                const Geometry& g, hipStream_t stream) {
+  if (g.group > kMaxGroupScores) return hipErrorInvalidValue;
+  const size_t nwg = (size_t)g.batch * g.hkv * ((g.nkb + kScoreKTile - 1) / kScoreKTile);
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_scores_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, q,
+                     k_summary, scores, g);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

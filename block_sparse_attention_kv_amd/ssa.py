@@ -1,0 +1,204 @@
+"""Thin Python binding of libssa (ctypes).  Argument marshalling only.
+
+Every function takes device tensors, allocates its outputs with ``torch.empty``
+on the same device, and calls the C-ABI entry point of the same name on the
+current HIP stream.  All computation happens in the HIP kernels of libssa;
+there is no CPU fallback: a missing library or a non-GPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssa.so")
+
+SSA_OK, SSA_ERR_INVALID_ARG, SSA_ERR_UNSUPPORTED, SSA_ERR_HIP, SSA_ERR_WORKSPACE = range(5)
+SSA_OP_BLOCK_SCORES, SSA_OP_SELECT_TOPK, SSA_OP_SPARSE_FWD, SSA_OP_FULL_FWD = range(4)
+
+EXPORTED_SYMBOLS = (
+    "ssa_block_summaries", "ssa_block_scores", "ssa_select_topk", "ssa_block_sparse_attn_fwd",
+    "ssa_full_attn_fwd_dropped_mass", "ssa_workspace_bytes", "ssa_status_string",
+    "ssa_last_error", "ssa_version",
+)
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``ssa_shape_t``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("seq_q", ctypes.c_int32), ("seq_kv", ctypes.c_int32), ("q_offset", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+    def __repr__(self):
+        return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class SSAError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libssa.so (built in-tree).  Raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libssa.so not found at {path}; build it with "
+            "`python -m block_sparse_attention_kv_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    sp = ctypes.POINTER(Shape)
+    lib.ssa_block_summaries.argtypes = [sp, vp, vp, vp]
+    lib.ssa_block_scores.argtypes = [sp, vp, vp, vp, ctypes.c_int, vp, vp]
+    lib.ssa_select_topk.argtypes = [sp, vp, vp, vp]
+    lib.ssa_block_sparse_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssa_full_attn_fwd_dropped_mass.argtypes = [sp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    for fn in ("ssa_block_summaries", "ssa_block_scores", "ssa_select_topk",
+               "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.ssa_workspace_bytes.argtypes = [sp, ctypes.c_int]
+    lib.ssa_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssa_status_string.argtypes = [ctypes.c_int]
+    lib.ssa_status_string.restype = ctypes.c_char_p
+    lib.ssa_last_error.argtypes = []
+    lib.ssa_last_error.restype = ctypes.c_char_p
+    lib.ssa_version.argtypes = []
+    lib.ssa_version.restype = ctypes.c_int32
+    _lib_handle = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != SSA_OK:
+        lib = load_library()
+        raise SSAError(fn, status, lib.ssa_last_error().decode() or lib.ssa_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libssa operates on GPU tensors only (no CPU fallback)")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("libssa expects contiguous tensors")
+
+
+def make_shape(q: torch.Tensor, kv_heads: int, seq_kv: int, *, block: int = 64, topk: int = 16,
+               scale: float = 0.0, causal: int = 1) -> Shape:
+    """Shape for Q [b, Hq, seq_q, d] against a K/V of ``seq_kv`` rows; the query
+    rows are the last ``seq_q`` positions (q_offset = seq_kv - seq_q)."""
+    b, hq, seq_q, d = q.shape
+    return Shape(batch=b, n_q_heads=hq, n_kv_heads=kv_heads, seq_q=seq_q, seq_kv=seq_kv,
+                 q_offset=seq_kv - seq_q, head_dim=d, block=block, topk=topk, causal=causal,
+                 scale=float(scale))
+
+
+def n_blocks(n: int, block: int) -> int:
+    return -(-n // block)
+
+
+def ssa_workspace_bytes(shape: Shape, op: int) -> int:
+    return int(load_library().ssa_workspace_bytes(ctypes.byref(shape), op))
+
+
+def ssa_block_summaries(k: torch.Tensor, *, block: int = 64) -> torch.Tensor:
+    """Key-block summaries fp32 [b, Hkv, nkb, d] of bf16 K [b, Hkv, seq_kv, d]."""
+    _require_gpu(k)
+    b, hkv, n, d = k.shape
+    shape = Shape(batch=b, n_q_heads=hkv, n_kv_heads=hkv, seq_q=n, seq_kv=n, q_offset=0,
+                  head_dim=d, block=block, topk=1, causal=1, scale=0.0)
+    ks = torch.empty((b, hkv, n_blocks(n, block), d), dtype=torch.float32, device=k.device)
+    _check("ssa_block_summaries", load_library().ssa_block_summaries(
+        ctypes.byref(shape), _ptr(k), _ptr(ks), _stream(k.device)))
+    return ks
+
+
+def ssa_block_scores(shape: Shape, q: torch.Tensor, k: Optional[torch.Tensor] = None,
+                     k_summary: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(scores [b, Hq, nqb, nkb] fp32, k_summary).  With ``k_summary`` given the
+    cached summaries are used (K may be None); otherwise they are computed from K."""
+    _require_gpu(q, k, k_summary)
+    summary_is_input = k_summary is not None
+    if not summary_is_input:
+        k_summary = torch.empty((shape.batch, shape.n_kv_heads, n_blocks(shape.seq_kv, shape.block),
+                                 shape.head_dim), dtype=torch.float32, device=q.device)
+    scores = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block),
+                          n_blocks(shape.seq_kv, shape.block)), dtype=torch.float32, device=q.device)
+    _check("ssa_block_scores", load_library().ssa_block_scores(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(k_summary), int(summary_is_input), _ptr(scores),
+        _stream(q.device)))
+    return scores, k_summary
+
+
+def ssa_select_topk(shape: Shape, scores: torch.Tensor) -> torch.Tensor:
+    """Selected key blocks int32 [b, Hq, nqb, topk], ascending, -1 padded."""
+    _require_gpu(scores)
+    idx = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block), shape.topk),
+                      dtype=torch.int32, device=scores.device)
+    _check("ssa_select_topk", load_library().ssa_select_topk(
+        ctypes.byref(shape), _ptr(scores), _ptr(idx), _stream(scores.device)))
+    return idx
+
+
+def ssa_block_sparse_attn_fwd(shape: Shape, q, k, v, block_idx, workspace: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q])."""
+    _require_gpu(q, k, v, block_idx, workspace, out, lse)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    need = ssa_workspace_bytes(shape, SSA_OP_SPARSE_FWD)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("ssa_block_sparse_attn_fwd", load_library().ssa_block_sparse_attn_fwd(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(q.device)))
+    return out, lse
+
+
+def ssa_full_attn_fwd_dropped_mass(shape: Shape, q, k, v, block_idx, q_block_begin: int = 0,
+                                   q_block_count: Optional[int] = None, out=None, lse=None, dropped=None):
+    """(out_full bf16, lse_full fp32, dropped_mass fp32) over query blocks
+    [q_block_begin, q_block_begin + q_block_count)."""
+    _require_gpu(q, k, v, block_idx, out, lse, dropped)
+    nqb = n_blocks(shape.seq_q, shape.block)
+    if q_block_count is None:
+        q_block_count = nqb - q_block_begin
+    rows = max(0, min(shape.seq_q, (q_block_begin + q_block_count) * shape.block) - q_block_begin * shape.block)
+    b, hq, d = shape.batch, shape.n_q_heads, shape.head_dim
+    if out is None:
+        out = torch.empty((b, hq, rows, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, hq, rows), dtype=torch.float32, device=q.device)
+    if dropped is None:
+        dropped = torch.empty((b, hq, rows), dtype=torch.float32, device=q.device)
+    _check("ssa_full_attn_fwd_dropped_mass", load_library().ssa_full_attn_fwd_dropped_mass(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), int(q_block_begin),
+        int(q_block_count), _ptr(out), _ptr(lse), _ptr(dropped), None, 0, _stream(q.device)))
+    return out, lse, dropped
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

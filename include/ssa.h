@@ -1,0 +1,183 @@
+/*
+ * ssa.h -- C ABI of libssa: causal block-sparse attention as used by SSA
+ * (Sparse Sparse Attention), hand-written HIP kernels for AMD gfx950 (MI355X).
+ *
+ * The operations follow these pages:
+ *   [SSA-summary] "Resumen Tecnico: SSA (Sparse Sparse Attention)" (gist.science 2511.20102)
+ *   [SSA-guide]   "SSA: Guida a Sparse Sparse Attention per LLM" (mauroscia.it)
+ *   [DashAttn]    "Resumen Tecnico: DashAttention" (gist.science 2605.18753)
+ *   [S2O]         "Resumen Tecnico: S2O - Parada Temprana para Atencion Escasa mediante
+ *                  Permutacion en Linea" (gist.science 2602.22575)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Shapes.  b = batch, Hq / Hkv = query / key-value heads (Hq % Hkv == 0; query
+ *   head h reads KV head h / (Hq/Hkv)), d = head_dim, B = block size,
+ *   nqb = ceil(seq_q / B) query blocks, nkb = ceil(seq_kv / B) key blocks.
+ * Positions.  Query row r sits at absolute position q_offset + r and sees keys
+ *   c <= q_offset + r (causal).  seq_kv must equal q_offset + seq_q.  A
+ *   multi-row query chunk must start on a block boundary (q_offset % B == 0);
+ *   decode is seq_q == 1, q_offset == L - 1 (any L).  Query block i holds rows
+ *   [i*B, (i+1)*B); its diagonal key block is (q_offset + i*B) / B.
+ * Layouts.  Every tensor is dense, row-major, in the order written, with the
+ *   last dimension contiguous.  Q [b,Hq,seq_q,d], K and V [b,Hkv,seq_kv,d] and
+ *   attention outputs [b,Hq,rows,d] are bf16; summaries, scores, LSE and
+ *   dropped mass are fp32; block indices are int32.  bf16 pointers must be
+ *   16-byte aligned, fp32/int32 pointers 4-byte aligned.
+ * Memory.  All pointers are device pointers owned by the caller (including
+ *   any workspace).  The library allocates no device memory and keeps no
+ *   mutable global state; concurrent calls on different streams are safe.
+ * Streams.  Work is enqueued on `stream` and never synchronised; outputs are
+ *   valid once the stream reaches that point.
+ * Errors.  Arguments are validated on the host before anything is launched:
+ *   SSA_ERR_INVALID_ARG (bad pointer, alignment, or inconsistent shape) or
+ *   SSA_ERR_UNSUPPORTED (a valid shape this build does not implement: d != 64,
+ *   B != 64, causal == 0, topk > 256).  A failed launch returns SSA_ERR_HIP.
+ *   On error nothing is written.  ssa_last_error() gives a message for the
+ *   calling thread's last failure.  Empty problems (batch == 0 or
+ *   seq_q == 0) return SSA_OK without launching.
+ * Determinism.  Identical inputs give bitwise-identical outputs (no
+ *   floating-point atomics; fixed reduction orders).
+ */
+#ifndef SSA_H_
+#define SSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssa_status {
+  SSA_OK = 0,
+  SSA_ERR_INVALID_ARG = 1,
+  SSA_ERR_UNSUPPORTED = 2,
+  SSA_ERR_HIP = 3,
+  SSA_ERR_WORKSPACE = 4
+} ssa_status_t;
+
+typedef struct ssa_shape {
+  int32_t batch;      /* b >= 0 */
+  int32_t n_q_heads;  /* Hq >= 1 */
+  int32_t n_kv_heads; /* Hkv >= 1, divides Hq */
+  int32_t seq_q;      /* query rows per (b, h): N for prefill, 1 for decode */
+  int32_t seq_kv;     /* key/value rows per (b, kv head); == q_offset + seq_q */
+  int32_t q_offset;   /* absolute position of query row 0 */
+  int32_t head_dim;   /* d; this build: 64 */
+  int32_t block;      /* B; this build: 64 */
+  int32_t topk;       /* k: blocks kept per query block, counting the forced diagonal
+                         (most recent) block; 1 <= k <= 256 */
+  int32_t causal;     /* must be 1 */
+  float scale;        /* softmax and score scale; 0 selects 1/sqrt(d) */
+} ssa_shape_t;
+
+typedef enum ssa_op {
+  SSA_OP_BLOCK_SCORES = 0,
+  SSA_OP_SELECT_TOPK = 1,
+  SSA_OP_SPARSE_FWD = 2,
+  SSA_OP_FULL_FWD = 3
+} ssa_op_t;
+
+/* Key-block summaries: k_summary[b,g,j,:] = fp32 rounding of the mean of the
+ * rows of key block j that exist (c < seq_kv), summed exactly.
+ * [SSA-guide] "Block-sparse attention e Receptive Field" (each contiguous
+ * block is represented by its mean); [DashAttn] "Etapa 0" (a zero-initialised
+ * learned chunk query is the uniform average; a finished chunk's summary is
+ * cached and never recomputed -- this call is how a decode cache fills it).
+ *   k          bf16 [b,Hkv,seq_kv,d]
+ *   k_summary  fp32 [b,Hkv,nkb,d]  (output) */
+ssa_status_t ssa_block_summaries(const ssa_shape_t* shape, const void* k, float* k_summary,
+                                 hipStream_t stream);
+
+/* Coarse block scores of each query block against the key-block summaries:
+ *   scores[b,h,i,j] = fp32( scale * dot(qbar[b,h,i], kbar[b,h/G,j]) )  for j <= diag(i)
+ *                   = -inf                                             for j >  diag(i)
+ * where qbar is the fp32-rounded exact mean of the query rows of block i (the
+ * row itself in decode) and kbar the key summaries; the dot product is
+ * accumulated in fp64 from the fp32 summaries and rounded once.
+ * [SSA-guide] "Block-sparse attention e Receptive Field" (query against the
+ * mean representation of the preceding blocks); [DashAttn] "Etapa 1" (routing
+ * logits of each query against the chunk summaries).
+ *   q                  bf16 [b,Hq,seq_q,d]
+ *   k                  bf16 [b,Hkv,seq_kv,d]; ignored (may be NULL) if summary_is_input
+ *   k_summary          fp32 [b,Hkv,nkb,d]; written from k if summary_is_input == 0,
+ *                      read (cached summaries) if summary_is_input != 0
+ *   scores             fp32 [b,Hq,nqb,nkb] (output) */
+ssa_status_t ssa_block_scores(const ssa_shape_t* shape, const void* q, const void* k,
+                              float* k_summary, int summary_is_input, float* scores,
+                              hipStream_t stream);
+
+/* Top-k block selection per (b, h, query block i) with diagonal block
+ * jd = diag(i) always kept: if jd + 1 <= topk every block 0..jd is kept,
+ * otherwise jd plus the topk-1 earlier blocks ranked by (higher score, then
+ * lower block index; NaN ranks below -inf).  Indices are written ascending
+ * and padded with -1 to topk entries.
+ * [SSA-guide] "Block-sparse attention e Receptive Field" (keep only the top-k
+ * most relevant blocks, a fixed budget: receptive field = B * k tokens);
+ * [DashAttn] "Declaracion del Problema" (fixed top-k budget) and "Etapa 2"
+ * (near-diagonal chunks kept by a separate branch).
+ *   scores     fp32 [b,Hq,nqb,nkb]
+ *   block_idx  int32 [b,Hq,nqb,topk] (output) */
+ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
+                             hipStream_t stream);
+
+/* Block-sparse attention forward: query row r of block i attends to the keys
+ * c <= q_offset + r whose block is listed in block_idx[b,h,i,:] (-1 entries
+ * ignored; entries must be ascending, distinct and <= diag(i), and the list
+ * must contain diag(i)):
+ *   out[b,h,r,:] = sum_c softmax_c(scale * q_r . k_c) v_c   (bf16, fp32 accumulation)
+ *   lse[b,h,r]   = natural log of sum_c exp(scale * q_r . k_c)  (fp32)
+ * [SSA-summary] 2 "Mecanismo Central" (the sparse attention stream);
+ * [SSA-guide] "Block-sparse attention e Receptive Field" (attention over the
+ * tokens of the selected blocks only); [S2O] "Permutacion en Linea" (tiles
+ * gathered by index from an unchanged HBM layout).
+ * With seq_q == 1 (decode) the work is split over the key blocks of each
+ * KV-head group and merged; that needs ssa_workspace_bytes(shape,
+ * SSA_OP_SPARSE_FWD) bytes of workspace (0 for prefill, workspace may be NULL).
+ *   q, k, v    bf16 as above;  block_idx int32 [b,Hq,nqb,topk]
+ *   out        bf16 [b,Hq,seq_q,d] (output);  lse fp32 [b,Hq,seq_q] (output) */
+ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, const void* k,
+                                       const void* v, const int32_t* block_idx, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/* Full causal attention (the counterpart output of the opposite mode) plus the
+ * per-row dropped attention mass, for query blocks
+ * [q_block_begin, q_block_begin + q_block_count) (rows past seq_q omitted):
+ *   out_full[b,h,r',:]  full causal softmax attention of row r = q_block_begin*B + r'
+ *   lse_full[b,h,r']    its natural-log log-sum-exp
+ *   dropped_mass[b,h,r'] = sum over causal keys whose block is NOT in block_idx[b,h,i,:]
+ *                          of the full-softmax probability (summed directly)
+ * [SSA-summary] "Alineacion Bidireccional" (auxiliary output computed in the
+ * opposite mode, used only for alignment) and 1 "Planteamiento del Problema"
+ * (approximation error linear in the attention weight on unselected tokens).
+ * Outputs hold rows_out = min(seq_q, (begin+count)*B) - begin*B rows per (b,h).
+ * No workspace is needed (workspace may be NULL). */
+ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void* q, const void* k,
+                                            const void* v, const int32_t* block_idx,
+                                            int32_t q_block_begin, int32_t q_block_count,
+                                            void* out_full, float* lse_full, float* dropped_mass,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+
+/* Workspace bytes an entry point needs for this shape (0 if none; SIZE_MAX if
+ * the shape is invalid). */
+size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op);
+
+/* Static description of a status code. */
+const char* ssa_status_string(ssa_status_t status);
+
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* ssa_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t ssa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H_ */

@@ -1,0 +1,128 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU runtime."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_kv_amd import ssa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10002)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssa.LIB_PATH):
+        from block_sparse_attention_kv_amd import build
+        build.build()
+    return ssa.load_library()
+
+
+def good_shape(**kw):
+    s = dict(batch=1, n_q_heads=4, n_kv_heads=2, seq_q=256, seq_kv=256, q_offset=0, head_dim=64,
+             block=64, topk=2, causal=1, scale=0.0)
+    s.update(kw)
+    return ssa.Shape(**s)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = header_functions()
+    assert set(declared) == set(ssa.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ssa_version() >= 10000
+    for st in range(5):
+        assert lib.ssa_status_string(st)
+    assert lib.ssa_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=3, n_kv_heads=2), ssa.SSA_ERR_INVALID_ARG),
+    (dict(n_kv_heads=0), ssa.SSA_ERR_INVALID_ARG),
+    (dict(seq_kv=255), ssa.SSA_ERR_INVALID_ARG),                     # seq_kv != q_offset + seq_q
+    (dict(seq_q=100, seq_kv=132, q_offset=32), ssa.SSA_ERR_INVALID_ARG),  # chunk not block aligned
+    (dict(topk=0), ssa.SSA_ERR_INVALID_ARG),
+    (dict(batch=-1), ssa.SSA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ssa.SSA_ERR_INVALID_ARG),
+    (dict(head_dim=128), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(block=32), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(causal=0), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(topk=257), ssa.SSA_ERR_UNSUPPORTED),
+])
+def test_shape_validation(lib, kw, status):
+    sh = good_shape(**kw)
+    p = ctypes.byref(sh)
+    assert lib.ssa_block_scores(p, FAKE, FAKE, FAKE, 0, FAKE, None) == status
+    assert lib.ssa_select_topk(p, FAKE, FAKE, None) == status
+    assert lib.ssa_block_sparse_attn_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == status
+    assert lib.ssa_full_attn_fwd_dropped_mass(p, FAKE, FAKE, FAKE, FAKE, 0, 1, FAKE, FAKE, FAKE, None, 0,
+                                              None) == status
+    assert lib.ssa_last_error()
+
+
+def test_pointer_validation(lib):
+    sh = good_shape()
+    p = ctypes.byref(sh)
+    assert lib.ssa_block_sparse_attn_fwd(p, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"q is NULL" in lib.ssa_last_error()
+    assert lib.ssa_block_sparse_attn_fwd(p, MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"aligned" in lib.ssa_last_error()
+    assert lib.ssa_block_scores(p, FAKE, None, FAKE, 0, FAKE, None) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_select_topk(p, FAKE, None, None) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_block_summaries(None, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID_ARG
+    # query-block range outside the problem
+    assert lib.ssa_full_attn_fwd_dropped_mass(p, FAKE, FAKE, FAKE, FAKE, 3, 2, FAKE, FAKE, FAKE, None, 0,
+                                              None) == ssa.SSA_ERR_INVALID_ARG
+
+
+def test_decode_workspace(lib):
+    sh = good_shape(batch=64, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=32768, q_offset=32767, topk=17)
+    need = lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_SPARSE_FWD)
+    assert need == 64 * 32 * 16 * 66 * 4       # 16 chunks of 32 key blocks, (max, sum, o[64]) each
+    assert lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_FULL_FWD) == 0
+    assert lib.ssa_workspace_bytes(ctypes.byref(good_shape()), ssa.SSA_OP_SPARSE_FWD) == 0
+    assert lib.ssa_workspace_bytes(ctypes.byref(good_shape(head_dim=8)), ssa.SSA_OP_SPARSE_FWD) == 2**64 - 1
+    # too small a workspace is refused before launch
+    assert lib.ssa_block_sparse_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
+                                         None) == ssa.SSA_ERR_WORKSPACE
+    # decode groups beyond 32 query heads per KV head are not implemented
+    big = good_shape(batch=1, n_q_heads=64, n_kv_heads=1, seq_q=1, seq_kv=100, q_offset=99, topk=2)
+    assert lib.ssa_block_sparse_attn_fwd(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                         None) == ssa.SSA_ERR_UNSUPPORTED
+
+
+def test_empty_problems_launch_nothing(lib):
+    # batch 0 or no query rows: SSA_OK with no HIP call (works without a GPU)
+    for sh in (good_shape(batch=0), good_shape(seq_q=0, seq_kv=0)):
+        p = ctypes.byref(sh)
+        assert lib.ssa_block_scores(p, FAKE, FAKE, FAKE, 0, FAKE, None) == ssa.SSA_OK
+        assert lib.ssa_select_topk(p, FAKE, FAKE, None) == ssa.SSA_OK
+        assert lib.ssa_block_sparse_attn_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ssa.SSA_OK
+        assert lib.ssa_full_attn_fwd_dropped_mass(p, FAKE, FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, None, 0,
+                                                  None) == ssa.SSA_OK
+    sh = good_shape()
+    assert lib.ssa_full_attn_fwd_dropped_mass(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, FAKE,
+                                              None, 0, None) == ssa.SSA_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ssa.ssa_block_summaries(q)

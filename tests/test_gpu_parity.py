@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Small problems are compared element by element; the
+full-size workloads are compared on every block index and on sampled rows,
+plus properties that hold at any size."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_kv_amd import ssa
+from block_sparse_attention_kv_amd import workloads as W
+from oracle import ssa_oracle as O
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+B = 64
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ssa.load_library()  # raises if the library is missing: there is no fallback
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def gpu_path(w: W.Workload, q, k, v, dev, full_range=None, with_full=True):
+    """Run summaries -> scores -> top-k -> sparse -> full on the GPU."""
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    res = {}
+    if w.seq_q == 1:
+        ks = ssa.ssa_block_summaries(kd, block=w.block)
+        res["scores"], res["k_summary"] = ssa.ssa_block_scores(shape, qd, None, ks)
+    else:
+        res["scores"], res["k_summary"] = ssa.ssa_block_scores(shape, qd, kd)
+    res["idx"] = ssa.ssa_select_topk(shape, res["scores"])
+    res["o"], res["lse"] = ssa.ssa_block_sparse_attn_fwd(shape, qd, kd, vd, res["idx"])
+    if with_full:
+        nqb = ssa.n_blocks(w.seq_q, w.block)
+        b0, cnt = (0, nqb) if full_range is None else full_range
+        res["of"], res["lf"], res["dm"] = ssa.ssa_full_attn_fwd_dropped_mass(shape, qd, kd, vd, res["idx"], b0, cnt)
+    torch.cuda.synchronize()
+    return {k2: v2.cpu() for k2, v2 in res.items()}
+
+
+def np_inputs(q, k, v):
+    return q.double().numpy(), k.double().numpy(), v.double().numpy()
+
+
+def check_small(w: W.Workload, dev, full_range=None):
+    say(w)
+    q, k, v = W.make_inputs(w)
+    g = gpu_path(w, q, k, v, dev, full_range)
+    qn, kn, vn = np_inputs(q, k, v)
+    off = w.q_offset
+    ks_ref = O.key_summaries(kn, B)
+    assert np.array_equal(P.np64(g["k_summary"]), ks_ref), "key summaries differ"
+    s_ref = O.block_scores(qn, kn, B, q_offset=off)
+    s_gpu = P.np64(g["scores"])
+    assert np.array_equal(np.isneginf(s_gpu), np.isneginf(s_ref))
+    fin = np.isfinite(s_ref)
+    assert np.all(np.abs(s_gpu[fin] - s_ref[fin]) <= 1e-6 * np.maximum(np.abs(s_ref[fin]), 1e-3))
+    idx_ref = O.select_blocks(s_ref, w.topk, B, q_offset=off)
+    P.check_indices(g["idx"], s_ref, idx_ref, w.topk, B, off)
+    gidx = g["idx"].numpy()
+    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, gidx, B, q_offset=off)
+    P.check_close_outputs(g["o"], o_ref, "O_sparse")
+    P.check_abs(g["lse"], lse_ref, P.LSE_ABS, "LSE_sparse")
+    nqb = ssa.n_blocks(w.seq_q, B)
+    b0, cnt = (0, nqb) if full_range is None else full_range
+    rr = (b0 * B, min(w.seq_q, (b0 + cnt) * B))
+    of_ref, lf_ref, dm_ref = O.full_attention_dropped_mass(qn, kn, vn, gidx, B, q_offset=off, row_range=rr)
+    P.check_close_outputs(g["of"], of_ref, "O_full")
+    P.check_abs(g["lf"], lf_ref, P.LSE_ABS, "LSE_full")
+    P.check_abs(g["dm"], dm_ref, P.DROP_ABS, "dropped_mass")
+    return g
+
+
+SMALL = [
+    W.TINY_512,
+    W.Workload("ragged_200", 2, 4, 2, 200, 200, 64, 64, 2, seed=11),
+    W.Workload("ragged_g3_1000", 1, 6, 2, 1000, 1000, 64, 64, 5, seed=12),
+    W.Workload("k1_blockdiag", 1, 4, 1, 384, 384, 64, 64, 1, seed=13),
+    W.Workload("mha_g1", 2, 2, 2, 256, 256, 64, 64, 2, seed=14),
+    W.Workload("single_row_block", 1, 2, 1, 65, 65, 64, 64, 1, seed=15),
+    W.Workload("chunked_prefill", 1, 4, 2, 192, 320, 64, 64, 3, seed=16),
+    W.Workload("planted_1k", 2, 32, 2, 1024, 1024, 64, 64, 4, seed=17, variant="planted"),
+    W.Workload("gqa16_2k", 1, 32, 2, 2048, 2048, 64, 64, 16, seed=18),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_parity(dev, w):
+    check_small(w, dev)
+
+
+def test_all_blocks_selected_equals_full(dev):
+    w = W.Workload("k_covers_all", 1, 4, 2, 320, 320, 64, 64, 8, seed=19)
+    g = check_small(w, dev)
+    assert torch.all(g["dm"] == 0)
+    P.check_close_outputs(g["o"].double(), g["of"].double(), "sparse vs full")
+
+
+def test_full_slice_with_ragged_tail(dev):
+    w = W.Workload("slice_ragged", 1, 4, 2, 400, 400, 64, 64, 2, seed=20)
+    check_small(w, dev, full_range=(2, 5))
+
+
+def test_max_topk(dev):
+    w = W.Workload("topk256", 1, 2, 1, 64 * 300, 64 * 300, 64, 64, 256, seed=21)
+    say(w)
+    q, k, v = W.make_inputs(w)
+    g = gpu_path(w, q, k, v, dev, with_full=False)
+    qn, kn, vn = np_inputs(q, k, v)
+    s_ref = O.block_scores(qn, kn, B)
+    idx_ref = O.select_blocks(s_ref, w.topk, B)
+    P.check_indices(g["idx"], s_ref, idx_ref, w.topk, B)
+    rows = P.sample_rows(np.random.default_rng(5), 1, 2, w.seq_q, 24)
+    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, g["idx"].numpy(), B, rows=rows)
+    P.check_close_outputs(torch.stack([g["o"][t] for t in rows]), o_ref, "O_sparse sampled")
+    P.check_abs(torch.stack([g["lse"][t] for t in rows]), lse_ref, P.LSE_ABS, "LSE sampled")
+
+
+DECODE_SMALL = [
+    W.Workload("decode_ragged_1000", 3, 8, 2, 1, 1000, 64, 64, 5, seed=31),
+    W.Workload("decode_gqa16_2560", 2, 32, 2, 1, 2560, 64, 64, 17, seed=32),
+    W.Workload("decode_one_key", 2, 4, 4, 1, 1, 64, 64, 3, seed=33),
+    W.Workload("decode_65", 1, 6, 2, 1, 65, 64, 64, 1, seed=34),
+    W.Workload("decode_long_scan", 1, 2, 1, 1, 64 * 700, 64, 64, 9, seed=35),   # > 512 candidate blocks
+]
+
+
+@pytest.mark.parametrize("w", DECODE_SMALL, ids=lambda w: w.name)
+def test_decode_parity(dev, w):
+    check_small(w, dev)
+
+
+def test_deterministic(dev):
+    w = W.Workload("det", 1, 8, 2, 640, 640, 64, 64, 3, seed=41)
+    say(w)
+    q, k, v = W.make_inputs(w)
+    a = gpu_path(w, q, k, v, dev)
+    b = gpu_path(w, q, k, v, dev)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_select_topk_nan_inf_ties(dev):
+    say("select_topk with NaN / -inf / exact ties")
+    rng = np.random.default_rng(3)
+    nb = 40
+    s = np.round(rng.standard_normal((2, 3, nb, nb)), 1).astype(np.float32)
+    s[0, 0, 30, 5] = np.nan
+    s[0, 1, 35, :10] = np.nan
+    s[1, 2, 39, :] = -np.inf
+    s[1, 0, 20, 3] = -0.0
+    s[1, 0, 20, 4] = 0.0
+    for i in range(nb):
+        s[..., i, i + 1:] = -np.inf
+    shape = ssa.Shape(batch=2, n_q_heads=3, n_kv_heads=1, seq_q=nb * B, seq_kv=nb * B, q_offset=0,
+                      head_dim=64, block=64, topk=6, causal=1, scale=0.0)
+    idx = ssa.ssa_select_topk(shape, torch.from_numpy(s).to(dev)).cpu().numpy()
+    ref = O.select_blocks(s.astype(np.float64), 6, B)
+    assert np.array_equal(idx, ref)
+
+
+def test_empty_problem_writes_nothing(dev):
+    say("empty problems")
+    import ctypes
+    lib = ssa.load_library()
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16, device=dev)
+    out = torch.full((1, 2, 64, 64), 7.0, dtype=torch.bfloat16, device=dev)
+    lse = torch.full((1, 2, 64), 7.0, device=dev)
+    idx = torch.zeros((1, 2, 1, 2), dtype=torch.int32, device=dev)
+    for kw in (dict(batch=0), dict(seq_q=0, seq_kv=0)):
+        sh = dict(batch=1, n_q_heads=2, n_kv_heads=1, seq_q=64, seq_kv=64, q_offset=0, head_dim=64,
+                  block=64, topk=2, causal=1, scale=0.0)
+        sh.update(kw)
+        shape = ssa.Shape(**sh)
+        st = lib.ssa_block_sparse_attn_fwd(ctypes.byref(shape), ssa._ptr(q), ssa._ptr(q), ssa._ptr(q),
+                                           ssa._ptr(idx), ssa._ptr(out), ssa._ptr(lse), None, 0, None)
+        assert st == ssa.SSA_OK
+        st = lib.ssa_full_attn_fwd_dropped_mass(ctypes.byref(shape), ssa._ptr(q), ssa._ptr(q), ssa._ptr(q),
+                                                ssa._ptr(idx), 0, 0, ssa._ptr(out), ssa._ptr(lse),
+                                                ssa._ptr(lse), None, 0, None)
+        assert st == ssa.SSA_OK
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(lse == 7.0)
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def check_full_size(w: W.Workload, dev, nrows=96, seq_subset=None):
+    say(w)
+    q, k, v = W.make_inputs(w)
+    nqb = ssa.n_blocks(w.seq_q, B)
+    if w.full_rows is None:
+        fr = (0, nqb)
+    else:
+        fr = (w.full_rows[0] // B, ssa.n_blocks(w.full_rows[1], B) - w.full_rows[0] // B)
+    g = gpu_path(w, q, k, v, dev, full_range=fr, with_full=True)
+    bsel = list(range(w.batch)) if seq_subset is None else seq_subset
+    qn = q[bsel].double().numpy()
+    kn = k[bsel].double().numpy()
+    vn = v[bsel].double().numpy()
+    off = w.q_offset
+    assert np.array_equal(P.np64(g["k_summary"][bsel]), O.key_summaries(kn, B))
+    s_ref = O.block_scores(qn, kn, B, q_offset=off)
+    idx_ref = O.select_blocks(s_ref, w.topk, B, q_offset=off)
+    ndiff = P.check_indices(g["idx"][bsel], s_ref, idx_ref, w.topk, B, off)
+    print(f"[case] {w.name}: index rows differing inside the tie band: {ndiff}", flush=True)
+    gidx = g["idx"][bsel].numpy()
+    rng = np.random.default_rng(w.seed)
+    rows = P.sample_rows(rng, len(bsel), w.n_q_heads, w.seq_q, nrows)
+    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, gidx, B, q_offset=off, rows=rows)
+    got_o = torch.stack([g["o"][bsel[b], h, r] for b, h, r in rows])
+    got_l = torch.stack([g["lse"][bsel[b], h, r] for b, h, r in rows])
+    P.check_close_outputs(got_o, o_ref, "O_sparse sampled")
+    P.check_abs(got_l, lse_ref, P.LSE_ABS, "LSE_sparse sampled")
+    lo = fr[0] * B
+    frows = [(b, h, lo + (r % (g["of"].shape[2]))) for b, h, r in rows]
+    of_ref, lf_ref, dm_ref = O.full_attention_dropped_mass(qn, kn, vn, gidx, B, q_offset=off, rows=frows)
+    P.check_close_outputs(torch.stack([g["of"][bsel[b], h, r - lo] for b, h, r in frows]), of_ref, "O_full sampled")
+    P.check_abs(torch.stack([g["lf"][bsel[b], h, r - lo] for b, h, r in frows]), lf_ref, P.LSE_ABS, "LSE_full sampled")
+    P.check_abs(torch.stack([g["dm"][bsel[b], h, r - lo] for b, h, r in frows]), dm_ref, P.DROP_ABS, "dropped sampled")
+    # properties at every row: 0 <= delta < 1, delta = 1 - exp(LSE_sparse - LSE_full)
+    dm = g["dm"].double()
+    assert torch.all(dm >= 0) and torch.all(dm < 1)
+    hi = lo + g["of"].shape[2]
+    ident = 1 - torch.exp(g["lse"][:, :, lo:hi].double() - g["lf"].double())
+    assert float((dm - ident).abs().max()) < 2e-3
+    return g
+
+
+def test_prefill_8k_full_size(dev):
+    g = check_full_size(W.PREFILL_8K, dev)
+    # rows of the first k blocks keep every causal key
+    assert torch.all(g["dm"][:, :, : W.PREFILL_8K.topk * B] == 0)
+
+
+def test_structured_8k_planted_full_size(dev):
+    check_full_size(W.STRUCTURED_8K, dev, nrows=64)
+
+
+def test_structured_8k_tie_full_size(dev):
+    w = W.STRUCTURED_8K_TIE
+    say(w)
+    q, k, v = W.make_inputs(w)
+    g = gpu_path(w, q, k, v, dev)
+    k_ = w.topk
+    nqb = ssa.n_blocks(w.seq_q, B)
+    idx = g["idx"].numpy()
+    # all scores tie exactly -> blocks 0..k-2 plus the diagonal, for every row
+    s = g["scores"].numpy()
+    for i in range(k_, nqb):
+        assert np.all(s[:, :, i, :i] == s[:, :, i, :1])
+    want = np.array([list(range(i + 1)) + [-1] * (k_ - i - 1) if i + 1 <= k_ else list(range(k_ - 1)) + [i]
+                     for i in range(nqb)])
+    assert np.array_equal(idx, np.broadcast_to(want, idx.shape))
+    # uniform softmax: closed forms at every row
+    r = np.arange(w.seq_q)
+    blk = r // B
+    kept = np.where(blk < k_, r + 1, (k_ - 1) * B + (r - blk * B + 1))
+    P.check_abs(g["dm"], np.broadcast_to(1 - kept / (r + 1), g["dm"].shape), P.DROP_ABS, "dropped closed form")
+    vn = v.double()
+    csum = torch.cumsum(vn, dim=2)
+    mean_full = csum / torch.arange(1, w.seq_q + 1, dtype=torch.float64)[:, None]
+    P.check_close_outputs(g["of"], mean_full.repeat_interleave(w.n_q_heads // w.n_kv_heads, dim=1), "O_full closed form")
+    # sparse: keys of blocks 0..k-2 plus the causal part of the row's own block
+    pre = csum[:, :, (k_ - 1) * B - 1]                                  # sum over the first k-1 blocks
+    blk_start = torch.from_numpy((blk * B).astype(np.int64))
+    before = torch.where(blk_start[None, None, :, None] > 0,
+                         csum[:, :, (blk_start - 1).clamp(min=0)], torch.zeros_like(csum))
+    num = torch.where(torch.from_numpy(blk < k_)[None, None, :, None], csum, pre[:, :, None, :] + csum - before)
+    mean_sp = num / torch.from_numpy(kept.astype(np.float64))[:, None]
+    P.check_close_outputs(g["o"], mean_sp.repeat_interleave(w.n_q_heads // w.n_kv_heads, dim=1), "O_sparse closed form")
+
+
+def test_extrap_32k_full_size(dev):
+    check_full_size(W.EXTRAP_32K, dev, nrows=64)
+
+
+def test_decode_32k_full_size(dev):
+    w = W.DECODE_32K
+    say(w)
+    q, k, v = W.make_inputs(w)
+    g = gpu_path(w, q, k, v, dev, with_full=False)
+    sub = [0, 17, 63]
+    qn, kn, vn = q[sub].double().numpy(), k[sub].double().numpy(), v[sub].double().numpy()
+    ks_ref = O.key_summaries(kn, B)
+    assert np.array_equal(P.np64(g["k_summary"][sub]), ks_ref)
+    s_ref = O.block_scores(qn, None, B, q_offset=w.q_offset, k_summary=ks_ref)
+    idx_ref = O.select_blocks(s_ref, w.topk, B, q_offset=w.q_offset)
+    P.check_indices(g["idx"][sub], s_ref, idx_ref, w.topk, B, w.q_offset)
+    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, g["idx"][sub].numpy(), B, q_offset=w.q_offset)
+    P.check_close_outputs(g["o"][sub], o_ref, "O_decode")
+    P.check_abs(g["lse"][sub], lse_ref, P.LSE_ABS, "LSE_decode")
+    # every sequence: the forced block is the most recent one
+    assert torch.all(g["idx"][..., -1] == (w.seq_kv - 1) // B)
