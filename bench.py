@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSA block-sparse attention hot path on one MI355X.
+
+One step = one pass of the whole path over the 8k prefill workload (batch 1,
+32 query heads on 2 KV heads, N=8192, d=64, B=64, k=16): block summaries and
+scores, top-k selection, block-sparse attention forward, and the full-attention
+counterpart with per-row dropped mass.  The decode workload (64 sequences x 1
+token against a 32768-entry cache, 16+1 blocks) is measured in the same run
+and reported under "decode".
+
+Prints ONE JSON line.  ``value`` is tokens/s of the whole step (inputs already
+resident in HBM); per-kernel timings come from HIP events recorded on the
+stream the kernels run on, averaged over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    from block_sparse_attention_kv_amd.profiling import source_hash
+    e = t.get(kernel)
+    if not e or e.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def sparse_useful_pairs(nqb: int, topk: int, block: int) -> int:
+    """(query row, key) pairs the sparse pattern attends to per (b, h) when every
+    block is full: per query block, (selected - 1) full tiles plus the causal
+    half of the diagonal tile."""
+    total = 0
+    for i in range(nqb):
+        n_sel = min(topk, i + 1)
+        total += (n_sel - 1) * block * block + block * (block + 1) // 2
+    return total
+
+
+def full_useful_pairs(lo: int, hi: int) -> int:
+    """Causal pairs of rows [lo, hi): sum of (r + 1)."""
+    return (hi * (hi + 1) - lo * (lo + 1)) // 2
+
+
+class KernelTimer:
+    """Accumulates HIP-event durations of named calls on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.total = {}
+        self.count = {}
+
+    def run(self, name, fn, *args, **kw):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn(*args, **kw)
+        e1.record()
+        self.pending.append((name, e0, e1))
+        return r
+
+    def collect(self):
+        for name, e0, e1 in self.pending:
+            self.total[name] = self.total.get(name, 0.0) + e0.elapsed_time(e1)
+            self.count[name] = self.count.get(name, 0) + 1
+        self.pending.clear()
+
+    def avg_ms(self, name):
+        return self.total[name] / self.count[name]
+
+
+def bench_prefill(args, torch, ssa, W):
+    w = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.make_inputs(w))
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    nqb, nkb = ssa.n_blocks(w.seq_q, w.block), ssa.n_blocks(w.seq_kv, w.block)
+    if w.full_rows is None:
+        fb0, fcnt = 0, nqb
+    else:
+        fb0 = w.full_rows[0] // w.block
+        fcnt = ssa.n_blocks(w.full_rows[1], w.block) - fb0
+    scores = torch.empty((w.batch, w.n_q_heads, nqb, nkb), dtype=torch.float32, device=dev)
+    ksum = torch.empty((w.batch, w.n_kv_heads, nkb, w.head_dim), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.batch, w.n_q_heads, nqb, w.topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    rows = min(w.seq_q, (fb0 + fcnt) * w.block) - fb0 * w.block
+    out_f = torch.empty((w.batch, w.n_q_heads, rows, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse_f = torch.empty((w.batch, w.n_q_heads, rows), dtype=torch.float32, device=dev)
+    drop = torch.empty_like(lse_f)
+    timer = KernelTimer(torch)
+
+    def step(t):
+        t.run("scores", ssa.ssa_block_scores, shape, q, k, summary_out=ksum, scores=scores)
+        t.run("topk", ssa.ssa_select_topk, shape, scores, idx)
+        t.run("sparse_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, out=out, lse=lse)
+        t.run("full_attn", ssa.ssa_full_attn_fwd_dropped_mass, shape, q, k, v, idx, fb0, fcnt,
+              out=out_f, lse=lse_f, dropped=drop)
+
+    for _ in range(args.warmup):
+        step(timer)
+    torch.cuda.synchronize()
+    timer.pending.clear()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record()
+    for _ in range(args.steps):
+        step(timer)
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e_start.elapsed_time(e_end) / args.steps
+    timer.collect()
+
+    pairs_sp = w.batch * w.n_q_heads * sparse_useful_pairs(nqb, w.topk, w.block)
+    pairs_full = w.batch * w.n_q_heads * full_useful_pairs(fb0 * w.block, fb0 * w.block + rows)
+    flops = {"sparse_attn": 4.0 * w.head_dim * pairs_sp, "full_attn": 4.0 * w.head_dim * pairs_full}
+    bytes_alg = {
+        # summaries read K once and write K-bar; scores read Q once and write S
+        "scores": (k.numel() * 2 + ksum.numel() * 4 + q.numel() * 2 + scores.numel() * 4),
+        "topk": scores.numel() * 4 + idx.numel() * 4,
+    }
+    kernels = {}
+    for name in ("scores", "topk", "sparse_attn", "full_attn"):
+        ms = timer.avg_ms(name)
+        e = {"avg_ms": round(ms, 5)}
+        if name in flops:
+            tf = flops[name] / (ms * 1e-3) / 1e12
+            e.update(bound="mfma", gflop_per_launch=round(flops[name] / 1e9, 3),
+                     tflops=round(tf, 2), frac_of_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        else:
+            gbs = bytes_alg[name] / (ms * 1e-3) / 1e9
+            e.update(bound="hbm", mbytes_per_launch=round(bytes_alg[name] / 1e6, 3),
+                     gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[name] = e
+    dominant = max(kernels, key=lambda n: kernels[n]["avg_ms"])
+    roof = roofline_entry(dominant, kernels[dominant], flops, bytes_alg)
+    return dict(w=w, ms_step=ms_step, wall=wall, kernels=kernels, roofline=roof, dominant=dominant,
+                tokens_per_s=w.batch * w.seq_q / (ms_step * 1e-3))
+
+
+def roofline_entry(name, e, flops, bytes_alg):
+    if e["bound"] == "mfma":
+        ach = e["tflops"]
+        r = {"kernel": name, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(ach / PEAK_BF16_TFLOPS, 4), "algorithmic_per_launch": flops[name]}
+    else:
+        ach = e["gbs"]
+        r = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_per_launch": bytes_alg[name]}
+    r["traffic"] = measured_traffic(name) if name in ("full_attn", "sparse_attn") else None
+    return r
+
+
+def bench_decode(args, torch, ssa, W):
+    w = W.DECODE_32K
+    dev = torch.device("cuda:0")
+    q0, k0, v0 = W.make_inputs(w)
+    copies = []
+    for c in range(args.decode_copies):      # distinct buffers defeat the 256 MB last-level cache
+        q, k, v = q0.to(dev), k0.to(dev), v0.to(dev)
+        ks = ssa.ssa_block_summaries(k, block=w.block)   # cached summaries (untimed, as in decoding)
+        copies.append((q, k, v, ks))
+    del q0, k0, v0
+    shape = ssa.make_shape(copies[0][0], w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    nkb = ssa.n_blocks(w.seq_kv, w.block)
+    scores = torch.empty((w.batch, w.n_q_heads, 1, nkb), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.batch, w.n_q_heads, 1, w.topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(copies[0][0])
+    lse = torch.empty((w.batch, w.n_q_heads, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD),), dtype=torch.uint8, device=dev)
+    timer = KernelTimer(torch)
+
+    def step(t, c):
+        q, k, v, ks = copies[c % len(copies)]
+        t.run("decode_scores", ssa.ssa_block_scores, shape, q, None, ks, scores=scores)
+        t.run("decode_topk", ssa.ssa_select_topk, shape, scores, idx)
+        t.run("decode_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, workspace=ws, out=out, lse=lse)
+
+    for i in range(args.warmup):
+        step(timer, i)
+    torch.cuda.synchronize()
+    timer.pending.clear()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.decode_steps):
+        step(timer, i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.decode_steps
+    timer.collect()
+    # Algorithmic bytes from the GPU's own selection (identical inputs in every copy):
+    # the union over the query heads of each KV group of selected K and V blocks.
+    G = w.n_q_heads // w.n_kv_heads
+    sel = torch.zeros((w.batch, w.n_kv_heads, nkb + 1), dtype=torch.bool, device=dev)
+    ii = idx.view(w.batch, w.n_kv_heads, G * w.topk).long()
+    sel.scatter_(2, torch.where(ii < 0, torch.full_like(ii, nkb), ii), True)
+    union_blocks = int(sel[..., :nkb].sum())
+    kv_bytes = union_blocks * w.block * w.head_dim * 2 * 2
+    attn_bytes = kv_bytes + copies[0][0].numel() * 2 * 2 + idx.numel() * 4 + lse.numel() * 4
+    score_bytes = copies[0][3].numel() * 4 + copies[0][0].numel() * 2 + scores.numel() * 4
+    topk_bytes = scores.numel() * 4 + idx.numel() * 4
+    kern = {}
+    for name, b in (("decode_scores", score_bytes), ("decode_topk", topk_bytes), ("decode_attn", attn_bytes)):
+        ms = timer.avg_ms(name)
+        gbs = b / (ms * 1e-3) / 1e9
+        kern[name] = {"avg_ms": round(ms, 5), "bound": "hbm", "mbytes_per_launch": round(b / 1e6, 3),
+                      "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    step_bytes = attn_bytes + score_bytes + topk_bytes
+    return {
+        "workload": w.name, "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5),
+        "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_hbm_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "union_blocks_per_group": round(union_blocks / (w.batch * w.n_kv_heads), 2),
+        "kernels": kern,
+        "roofline": {"kernel": "decode_attn", "bound": "hbm", "achieved": kern["decode_attn"]["gbs"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kern["decode_attn"]["frac_of_peak"],
+                     "algorithmic_per_launch": attn_bytes, "traffic": measured_traffic("decode_attn")},
+        "cache_copies_rotated": len(copies), "steps": args.decode_steps,
+    }
+
+
+def cpu_baseline(args, W):
+    """The fp64 oracle, as it stands, on a bounded sample of the prefill workload:
+    whole query heads (all rows, all five steps) until ~target seconds elapse."""
+    import numpy as np
+    from oracle import ssa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    w = W.BY_NAME[args.workload]
+    q, k, v = W.make_inputs(w)
+    G = w.n_q_heads // w.n_kv_heads
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < w.n_q_heads:
+        h = heads
+        g = h // G
+        qh = q[:1, h:h + 1].double().numpy()
+        kh = k[:1, g:g + 1].double().numpy()
+        vh = v[:1, g:g + 1].double().numpy()
+        O.hot_path(qh, kh, vh, w.block, w.topk, full_row_range=w.full_rows)
+        heads += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    tokens = w.seq_q * heads / w.n_q_heads   # fraction of one batch row's work
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"{heads} of {w.n_q_heads} query heads of batch row 0 of {w.name}, all {w.seq_q} rows, "
+                      f"summaries+scores+top-k+sparse+full+dropped mass in fp64 NumPy ({dt:.1f} s; "
+                      f"BLAS threads {blas_threads}, elementwise ops single-threaded); "
+                      f"tokens/s scaled by the head fraction"}
+
+
+def counter_pass(args, torch, ssa, W):
+    """Dispatches for a rocprofv3 --pmc run: a plain copy of known size (the
+    counter calibration), then the prefill and decode attention kernels."""
+    from block_sparse_attention_kv_amd.profiling import COPY_BYTES
+    dev = torch.device("cuda:0")
+    src = torch.empty((COPY_BYTES // 2,), dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    args.warmup, args.steps, args.decode_steps, args.decode_copies = 0, 3, 3, 1
+    bench_prefill(args, torch, ssa, W)
+    bench_decode(args, torch, ssa, W)
+    torch.cuda.synchronize()
+    print("counter pass done", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_8k")
+    ap.add_argument("--decode-steps", type=int, default=60)
+    ap.add_argument("--decode-copies", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="only issue the dispatches a rocprofv3 --pmc run needs (no JSON line)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(the path shards with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_kv_amd import ssa
+    from block_sparse_attention_kv_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (there is no CPU fallback)", file=sys.stderr)
+        sys.exit(1)
+    ssa.load_library()
+    if args.counter_pass:
+        counter_pass(args, torch, ssa, W)
+        return
+
+    pre = bench_prefill(args, torch, ssa, W)
+    dec = None if args.no_decode else bench_decode(args, torch, ssa, W)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, W)
+    w = pre["w"]
+    line = {
+        "metric": "block-sparse attn fwd tokens/s + % bf16 MFMA peak at N=8k; decode HBM GB/s",
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V cast to bf16)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "seq_len": w.seq_q, "head_dim": w.head_dim, "block": w.block, "topk": w.topk,
+                   "step": "summaries+scores, top-k, block-sparse fwd, full fwd + dropped mass"},
+        "roofline": pre["roofline"],
+        "kernels": pre["kernels"],
+        "sparse_fwd": {"tokens_per_s": round(w.batch * w.seq_q / (pre["kernels"]["sparse_attn"]["avg_ms"] * 1e-3), 1),
+                       "tflops": pre["kernels"]["sparse_attn"]["tflops"],
+                       "frac_of_bf16_peak": pre["kernels"]["sparse_attn"]["frac_of_peak"],
+                       "traffic": measured_traffic("sparse_attn")},
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+"""Summaries of rocprofv3 output for the kernels of libssa.
+
+  python -m block_sparse_attention_kv_amd.profiling stats <rocprof_dir> [--title T] [--command C]
+      -> markdown table of per-kernel dispatch counts and durations (kernel_stats.csv)
+  python -m block_sparse_attention_kv_amd.profiling traffic <fetch_dir> <write_dir> --out profiles/traffic.json
+      -> HBM bytes per dispatch of the attention kernels from FETCH_SIZE / WRITE_SIZE
+         counter runs, scaled by what the same counters read for a plain copy of
+         known size (the calibration dispatch in the same run)
+
+Kernel names are matched by substring: attn_prefill_kernel<true> is the full
+counterpart, attn_prefill_kernel<false> the block-sparse forward,
+attn_decode_partial_kernel the decode gather.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+KERNEL_SOURCES = {
+    "full_attn": ["ssa_attn.hip", "ssa_common.hpp", "ssa_internal.hpp"],
+    "sparse_attn": ["ssa_attn.hip", "ssa_common.hpp", "ssa_internal.hpp"],
+    "decode_attn": ["ssa_decode.hip", "ssa_common.hpp", "ssa_internal.hpp"],
+}
+# calibration copy: bench.py --counter-pass copies this many bytes (read + write) per dispatch
+COPY_BYTES = 512 * 1024 * 1024
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def classify(name: str):
+    if "attn_prefill_kernel<true>" in name or "attn_prefill_kernelILb1E" in name:
+        return "full_attn"
+    if "attn_prefill_kernel<false>" in name or "attn_prefill_kernelILb0E" in name:
+        return "sparse_attn"
+    if "attn_decode_partial_kernel" in name:
+        return "decode_attn"
+    if "attn_decode_combine_kernel" in name:
+        return "decode_combine"
+    if "prefill_scores_kernel" in name:
+        return "prefill_scores"
+    if "decode_scores_kernel" in name:
+        return "decode_scores"
+    if "block_summaries_kernel" in name:
+        return "block_summaries"
+    if "select_topk_kernel" in name:
+        return "select_topk"
+    if "copyBuffer" in name:
+        return "copy"
+    return None
+
+
+def _csvs(d: str, pattern: str):
+    return sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+
+
+def stats_markdown(d: str, title: str = "", command: str = "") -> str:
+    files = _csvs(d, "*kernel_stats.csv")
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    out = [f"# {title}".rstrip(), ""]
+    if command:
+        out += ["Command:", "", "```", command, "```", ""]
+    out += ["| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name", "")
+        short = classify(name) or name[:60]
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        mn = float(r.get("MinNs", 0)) / 1e3
+        mx = float(r.get("MaxNs", 0)) / 1e3
+        out.append(f"| {short} | {r.get('Calls')} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {float(r.get('Percentage', 0)):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _counter_per_kernel(d: str, counter: str):
+    """kernel class -> list of per-dispatch counter values (summed over the
+    per-dimension rows a dispatch may have)."""
+    per = defaultdict(lambda: defaultdict(float))
+    for fpath in _csvs(d, "*counter_collection.csv"):
+        with open(fpath) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                cls = classify(r.get("Kernel_Name", ""))
+                if cls is None:
+                    continue
+                per[cls][r.get("Dispatch_Id")] += float(r.get("Counter_Value", 0))
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str, out_json: str, command: str = ""):
+    fetch = _counter_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_kernel(write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("calibration copy dispatch not found in the counter output")
+    copy_f = max(fetch["copy"])   # KiB per dispatch
+    copy_w = max(write["copy"])
+    f_scale = (COPY_BYTES / 2) / (copy_f * 1024.0)   # a copy reads half and writes half of COPY_BYTES
+    w_scale = (COPY_BYTES / 2) / (copy_w * 1024.0)
+    res = {"_about": "HBM bytes per dispatch = FETCH_SIZE*1024*f_scale + WRITE_SIZE*1024*w_scale; "
+                     "scales from a plain copy of known size measured in the same runs",
+           "_command": command, "_copy_fetch_kib": copy_f, "_copy_write_kib": copy_w,
+           "_f_scale": f_scale, "_w_scale": w_scale}
+    for k in ("full_attn", "sparse_attn", "decode_attn"):
+        if k not in fetch or k not in write:
+            continue
+        fk = sum(fetch[k]) / len(fetch[k])
+        wk = sum(write[k]) / len(write[k])
+        res[k] = {"fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                  "bytes_per_launch": round(fk * 1024 * f_scale + wk * 1024 * w_scale),
+                  "source_sha256_16": source_hash(k), "dispatches": len(fetch[k])}
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--title", default="")
+    s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        sys.stdout.write(stats_markdown(a.dir, a.title, a.command))
+    else:
+        print(json.dumps(traffic(a.fetch_dir, a.write_dir, a.out, a.command), indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -134,27 +134,32 @@ def ssa_block_summaries(k: torch.Tensor, *, block: int = 64) -> torch.Tensor:
 
 
 def ssa_block_scores(shape: Shape, q: torch.Tensor, k: Optional[torch.Tensor] = None,
-                     k_summary: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     k_summary: Optional[torch.Tensor] = None, *, summary_out: Optional[torch.Tensor] = None,
+                     scores: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """(scores [b, Hq, nqb, nkb] fp32, k_summary).  With ``k_summary`` given the
-    cached summaries are used (K may be None); otherwise they are computed from K."""
-    _require_gpu(q, k, k_summary)
+    cached summaries are used (K may be None); otherwise they are computed from K
+    (into ``summary_out`` when given)."""
+    _require_gpu(q, k, k_summary, summary_out, scores)
     summary_is_input = k_summary is not None
     if not summary_is_input:
-        k_summary = torch.empty((shape.batch, shape.n_kv_heads, n_blocks(shape.seq_kv, shape.block),
-                                 shape.head_dim), dtype=torch.float32, device=q.device)
-    scores = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block),
-                          n_blocks(shape.seq_kv, shape.block)), dtype=torch.float32, device=q.device)
+        k_summary = summary_out if summary_out is not None else torch.empty(
+            (shape.batch, shape.n_kv_heads, n_blocks(shape.seq_kv, shape.block), shape.head_dim),
+            dtype=torch.float32, device=q.device)
+    if scores is None:
+        scores = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block),
+                              n_blocks(shape.seq_kv, shape.block)), dtype=torch.float32, device=q.device)
     _check("ssa_block_scores", load_library().ssa_block_scores(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(k_summary), int(summary_is_input), _ptr(scores),
         _stream(q.device)))
     return scores, k_summary
 
 
-def ssa_select_topk(shape: Shape, scores: torch.Tensor) -> torch.Tensor:
+def ssa_select_topk(shape: Shape, scores: torch.Tensor, idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Selected key blocks int32 [b, Hq, nqb, topk], ascending, -1 padded."""
-    _require_gpu(scores)
-    idx = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block), shape.topk),
-                      dtype=torch.int32, device=scores.device)
+    _require_gpu(scores, idx)
+    if idx is None:
+        idx = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block), shape.topk),
+                          dtype=torch.int32, device=scores.device)
     _check("ssa_select_topk", load_library().ssa_select_topk(
         ctypes.byref(shape), _ptr(scores), _ptr(idx), _stream(scores.device)))
     return idx
