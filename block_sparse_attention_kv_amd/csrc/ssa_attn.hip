@@ -1,16 +1,24 @@
 // Prefill attention kernels (gfx950): block-sparse forward over the selected
 // key blocks, and the full causal counterpart that also emits the dropped mass.
 //
-// One wavefront owns one unit = (b, query head, 64-row query block) and walks
-// its key tiles (64 keys each): the selected blocks (sparse) or every causal
-// block (full).  Per tile, computed transposed so a lane owns query columns:
-//   S^T = K Q^T          (bf16 MFMA 32x32x16, fp32 accumulate; Q^T stays in registers)
-//   online softmax       (fp32, log2 domain; row max/sum are lane-local plus one swap)
-//   O^T += V^T P^T       (bf16 MFMA; P^T comes straight from the S^T accumulators,
-//                          V^T read from a transposed LDS copy in the same key order)
-// The full kernel keeps a second running sum over tiles that are not selected,
-// under the same running max, so dropped mass = l_dropped / l_total falls out of
-// the single pass.
+// A wavefront owns one unit = (b, query head, 64-row query block) and walks
+// its 64-key tiles: the selected blocks (sparse) or every causal block (full).
+// Per tile, computed transposed so that a lane owns query columns:
+//   S^T = K Q^T      bf16 MFMA 32x32x16, fp32 accumulate; Q^T stays in registers
+//   softmax          fp32 in the log2 domain; the row max is lane-local plus one
+//                    swap between lane halves; the reference max only moves when
+//                    a row's max grows by more than 2^8 (lazy rescale); row sums
+//                    accumulate the fp32 probabilities
+//   O^T += V^T P^T   bf16 MFMA; P^T comes straight from the S^T accumulators, V^T
+//                    from transposing LDS reads of the row-major V tile
+// Tiles move HBM/L2 -> LDS by direct-to-LDS loads (no register staging) into
+// 16-byte-chunk XOR-swizzled buffers.  The sparse kernel gives each wave its
+// own K and V buffers and refills K while the softmax and PV of the current
+// tile run, V while the next S runs.  The full kernel runs 4 query heads of a
+// KV group per workgroup; they need the same tiles, so each tile is fetched
+// once into a double buffer shared by the 4 waves.  The full kernel keeps a
+// second running sum over tiles that are not selected, under the same
+// reference max, so dropped mass = l_dropped / l_total falls out of one pass.
 //
 // Method: SSA summary (gist.science 2511.20102), "Mecanismo Central" (sparse
 // and full attention streams) and "Alineacion Bidireccional" (counterpart
@@ -23,178 +31,265 @@
 namespace ssa {
 namespace {
 
-constexpr int kRow = 72;  // LDS row stride in bf16 elements (144 B; 16-byte aligned rows)
+constexpr int kTileBytes = kBlock * kHeadDim * 2;  // 8 KB: 64 rows x 128 B
+constexpr float kRescaleSlack = 8.f;               // log2 headroom before the reference max moves
 
-template <bool FULL>
-__global__ __launch_bounds__(64) void attn_prefill_kernel(AttnArgs a, Geometry geo) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kHeadDim * kRow];
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
-  const int lane = threadIdx.x, hl = lane >> 5, l32 = lane & 31;
-  const int nbh = geo.batch * geo.hq;
-  const int i_rel = blockIdx.x / nbh;
-  const int bh = blockIdx.x - i_rel * nbh;
-  const int i = a.qb_begin + (a.qb_count - 1 - i_rel);  // longest rows first
-  const int b = bh / geo.hq, h = bh - b * geo.hq, g = h / geo.group;
-  const int jd = (geo.q_offset + i * kBlock) / kBlock;
-  const uint16_t* qbase = a.q + (size_t)bh * geo.seq_q * kHeadDim;
-  const size_t kvoff = (size_t)(b * geo.hkv + g) * geo.seq_kv * kHeadDim;
-  const uint16_t* kbase = a.k + kvoff;
-  const uint16_t* vbase = a.v + kvoff;
-  const int32_t* irow = a.idx + ((size_t)bh * geo.nqb + i) * geo.topk;
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.
+__device__ __forceinline__ uint32_t swz(int row, int chunk) {
+  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+}
 
-  // Q^T as MFMA B operand: column = query row 32*qb + l32, k-slots = d 16*ks + 8*hl .. +8.
-  bf16x8 qop[2][4];
+__device__ __forceinline__ lds_void* to_lds(void* p) { return (lds_void*)p; }
+
+// The direct-to-LDS loads are not ordered against later LDS reads by the
+// compiler, so the pipeline waits explicitly: vmcnt(N) = at most the N most
+// recent vector-memory instructions still in flight (in-order completion for
+// loads).  The empty asm and scheduling barriers keep every LDS access on its
+// side of the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// All LDS reads of this wave have returned (before a DMA overwrites their buffer).
+__device__ __forceinline__ void wait_lds_reads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Compact this unit's index list into LDS: the entries before the first -1
+// that name a causal block (j <= jd), in list order.  Returns their count.
+// Whole-wave operation; `lst` has room for kMaxTopk entries.
+__device__ __forceinline__ int stage_tile_list(const int32_t* __restrict__ irow, int topk, int jd, int* lst,
+                                               int lane) {
+  int first_neg = topk;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const int j = e < topk ? irow[e] : 0;
+    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < topk && j < 0);
+    if (neg != 0ull && first_neg == topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
+  }
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const int j = e < topk ? irow[e] : -1;
+    const bool keep = e < first_neg && j >= 0 && j <= jd;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+    if (keep) lst[n + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = j;
+    n += (int)__builtin_popcountll(m);
+  }
+  return n;
+}
+
+// One direct-to-LDS load: every lane fetches the 16 bytes at gtile + voff and
+// the wave's 1 KB lands at LDS byte address lds_base + 16 * lane.  Issued from
+// inline asm so the compiler does not track it; each use is ordered by the
+// explicit waits of the pipeline (it has no register outputs: the address
+// registers are read at issue).
+__device__ __forceinline__ void dma_1k(const uint16_t* gtile, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gtile), "s"(lds_base)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
+}
+
+// Request slices first, first+step, ... of the eight 1 KB slices of one tile
+// (slice c = rows 8c..8c+7), storing chunk q of row r at swz(r, q).  Rows at or
+// past `nvalid` re-read row 0 of the tile (always present); their contents
+// never reach an output (causal mask / unwritten rows).
+__device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds,
+                                          int first, int step, int lane) {
+  const uint32_t base = lds_addr(lds);
+  for (int c = first; c < 8; c += step) {
+    const int row = 8 * c + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    const uint32_t voff = (uint32_t)((row < nvalid ? row * kHeadDim : 0) + chunk * 8) * 2u;
+    dma_1k(gtile, voff, __builtin_amdgcn_readfirstlane(base + c * 1024));
+  }
+}
+
+struct UnitState {
+  f32x16 o[2][2];  // O^T accumulators [d block][query block]
+  float m[2];      // reference max (log2 units) per owned query column
+  float l[2];      // running sum (this lane's keys)
+  float ld[2];     // running sum over unselected tiles (full kernel)
+};
+
+__device__ __forceinline__ void load_q(const uint16_t* qbase, int i, int seq_q, int l32, int hl, bf16x8 qop[2][4]) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = i * kBlock + 32 * qb + l32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < geo.seq_q)
-        v = *reinterpret_cast<const u32x4*>(qbase + (size_t)row * kHeadDim + 16 * ks + 8 * hl);
+      if (row < seq_q) v = *reinterpret_cast<const u32x4*>(qbase + (size_t)row * kHeadDim + 16 * ks + 8 * hl);
       qop[qb][ks] = as_bf16x8(v);
     }
   }
+}
 
-  f32x16 o[2][2];  // O^T accumulators [d block][query block]
+__device__ __forceinline__ void init_state(UnitState& st) {
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < 2; ++y)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[x][y][r] = 0.f;
-  float m[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l[2] = {0.f, 0.f};
-  float ld[2] = {0.f, 0.f};
+      for (int r = 0; r < 16; ++r) st.o[x][y][r] = 0.f;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    st.m[qb] = -__builtin_inff();
+    st.l[qb] = 0.f;
+    st.ld[qb] = 0.f;
+  }
+}
 
-  const int ntiles = FULL ? jd + 1 : geo.topk;
-  int sel_ptr = 0;
-  for (int t = 0; t < ntiles; ++t) {
-    int j = t;
-    bool selected = true;
-    if (FULL) {
-      const int nxt = sel_ptr < geo.topk ? irow[sel_ptr] : -1;
-      selected = (nxt == j);
-      sel_ptr += selected ? 1 : 0;
-    } else {
-      j = irow[t];
-      if (j < 0) break;
-      if (j > jd) continue;  // not a causal block of this query block: ignored
+// S^T = K Q^T for one tile: rows = keys 32*kb + 8*(r/4) + 4*hl + r%4, columns = queries.
+__device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[2][4], int l32, int hl,
+                                            f32x16 s[2][2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz(32 * kb + l32, 2 * ks + hl));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(ka, qop[qb][ks], s[kb][qb]);
     }
+  }
+}
 
-    __syncthreads();
-    // Stage the tile: K row-major, V transposed (d-major) for the PV operand.
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int chunk = it * 64 + lane, row = chunk >> 3, c8 = chunk & 7;
-      const int key = j * kBlock + row;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < geo.seq_kv) {
-        kv = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kHeadDim + c8 * 8);
-        vv = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * kHeadDim + c8 * 8);
-      }
-      *reinterpret_cast<u32x4*>(&sK[row * kRow + c8 * 8]) = kv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[(c8 * 8 + 2 * e) * kRow + row] = (uint16_t)(vv[e] & 0xffffu);
-        sVt[(c8 * 8 + 2 * e + 1) * kRow + row] = (uint16_t)(vv[e] >> 16);
-      }
-    }
-    __syncthreads();
-
-    // S^T = K Q^T: rows = keys 32*kb + ..., columns = queries 32*qb + l32.
-    f32x16 s[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sK[(32 * kb + l32) * kRow + 16 * ks + 8 * hl]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(ka, qop[qb][ks], s[kb][qb]);
-      }
-    }
-
-    const bool diag = (j == jd);
+// Online-softmax update for one tile; leaves packed bf16 probabilities in pk.
+template <bool FULL>
+__device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x4 pk[2][2][2], bool diag,
+                                             bool selected, int key0, int pos0, int l32, int hl, float c) {
+  if (diag) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int pos = geo.q_offset + i * kBlock + 32 * qb + l32;
-      float mx = -__builtin_inff();
+      const int pos = pos0 + 32 * qb + l32;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][qb][r] * geo.scale_log2;
-          if (diag) {
-            const int key = j * kBlock + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key > pos) x = -__builtin_inff();
-          }
-          s[kb][qb][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m[qb], mx);
-      const float alpha = fast_exp2(m[qb] - mnew);
-      m[qb] = mnew;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(s[kb][qb][r] - mnew);
-          s[kb][qb][r] = p;
-          rs += p;
+          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key > pos) s[kb][qb][r] = -__builtin_inff();
         }
-      }
-      l[qb] = l[qb] * alpha + rs;
-      if (FULL) ld[qb] = ld[qb] * alpha + (selected ? 0.f : rs);
+    }
+  }
+  float mt[2];
+  bool grow = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = fmaxf(s[0][qb][0], s[0][qb][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[0][qb][r]), s[0][qb][r + 1]);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[1][qb][r]), s[1][qb][r + 1]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mt[qb] = mx * c;
+    grow |= !(mt[qb] <= st.m[qb] + kRescaleSlack);
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mn = fmaxf(st.m[qb], mt[qb]);
+      const float alpha = fast_exp2(st.m[qb] - mn);
+      st.m[qb] = mn;
+      st.l[qb] *= alpha;
+      if (FULL) st.ld[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
+        for (int r = 0; r < 16; ++r) st.o[db][qb][r] *= alpha;
     }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float nm = -st.m[qb];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[kb][qb][8 * ap + 2 * e], c, nm));
+          const float p1 = fast_exp2(fmaf(s[kb][qb][8 * ap + 2 * e + 1], c, nm));
+          pk[kb][ap][qb][e] = pack_bf16x2(p0, p1);
+          rs0 += p0;
+          rs1 += p1;
+        }
+    const float rs = rs0 + rs1;
+    st.l[qb] += rs;
+    if (FULL && !selected) st.ld[qb] += rs;
+  }
+}
 
-    // O^T += V^T P^T over four 16-key steps (kb, ap).  Lane half hl holds, in
-    // k-slot t, key 32*kb + 16*ap + 8*(t/4) + 4*hl + t%4 -- the keys its S^T
-    // accumulator registers 8*ap .. 8*ap+7 already hold.
+// O^T += V^T P^T.  16-key step (kb, ap): lane half hl holds in k-slot t the key
+// 32*kb + 16*ap + 8*(t/4) + 4*hl + t%4, i.e. the keys its S^T registers
+// 8*ap .. 8*ap+7 hold.  The V^T operand for d block db is two transposing
+// reads of 4 keys x 16 d columns per 16-lane group.
+__device__ __forceinline__ void tile_pv(const uint8_t* sV, const u32x4 pk[2][2][2], UnitState& st, int lane) {
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int tq = s16 >> 2, qq = s16 & 3;
+  const int hh = grp >> 1, gd = grp & 1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int ap = 0; ap < 2; ++ap) {
-        bf16x8 pop[2];
+    for (int ap = 0; ap < 2; ++ap) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          u32x4 pk;
+      for (int db = 0; db < 2; ++db) {
+        uint32_t w[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(s[kb][qb][8 * ap + 2 * e], s[kb][qb][8 * ap + 2 * e + 1]);
-          pop[qb] = as_bf16x8(pk);
+        for (int rr = 0; rr < 2; ++rr) {
+          const int row = 32 * kb + 16 * ap + 8 * rr + 4 * hh + tq;
+          const int chunk = 4 * db + 2 * gd + (qq >> 1);
+          const uint32_t off = swz(row, chunk) + 8 * (qq & 1);
+          const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)to_lds((void*)(sV + off)));
+          const u32x2 tw = __builtin_bit_cast(u32x2, t);
+          w[2 * rr] = tw[0];
+          w[2 * rr + 1] = tw[1];
         }
+        u32x4 va;
+        va[0] = w[0]; va[1] = w[1]; va[2] = w[2]; va[3] = w[3];
+        const bf16x8 vop = as_bf16x8(va);
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const uint16_t* vr = &sVt[(32 * db + l32) * kRow + 32 * kb + 16 * ap + 4 * hl];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-          u32x4 va;
-          va[0] = lo[0]; va[1] = lo[1]; va[2] = hi[0]; va[3] = hi[1];
-          const bf16x8 vop = as_bf16x8(va);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma32(vop, pop[qb], o[db][qb]);
-        }
+        for (int qb = 0; qb < 2; ++qb) st.o[db][qb] = mfma32(vop, as_bf16x8(pk[kb][ap][qb]), st.o[db][qb]);
       }
     }
   }
+}
 
-  // Epilogue: fold the two lane halves' partial sums (all lanes take part in
-  // the swaps), normalise, store.
+template <bool FULL>
+__device__ __forceinline__ void unit_epilogue(const UnitState& st, const AttnArgs& a, const Geometry& geo, int bh,
+                                              int i, int l32, int hl) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32, 64);
-    const float dt = FULL ? ld[qb] + __shfl_xor(ld[qb], 32, 64) : 0.f;
+    const float lt = st.l[qb] + __shfl_xor(st.l[qb], 32, 64);
+    const float dt = FULL ? st.ld[qb] + __shfl_xor(st.ld[qb], 32, 64) : 0.f;
     const float inv = 1.f / lt;
     const int row = i * kBlock + 32 * qb + l32;
     if (row < geo.seq_q) {
@@ -205,17 +300,158 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnArgs a, Geometry g
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           u32x2 w;
-          w[0] = pack_bf16x2(o[db][qb][4 * rg] * inv, o[db][qb][4 * rg + 1] * inv);
-          w[1] = pack_bf16x2(o[db][qb][4 * rg + 2] * inv, o[db][qb][4 * rg + 3] * inv);
+          w[0] = pack_bf16x2(st.o[db][qb][4 * rg] * inv, st.o[db][qb][4 * rg + 1] * inv);
+          w[1] = pack_bf16x2(st.o[db][qb][4 * rg + 2] * inv, st.o[db][qb][4 * rg + 3] * inv);
           *reinterpret_cast<u32x2*>(op + 32 * db + 8 * rg + 4 * hl) = w;
         }
       }
       if (hl == 0) {
-        a.lse[(size_t)bh * a.rows_out + orow] = (m[qb] + fast_log2(lt)) * kLn2;
+        a.lse[(size_t)bh * a.rows_out + orow] = (st.m[qb] + fast_log2(lt)) * kLn2;
         if (FULL) a.dropped[(size_t)bh * a.rows_out + orow] = dt * inv;
       }
     }
   }
+}
+
+// Workgroup id -> (KV group gi = b*Hkv + g, unit index within the group, 0 = heaviest).
+// Workgroups are dealt to the 8 XCDs round-robin; when the counts allow, each
+// KV group's units stay on a fixed subset of XCDs so its K/V stay in that L2.
+__device__ __forceinline__ void map_unit(int w, int n_groups, int per_group, int& gi, int& u) {
+  const int n = n_groups * per_group;
+  if ((n & 7) == 0 && n_groups <= 8 && (8 % n_groups) == 0) {
+    const int x = w & 7, k = w >> 3, xpg = 8 / n_groups;
+    gi = x / xpg;
+    u = k * xpg + (x - gi * xpg);
+  } else if ((n & 7) == 0 && (n_groups & 7) == 0) {
+    const int x = w & 7, k = w >> 3, gpx = n_groups >> 3;
+    gi = x + 8 * (k % gpx);
+    u = k / gpx;
+  } else {
+    gi = w % n_groups;
+    u = w / n_groups;
+  }
+}
+
+// Tile loop of the block-sparse forward.  The LDS buffers arrive as distinct
+// restrict pointers so that, once inlined, the compiler can tell a K read from
+// an in-flight V load (and the tile list from both) and waits only for the
+// buffer it reads.  Pipeline per tile t (K_t, V_t already requested):
+//   wait K_t | S_t | request K_{t+1} | softmax_t | wait V_t | PV_t | request V_{t+1}
+__device__ __attribute__((always_inline)) inline void sparse_tiles(
+    uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, const int* __restrict__ sList, int nt,
+    const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int seq_kv, int jd, int pos0,
+    float c, const bf16x8 qop[2][4], UnitState& st, int lane, int l32, int hl) {
+  if (nt > 0) {
+    const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
+    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sK, 0, 1, lane);
+    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sV, 0, 1, lane);
+  }
+  for (int t = 0; t < nt; ++t) {
+    const int j = __builtin_amdgcn_readfirstlane(sList[t]);
+    const bool more = t + 1 < nt;
+    const int jn = more ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : 0;
+    wait_vmem<8>();  // K_t landed (V_t may still be in flight)
+    f32x16 s[2][2];
+    tile_scores(sK, qop, l32, hl, s);
+    wait_lds_reads();
+    if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sK, 0, 1, lane);
+    u32x4 pk[2][2][2];
+    tile_softmax<false>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c);
+    if (more)
+      wait_vmem<8>();  // V_t landed (K_{t+1} may still be in flight)
+    else
+      wait_vmem<0>();
+    tile_pv(sV, pk, st, lane);
+    wait_lds_reads();
+    if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sV, 0, 1, lane);
+  }
+}
+
+// Block-sparse forward: one wavefront per unit, private K and V buffers.
+__global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry geo) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[kTileBytes];
+  __shared__ int sList[kMaxTopk];
+  const int lane = threadIdx.x, hl = lane >> 5, l32 = lane & 31;
+  const int G = geo.group;
+  int gi, u;
+  map_unit(blockIdx.x, geo.batch * geo.hkv, G * a.qb_count, gi, u);
+  const int i = a.qb_begin + a.qb_count - 1 - u / G;  // longest rows first
+  const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+  const int h = g * G + (u - (u / G) * G);
+  const int bh = b * geo.hq + h;
+  const int jd = (geo.q_offset + i * kBlock) / kBlock;
+  const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
+
+  const int nt = stage_tile_list(a.idx + ((size_t)bh * geo.nqb + i) * geo.topk, geo.topk, jd, sList, lane);
+  bf16x8 qop[2][4];
+  load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
+  UnitState st;
+  init_state(st);
+  wait_vmem<0>();  // Q and the index row are in; from here only tile loads use vmcnt
+  __builtin_amdgcn_wave_barrier();
+  sparse_tiles(sK, sV, sList, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd, geo.q_offset + i * kBlock,
+               geo.scale_log2, qop, st, lane, l32, hl);
+  unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
+}
+
+// Full causal counterpart with dropped mass: NW query heads of one KV group per
+// workgroup (one per wave) share every tile through a double buffer; tile t+1
+// is requested as soon as every wave has finished tile t-1.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geometry geo) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kTileBytes];
+  __shared__ int sList[NW][kMaxTopk];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = geo.group, GS = G / NW;
+  int gi, u;
+  map_unit(blockIdx.x, geo.batch * geo.hkv, GS * a.qb_count, gi, u);
+  const int i = a.qb_begin + a.qb_count - 1 - u / GS;
+  const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+  const int h = g * G + (u - (u / GS) * GS) * NW + wave;
+  const int bh = b * geo.hq + h;
+  const int jd = (geo.q_offset + i * kBlock) / kBlock;
+  const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
+  const uint16_t* kbase = a.k + kvoff;
+  const uint16_t* vbase = a.v + kvoff;
+
+  const int nsel = stage_tile_list(a.idx + ((size_t)bh * geo.nqb + i) * geo.topk, geo.topk, jd, sList[wave], lane);
+  bf16x8 qop[2][4];
+  load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
+  UnitState st;
+  init_state(st);
+  wait_vmem<0>();
+  __builtin_amdgcn_wave_barrier();
+  const float c = geo.scale_log2;
+  const int pos0 = geo.q_offset + i * kBlock;
+  const int nt = jd + 1;
+  tile_load(kbase, geo.seq_kv, sK[0], wave, NW, lane);
+  tile_load(vbase, geo.seq_kv, sV[0], wave, NW, lane);
+  int sel_ptr = 0;
+  int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
+  for (int t = 0; t < nt; ++t) {
+    wait_vmem<0>();   // this wave's share of tile t landed
+    __syncthreads();  // ... every wave's share; and every wave is done with tile t-1
+    if (t + 1 < nt) {
+      const size_t off = (size_t)(t + 1) * kBlock * kHeadDim;
+      const int nv = geo.seq_kv - (t + 1) * kBlock;
+      tile_load(kbase + off, nv, sK[(t + 1) & 1], wave, NW, lane);
+      tile_load(vbase + off, nv, sV[(t + 1) & 1], wave, NW, lane);
+    }
+    const bool selected = (nxt == t);
+    if (selected) {
+      ++sel_ptr;
+      nxt = sel_ptr < nsel ? __builtin_amdgcn_readfirstlane(sList[wave][sel_ptr]) : -1;
+    }
+    f32x16 s[2][2];
+    tile_scores(sK[t & 1], qop, l32, hl, s);
+    u32x4 pk[2][2][2];
+    tile_softmax<true>(s, st, pk, t == jd, selected, t * kBlock, pos0, l32, hl, c);
+    tile_pv(sV[t & 1], pk, st, lane);
+  }
+  unit_epilogue<true>(st, a, geo, bh, i, l32, hl);
 }
 
 }  // namespace
@@ -223,10 +459,15 @@ __global__ __launch_bounds__(64) void attn_prefill_kernel(AttnArgs a, Geometry g
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream) {
   const size_t units = (size_t)g.batch * g.hq * a.qb_count;
   if (units == 0) return hipSuccess;
-  if (full)
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
-  else
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+  if (!full) {
+    hipLaunchKernelGGL(attn_sparse_kernel, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+  } else if (g.group % 4 == 0) {
+    hipLaunchKernelGGL(attn_full_kernel<4>, dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
+  } else if (g.group % 2 == 0) {
+    hipLaunchKernelGGL(attn_full_kernel<2>, dim3((unsigned)(units / 2)), dim3(128), 0, stream, a, g);
+  } else {
+    hipLaunchKernelGGL(attn_full_kernel<1>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+  }
   return hipGetLastError();
 }
 
