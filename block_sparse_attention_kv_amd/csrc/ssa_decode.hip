@@ -1,14 +1,16 @@
 // Decode attention (gfx950): one query token per (sequence, query head) against
 // a long KV cache, over the key blocks each head selected.
 //
-// The key blocks of one (sequence, KV head) group are cut into chunks.  A
-// workgroup owns one chunk: it forms, per block, the bitmask of the group's
-// query heads that selected it, and streams every block of the chunk that any
-// head selected exactly once from HBM (the union over the group), applying it
-// to each selecting head.  Each workgroup writes one partial online-softmax
-// state (max, sum, unnormalised output) per head; a second kernel merges the
-// chunk partials.  The work is bound by HBM reads of the union of selected
-// K/V blocks.
+// One wavefront owns one (sequence, KV head, chunk of 64 key blocks).  It forms,
+// per block of the chunk, the bitmask of the group's query heads that selected
+// it, compacts the blocks any head selected (the union over the group), and
+// streams exactly those K/V blocks from HBM through a ring of LDS slots filled
+// by direct-to-LDS loads, keeping kRing-1 blocks in flight while it computes.
+// Every union block is applied to all query heads of the group at once with
+// bf16 MFMAs (16 heads per 16x16x32 tile): heads that did not select the block
+// see it masked.  Each wavefront writes one partial online-softmax state
+// (reference max, sum, unnormalised output) per head; a second kernel merges
+// the chunk partials.  The kernel is bound by HBM reads of the union blocks.
 //
 // Method: DashAttention summary, "Etapa 0" (chunk summaries cached once
 // complete, no recomputation at inference) and "Resultados Experimentales"
@@ -17,157 +19,234 @@
 // "Block-sparse attention e Receptive Field".
 #include "ssa_common.hpp"
 #include "ssa_internal.hpp"
+#include "ssa_tiles.hpp"
 
 namespace ssa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kKRow = 66;  // LDS row stride (bf16) of the key tile: 33 dwords -> one row per lane, no conflicts
+constexpr int kRing = 3;  // K/V block slots per wavefront (kRing - 1 in flight while computing)
+static_assert(kDecodeChunk == 64, "one wavefront lane per key block of the chunk");
 
-struct DecodeSmem {
-  uint32_t mask[kDecodeChunk];
-  union {
-    struct {
-      uint16_t k[kWaves][kBlock * kKRow];
-      uint16_t v[kWaves][kBlock * kHeadDim];
-      float p[kWaves][kBlock];
-    } tile;
-    float merge[kWaves][32][kPartialFloats];
-  } u;
-};
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
-template <int GMAX>
-__global__ __launch_bounds__(256) void attn_decode_partial_kernel(AttnArgs a, float* __restrict__ ws,
-                                                                  Geometry geo, int nchunks) {
-  __shared__ __attribute__((aligned(16))) DecodeSmem sm;
-  __shared__ __attribute__((aligned(16))) float sQ[GMAX][kHeadDim];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// Wait until the DMA of the block being computed landed, leaving the `later`
+// younger blocks (16 load instructions each) in flight.
+__device__ __forceinline__ void wait_block(int later) {
+  if (later >= 2)
+    wait_vmem<32>();
+  else if (later == 1)
+    wait_vmem<16>();
+  else
+    wait_vmem<0>();
+}
+
+template <int NHB>  // 16-head blocks per KV group: 1 (G <= 16) or 2 (G <= 32)
+__global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, float* __restrict__ ws,
+                                                                    Geometry geo, int nchunks) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sKV[kRing][2][kTileBytes];
+  __shared__ uint32_t sMask[kDecodeChunk];
+  __shared__ int sBlk[kDecodeChunk];
+  __shared__ uint32_t sHm[kDecodeChunk];
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, g4 = lane >> 4;
   const int bg = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - bg * nchunks;
   const int b = bg / geo.hkv, g = bg - b * geo.hkv;
   const int G = geo.group;
   const int j0 = chunk * kDecodeChunk;
   const int nj = min(kDecodeChunk, geo.nkb - j0);
+  const int head0 = b * geo.hq + g * G;  // (b, first query head of the group)
 
-  if (tid < kDecodeChunk) sm.mask[tid] = 0u;
-  for (int e = tid; e < G * kHeadDim; e += 256)
-    sQ[e >> 6][e & 63] = bf16_to_f32(a.q[(size_t)(b * geo.hq + g * G) * kHeadDim + e]);
-  __syncthreads();
-  // Which heads of the group selected each block of this chunk.
-  for (int e = tid; e < G * geo.topk; e += 256) {
+  // Heads of the group that selected each block of the chunk, then the union list.
+  sMask[lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int e = lane; e < G * geo.topk; e += 64) {
     const int hh = e / geo.topk;
-    const int j = a.idx[(size_t)(b * geo.hq + g * G) * geo.topk + e];
-    if (j >= j0 && j < j0 + nj) atomicOr(&sm.mask[j - j0], 1u << hh);
+    const int j = a.idx[(size_t)head0 * geo.topk + e];
+    if (j >= j0 && j < j0 + nj) atomicOr(&sMask[j - j0], 1u << hh);
   }
-  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint32_t my_mask = sMask[lane];
+  const bool keep = lane < nj && my_mask != 0u;
+  const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
+  const int nu = (int)__builtin_popcountll(kb);
+  if (keep) {
+    const int pos = (int)__builtin_popcountll(kb & ((1ull << lane) - 1ull));
+    sBlk[pos] = j0 + lane;
+    sHm[pos] = my_mask;
+  }
 
-  float m[GMAX], l[GMAX], o[GMAX];
+  // Q^T as the B operand: column = head 16*hb + l16, k-slots = d 32*ks + 8*g4 .. +8.
+  bf16x8 qop[NHB][2];
 #pragma unroll
-  for (int hh = 0; hh < GMAX; ++hh) {
-    m[hh] = -__builtin_inff();
-    l[hh] = 0.f;
-    o[hh] = 0.f;
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int hh = 16 * hb + l16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hh < G) v = *reinterpret_cast<const u32x4*>(a.q + (size_t)(head0 + hh) * kHeadDim + 32 * ks + 8 * g4);
+      qop[hb][ks] = as_bf16x8(v);
+    }
   }
-  const size_t kvoff = (size_t)(b * geo.hkv + g) * geo.seq_kv * kHeadDim;
-  uint16_t* sk = sm.u.tile.k[wave];
-  uint16_t* sv = sm.u.tile.v[wave];
-  float* sp = sm.u.tile.p[wave];
+  f32x4 o[NHB][4];
+  float m[NHB], l[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    m[hb] = -__builtin_inff();
+    l[hb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[hb][db][r] = 0.f;
+  }
+  wait_vmem<0>();  // Q and the index rows are in; from here only block loads use vmcnt
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const size_t kvoff = (size_t)bg * geo.seq_kv * kHeadDim;
+  const uint16_t* kbase = a.k + kvoff;
+  const uint16_t* vbase = a.v + kvoff;
+  const float c = geo.scale_log2;
   const int pos = geo.q_offset;  // absolute position of the query token
-  int rank = 0;
-  for (int jj = 0; jj < nj; ++jj) {
-    const uint32_t hm = sm.mask[jj];
-    if (hm == 0u) continue;
-    if ((rank++ & (kWaves - 1)) != wave) continue;
-    const int j = j0 + jj;
-    // Stage K (padded rows) and V (dense rows) of block j.
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c = it * 64 + lane, row = c >> 3, c8 = c & 7;
-      const int key = j * kBlock + row;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < geo.seq_kv) {
-        kv = *reinterpret_cast<const u32x4*>(a.k + kvoff + (size_t)key * kHeadDim + c8 * 8);
-        vv = *reinterpret_cast<const u32x4*>(a.v + kvoff + (size_t)key * kHeadDim + c8 * 8);
-      }
-      uint32_t* kd = reinterpret_cast<uint32_t*>(&sk[row * kKRow + c8 * 8]);
-      kd[0] = kv[0]; kd[1] = kv[1]; kd[2] = kv[2]; kd[3] = kv[3];
-      *reinterpret_cast<u32x4*>(&sv[row * kHeadDim + c8 * 8]) = vv;
+
+  for (int n = 0; n < kRing - 1 && n < nu; ++n) {
+    const int j = __builtin_amdgcn_readfirstlane(sBlk[n]);
+    tile_load(kbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][0], 0, 1, lane);
+    tile_load(vbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][1], 0, 1, lane);
+  }
+  for (int n = 0; n < nu; ++n) {
+    const int slot = n % kRing;
+    // Request block n + kRing - 1 into the slot block n - 1 used (already consumed).
+    const int nn = n + kRing - 1;
+    if (nn < nu) {
+      wait_lds_reads();
+      const int jn = __builtin_amdgcn_readfirstlane(sBlk[nn]);
+      const int sn = nn % kRing;
+      tile_load(kbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][0], 0, 1, lane);
+      tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][1], 0, 1, lane);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // This lane's key row.
-    uint32_t kr[32];
+    const int j = __builtin_amdgcn_readfirstlane(sBlk[n]);
+    const uint32_t hm = __builtin_amdgcn_readfirstlane(sHm[n]);
+    wait_block(min(kRing - 1, nu - 1 - n));
+    const uint8_t* sK = sKV[slot][0];
+    const uint8_t* sV = sKV[slot][1];
+
+    // S^T = K Q^T: rows = keys 16*mb + 4*g4 + r, column = head.
+    f32x4 s[NHB][4];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) kr[u] = reinterpret_cast<const uint32_t*>(&sk[lane * kKRow])[u];
-    const int key = j * kBlock + lane;
-    const bool visible = key <= pos && key < geo.seq_kv;
+    for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh) {
-      if (hh >= G || !((hm >> hh) & 1u)) continue;
-      float s = 0.f;
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        s = fmaf(bf16_to_f32((uint16_t)(kr[u] & 0xffffu)), sQ[hh][2 * u], s);
-        s = fmaf(bf16_to_f32((uint16_t)(kr[u] >> 16)), sQ[hh][2 * u + 1], s);
+        for (int r = 0; r < 4; ++r) s[hb][mb][r] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz(16 * mb + l16, 4 * ks + g4));
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) s[hb][mb] = mfma16(ka, qop[hb][ks], s[hb][mb]);
       }
-      const float x = visible ? s * geo.scale_log2 : -__builtin_inff();
-      const float mx = wave_max(x);
-      const float mn = fmaxf(m[hh], mx);
-      const float alpha = fast_exp2(m[hh] - mn);
-      const float p = fast_exp2(x - mn);
-      l[hh] = l[hh] * alpha + wave_sum(p);
-      m[hh] = mn;
-      sp[lane] = p;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float acc = 0.f;
-#pragma unroll 16
-      for (int t = 0; t < kBlock; ++t) acc = fmaf(sp[t], bf16_to_f32(sv[t * kHeadDim + lane]), acc);
-      o[hh] = o[hh] * alpha + acc;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    u32x4 pk[NHB][2];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int hh = 16 * hb + l16;
+      const bool sel = hh < G && ((hm >> hh) & 1u);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = j * kBlock + 16 * mb + 4 * g4 + r;
+          const bool vis = sel && key <= pos && key < geo.seq_kv;
+          const float x = vis ? s[hb][mb][r] : -__builtin_inff();
+          s[hb][mb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mt = mx * c;
+      if (!(mt <= m[hb] + kRescaleSlack)) {  // per-lane: its head's reference max moves
+        const float mn = fmaxf(m[hb], mt);
+        const float alpha = fast_exp2(m[hb] - mn);
+        m[hb] = mn;
+        l[hb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[hb][db][r] *= alpha;
+      }
+      const float nm = m[hb] == -__builtin_inff() ? 0.f : -m[hb];  // head not reached yet: p = 0
+      float rs = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int mb = 2 * ks + half;
+          const float p0 = fast_exp2(fmaf(s[hb][mb][0], c, nm));
+          const float p1 = fast_exp2(fmaf(s[hb][mb][1], c, nm));
+          const float p2 = fast_exp2(fmaf(s[hb][mb][2], c, nm));
+          const float p3 = fast_exp2(fmaf(s[hb][mb][3], c, nm));
+          rs += (p0 + p1) + (p2 + p3);
+          pk[hb][ks][2 * half] = pack_bf16x2(p0, p1);
+          pk[hb][ks][2 * half + 1] = pack_bf16x2(p2, p3);
+        }
+      }
+      l[hb] += rs;
+    }
+    // O^T += V^T P^T: 32-key step ks, lane group g4 holds in k-slot t the key
+    // 32*ks + 4*g4 + t (t < 4) or 32*ks + 16 + 4*g4 + (t - 4) -- the keys of its
+    // S^T registers; V^T for d block db comes from two transposing reads.
+    const int tq = l16 >> 2, qq = l16 & 3;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint32_t w[4];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int row = 32 * ks + 16 * rr + 4 * g4 + tq;
+          const int chunkq = 2 * db + (qq >> 1);
+          const uint32_t off = swz(row, chunkq) + 8 * (qq & 1);
+          const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)to_lds((void*)(sV + off)));
+          const u32x2 tw = __builtin_bit_cast(u32x2, t);
+          w[2 * rr] = tw[0];
+          w[2 * rr + 1] = tw[1];
+        }
+        u32x4 va;
+        va[0] = w[0]; va[1] = w[1]; va[2] = w[2]; va[3] = w[3];
+        const bf16x8 vop = as_bf16x8(va);
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) o[hb][db] = mfma16(vop, as_bf16x8(pk[hb][ks]), o[hb][db]);
+      }
+    }
   }
 
-  // Merge the waves' states per head, then write this chunk's partials.
-  __syncthreads();
+  // Partial state per head: reference max (log2 units), sum, unnormalised output.
 #pragma unroll
-  for (int hh = 0; hh < GMAX; ++hh) {
-    if (hh >= G) continue;
-    sm.u.merge[wave][hh][2 + lane] = o[hh];
-    if (lane == 0) {
-      sm.u.merge[wave][hh][0] = m[hh];
-      sm.u.merge[wave][hh][1] = l[hh];
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < G * kHeadDim; e += 256) {
-    const int hh = e >> 6, d = e & 63;
-    float M = -__builtin_inff();
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int hh = 16 * hb + l16;
+    float lt = l[hb] + __shfl_xor(l[hb], 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (hh < G) {
+      float* part = ws + ((size_t)(head0 + hh) * nchunks + chunk) * kPartialFloats;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge[w][hh][0]);
-    float L = 0.f, O = 0.f;
-    if (M != -__builtin_inff()) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.u.merge[w][hh][0];
-        if (mw == -__builtin_inff()) continue;
-        const float f = fast_exp2(mw - M);
-        L += sm.u.merge[w][hh][1] * f;
-        O += sm.u.merge[w][hh][2 + d] * f;
+      for (int db = 0; db < 4; ++db) {
+        f32x4 v = o[hb][db];
+        *reinterpret_cast<f32x4*>(part + 2 + 16 * db + 4 * g4) = v;
       }
-    }
-    float* part = ws + ((size_t)(b * geo.hq + g * G + hh) * nchunks + chunk) * kPartialFloats;
-    part[2 + d] = O;
-    if (d == 0) {
-      part[0] = M;
-      part[1] = L;
+      if (g4 == 0) {
+        part[0] = m[hb];
+        part[1] = lt;
+      }
     }
   }
 }
@@ -202,19 +281,12 @@ hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometr
   const int nchunks = decode_chunks(g.nkb);
   const size_t nwg = (size_t)g.batch * g.hkv * nchunks;
   if (nwg == 0) return hipSuccess;
-  const dim3 grid((unsigned)nwg), block(256);
-  if (g.group <= 1)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<1>, grid, block, 0, stream, a, workspace, g, nchunks);
-  else if (g.group <= 2)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<2>, grid, block, 0, stream, a, workspace, g, nchunks);
-  else if (g.group <= 4)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<4>, grid, block, 0, stream, a, workspace, g, nchunks);
-  else if (g.group <= 8)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<8>, grid, block, 0, stream, a, workspace, g, nchunks);
-  else if (g.group <= 16)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<16>, grid, block, 0, stream, a, workspace, g, nchunks);
+  if (g.group <= 16)
+    hipLaunchKernelGGL(attn_decode_partial_kernel<1>, dim3((unsigned)nwg), dim3(64), 0, stream, a, workspace, g,
+                       nchunks);
   else if (g.group <= 32)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<32>, grid, block, 0, stream, a, workspace, g, nchunks);
+    hipLaunchKernelGGL(attn_decode_partial_kernel<2>, dim3((unsigned)nwg), dim3(64), 0, stream, a, workspace, g,
+                       nchunks);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();

@@ -36,7 +36,7 @@ struct AttnArgs {
 // Decode split: key blocks of one (batch, KV head) group are cut into chunks
 // of kDecodeChunk blocks; each chunk writes one partial (m, l, o[64]) per query
 // head, merged afterwards.
-constexpr int kDecodeChunk = 32;
+constexpr int kDecodeChunk = 64;
 constexpr int kPartialFloats = 2 + 64;
 
 inline int decode_chunks(int nkb) { return (nkb + kDecodeChunk - 1) / kDecodeChunk; }

@@ -1,0 +1,109 @@
+// LDS tile helpers shared by the attention kernels (gfx950): 64x64 bf16 tiles
+// stored as 64 rows x 128 B with 16-byte chunks XOR-swizzled by row, filled by
+// direct-to-LDS loads, and the explicit waits that order those loads.
+#pragma once
+
+#include "ssa_common.hpp"
+
+namespace ssa {
+
+constexpr int kTileBytes = kBlock * kHeadDim * 2;  // 8 KB: 64 rows x 128 B
+constexpr float kRescaleSlack = 8.f;               // log2 headroom before the reference max moves
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_cvoid;
+
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.
+__device__ __forceinline__ uint32_t swz(int row, int chunk) {
+  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+}
+
+__device__ __forceinline__ lds_void* to_lds(void* p) { return (lds_void*)p; }
+
+// The direct-to-LDS loads are not ordered against later LDS reads by the
+// compiler, so the pipeline waits explicitly: vmcnt(N) = at most the N most
+// recent vector-memory instructions still in flight (in-order completion for
+// loads).  The empty asm and scheduling barriers keep every LDS access on its
+// side of the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// All LDS reads of this wave have returned (before a DMA overwrites their buffer).
+__device__ __forceinline__ void wait_lds_reads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Compact this unit's index list into LDS: the entries before the first -1
+// that name a causal block (j <= jd), in list order.  Returns their count.
+// Whole-wave operation; `lst` has room for kMaxTopk entries.
+__device__ __forceinline__ int stage_tile_list(const int32_t* __restrict__ irow, int topk, int jd, int* lst,
+                                               int lane) {
+  int first_neg = topk;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const int j = e < topk ? irow[e] : 0;
+    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < topk && j < 0);
+    if (neg != 0ull && first_neg == topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
+  }
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const int j = e < topk ? irow[e] : -1;
+    const bool keep = e < first_neg && j >= 0 && j <= jd;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+    if (keep) lst[n + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = j;
+    n += (int)__builtin_popcountll(m);
+  }
+  return n;
+}
+
+// One direct-to-LDS load: every lane fetches the 16 bytes at gtile + voff and
+// the wave's 1 KB lands at LDS byte address lds_base + 16 * lane.  Issued from
+// inline asm so the compiler does not track it; each use is ordered by the
+// explicit waits of the pipeline (it has no register outputs: the address
+// registers are read at issue).
+__device__ __forceinline__ void dma_1k(const uint16_t* gtile, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gtile), "s"(lds_base)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
+}
+
+// Request slices first, first+step, ... of the eight 1 KB slices of one tile
+// (slice c = rows 8c..8c+7), storing chunk q of row r at swz(r, q).  Rows at or
+// past `nvalid` re-read row 0 of the tile (always present); their contents
+// never reach an output (causal mask / unwritten rows).
+__device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds,
+                                          int first, int step, int lane) {
+  const uint32_t base = lds_addr(lds);
+  for (int c = first; c < 8; c += step) {
+    const int row = 8 * c + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    const uint32_t voff = (uint32_t)((row < nvalid ? row * kHeadDim : 0) + chunk * 8) * 2u;
+    dma_1k(gtile, voff, __builtin_amdgcn_readfirstlane(base + c * 1024));
+  }
+}
+
+
+}  // namespace ssa

@@ -26,9 +26,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
 KERNEL_SOURCES = {
-    "full_attn": ["ssa_attn.hip", "ssa_common.hpp", "ssa_internal.hpp"],
-    "sparse_attn": ["ssa_attn.hip", "ssa_common.hpp", "ssa_internal.hpp"],
-    "decode_attn": ["ssa_decode.hip", "ssa_common.hpp", "ssa_internal.hpp"],
+    "full_attn": ["ssa_attn.hip", "ssa_tiles.hpp", "ssa_common.hpp", "ssa_internal.hpp"],
+    "sparse_attn": ["ssa_attn.hip", "ssa_tiles.hpp", "ssa_common.hpp", "ssa_internal.hpp"],
+    "decode_attn": ["ssa_decode.hip", "ssa_tiles.hpp", "ssa_common.hpp", "ssa_internal.hpp"],
 }
 # calibration copy: bench.py --counter-pass copies this many bytes (read + write) per dispatch
 COPY_BYTES = 512 * 1024 * 1024

@@ -94,7 +94,7 @@ def test_pointer_validation(lib):
 def test_decode_workspace(lib):
     sh = good_shape(batch=64, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=32768, q_offset=32767, topk=17)
     need = lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_SPARSE_FWD)
-    assert need == 64 * 32 * 16 * 66 * 4       # 16 chunks of 32 key blocks, (max, sum, o[64]) each
+    assert need == 64 * 32 * 8 * 66 * 4        # 8 chunks of 64 key blocks, (max, sum, o[64]) each
     assert lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_FULL_FWD) == 0
     assert lib.ssa_workspace_bytes(ctypes.byref(good_shape()), ssa.SSA_OP_SPARSE_FWD) == 0
     assert lib.ssa_workspace_bytes(ctypes.byref(good_shape(head_dim=8)), ssa.SSA_OP_SPARSE_FWD) == 2**64 - 1
