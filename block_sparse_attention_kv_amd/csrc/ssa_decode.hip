@@ -24,7 +24,8 @@
 namespace ssa {
 namespace {
 
-constexpr int kRing = 3;  // K/V block slots per wavefront (kRing - 1 in flight while computing)
+constexpr int kRing = 2;  // K/V block slots per wavefront (kRing - 1 in flight while computing);
+                          // 2 keeps four wavefronts resident per CU
 static_assert(kDecodeChunk == 64, "one wavefront lane per key block of the chunk");
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const uint16_t* __re
                                                             const float* __restrict__ ksum,
                                                             float* __restrict__ scores,
                                                             Geometry geo) {
-  __shared__ double sQ[kMaxGroupScores][kHeadDim];
+  extern __shared__ float sQ[];  // [G][kHeadDim]: the group's query rows (bf16 values, exact in fp32)
   __shared__ float sKb[kScoreKTile * kKbStride];
   const int tid = threadIdx.x;
   const int npass = (geo.nkb + kScoreKTile - 1) / kScoreKTile;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const uint16_t* __re
   const int G = geo.group;
   const int nj = min(kScoreKTile, geo.nkb - jc);
   const uint16_t* qg = q + (size_t)(b * geo.hq + g * G) * kHeadDim;  // seq_q == 1
-  for (int e = tid; e < G * kHeadDim; e += 256) sQ[e >> 6][e & 63] = (double)bf16_to_f32(qg[e]);
+  for (int e = tid; e < G * kHeadDim; e += 256) sQ[e] = bf16_to_f32(qg[e]);
   const float* kb = ksum + ((size_t)bg * geo.nkb + jc) * kHeadDim;
   for (int e = tid; e < nj * 16; e += 256) {
     const int jj = e >> 4, c4 = e & 15;
@@ -170,7 +170,8 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const uint16_t* __re
     } else {
       double acc = 0.0;
 #pragma unroll 16
-      for (int d = 0; d < kHeadDim; ++d) acc = fma(sQ[hh][d], (double)sKb[jj * kKbStride + d], acc);
+      for (int d = 0; d < kHeadDim; ++d)
+        acc = fma((double)sQ[hh * kHeadDim + d], (double)sKb[jj * kKbStride + d], acc);
       out = (float)(scale * acc);
     }
     scores[(size_t)(b * geo.hq + g * G + hh) * geo.nkb + j] = out;
@@ -202,8 +203,8 @@ hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float
   if (g.group > kMaxGroupScores) return hipErrorInvalidValue;
   const size_t nwg = (size_t)g.batch * g.hkv * ((g.nkb + kScoreKTile - 1) / kScoreKTile);
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_scores_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, q,
-                     k_summary, scores, g);
+  hipLaunchKernelGGL(decode_scores_kernel, dim3((unsigned)nwg), dim3(256),
+                     (size_t)g.group * kHeadDim * sizeof(float), stream, q, k_summary, scores, g);
   return hipGetLastError();
 }
 

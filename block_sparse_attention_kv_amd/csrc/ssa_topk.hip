@@ -1,11 +1,14 @@
 // Top-k block selection with the diagonal (most recent) block always kept (gfx950).
 //
 // One wavefront per (b, h, query block).  Each earlier block j < jd gets a
-// unique 64-bit key (orderable fp32 score, then ~j), so "higher score, then
-// lower index" is plain unsigned order.  The (k-1)-th largest key is found by
-// k-1 rounds of "largest key below the previous one" (a wave max-reduction per
-// round; no state besides the previous key), then the kept blocks are
-// compacted in ascending order with a ballot scan and the diagonal appended.
+// 32-bit key that orders scores (larger score -> larger key; -0 == +0; NaN
+// below -inf; empty slots 0).  The (k-1)-th largest key T is found by a
+// most-significant-bit-first binary search: each of the 32 steps counts the
+// candidates at or above a trial value with compares whose results are
+// wave-wide bitmasks (popcounted on the scalar unit), so no data moves between
+// lanes.  Blocks above T are kept, plus the lowest-index blocks equal to T
+// until k-1 are kept ("higher score, then lower index"); a ballot scan writes
+// them in ascending order and the diagonal goes last.
 // Method: SSA guide (mauroscia.it), "Block-sparse attention e Receptive
 // Field" (fixed top-k block budget); DashAttention summary, "Etapa 2"
 // (near-diagonal chunk kept by its own branch).
@@ -16,15 +19,90 @@ namespace ssa {
 namespace {
 
 constexpr int kRowsPerWg = 4;
-constexpr int kRegCands = 8;  // candidates held in registers per lane (jd <= 512)
 
-__device__ __forceinline__ uint64_t cand_key(float s, int j) {
-  return ((uint64_t)orderable_score(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+// 0 = empty slot; NaN = 1 (below every number); numbers keep their order above.
+__device__ __forceinline__ uint32_t cand_key(float s) {
+  const uint32_t o = orderable_score(s);
+  return o == 0u ? 1u : o;
 }
 
+__device__ __forceinline__ int wave_count(bool pred) {
+  return (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(pred));
+}
+
+// Keys of candidates j = lane + 64*c, c < NPER, held in registers.
+template <int NPER>
+__device__ __forceinline__ void select_rows(const float* __restrict__ srow, int32_t* __restrict__ orow, int jd,
+                                            int need, int lane) {
+  uint32_t key[NPER];
+#pragma unroll
+  for (int c = 0; c < NPER; ++c) {
+    const int j = lane + 64 * c;
+    key[c] = j < jd ? cand_key(srow[j]) : 0u;
+  }
+  uint32_t t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t trial = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < NPER; ++c) cnt += wave_count(key[c] >= trial);
+    if (cnt >= need) t = trial;
+  }
+  int greater = 0;
+#pragma unroll
+  for (int c = 0; c < NPER; ++c) greater += wave_count(key[c] > t);
+  const int ties = need - greater;  // blocks equal to t to keep, lowest index first
+  int count = 0, tie_seen = 0;
+#pragma unroll
+  for (int c = 0; c < NPER; ++c) {
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const uint64_t tm = __builtin_amdgcn_ballot_w64(key[c] == t);
+    const int tie_rank = tie_seen + (int)__builtin_popcountll(tm & lt);
+    const bool keep = key[c] > t || (key[c] == t && tie_rank < ties);
+    const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
+    if (keep) orow[count + (int)__builtin_popcountll(km & lt)] = lane + 64 * c;
+    count += (int)__builtin_popcountll(km);
+    tie_seen += (int)__builtin_popcountll(tm);
+  }
+}
+
+// Same selection for long rows: keys recomputed from the (cached) score row.
+__device__ __forceinline__ void select_rows_long(const float* __restrict__ srow, int32_t* __restrict__ orow, int jd,
+                                                 int need, int lane) {
+  uint32_t t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t trial = t | (1u << bit);
+    int cnt = 0;
+    for (int jb = 0; jb < jd; jb += 64) {
+      const int j = jb + lane;
+      cnt += wave_count(j < jd && cand_key(srow[j]) >= trial);
+    }
+    if (cnt >= need) t = trial;
+  }
+  int greater = 0;
+  for (int jb = 0; jb < jd; jb += 64) {
+    const int j = jb + lane;
+    greater += wave_count(j < jd && cand_key(srow[j]) > t);
+  }
+  const int ties = need - greater;
+  int count = 0, tie_seen = 0;
+  for (int jb = 0; jb < jd; jb += 64) {
+    const int j = jb + lane;
+    const uint32_t k = j < jd ? cand_key(srow[j]) : 0u;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const uint64_t tm = __builtin_amdgcn_ballot_w64(k == t && j < jd);
+    const int tie_rank = tie_seen + (int)__builtin_popcountll(tm & lt);
+    const bool keep = j < jd && (k > t || (k == t && tie_rank < ties));
+    const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
+    if (keep) orow[count + (int)__builtin_popcountll(km & lt)] = j;
+    count += (int)__builtin_popcountll(km);
+    tie_seen += (int)__builtin_popcountll(tm);
+  }
+}
+
+template <int NPER>
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
-                                                          int32_t* __restrict__ idx, Geometry geo,
-                                                          int nrows) {
+                                                          int32_t* __restrict__ idx, Geometry geo, int nrows) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerWg + wave;
   if (row >= nrows) return;  // whole wavefront leaves together; no block barriers below
@@ -33,47 +111,14 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
   const int k = geo.topk;
   const float* srow = scores + (size_t)row * geo.nkb;
   int32_t* orow = idx + (size_t)row * k;
-
   if (jd + 1 <= k) {
     for (int e = lane; e < k; e += 64) orow[e] = e <= jd ? e : -1;
     return;
   }
-
-  uint64_t thresh = ~0ull;  // after the loop: the (k-1)-th largest key
-  if (jd <= kRegCands * 64) {
-    uint64_t key[kRegCands];
-#pragma unroll
-    for (int c = 0; c < kRegCands; ++c) {
-      const int j = lane + 64 * c;
-      key[c] = j < jd ? cand_key(srow[j], j) : 0ull;
-    }
-    for (int it = 0; it < k - 1; ++it) {
-      uint64_t best = 0ull;
-#pragma unroll
-      for (int c = 0; c < kRegCands; ++c) best = (key[c] < thresh && key[c] > best) ? key[c] : best;
-      thresh = wave_max_u64(best);
-    }
-  } else {
-    for (int it = 0; it < k - 1; ++it) {
-      uint64_t best = 0ull;
-      for (int j = lane; j < jd; j += 64) {
-        const uint64_t kk = cand_key(srow[j], j);
-        best = (kk < thresh && kk > best) ? kk : best;
-      }
-      thresh = wave_max_u64(best);
-    }
-  }
-
-  // Ascending compaction of {j < jd : key(j) >= thresh}; exactly k-1 of them.
-  int count = 0;
-  for (int jb = 0; jb < jd; jb += 64) {
-    const int j = jb + lane;
-    const bool keep = j < jd && cand_key(srow[j], j) >= thresh;
-    const uint64_t m = __ballot(keep);
-    const int pos = count + (int)__popcll(m & ((1ull << lane) - 1ull));
-    if (keep) orow[pos] = j;
-    count += (int)__popcll(m);
-  }
+  if (NPER > 0)
+    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane);
+  else
+    select_rows_long(srow, orow, jd, k - 1, lane);
   if (lane == 0) orow[k - 1] = jd;
 }
 
@@ -83,9 +128,14 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry&
                               hipStream_t stream) {
   const size_t nrows = (size_t)g.batch * g.hq * g.nqb;
   if (nrows == 0) return hipSuccess;
-  const size_t nwg = (nrows + kRowsPerWg - 1) / kRowsPerWg;
-  hipLaunchKernelGGL(select_topk_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, scores, idx,
-                     g, (int)nrows);
+  const dim3 grid((unsigned)((nrows + kRowsPerWg - 1) / kRowsPerWg)), block(256);
+  const int maxjd = (g.q_offset + (g.nqb - 1) * kBlock) / kBlock;  // largest candidate count
+  if (maxjd <= 128)
+    hipLaunchKernelGGL(select_topk_kernel<2>, grid, block, 0, stream, scores, idx, g, (int)nrows);
+  else if (maxjd <= 512)
+    hipLaunchKernelGGL(select_topk_kernel<8>, grid, block, 0, stream, scores, idx, g, (int)nrows);
+  else
+    hipLaunchKernelGGL(select_topk_kernel<0>, grid, block, 0, stream, scores, idx, g, (int)nrows);
   return hipGetLastError();
 }
 
