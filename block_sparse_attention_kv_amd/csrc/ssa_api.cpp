@@ -169,7 +169,10 @@ ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, 
   if (g.seq_q == 1) {
     if (g.group > 32)
       return fail(SSA_ERR_UNSUPPORTED, "%s: decode with more than 32 query heads per KV head", fn);
-    const size_t need = ssa::decode_workspace_bytes(g.batch, g.hq, g.nkb);
+    if ((int64_t)g.group * g.topk > ssa::kDecodeMaxList || g.nkb > ssa::kDecodeMaxBlocks)
+      return fail(SSA_ERR_UNSUPPORTED, "%s: decode needs (query heads per KV head) x topk <= %d and <= %d key blocks",
+                  fn, ssa::kDecodeMaxList, ssa::kDecodeMaxBlocks);
+    const size_t need = ssa::decode_workspace_bytes(g.batch, g.hq, g.hkv);
     if (workspace_bytes < need)
       return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
     CHECK_PTR(workspace, 16, fn);
@@ -224,7 +227,7 @@ size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {
   bool empty;
   if (make_geometry(shape, &g, &empty, "ssa_workspace_bytes") != SSA_OK) return SIZE_MAX;
   if (empty) return 0;
-  if (op == SSA_OP_SPARSE_FWD && g.seq_q == 1) return ssa::decode_workspace_bytes(g.batch, g.hq, g.nkb);
+  if (op == SSA_OP_SPARSE_FWD && g.seq_q == 1) return ssa::decode_workspace_bytes(g.batch, g.hq, g.hkv);
   return 0;
 }
 

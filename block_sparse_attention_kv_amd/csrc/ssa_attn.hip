@@ -244,10 +244,12 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, const int* __restrict__ sList, int nt,
     const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int seq_kv, int jd, int pos0,
     float c, const bf16x8 qop[2][4], UnitState& st, int lane, int l32, int hl) {
+  TileOffsets toff;
+  toff.init(lane);
   if (nt > 0) {
     const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
-    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sK, 0, 1, lane);
-    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sV, 0, 1, lane);
+    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sK, 0, 1, lane, toff);
+    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sV, 0, 1, lane, toff);
   }
   for (int t = 0; t < nt; ++t) {
     const int j = __builtin_amdgcn_readfirstlane(sList[t]);
@@ -257,7 +259,7 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     f32x16 s[2][2];
     tile_scores(sK, qop, l32, hl, s);
     wait_lds_reads();
-    if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sK, 0, 1, lane);
+    if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sK, 0, 1, lane, toff);
     u32x4 pk[2][2][2];
     tile_softmax<false>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c);
     if (more)
@@ -266,7 +268,7 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
       wait_vmem<0>();
     tile_pv(sV, pk, st, lane);
     wait_lds_reads();
-    if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sV, 0, 1, lane);
+    if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sV, 0, 1, lane, toff);
   }
 }
 
@@ -330,8 +332,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
   const float c = geo.scale_log2;
   const int pos0 = geo.q_offset + i * kBlock;
   const int nt = jd + 1;
-  tile_load(kbase, geo.seq_kv, sK[0], wave, NW, lane);
-  tile_load(vbase, geo.seq_kv, sV[0], wave, NW, lane);
+  TileOffsets toff;
+  toff.init(lane);
+  tile_load(kbase, geo.seq_kv, sK[0], wave, NW, lane, toff);
+  tile_load(vbase, geo.seq_kv, sV[0], wave, NW, lane, toff);
   int sel_ptr = 0;
   int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
   for (int t = 0; t < nt; ++t) {
@@ -340,8 +344,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
     if (t + 1 < nt) {
       const size_t off = (size_t)(t + 1) * kBlock * kHeadDim;
       const int nv = geo.seq_kv - (t + 1) * kBlock;
-      tile_load(kbase + off, nv, sK[(t + 1) & 1], wave, NW, lane);
-      tile_load(vbase + off, nv, sV[(t + 1) & 1], wave, NW, lane);
+      tile_load(kbase + off, nv, sK[(t + 1) & 1], wave, NW, lane, toff);
+      tile_load(vbase + off, nv, sV[(t + 1) & 1], wave, NW, lane, toff);
     }
     const bool selected = (nxt == t);
     if (selected) {

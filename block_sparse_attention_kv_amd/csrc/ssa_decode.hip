@@ -1,16 +1,18 @@
 // Decode attention (gfx950): one query token per (sequence, query head) against
 // a long KV cache, over the key blocks each head selected.
 //
-// One wavefront owns one (sequence, KV head, chunk of 64 key blocks).  It forms,
-// per block of the chunk, the bitmask of the group's query heads that selected
-// it, compacts the blocks any head selected (the union over the group), and
-// streams exactly those K/V blocks from HBM through a ring of LDS slots filled
-// by direct-to-LDS loads, keeping kRing-1 blocks in flight while it computes.
+// The wavefronts of one (sequence, KV head) group each rebuild, in LDS, the
+// ascending union of the key blocks the group's query heads selected (a
+// bitmap over the blocks, a popcount prefix for ranks) with the bitmask of the
+// heads that chose each, and take an equal slice of it, so the work is
+// balanced whatever the selection.  A wavefront streams exactly its union
+// blocks from HBM through a ring of LDS slots filled by direct-to-LDS loads,
+// keeping kRing-1 blocks in flight while it computes.
 // Every union block is applied to all query heads of the group at once with
 // bf16 MFMAs (16 heads per 16x16x32 tile): heads that did not select the block
 // see it masked.  Each wavefront writes one partial online-softmax state
 // (reference max, sum, unnormalised output) per head; a second kernel merges
-// the chunk partials.  The kernel is bound by HBM reads of the union blocks.
+// the slice partials.  The kernel is bound by HBM reads of the union blocks.
 //
 // Method: DashAttention summary, "Etapa 0" (chunk summaries cached once
 // complete, no recomputation at inference) and "Resultados Experimentales"
@@ -24,9 +26,8 @@
 namespace ssa {
 namespace {
 
-constexpr int kRing = 2;  // K/V block slots per wavefront (kRing - 1 in flight while computing);
-                          // 2 keeps four wavefronts resident per CU
-static_assert(kDecodeChunk == 64, "one wavefront lane per key block of the chunk");
+constexpr int kRing = kDecodeRing;  // K/V block slots per wavefront (kRing - 1 in flight while computing)
+static_assert(kRing >= 2 && (kRing - 1) * 16 <= 63, "in-flight block loads must fit the vmcnt counter");
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -35,7 +36,9 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // Wait until the DMA of the block being computed landed, leaving the `later`
 // younger blocks (16 load instructions each) in flight.
 __device__ __forceinline__ void wait_block(int later) {
-  if (later >= 2)
+  if (later >= 3)
+    wait_vmem<48>();
+  else if (later == 2)
     wait_vmem<32>();
   else if (later == 1)
     wait_vmem<16>();
@@ -43,45 +46,67 @@ __device__ __forceinline__ void wait_block(int later) {
     wait_vmem<0>();
 }
 
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int NHB>  // 16-head blocks per KV group: 1 (G <= 16) or 2 (G <= 32)
 __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, float* __restrict__ ws,
-                                                                    Geometry geo, int nchunks) {
+                                                                    Geometry geo, int npieces) {
   __shared__ __attribute__((aligned(1024))) uint8_t sKV[kRing][2][kTileBytes];
-  __shared__ uint32_t sMask[kDecodeChunk];
-  __shared__ int sBlk[kDecodeChunk];
-  __shared__ uint32_t sHm[kDecodeChunk];
+  extern __shared__ uint32_t sDyn[];  // bitmap[nw] | prefix[nw] | list[cap] | heads[cap]
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int bg = blockIdx.x / nchunks;
-  const int chunk = blockIdx.x - bg * nchunks;
+  const int bg = blockIdx.x / npieces;
+  const int piece = blockIdx.x - bg * npieces;
   const int b = bg / geo.hkv, g = bg - b * geo.hkv;
   const int G = geo.group;
-  const int j0 = chunk * kDecodeChunk;
-  const int nj = min(kDecodeChunk, geo.nkb - j0);
   const int head0 = b * geo.hq + g * G;  // (b, first query head of the group)
+  const int nw = (geo.nkb + 31) >> 5;
+  const int cap = G * geo.topk;
+  uint32_t* bitmap = sDyn;
+  int* prefix = reinterpret_cast<int*>(sDyn + nw);
+  int* sBlk = reinterpret_cast<int*>(sDyn + 2 * nw);
+  uint32_t* sHm = sDyn + 2 * nw + cap;
+  const int32_t* gidx = a.idx + (size_t)head0 * geo.topk;
 
-  // Heads of the group that selected each block of the chunk, then the union list.
-  sMask[lane] = 0u;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (int e = lane; e < G * geo.topk; e += 64) {
-    const int hh = e / geo.topk;
-    const int j = a.idx[(size_t)head0 * geo.topk + e];
-    if (j >= j0 && j < j0 + nj) atomicOr(&sMask[j - j0], 1u << hh);
+  // Union of the group's selected blocks: bitmap, ranks, ascending list and
+  // the heads that selected each listed block.
+  for (int w = lane; w < nw; w += 64) bitmap[w] = 0u;
+  for (int e = lane; e < cap; e += 64) sHm[e] = 0u;
+  wave_sync_lds();
+  for (int e = lane; e < cap; e += 64) {
+    const int j = gidx[e];
+    if (j >= 0 && j < geo.nkb) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint32_t my_mask = sMask[lane];
-  const bool keep = lane < nj && my_mask != 0u;
-  const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
-  const int nu = (int)__builtin_popcountll(kb);
-  if (keep) {
-    const int pos = (int)__builtin_popcountll(kb & ((1ull << lane) - 1ull));
-    sBlk[pos] = j0 + lane;
-    sHm[pos] = my_mask;
+  wave_sync_lds();
+  int nu = 0;
+  for (int w0 = 0; w0 < nw; w0 += 64) {
+    const int w = w0 + lane;
+    const int cnt = w < nw ? __builtin_popcount(bitmap[w]) : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (w < nw) prefix[w] = nu + incl - cnt;
+    nu += __shfl(incl, 63, 64);
   }
+  wave_sync_lds();
+  for (int e = lane; e < cap; e += 64) {
+    const int j = gidx[e];
+    if (j >= 0 && j < geo.nkb) {
+      const int r = prefix[j >> 5] + __builtin_popcount(bitmap[j >> 5] & ((1u << (j & 31)) - 1u));
+      sBlk[r] = j;
+      atomicOr(&sHm[r], 1u << (e / geo.topk));
+    }
+  }
+  wave_sync_lds();
+  const int u0 = (int)(((int64_t)nu * piece) / npieces);
+  const int u1 = (int)(((int64_t)nu * (piece + 1)) / npieces);
 
   // Q^T as the B operand: column = head 16*hb + l16, k-slots = d 32*ks + 8*g4 .. +8.
   bf16x8 qop[NHB][2];
@@ -117,25 +142,28 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   const float c = geo.scale_log2;
   const int pos = geo.q_offset;  // absolute position of the query token
 
-  for (int n = 0; n < kRing - 1 && n < nu; ++n) {
-    const int j = __builtin_amdgcn_readfirstlane(sBlk[n]);
-    tile_load(kbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][0], 0, 1, lane);
-    tile_load(vbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][1], 0, 1, lane);
+  TileOffsets toff;
+  toff.init(lane);
+  const int nmine = u1 - u0;
+  for (int n = 0; n < kRing - 1 && n < nmine; ++n) {
+    const int j = __builtin_amdgcn_readfirstlane(sBlk[u0 + n]);
+    tile_load(kbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][0], 0, 1, lane, toff);
+    tile_load(vbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][1], 0, 1, lane, toff);
   }
-  for (int n = 0; n < nu; ++n) {
+  for (int n = 0; n < nmine; ++n) {
     const int slot = n % kRing;
     // Request block n + kRing - 1 into the slot block n - 1 used (already consumed).
     const int nn = n + kRing - 1;
-    if (nn < nu) {
+    if (nn < nmine) {
       wait_lds_reads();
-      const int jn = __builtin_amdgcn_readfirstlane(sBlk[nn]);
+      const int jn = __builtin_amdgcn_readfirstlane(sBlk[u0 + nn]);
       const int sn = nn % kRing;
-      tile_load(kbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][0], 0, 1, lane);
-      tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][1], 0, 1, lane);
+      tile_load(kbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][0], 0, 1, lane, toff);
+      tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][1], 0, 1, lane, toff);
     }
-    const int j = __builtin_amdgcn_readfirstlane(sBlk[n]);
-    const uint32_t hm = __builtin_amdgcn_readfirstlane(sHm[n]);
-    wait_block(min(kRing - 1, nu - 1 - n));
+    const int j = __builtin_amdgcn_readfirstlane(sBlk[u0 + n]);
+    const uint32_t hm = __builtin_amdgcn_readfirstlane(sHm[u0 + n]);
+    wait_block(min(kRing - 1, nmine - 1 - n));
     const uint8_t* sK = sKV[slot][0];
     const uint8_t* sV = sKV[slot][1];
 
@@ -157,21 +185,28 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
       }
     }
     u32x4 pk[NHB][2];
+    // Only the block holding the query position (or the cache end) needs a
+    // per-key mask; a head that did not select the block gets p = 0 through
+    // an exponent offset of -inf.
+    const bool edge = j * kBlock + kBlock - 1 > pos || j * kBlock + kBlock > geo.seq_kv;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const int hh = 16 * hb + l16;
       const bool sel = hh < G && ((hm >> hh) & 1u);
-      float mx = -__builtin_inff();
+      if (edge) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = j * kBlock + 16 * mb + 4 * g4 + r;
-          const bool vis = sel && key <= pos && key < geo.seq_kv;
-          const float x = vis ? s[hb][mb][r] : -__builtin_inff();
-          s[hb][mb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int key = j * kBlock + 16 * mb + 4 * g4 + r;
+            if (key > pos || key >= geo.seq_kv) s[hb][mb][r] = -__builtin_inff();
+          }
+      }
+      float mx = fmaxf(fmaxf(s[hb][0][0], s[hb][0][1]), fmaxf(s[hb][0][2], s[hb][0][3]));
+#pragma unroll
+      for (int mb = 1; mb < 4; ++mb)
+        mx = fmaxf(fmaxf(mx, fmaxf(s[hb][mb][0], s[hb][mb][1])), fmaxf(s[hb][mb][2], s[hb][mb][3]));
+      mx = sel ? mx : -__builtin_inff();
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mt = mx * c;
@@ -185,7 +220,8 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[hb][db][r] *= alpha;
       }
-      const float nm = m[hb] == -__builtin_inff() ? 0.f : -m[hb];  // head not reached yet: p = 0
+      // unselected head: p = exp2(-inf) = 0; selected head: exponent relative to its reference max
+      const float nm = !sel ? -__builtin_inff() : -m[hb];
       float rs = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -238,7 +274,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
     float lt = l[hb] + __shfl_xor(l[hb], 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     if (hh < G) {
-      float* part = ws + ((size_t)(head0 + hh) * nchunks + chunk) * kPartialFloats;
+      float* part = ws + ((size_t)(head0 + hh) * npieces + piece) * kPartialFloats;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         f32x4 v = o[hb][db];
@@ -252,17 +288,17 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   }
 }
 
-// Merge the chunk partials of one (sequence, head): lane = output column.
+// Merge the slice partials of one (sequence, head): lane = output column.
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float* __restrict__ ws,
                                                                  uint16_t* __restrict__ out,
-                                                                 float* __restrict__ lse, int nchunks) {
+                                                                 float* __restrict__ lse, int npieces) {
   const int lane = threadIdx.x;
   const size_t bh = blockIdx.x;
-  const float* part = ws + bh * nchunks * kPartialFloats;
+  const float* part = ws + bh * npieces * kPartialFloats;
   float M = -__builtin_inff();
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part[c * kPartialFloats]);
+  for (int c = 0; c < npieces; ++c) M = fmaxf(M, part[c * kPartialFloats]);
   float L = 0.f, O = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = 0; c < npieces; ++c) {
     const float mc = part[c * kPartialFloats];
     if (mc == -__builtin_inff()) continue;
     const float f = fast_exp2(mc - M);
@@ -279,21 +315,22 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float* __
 
 hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometry& g,
                               hipStream_t stream) {
-  const int nchunks = decode_chunks(g.nkb);
-  const size_t nwg = (size_t)g.batch * g.hkv * nchunks;
+  const int npieces = decode_pieces(g.batch, g.hkv);
+  const size_t nwg = (size_t)g.batch * g.hkv * npieces;
   if (nwg == 0) return hipSuccess;
+  const size_t dyn = (2 * (size_t)((g.nkb + 31) / 32) + 2 * (size_t)g.group * g.topk) * sizeof(uint32_t);
   if (g.group <= 16)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<1>, dim3((unsigned)nwg), dim3(64), 0, stream, a, workspace, g,
-                       nchunks);
+    hipLaunchKernelGGL(attn_decode_partial_kernel<1>, dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace, g,
+                       npieces);
   else if (g.group <= 32)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<2>, dim3((unsigned)nwg), dim3(64), 0, stream, a, workspace, g,
-                       nchunks);
+    hipLaunchKernelGGL(attn_decode_partial_kernel<2>, dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace, g,
+                       npieces);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((unsigned)(g.batch * g.hq)), dim3(64), 0, stream,
-                     workspace, a.out, a.lse, nchunks);
+                     workspace, a.out, a.lse, npieces);
   return hipGetLastError();
 }
 

@@ -33,15 +33,31 @@ struct AttnArgs {
   int rows_out;      // rows per (b, h) in the output tensors
 };
 
-// Decode split: key blocks of one (batch, KV head) group are cut into chunks
-// of kDecodeChunk blocks; each chunk writes one partial (m, l, o[64]) per query
-// head, merged afterwards.
-constexpr int kDecodeChunk = 64;
+// Decode split: the union of the key blocks that the query heads of one
+// (batch, KV head) group selected is cut into `decode_pieces` equal slices, one
+// wavefront each; every slice writes one partial (m, l, o[64]) per query head,
+// merged afterwards.
+#ifndef SSA_DECODE_RING
+#define SSA_DECODE_RING 2
+#endif
+#ifndef SSA_DECODE_WAVES
+#define SSA_DECODE_WAVES 1024
+#endif
+constexpr int kDecodeRing = SSA_DECODE_RING;        // K/V block slots per wavefront
+constexpr int kDecodeTargetWaves = SSA_DECODE_WAVES;  // wavefronts the split aims for
+constexpr int kDecodeMaxPieces = 64;
+constexpr int kDecodeMaxList = 2048;    // query heads per group x topk
+constexpr int kDecodeMaxBlocks = 65536; // key blocks of the cache
 constexpr int kPartialFloats = 2 + 64;
 
-inline int decode_chunks(int nkb) { return (nkb + kDecodeChunk - 1) / kDecodeChunk; }
-inline size_t decode_workspace_bytes(int batch, int hq, int nkb) {
-  return (size_t)batch * hq * decode_chunks(nkb) * kPartialFloats * sizeof(float);
+inline int decode_pieces(int batch, int hkv) {
+  const int groups = batch * hkv;
+  if (groups <= 0) return 1;
+  int p = (kDecodeTargetWaves + groups - 1) / groups;
+  return p < 1 ? 1 : (p > kDecodeMaxPieces ? kDecodeMaxPieces : p);
+}
+inline size_t decode_workspace_bytes(int batch, int hq, int hkv) {
+  return (size_t)batch * hq * decode_pieces(batch, hkv) * kPartialFloats * sizeof(float);
 }
 
 hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geometry& g,

@@ -90,20 +90,37 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
 }
 
-// Request slices first, first+step, ... of the eight 1 KB slices of one tile
-// (slice c = rows 8c..8c+7), storing chunk q of row r at swz(r, q).  Rows at or
+// Per-lane byte offset (within a tile) of the 16 bytes this lane fetches for
+// slice c (rows 8c..8c+7): chunk q of row r is stored at swz(r, q).  Rows at or
 // past `nvalid` re-read row 0 of the tile (always present); their contents
 // never reach an output (causal mask / unwritten rows).
-__device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds,
-                                          int first, int step, int lane) {
-  const uint32_t base = lds_addr(lds);
-  for (int c = first; c < 8; c += step) {
-    const int row = 8 * c + (lane >> 3);
-    const int chunk = (lane & 7) ^ (row & 7);
-    const uint32_t voff = (uint32_t)((row < nvalid ? row * kHeadDim : 0) + chunk * 8) * 2u;
-    dma_1k(gtile, voff, __builtin_amdgcn_readfirstlane(base + c * 1024));
-  }
+__device__ __forceinline__ uint32_t slice_offset(int c, int lane, int nvalid) {
+  const int row = 8 * c + (lane >> 3);
+  const int chunk = (lane & 7) ^ (row & 7);
+  return (uint32_t)((row < nvalid ? row * kHeadDim : 0) + chunk * 8) * 2u;
 }
 
+// The eight slice offsets of a full tile, computed once per wavefront.
+struct TileOffsets {
+  uint32_t v[8];
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = slice_offset(c, lane, kBlock);
+  }
+};
+
+// Request slices first, first+step, ... of one tile into LDS at `lds`.
+// Full tiles use the precomputed offsets; a partial last tile clamps rows.
+__device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds,
+                                          int first, int step, int lane, const TileOffsets& off) {
+  const uint32_t base = lds_addr(lds);
+  if (nvalid >= kBlock) {
+    for (int c = first; c < 8; c += step)
+      dma_1k(gtile, off.v[c], __builtin_amdgcn_readfirstlane(base + c * 1024));
+  } else {
+    for (int c = first; c < 8; c += step)
+      dma_1k(gtile, slice_offset(c, lane, nvalid), __builtin_amdgcn_readfirstlane(base + c * 1024));
+  }
+}
 
 }  // namespace ssa

@@ -94,13 +94,17 @@ def test_pointer_validation(lib):
 def test_decode_workspace(lib):
     sh = good_shape(batch=64, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=32768, q_offset=32767, topk=17)
     need = lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_SPARSE_FWD)
-    assert need == 64 * 32 * 8 * 66 * 4        # 8 chunks of 64 key blocks, (max, sum, o[64]) each
+    assert need == 64 * 32 * 8 * 66 * 4        # 8 slices per KV group, (max, sum, o[64]) per head each
     assert lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_FULL_FWD) == 0
     assert lib.ssa_workspace_bytes(ctypes.byref(good_shape()), ssa.SSA_OP_SPARSE_FWD) == 0
     assert lib.ssa_workspace_bytes(ctypes.byref(good_shape(head_dim=8)), ssa.SSA_OP_SPARSE_FWD) == 2**64 - 1
     # too small a workspace is refused before launch
     assert lib.ssa_block_sparse_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,
                                          None) == ssa.SSA_ERR_WORKSPACE
+    # decode lists beyond 2048 (heads per KV head x topk) are not implemented
+    wide = good_shape(batch=1, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=64 * 300, q_offset=64 * 300 - 1, topk=200)
+    assert lib.ssa_block_sparse_attn_fwd(ctypes.byref(wide), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                         None) == ssa.SSA_ERR_UNSUPPORTED
     # decode groups beyond 32 query heads per KV head are not implemented
     big = good_shape(batch=1, n_q_heads=64, n_kv_heads=1, seq_q=1, seq_kv=100, q_offset=99, topk=2)
     assert lib.ssa_block_sparse_attn_fwd(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
