@@ -68,8 +68,15 @@ __device__ __forceinline__ void init_state(UnitState& st) {
 }
 
 // S^T = K Q^T for one tile: rows = keys 32*kb + 8*(r/4) + 4*hl + r%4, columns = queries.
+// All K operands are read before the MFMA burst so the LDS latency overlaps.
 __device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[2][4], int l32, int hl,
                                             f32x16 s[2][2]) {
+  bf16x8 ka[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      ka[kb][ks] = *reinterpret_cast<const bf16x8*>(sK + swz(32 * kb + l32, 2 * ks + hl));
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -77,11 +84,9 @@ __device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz(32 * kb + l32, 2 * ks + hl));
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(ka, qop[qb][ks], s[kb][qb]);
-    }
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(ka[kb][ks], qop[qb][ks], s[kb][qb]);
   }
 }
 
@@ -111,7 +116,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
     for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[0][qb][r]), s[0][qb][r + 1]);
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[1][qb][r]), s[1][qb][r + 1]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor32(mx);
     mt[qb] = mx * c;
     grow |= !(mt[qb] <= st.m[qb] + kRescaleSlack);
   }
@@ -161,6 +166,8 @@ __device__ __forceinline__ void tile_pv(const uint8_t* sV, const u32x4 pk[2][2][
   const int hh = grp >> 1, gd = grp & 1;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    // the four V^T operands of this 32-key half, read before its MFMAs
+    bf16x8 vop[2][2];
 #pragma unroll
     for (int ap = 0; ap < 2; ++ap) {
 #pragma unroll
@@ -178,11 +185,15 @@ __device__ __forceinline__ void tile_pv(const uint8_t* sV, const u32x4 pk[2][2][
         }
         u32x4 va;
         va[0] = w[0]; va[1] = w[1]; va[2] = w[2]; va[3] = w[3];
-        const bf16x8 vop = as_bf16x8(va);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) st.o[db][qb] = mfma32(vop, as_bf16x8(pk[kb][ap][qb]), st.o[db][qb]);
+        vop[ap][db] = as_bf16x8(va);
       }
     }
+#pragma unroll
+    for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) st.o[db][qb] = mfma32(vop[ap][db], as_bf16x8(pk[kb][ap][qb]), st.o[db][qb]);
   }
 }
 
@@ -191,8 +202,8 @@ __device__ __forceinline__ void unit_epilogue(const UnitState& st, const AttnArg
                                               int i, int l32, int hl) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lt = st.l[qb] + __shfl_xor(st.l[qb], 32, 64);
-    const float dt = FULL ? st.ld[qb] + __shfl_xor(st.ld[qb], 32, 64) : 0.f;
+    const float lt = sum_xor32(st.l[qb]);
+    const float dt = FULL ? sum_xor32(st.ld[qb]) : 0.f;
     const float inv = 1.f / lt;
     const int row = i * kBlock + 32 * qb + l32;
     if (row < geo.seq_q) {
@@ -244,12 +255,12 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, const int* __restrict__ sList, int nt,
     const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int seq_kv, int jd, int pos0,
     float c, const bf16x8 qop[2][4], UnitState& st, int lane, int l32, int hl) {
-  TileOffsets toff;
-  toff.init(lane);
+  TileOffsets<1> toff;
+  toff.init(lane, 0);
   if (nt > 0) {
     const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
-    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sK, 0, 1, lane, toff);
-    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sV, 0, 1, lane, toff);
+    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sK, lane, toff);
+    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sV, lane, toff);
   }
   for (int t = 0; t < nt; ++t) {
     const int j = __builtin_amdgcn_readfirstlane(sList[t]);
@@ -259,7 +270,7 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     f32x16 s[2][2];
     tile_scores(sK, qop, l32, hl, s);
     wait_lds_reads();
-    if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sK, 0, 1, lane, toff);
+    if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sK, lane, toff);
     u32x4 pk[2][2][2];
     tile_softmax<false>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c);
     if (more)
@@ -268,7 +279,7 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
       wait_vmem<0>();
     tile_pv(sV, pk, st, lane);
     wait_lds_reads();
-    if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sV, 0, 1, lane, toff);
+    if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sV, lane, toff);
   }
 }
 
@@ -332,10 +343,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
   const float c = geo.scale_log2;
   const int pos0 = geo.q_offset + i * kBlock;
   const int nt = jd + 1;
-  TileOffsets toff;
-  toff.init(lane);
-  tile_load(kbase, geo.seq_kv, sK[0], wave, NW, lane, toff);
-  tile_load(vbase, geo.seq_kv, sV[0], wave, NW, lane, toff);
+  TileOffsets<NW> toff;
+  toff.init(lane, wave);
+  tile_load(kbase, geo.seq_kv, sK[0], lane, toff);
+  tile_load(vbase, geo.seq_kv, sV[0], lane, toff);
   int sel_ptr = 0;
   int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
   for (int t = 0; t < nt; ++t) {
@@ -344,8 +355,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
     if (t + 1 < nt) {
       const size_t off = (size_t)(t + 1) * kBlock * kHeadDim;
       const int nv = geo.seq_kv - (t + 1) * kBlock;
-      tile_load(kbase + off, nv, sK[(t + 1) & 1], wave, NW, lane, toff);
-      tile_load(vbase + off, nv, sV[(t + 1) & 1], wave, NW, lane, toff);
+      tile_load(kbase + off, nv, sK[(t + 1) & 1], lane, toff);
+      tile_load(vbase + off, nv, sV[(t + 1) & 1], lane, toff);
     }
     const bool selected = (nxt == t);
     if (selected) {

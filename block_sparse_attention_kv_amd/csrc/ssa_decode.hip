@@ -142,13 +142,13 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   const float c = geo.scale_log2;
   const int pos = geo.q_offset;  // absolute position of the query token
 
-  TileOffsets toff;
-  toff.init(lane);
+  TileOffsets<1> toff;
+  toff.init(lane, 0);
   const int nmine = u1 - u0;
   for (int n = 0; n < kRing - 1 && n < nmine; ++n) {
     const int j = __builtin_amdgcn_readfirstlane(sBlk[u0 + n]);
-    tile_load(kbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][0], 0, 1, lane, toff);
-    tile_load(vbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][1], 0, 1, lane, toff);
+    tile_load(kbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][0], lane, toff);
+    tile_load(vbase + (size_t)j * kBlock * kHeadDim, geo.seq_kv - j * kBlock, sKV[n][1], lane, toff);
   }
   for (int n = 0; n < nmine; ++n) {
     const int slot = n % kRing;
@@ -158,8 +158,8 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
       wait_lds_reads();
       const int jn = __builtin_amdgcn_readfirstlane(sBlk[u0 + nn]);
       const int sn = nn % kRing;
-      tile_load(kbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][0], 0, 1, lane, toff);
-      tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][1], 0, 1, lane, toff);
+      tile_load(kbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][0], lane, toff);
+      tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sKV[sn][1], lane, toff);
     }
     const int j = __builtin_amdgcn_readfirstlane(sBlk[u0 + n]);
     const uint32_t hm = __builtin_amdgcn_readfirstlane(sHm[u0 + n]);
@@ -167,23 +167,23 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
     const uint8_t* sK = sKV[slot][0];
     const uint8_t* sV = sKV[slot][1];
 
-    // S^T = K Q^T: rows = keys 16*mb + 4*g4 + r, column = head.
+    // S^T = K Q^T: rows = keys 16*mb + 4*g4 + r, column = head.  All K operands
+    // are read before the MFMA burst.
+    bf16x8 ka[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) ka[mb][ks] = *reinterpret_cast<const bf16x8*>(sK + swz(16 * mb + l16, 4 * ks + g4));
     f32x4 s[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[hb][mb][r] = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(sK + swz(16 * mb + l16, 4 * ks + g4));
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) s[hb][mb] = mfma16(ka, qop[hb][ks], s[hb][mb]);
+        for (int ks = 0; ks < 2; ++ks) s[hb][mb] = mfma16(ka[mb][ks], qop[hb][ks], s[hb][mb]);
       }
-    }
     u32x4 pk[NHB][2];
     // Only the block holding the query position (or the cache end) needs a
     // per-key mask; a head that did not select the block gets p = 0 through
@@ -207,8 +207,8 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
       for (int mb = 1; mb < 4; ++mb)
         mx = fmaxf(fmaxf(mx, fmaxf(s[hb][mb][0], s[hb][mb][1])), fmaxf(s[hb][mb][2], s[hb][mb][3]));
       mx = sel ? mx : -__builtin_inff();
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
       const float mt = mx * c;
       if (!(mt <= m[hb] + kRescaleSlack)) {  // per-lane: its head's reference max moves
         const float mn = fmaxf(m[hb], mt);
@@ -243,6 +243,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
     // 32*ks + 4*g4 + t (t < 4) or 32*ks + 16 + 4*g4 + (t - 4) -- the keys of its
     // S^T registers; V^T for d block db comes from two transposing reads.
     const int tq = l16 >> 2, qq = l16 & 3;
+    bf16x8 vop[4][2];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -260,19 +261,22 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
         }
         u32x4 va;
         va[0] = w[0]; va[1] = w[1]; va[2] = w[2]; va[3] = w[3];
-        const bf16x8 vop = as_bf16x8(va);
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) o[hb][db] = mfma16(vop, as_bf16x8(pk[hb][ks]), o[hb][db]);
+        vop[db][ks] = as_bf16x8(va);
       }
     }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) o[hb][db] = mfma16(vop[db][ks], as_bf16x8(pk[hb][ks]), o[hb][db]);
   }
 
   // Partial state per head: reference max (log2 units), sum, unnormalised output.
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int hh = 16 * hb + l16;
-    float lt = l[hb] + __shfl_xor(l[hb], 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = sum_xor32(sum_xor16(l[hb]));
     if (hh < G) {
       float* part = ws + ((size_t)(head0 + hh) * npieces + piece) * kPartialFloats;
 #pragma unroll

@@ -100,26 +100,31 @@ __device__ __forceinline__ uint32_t slice_offset(int c, int lane, int nvalid) {
   return (uint32_t)((row < nvalid ? row * kHeadDim : 0) + chunk * 8) * 2u;
 }
 
-// The eight slice offsets of a full tile, computed once per wavefront.
+// The offsets of the slices first, first+STEP, ... of a full tile that this
+// wavefront requests, computed once (indexed by a compile-time slot).
+template <int STEP>
 struct TileOffsets {
-  uint32_t v[8];
-  __device__ __forceinline__ void init(int lane) {
+  static constexpr int kN = 8 / STEP;
+  int first;
+  uint32_t v[kN];
+  __device__ __forceinline__ void init(int lane, int first_slice) {
+    first = first_slice;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = slice_offset(c, lane, kBlock);
+    for (int k = 0; k < kN; ++k) v[k] = slice_offset(first_slice + k * STEP, lane, kBlock);
   }
 };
 
-// Request slices first, first+step, ... of one tile into LDS at `lds`.
-// Full tiles use the precomputed offsets; a partial last tile clamps rows.
-__device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds,
-                                          int first, int step, int lane, const TileOffsets& off) {
+// Request this wavefront's slices of one tile into LDS at `lds`.  Full tiles
+// use the precomputed offsets; a partial last tile clamps rows.
+template <int STEP>
+__device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds, int lane,
+                                          const TileOffsets<STEP>& off) {
   const uint32_t base = lds_addr(lds);
-  if (nvalid >= kBlock) {
-    for (int c = first; c < 8; c += step)
-      dma_1k(gtile, off.v[c], __builtin_amdgcn_readfirstlane(base + c * 1024));
-  } else {
-    for (int c = first; c < 8; c += step)
-      dma_1k(gtile, slice_offset(c, lane, nvalid), __builtin_amdgcn_readfirstlane(base + c * 1024));
+#pragma unroll
+  for (int k = 0; k < TileOffsets<STEP>::kN; ++k) {
+    const int c = off.first + k * STEP;
+    const uint32_t voff = nvalid >= kBlock ? off.v[k] : slice_offset(c, lane, nvalid);
+    dma_1k(gtile, voff, __builtin_amdgcn_readfirstlane(base + c * 1024));
   }
 }
 
