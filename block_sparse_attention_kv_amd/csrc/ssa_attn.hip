@@ -76,7 +76,7 @@ __device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      ka[kb][ks] = *reinterpret_cast<const bf16x8*>(sK + swz(32 * kb + l32, 2 * ks + hl));
+      ka[kb][ks] = *reinterpret_cast<const bf16x8*>(sK + swz<0>(32 * kb + l32, 2 * ks + hl));
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -95,6 +95,9 @@ template <bool FULL>
 __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x4 pk[2][2][2], bool diag,
                                              bool selected, int key0, int pos0, int l32, int hl, float c) {
   if (diag) {
+    // Opaque copy: keeps the compares of this once-per-unit branch from being
+    // hoisted out of the tile loop (their masks would pin dozens of SGPRs).
+    asm volatile("" : "+v"(key0));
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int pos = pos0 + 32 * qb + l32;
@@ -177,7 +180,7 @@ __device__ __forceinline__ void tile_pv(const uint8_t* sV, const u32x4 pk[2][2][
         for (int rr = 0; rr < 2; ++rr) {
           const int row = 32 * kb + 16 * ap + 8 * rr + 4 * hh + tq;
           const int chunk = 4 * db + 2 * gd + (qq >> 1);
-          const uint32_t off = swz(row, chunk) + 8 * (qq & 1);
+          const uint32_t off = swz<0>(row, chunk) + 8 * (qq & 1);
           const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)to_lds((void*)(sV + off)));
           const u32x2 tw = __builtin_bit_cast(u32x2, t);
           w[2 * rr] = tw[0];
@@ -255,7 +258,7 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, const int* __restrict__ sList, int nt,
     const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int seq_kv, int jd, int pos0,
     float c, const bf16x8 qop[2][4], UnitState& st, int lane, int l32, int hl) {
-  TileOffsets<1> toff;
+  TileOffsets<1, 0> toff;
   toff.init(lane, 0);
   if (nt > 0) {
     const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
   const float c = geo.scale_log2;
   const int pos0 = geo.q_offset + i * kBlock;
   const int nt = jd + 1;
-  TileOffsets<NW> toff;
+  TileOffsets<NW, 0> toff;
   toff.init(lane, wave);
   tile_load(kbase, geo.seq_kv, sK[0], lane, toff);
   tile_load(vbase, geo.seq_kv, sV[0], lane, toff);

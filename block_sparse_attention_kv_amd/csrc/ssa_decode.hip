@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   const float c = geo.scale_log2;
   const int pos = geo.q_offset;  // absolute position of the query token
 
-  TileOffsets<1> toff;
+  TileOffsets<1, 1> toff;
   toff.init(lane, 0);
   const int nmine = u1 - u0;
   for (int n = 0; n < kRing - 1 && n < nmine; ++n) {
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) ka[mb][ks] = *reinterpret_cast<const bf16x8*>(sK + swz(16 * mb + l16, 4 * ks + g4));
+      for (int ks = 0; ks < 2; ++ks) ka[mb][ks] = *reinterpret_cast<const bf16x8*>(sK + swz<1>(16 * mb + l16, 4 * ks + g4));
     f32x4 s[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb)
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
         for (int rr = 0; rr < 2; ++rr) {
           const int row = 32 * ks + 16 * rr + 4 * g4 + tq;
           const int chunkq = 2 * db + (qq >> 1);
-          const uint32_t off = swz(row, chunkq) + 8 * (qq & 1);
+          const uint32_t off = swz<1>(row, chunkq) + 8 * (qq & 1);
           const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)to_lds((void*)(sV + off)));
           const u32x2 tw = __builtin_bit_cast(u32x2, t);
           w[2 * rr] = tw[0];

@@ -1,6 +1,19 @@
 // LDS tile helpers shared by the attention kernels (gfx950): 64x64 bf16 tiles
 // stored as 64 rows x 128 B with 16-byte chunks XOR-swizzled by row, filled by
 // direct-to-LDS loads, and the explicit waits that order those loads.
+//
+// Swizzles.  The LDS has 64 four-byte banks (256 bytes per cycle): two rows of
+// a tile share a bank set when they have the same parity, so for each read
+// pattern the chunk permutation must separate same-parity rows:
+//   * MFMA K operand (16-byte reads): 16 consecutive rows, one chunk -> the
+//     eight rows of each parity need eight different chunk positions;
+//   * transposing V reads of the prefill kernels: rows 4m..4m+3, four aligned
+//     chunks -> rows 4m and 4m+2 need disjoint aligned chunk quads;
+//   * transposing V reads of the decode kernel: rows 16m..16m+7, two aligned
+//     chunks -> rows 16m, +2, +4, +6 need disjoint aligned chunk pairs.
+// With u = (row >> 1) & 7, swizzle kind 0 XORs the chunk with rot(u) =
+// ((u & 1) << 2) | (u >> 1), kind 1 with ((u & 3) << 1) | (u >> 2); both are
+// bijections of u, which serves the K reads.
 #pragma once
 
 #include "ssa_common.hpp"
@@ -15,9 +28,17 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.
+// Chunk XOR of row `row` under swizzle kind S.
+template <int S>
+__device__ __forceinline__ int swz_x(int row) {
+  const int u = (row >> 1) & 7;
+  return S == 0 ? (((u & 1) << 2) | (u >> 1)) : (((u & 3) << 1) | (u >> 2));
+}
+
+// Byte offset of 16-byte chunk `chunk` (0..7) of tile row `row` under swizzle kind S.
+template <int S>
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
-  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+  return (uint32_t)(row * 128 + ((chunk ^ swz_x<S>(row)) << 4));
 }
 
 __device__ __forceinline__ lds_void* to_lds(void* p) { return (lds_void*)p; }
@@ -94,15 +115,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // slice c (rows 8c..8c+7): chunk q of row r is stored at swz(r, q).  Rows at or
 // past `nvalid` re-read row 0 of the tile (always present); their contents
 // never reach an output (causal mask / unwritten rows).
+template <int S>
 __device__ __forceinline__ uint32_t slice_offset(int c, int lane, int nvalid) {
   const int row = 8 * c + (lane >> 3);
-  const int chunk = (lane & 7) ^ (row & 7);
+  // this lane fills LDS slot (row, lane & 7), which holds chunk (lane & 7) ^ x(row)
+  const int chunk = (lane & 7) ^ swz_x<S>(row);
   return (uint32_t)((row < nvalid ? row * kHeadDim : 0) + chunk * 8) * 2u;
 }
 
 // The offsets of the slices first, first+STEP, ... of a full tile that this
 // wavefront requests, computed once (indexed by a compile-time slot).
-template <int STEP>
+template <int STEP, int S>
 struct TileOffsets {
   static constexpr int kN = 8 / STEP;
   int first;
@@ -110,20 +133,20 @@ struct TileOffsets {
   __device__ __forceinline__ void init(int lane, int first_slice) {
     first = first_slice;
 #pragma unroll
-    for (int k = 0; k < kN; ++k) v[k] = slice_offset(first_slice + k * STEP, lane, kBlock);
+    for (int k = 0; k < kN; ++k) v[k] = slice_offset<S>(first_slice + k * STEP, lane, kBlock);
   }
 };
 
 // Request this wavefront's slices of one tile into LDS at `lds`.  Full tiles
 // use the precomputed offsets; a partial last tile clamps rows.
-template <int STEP>
+template <int STEP, int S>
 __device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds, int lane,
-                                          const TileOffsets<STEP>& off) {
+                                          const TileOffsets<STEP, S>& off) {
   const uint32_t base = lds_addr(lds);
 #pragma unroll
-  for (int k = 0; k < TileOffsets<STEP>::kN; ++k) {
+  for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k) {
     const int c = off.first + k * STEP;
-    const uint32_t voff = nvalid >= kBlock ? off.v[k] : slice_offset(c, lane, nvalid);
+    const uint32_t voff = nvalid >= kBlock ? off.v[k] : slice_offset<S>(c, lane, nvalid);
     dma_1k(gtile, voff, __builtin_amdgcn_readfirstlane(base + c * 1024));
   }
 }

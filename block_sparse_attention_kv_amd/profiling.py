@@ -7,8 +7,8 @@
          counter runs, scaled by what the same counters read for a plain copy of
          known size (the calibration dispatch in the same run)
 
-Kernel names are matched by substring: attn_prefill_kernel<true> is the full
-counterpart, attn_prefill_kernel<false> the block-sparse forward,
+Kernel names are matched by substring: attn_full_kernel is the full
+counterpart, attn_sparse_kernel the block-sparse forward,
 attn_decode_partial_kernel the decode gather.
 """
 from __future__ import annotations
@@ -43,9 +43,9 @@ def source_hash(kernel: str) -> str:
 
 
 def classify(name: str):
-    if "attn_prefill_kernel<true>" in name or "attn_prefill_kernelILb1E" in name:
+    if "attn_full_kernel" in name:
         return "full_attn"
-    if "attn_prefill_kernel<false>" in name or "attn_prefill_kernelILb0E" in name:
+    if "attn_sparse_kernel" in name:
         return "sparse_attn"
     if "attn_decode_partial_kernel" in name:
         return "decode_attn"
