@@ -95,20 +95,20 @@ template <bool FULL>
 __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x4 pk[2][2][2], bool diag,
                                              bool selected, int key0, int pos0, int l32, int hl, float c) {
   if (diag) {
-    // Opaque copy: keeps the compares of this once-per-unit branch from being
-    // hoisted out of the tile loop (their masks would pin dozens of SGPRs).
-    asm volatile("" : "+v"(key0));
+    // Causal mask of the tile holding the query rows' own positions: key > pos
+    // becomes -inf.  Branch-free sign arithmetic (no compare masks to keep live).
+    int base = key0 - pos0 + 4 * hl - l32;  // key - pos at kb = qb = r = 0
+    asm volatile("" : "+v"(base));  // opaque: the mask is built here, not hoisted out of the tile loop
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int pos = pos0 + 32 * qb + l32;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key > pos) s[kb][qb][r] = -__builtin_inff();
+          const int e = base + 32 * (kb - qb) + 8 * (r >> 2) + (r & 3);  // key - pos
+          const uint32_t neg_inf_if_future = (uint32_t)((-e) >> 31) & 0xFF800000u;
+          s[kb][qb][r] += __uint_as_float(neg_inf_if_future);
         }
-    }
   }
   float mt[2];
   bool grow = false;

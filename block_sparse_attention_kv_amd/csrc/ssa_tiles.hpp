@@ -107,6 +107,18 @@ __device__ __forceinline__ void dma_1k(const uint16_t* gtile, uint32_t voff, uin
       : "memory", "m0");
 }
 
+// Same load for the partial last tile of a sequence.  The asm text differs so
+// the compiler keeps it on its own (rare) path instead of merging the two
+// paths into per-load selects.
+__device__ __forceinline__ void dma_1k_ragged(const uint16_t* gtile, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1 ; partial tile"
+      :
+      : "v"(voff), "s"(gtile), "s"(lds_base)
+      : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
 }
@@ -143,11 +155,16 @@ template <int STEP, int S>
 __device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds, int lane,
                                           const TileOffsets<STEP, S>& off) {
   const uint32_t base = lds_addr(lds);
+  if (nvalid >= kBlock) {
 #pragma unroll
-  for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k) {
-    const int c = off.first + k * STEP;
-    const uint32_t voff = nvalid >= kBlock ? off.v[k] : slice_offset<S>(c, lane, nvalid);
-    dma_1k(gtile, voff, __builtin_amdgcn_readfirstlane(base + c * 1024));
+    for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k)
+      dma_1k(gtile, off.v[k], __builtin_amdgcn_readfirstlane(base + (off.first + k * STEP) * 1024));
+  } else {
+#pragma unroll
+    for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k) {
+      const int c = off.first + k * STEP;
+      dma_1k_ragged(gtile, slice_offset<S>(c, lane, nvalid), __builtin_amdgcn_readfirstlane(base + c * 1024));
+    }
   }
 }
 
