@@ -14,19 +14,27 @@ namespace ssa {
 namespace {
 
 // Sum the rows [0, nrows) of a 64-wide bf16 block in fp64.  Lane layout: lane
-// covers columns 8*(lane%8) .. +8 of rows lane/8, lane/8 + 8, ...; the eight
-// row groups are then folded together, so lanes 0..7 end with the column sums.
+// covers columns 8*(lane%8) .. +8 of rows lane/8, lane/8 + 8, ...; all eight
+// loads are issued before any is used.  The eight row groups are then folded
+// together, so lanes 0..7 end with the column sums.
 __device__ __forceinline__ void pool_rows_f64(const uint16_t* __restrict__ base, int nrows,
                                               int lane, double acc[8]) {
   const int c8 = lane & 7, rg = lane >> 3;
+  u32x4 v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = rg + 8 * k;
+    v[k] = *reinterpret_cast<const u32x4*>(base + (size_t)(r < nrows ? r : 0) * kHeadDim + c8 * 8);
+    if (r >= nrows) v[k] = u32x4{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-  for (int r = rg; r < nrows; r += 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (size_t)r * kHeadDim + c8 * 8);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += (double)bf16_to_f32((uint16_t)(v[e] & 0xffffu));
-      acc[2 * e + 1] += (double)bf16_to_f32((uint16_t)(v[e] >> 16));
+      acc[2 * e] += (double)bf16_to_f32((uint16_t)(v[k][e] & 0xffffu));
+      acc[2 * e + 1] += (double)bf16_to_f32((uint16_t)(v[k][e] >> 16));
     }
   }
 #pragma unroll
@@ -59,75 +67,76 @@ __global__ __launch_bounds__(64) void block_summaries_kernel(const uint16_t* __r
   }
 }
 
-constexpr int kScoreQTile = 16;   // query blocks per workgroup (prefill)
-constexpr int kScoreKTile = 64;   // key blocks staged per pass
-constexpr int kKbStride = 65;     // padded LDS row (floats) -> conflict-free row-per-lane reads
+constexpr int kScoreQb = 4;     // query blocks per workgroup (prefill): one per wavefront
+constexpr int kScoreKTile = 64;  // key blocks staged per pass (decode)
+constexpr int kKbStride = 65;    // padded LDS row (floats) -> conflict-free row-per-lane reads
 
-// One workgroup: (b, h) x kScoreQTile query blocks.  Pools its query blocks
-// (Q is read exactly once overall), then sweeps the key summaries in passes of
-// kScoreKTile blocks staged through LDS.
+// One workgroup of four wavefronts per (b, h, 4 query blocks, 256 key
+// blocks).  Each wavefront pools one query block (Q is read once per 256 key
+// blocks: once overall up to 16k tokens); then each thread scores one key
+// block's summary (read straight from global memory, L2-resident) against
+// the pooled blocks.
 __global__ __launch_bounds__(256) void prefill_scores_kernel(const uint16_t* __restrict__ q,
                                                              const float* __restrict__ ksum,
                                                              float* __restrict__ scores,
                                                              Geometry geo) {
-  __shared__ double sQ[kScoreQTile][kHeadDim];
-  __shared__ float sKb[kScoreKTile * kKbStride];
+  __shared__ double sQ[kScoreQb][kHeadDim];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ntile = (geo.nqb + kScoreQTile - 1) / kScoreQTile;
+  const int ntile = (geo.nqb + kScoreQb - 1) / kScoreQb;
   const int bh = blockIdx.x / ntile;
-  const int i0 = (blockIdx.x - bh * ntile) * kScoreQTile;
+  const int j = blockIdx.y * 256 + tid;
+  const int i0 = (blockIdx.x - bh * ntile) * kScoreQb;
   const int b = bh / geo.hq, h = bh - b * geo.hq, g = h / geo.group;
-  const int nq = min(kScoreQTile, geo.nqb - i0);
+  const int nq = min(kScoreQb, geo.nqb - i0);
 
-  for (int qi = wave; qi < nq; qi += 4) {
-    const int r0 = (i0 + qi) * kBlock;
+  const int jd0 = geo.q_offset / kBlock + i0;  // diagonal block of the first query block
+  float* srow = scores + ((size_t)bh * geo.nqb + i0) * geo.nkb;
+  if ((int)blockIdx.y * 256 > jd0 + nq - 1) {  // every key block here is past the diagonal
+    if (j < geo.nkb)
+      for (int qi = 0; qi < nq; ++qi) srow[(size_t)qi * geo.nkb + j] = -__builtin_inff();
+    return;
+  }
+  if (wave < nq) {
+    const int r0 = (i0 + wave) * kBlock;
     const int nrows = min(kBlock, geo.seq_q - r0);
     double acc[8];
     pool_rows_f64(q + ((size_t)bh * geo.seq_q + r0) * kHeadDim, nrows, lane, acc);
     if (lane < 8) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sQ[qi][lane * 8 + e] = (double)(float)(acc[e] / nrows);
+      for (int e = 0; e < 8; ++e) sQ[wave][lane * 8 + e] = (double)(float)(acc[e] / nrows);
     }
   }
   __syncthreads();
 
   const float* kb = ksum + (size_t)(b * geo.hkv + g) * geo.nkb * kHeadDim;
-  float* srow = scores + (size_t)bh * geo.nqb * geo.nkb;
-  const int jd0 = geo.q_offset / kBlock + i0;  // diagonal block of the first query block
-  const int jd_last = jd0 + nq - 1;
   const double scale = (double)geo.scale;
-  for (int jc = 0; jc < geo.nkb; jc += kScoreKTile) {
-    const int nj = min(kScoreKTile, geo.nkb - jc);
-    if (jc > jd_last) {
-      for (int e = tid; e < nq * nj; e += 256) {
-        const int qi = e / nj, jj = e - qi * nj;
-        srow[(size_t)(i0 + qi) * geo.nkb + jc + jj] = -__builtin_inff();
+  if (j < geo.nkb) {
+    float out[kScoreQb];
+#pragma unroll
+    for (int qi = 0; qi < kScoreQb; ++qi) out[qi] = -__builtin_inff();
+    if (j <= jd0 + nq - 1) {
+      const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * kHeadDim);
+      float4 kv[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) kv[x] = kr[x];
+      double acc[kScoreQb] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float kk[4] = {kv[x].x, kv[x].y, kv[x].z, kv[x].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double kd = (double)kk[e];
+#pragma unroll
+          for (int qi = 0; qi < kScoreQb; ++qi) acc[qi] = fma(sQ[qi][4 * x + e], kd, acc[qi]);
+        }
       }
-      continue;
+#pragma unroll
+      for (int qi = 0; qi < kScoreQb; ++qi)
+        if (j <= jd0 + qi) out[qi] = (float)(scale * acc[qi]);
     }
-    __syncthreads();
-    for (int e = tid; e < nj * 16; e += 256) {
-      const int jj = e >> 4, c4 = e & 15;
-      const float4 v = reinterpret_cast<const float4*>(kb + (size_t)(jc + jj) * kHeadDim)[c4];
-      float* d = &sKb[jj * kKbStride + c4 * 4];
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-    }
-    __syncthreads();
-    const int jj = tid & 63;
-    for (int qi = wave; qi < nq; qi += 4) {
-      if (jj >= nj) continue;
-      const int j = jc + jj, jd = jd0 + qi;
-      float out;
-      if (j > jd) {
-        out = -__builtin_inff();
-      } else {
-        double acc = 0.0;
-#pragma unroll 16
-        for (int d = 0; d < kHeadDim; ++d) acc = fma(sQ[qi][d], (double)sKb[jj * kKbStride + d], acc);
-        out = (float)(scale * acc);
-      }
-      srow[(size_t)(i0 + qi) * geo.nkb + j] = out;
-    }
+#pragma unroll
+    for (int qi = 0; qi < kScoreQb; ++qi)
+      if (qi < nq) srow[(size_t)qi * geo.nkb + j] = out[qi];
   }
 }
 
@@ -191,10 +200,10 @@ hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geo
 
 hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, float* scores,
                                  const Geometry& g, hipStream_t stream) {
-  const size_t nwg = (size_t)g.batch * g.hq * ((g.nqb + kScoreQTile - 1) / kScoreQTile);
-  if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_scores_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, q,
-                     k_summary, scores, g);
+  const size_t nwg = (size_t)g.batch * g.hq * ((g.nqb + kScoreQb - 1) / kScoreQb);
+  if (nwg == 0 || g.nkb == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_scores_kernel, dim3((unsigned)nwg, (unsigned)((g.nkb + 255) / 256)), dim3(256), 0,
+                     stream, q, k_summary, scores, g);
   return hipGetLastError();
 }
 
