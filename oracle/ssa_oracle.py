@@ -18,15 +18,20 @@ What is computed (all arithmetic in float64 unless a step says it rounds):
   2. coarse block scores  s = scale * qbar . kbar  for causal blocks [SSA-guide] same section; [DashAttn] "Etapa 1"
   3. top-k block selection per query block, diagonal always kept    [SSA-guide] same section; [DashAttn] "Etapa 2"
                                                                      (separate branch for near-diagonal chunks)
+  3'. optional group-shared selection: one list per KV group from the
+     mean of its query heads' block scores                          [DashAttn] "Etapa 1" (GQA: routing averaged
+                                                                     over the heads sharing a KV head)
   4. softmax attention restricted to the selected blocks            [SSA-summary] 2 "Mecanismo Central" (SA stream)
   5. full causal softmax attention (the counterpart output)         [SSA-summary] "Alineacion Bidireccional"
   6. dropped attention mass: full-softmax probability on keys the
      sparse pattern leaves out                                      [SSA-summary] 1 "Planteamiento del Problema",
                                                                      "Alineacion Bidireccional" (delta(t))
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
   * selection is per query block (block-mean query), per query head; the
     budget ``topk`` counts the forced diagonal block;
+  * group-shared selection (one list per KV group) ranks blocks by the mean
+    of the group's per-head block scores;
   * summaries are held in fp32 and scores are rounded to fp32 before the
     top-k decision (the decision is taken in the precision the scores are
     stored in, on both sides);
@@ -181,6 +186,43 @@ def select_blocks(scores, topk: int, block: int, q_offset: int = 0) -> np.ndarra
     return out
 
 
+# --------------------------------------------------------------------------- group-shared selection
+
+def shared_block_scores(scores, n_kv_heads: int) -> np.ndarray:
+    """Block scores shared by the query heads of each KV group: the mean of the
+    group's per-head block scores (summed in head order in float64, divided by
+    the group size, rounded to fp32); -inf where the heads have -inf.
+
+    [DashAttn] "Etapa 1" (with grouped-query attention, the routing of the
+    query heads that share a KV head is averaged into one shared selection).
+    Returns float64 [b, Hkv, nqb, nkb]."""
+    s = _f64(scores)
+    b, hq, nqb, nkb = s.shape
+    group = hq // n_kv_heads
+    out = np.empty((b, n_kv_heads, nqb, nkb))
+    for g in range(n_kv_heads):
+        acc = np.zeros((b, nqb, nkb))
+        for hh in range(group):
+            acc = acc + s[:, g * group + hh]
+        out[:, g] = round_f32(acc / group)
+    return out
+
+
+def select_blocks_shared(scores, n_kv_heads: int, topk: int, block: int, q_offset: int = 0) -> np.ndarray:
+    """Group-shared selection: the selection rule of select_blocks applied to
+    shared_block_scores, one list per (b, KV head, query block).
+    Returns int64 [b, Hkv, nqb, topk]."""
+    return select_blocks(shared_block_scores(scores, n_kv_heads), topk, block, q_offset)
+
+
+def expand_shared(sel_shared, n_q_heads: int) -> np.ndarray:
+    """Per-query-head view of a group-shared selection (query head h uses the
+    list of its KV head h // G), for sparse_attention and
+    full_attention_dropped_mass."""
+    sel_shared = np.asarray(sel_shared)
+    return np.repeat(sel_shared, n_q_heads // sel_shared.shape[1], axis=1)
+
+
 # --------------------------------------------------------------------------- steps 4-6: attention
 
 def _row_attention(qrow, keys, vals, scale):
@@ -321,14 +363,21 @@ def full_attention_dropped_mass(q, k, v, sel, block: int, scale: Optional[float]
 # --------------------------------------------------------------------------- the whole path
 
 def hot_path(q, k, v, block: int, topk: int, scale: Optional[float] = None, q_offset: int = 0,
-             k_summary=None, full_row_range: Optional[Tuple[int, int]] = None, with_full: bool = True):
+             k_summary=None, full_row_range: Optional[Tuple[int, int]] = None, with_full: bool = True,
+             shared: bool = False):
     """Summaries -> scores -> selection -> sparse attention -> full attention and
-    dropped mass, as one dict of float64 / int64 arrays."""
+    dropped mass, as one dict of float64 / int64 arrays.  ``shared`` selects one
+    list per KV group (select_blocks_shared; "idx_shared" holds it and "idx" its
+    per-head view)."""
     res = {}
     if k_summary is None:
         res["k_summary"] = key_summaries(k, block)
     res["scores"] = block_scores(q, k, block, scale, q_offset, k_summary=k_summary)
-    res["idx"] = select_blocks(res["scores"], topk, block, q_offset)
+    if shared:
+        res["idx_shared"] = select_blocks_shared(res["scores"], _f64(v).shape[1], topk, block, q_offset)
+        res["idx"] = expand_shared(res["idx_shared"], _f64(q).shape[1])
+    else:
+        res["idx"] = select_blocks(res["scores"], topk, block, q_offset)
     res["o_sparse"], res["lse_sparse"] = sparse_attention(q, k, v, res["idx"], block, scale, q_offset)
     if with_full:
         res["o_full"], res["lse_full"], res["dropped"] = full_attention_dropped_mass(

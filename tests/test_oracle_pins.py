@@ -316,10 +316,83 @@ def check_decode(O):
     np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
 
 
+
+def check_shared_hand_example(O):
+    # Two query heads share one KV head; four earlier blocks plus the diagonal
+    # (block 4), budget 3 = 2 earlier blocks + diagonal.  Worked by hand:
+    #   head 0 scores 3.0 1.0 2.0 0.0   -> its own choice {0, 2}
+    #   head 1 scores 0.0 2.5 1.0 3.0   -> its own choice {1, 3}
+    #   mean          1.5 1.75 1.5 1.5  -> block 1, then the lowest of the
+    #                                      three tied at 1.5 (block 0)
+    s = np.full((1, 2, 5, 5), -np.inf)
+    s[0, 0, 4, :5] = [3.0, 1.0, 2.0, 0.0, 0.5]
+    s[0, 1, 4, :5] = [0.0, 2.5, 1.0, 3.0, 0.5]
+    for i in range(4):                       # earlier query blocks: any finite values
+        s[0, :, i, : i + 1] = 1.0
+    own = O.select_blocks(s, 3, 1)
+    assert list(own[0, 0, 4]) == [0, 2, 4] and list(own[0, 1, 4]) == [1, 3, 4]
+    sh = O.shared_block_scores(s, 1)
+    assert list(sh[0, 0, 4]) == [1.5, 1.75, 1.5, 1.5, 0.5]
+    assert list(O.select_blocks_shared(s, 1, 3, 1)[0, 0, 4]) == [0, 1, 4]
+
+
+def check_shared_scores_pool_queries(O):
+    # The mean of the heads' scores is the score of the head-averaged block
+    # query (the score is linear in the query); pooled independently here.
+    q, k, _ = rand_qkv(2, 8, 2, 256, 16)
+    s = O.block_scores(q, k, 64)
+    sh = O.shared_block_scores(s, 2)
+    qt = torch.from_numpy(q)
+    qbar = torch.nn.functional.avg_pool1d(qt.reshape(-1, 256, 16).transpose(1, 2), 64).transpose(1, 2)
+    qbar = qbar.to(torch.float32).to(torch.float64).reshape(2, 2, 4, 4, 16).mean(dim=2)   # [b, g, nqb, d]
+    kbar = torch.nn.functional.avg_pool1d(torch.from_numpy(k).reshape(-1, 256, 16).transpose(1, 2), 64)
+    kbar = kbar.transpose(1, 2).to(torch.float32).to(torch.float64).reshape(2, 2, 4, 16)
+    ref = (qbar @ kbar.transpose(-1, -2) / 4.0).numpy()
+    causal = np.tril(np.ones((4, 4), bool))
+    assert np.all(np.isneginf(sh[..., ~causal]))
+    np.testing.assert_allclose(sh[..., causal], ref[..., causal], rtol=2e-6, atol=1e-7)
+
+
+def check_shared_reductions(O):
+    # one query head per KV head: the shared selection is the per-head one
+    q, k, _ = rand_qkv(1, 3, 3, 512, 8)
+    s = O.block_scores(q, k, 64)
+    assert np.array_equal(O.shared_block_scores(s, 3), s)
+    assert np.array_equal(O.select_blocks_shared(s, 3, 3, 64), O.select_blocks(s, 3, 64))
+    # identical query heads within each group: shared == every head's own choice
+    q1 = np.repeat(q[:, :1], 4, axis=1)
+    k1 = k[:, :1]
+    s1 = O.block_scores(q1, k1, 64)
+    own = O.select_blocks(s1, 3, 64)
+    shared = O.select_blocks_shared(s1, 1, 3, 64)
+    assert np.array_equal(O.expand_shared(shared, 4), own)
+
+
+def check_shared_brute_force(O):
+    # the shared choice is the best pair under (group-mean score desc, index
+    # asc), found by enumerating every pair
+    rng = np.random.default_rng(7)
+    s = np.full((1, 3, 6, 6), -np.inf)
+    for i in range(6):
+        s[0, :, i, : i + 1] = np.round(rng.standard_normal((3, i + 1)), 1)   # many ties
+    sel = O.select_blocks_shared(s, 1, 3, 1)
+    for i in range(6):
+        if i + 1 <= 3:
+            assert list(sel[0, 0, i][: i + 1]) == list(range(i + 1))
+            continue
+        tot = s[0, 0, i, :i] + s[0, 1, i, :i] + s[0, 2, i, :i]
+        # the chosen pair is the one whose (fp32 mean desc, index asc) sorted
+        # list is smallest: it holds the two best blocks under that order
+        best = min(itertools.combinations(range(i), 2),
+                   key=lambda comb: sorted((-float(np.float32(tot[j] / 3)), j) for j in comb))
+        assert list(sel[0, 0, i]) == sorted(list(best) + [i]), (i, sel[0, 0, i], best)
+
 ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_causal,
               check_select_brute_force, check_select_ties_and_decode, check_sparse_vs_sdpa,
               check_sparse_special_cases, check_sparse_brute_force_loops,
-              check_full_and_dropped_identities, check_tie_closed_form, check_decode]
+              check_full_and_dropped_identities, check_tie_closed_form, check_decode,
+              check_shared_hand_example, check_shared_scores_pool_queries, check_shared_reductions,
+              check_shared_brute_force]
 
 
 # ----------------------------------------------------------------------------- the pins
@@ -368,6 +441,8 @@ MUTANTS = {
     "scale_one_over_d": ("default_scale", lambda d: 1.0 / d),
     "no_fp32_rounding": ("round_f32", lambda x: np.asarray(x, dtype=np.float64)),
     "drops_last_selected_block": ("_allowed_keys", None),
+    "shared_uses_first_head": ("shared_block_scores", None),
+    "shared_sum_not_mean": ("shared_block_scores", None),
 }
 
 
@@ -389,9 +464,27 @@ def _mutant_allowed(sel_row, pos, block, seq_kv):
     return _orig_allowed(kept[:-1] if len(kept) > 1 else kept, pos, block, seq_kv)
 
 
+_orig_shared = ssa_oracle.shared_block_scores
+
+
+def _mutant_shared_first_head(scores, n_kv_heads):
+    s = np.asarray(scores, dtype=np.float64)
+    g = s.shape[1] // n_kv_heads
+    return s[:, ::g].copy()
+
+
+def _mutant_shared_sum(scores, n_kv_heads):
+    g = np.asarray(scores).shape[1] // n_kv_heads
+    return _orig_shared(scores, n_kv_heads) * g
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch, golden_dir):
     attr, fn = MUTANTS[name]
+    if name == "shared_uses_first_head":
+        fn = _mutant_shared_first_head
+    if name == "shared_sum_not_mean":
+        fn = _mutant_shared_sum
     if name == "partial_block_divides_by_block":
         fn = _mutant_block_means
     if name == "drops_last_selected_block":
