@@ -44,6 +44,7 @@ ssa_status_t make_geometry(const ssa_shape_t* s, ssa::Geometry* g, bool* empty, 
   if (s->seq_q > 1 && s->q_offset % s->block != 0)
     return fail(SSA_ERR_INVALID_ARG, "%s: a multi-row query chunk must start on a block boundary", fn);
   if (!isfinite(s->scale)) return fail(SSA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (s->scale < 0.f) return fail(SSA_ERR_UNSUPPORTED, "%s: negative scale", fn);
   if (s->causal != 1) return fail(SSA_ERR_UNSUPPORTED, "%s: only causal attention is implemented", fn);
   if (s->head_dim != ssa::kHeadDim)
     return fail(SSA_ERR_UNSUPPORTED, "%s: head_dim %d (this build: %d)", fn, s->head_dim, ssa::kHeadDim);
@@ -126,9 +127,12 @@ ssa_status_t ssa_block_scores(const ssa_shape_t* shape, const void* q, const voi
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
 
-ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
-                             hipStream_t stream) {
-  const char* fn = "ssa_select_topk";
+}  // extern "C"
+
+namespace {
+
+ssa_status_t select_topk_impl(const ssa_shape_t* shape, const float* scores, int32_t* block_idx, bool shared,
+                              hipStream_t stream, const char* fn) {
   ssa::Geometry g;
   bool empty;
   ssa_status_t st = make_geometry(shape, &g, &empty, fn);
@@ -136,14 +140,13 @@ ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int3
   if (empty) return SSA_OK;
   CHECK_PTR(scores, 4, fn);
   CHECK_PTR(block_idx, 4, fn);
-  hipError_t e = ssa::launch_select_topk(scores, block_idx, g, stream);
+  hipError_t e = ssa::launch_select_topk(scores, block_idx, g, shared, stream);
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
 
-ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, const void* k,
-                                       const void* v, const int32_t* block_idx, void* out, float* lse,
-                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "ssa_block_sparse_attn_fwd";
+ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
+                             const int32_t* block_idx, bool shared, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream, const char* fn) {
   ssa::Geometry g;
   bool empty;
   ssa_status_t st = make_geometry(shape, &g, &empty, fn);
@@ -160,6 +163,7 @@ ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, 
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.idx = block_idx;
+  a.idx_shared = shared ? 1 : 0;
   a.out = (uint16_t*)out;
   a.lse = lse;
   a.qb_begin = 0;
@@ -183,14 +187,9 @@ ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, 
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
 
-ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void* q, const void* k,
-                                            const void* v, const int32_t* block_idx, int32_t q_block_begin,
-                                            int32_t q_block_count, void* out_full, float* lse_full,
-                                            float* dropped_mass, void* workspace, size_t workspace_bytes,
-                                            hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  const char* fn = "ssa_full_attn_fwd_dropped_mass";
+ssa_status_t full_impl(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
+                       const int32_t* block_idx, bool shared, int32_t q_block_begin, int32_t q_block_count,
+                       void* out_full, float* lse_full, float* dropped_mass, hipStream_t stream, const char* fn) {
   ssa::Geometry g;
   bool empty;
   ssa_status_t st = make_geometry(shape, &g, &empty, fn);
@@ -211,6 +210,7 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.idx = block_idx;
+  a.idx_shared = shared ? 1 : 0;
   a.out = (uint16_t*)out_full;
   a.lse = lse_full;
   a.dropped = dropped_mass;
@@ -220,6 +220,56 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void
   a.rows_out = (int)((end_row < g.seq_q ? end_row : g.seq_q) - (int64_t)q_block_begin * ssa::kBlock);
   hipError_t e = ssa::launch_attn_prefill(a, true, g, stream);
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
+                             hipStream_t stream) {
+  return select_topk_impl(shape, scores, block_idx, false, stream, "ssa_select_topk");
+}
+
+ssa_status_t ssa_select_topk_shared(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
+                                    hipStream_t stream) {
+  return select_topk_impl(shape, scores, block_idx, true, stream, "ssa_select_topk_shared");
+}
+
+ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, const void* k,
+                                       const void* v, const int32_t* block_idx, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return sparse_fwd_impl(shape, q, k, v, block_idx, false, out, lse, workspace, workspace_bytes, stream,
+                         "ssa_block_sparse_attn_fwd");
+}
+
+ssa_status_t ssa_block_sparse_attn_fwd_shared(const ssa_shape_t* shape, const void* q, const void* k,
+                                              const void* v, const int32_t* block_idx, void* out, float* lse,
+                                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return sparse_fwd_impl(shape, q, k, v, block_idx, true, out, lse, workspace, workspace_bytes, stream,
+                         "ssa_block_sparse_attn_fwd_shared");
+}
+
+ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void* q, const void* k,
+                                            const void* v, const int32_t* block_idx, int32_t q_block_begin,
+                                            int32_t q_block_count, void* out_full, float* lse_full,
+                                            float* dropped_mass, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return full_impl(shape, q, k, v, block_idx, false, q_block_begin, q_block_count, out_full, lse_full,
+                   dropped_mass, stream, "ssa_full_attn_fwd_dropped_mass");
+}
+
+ssa_status_t ssa_full_attn_fwd_dropped_mass_shared(const ssa_shape_t* shape, const void* q, const void* k,
+                                                   const void* v, const int32_t* block_idx,
+                                                   int32_t q_block_begin, int32_t q_block_count, void* out_full,
+                                                   float* lse_full, float* dropped_mass, void* workspace,
+                                                   size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return full_impl(shape, q, k, v, block_idx, true, q_block_begin, q_block_count, out_full, lse_full,
+                   dropped_mass, stream, "ssa_full_attn_fwd_dropped_mass_shared");
 }
 
 size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {

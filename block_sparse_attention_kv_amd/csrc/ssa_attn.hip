@@ -302,7 +302,8 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   const int jd = (geo.q_offset + i * kBlock) / kBlock;
   const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
 
-  const int nt = stage_tile_list(a.idx + ((size_t)bh * geo.nqb + i) * geo.topk, geo.topk, jd, sList, lane);
+  const int irow = a.idx_shared ? gi : bh;  // index row: per query head, or per KV group when shared
+  const int nt = stage_tile_list(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, jd, sList, lane);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
   UnitState st;
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
   const uint16_t* kbase = a.k + kvoff;
   const uint16_t* vbase = a.v + kvoff;
 
-  const int nsel = stage_tile_list(a.idx + ((size_t)bh * geo.nqb + i) * geo.topk, geo.topk, jd, sList[wave], lane);
+  const int irow = a.idx_shared ? gi : bh;  // index row: per query head, or per KV group when shared
+  const int nsel = stage_tile_list(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, jd, sList[wave], lane);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
   UnitState st;

@@ -65,12 +65,14 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   const int G = geo.group;
   const int head0 = b * geo.hq + g * G;  // (b, first query head of the group)
   const int nw = (geo.nkb + 31) >> 5;
-  const int cap = G * geo.topk;
+  const int cap = a.idx_shared ? geo.topk : G * geo.topk;  // index entries of the group
   uint32_t* bitmap = sDyn;
   int* prefix = reinterpret_cast<int*>(sDyn + nw);
   int* sBlk = reinterpret_cast<int*>(sDyn + 2 * nw);
   uint32_t* sHm = sDyn + 2 * nw + cap;
-  const int32_t* gidx = a.idx + (size_t)head0 * geo.topk;
+  // the group's index rows: one per query head, or one shared row
+  const int32_t* gidx = a.idx + (size_t)(a.idx_shared ? bg : head0) * geo.topk;
+  const uint32_t all_heads = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
 
   // Union of the group's selected blocks: bitmap, ranks, ascending list and
   // the heads that selected each listed block.
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
     if (j >= 0 && j < geo.nkb) {
       const int r = prefix[j >> 5] + __builtin_popcount(bitmap[j >> 5] & ((1u << (j & 31)) - 1u));
       sBlk[r] = j;
-      atomicOr(&sHm[r], 1u << (e / geo.topk));
+      atomicOr(&sHm[r], a.idx_shared ? all_heads : 1u << (e / geo.topk));
     }
   }
   wave_sync_lds();

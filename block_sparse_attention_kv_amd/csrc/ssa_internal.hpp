@@ -25,6 +25,7 @@ struct AttnArgs {
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* idx;
+  int idx_shared;    // 1: one index row per (b, KV head, query block), else per query head
   uint16_t* out;
   float* lse;
   float* dropped;    // full mode only
@@ -66,7 +67,7 @@ hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, floa
                                  const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float* scores,
                                 const Geometry& g, hipStream_t stream);
-hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g,
+hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g, bool shared,
                               hipStream_t stream);
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometry& g,

@@ -9,9 +9,12 @@
 // lanes.  Blocks above T are kept, plus the lowest-index blocks equal to T
 // until k-1 are kept ("higher score, then lower index"); a ballot scan writes
 // them in ascending order and the diagonal goes last.
+// With group-shared selection one row per (b, KV head, query block) ranks the
+// mean of the group's per-head scores.
 // Method: SSA guide (mauroscia.it), "Block-sparse attention e Receptive
 // Field" (fixed top-k block budget); DashAttention summary, "Etapa 2"
-// (near-diagonal chunk kept by its own branch).
+// (near-diagonal chunk kept by its own branch) and "Etapa 1" (routing of the
+// query heads sharing a KV head averaged into one shared selection).
 #include "ssa_common.hpp"
 #include "ssa_internal.hpp"
 
@@ -30,15 +33,30 @@ __device__ __forceinline__ int wave_count(bool pred) {
   return (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(pred));
 }
 
+// Score of candidate j of one row: the row's own score, or (group-shared
+// selection) the mean of the group's per-head scores, summed in head order in
+// fp64, divided by the group size and rounded once to fp32.
+struct RowScores {
+  const float* s0;  // the row (first head of the group when shared)
+  size_t hstride;   // distance between the heads' rows
+  int heads;        // 1, or the group size when shared
+  __device__ __forceinline__ float operator()(int j) const {
+    if (heads == 1) return s0[j];
+    double acc = 0.0;
+    for (int h = 0; h < heads; ++h) acc += (double)s0[(size_t)h * hstride + j];
+    return (float)(acc / heads);
+  }
+};
+
 // Keys of candidates j = lane + 64*c, c < NPER, held in registers.
 template <int NPER>
-__device__ __forceinline__ void select_rows(const float* __restrict__ srow, int32_t* __restrict__ orow, int jd,
+__device__ __forceinline__ void select_rows(const RowScores& srow, int32_t* __restrict__ orow, int jd,
                                             int need, int lane) {
   uint32_t key[NPER];
 #pragma unroll
   for (int c = 0; c < NPER; ++c) {
     const int j = lane + 64 * c;
-    key[c] = j < jd ? cand_key(srow[j]) : 0u;
+    key[c] = j < jd ? cand_key(srow(j)) : 0u;
   }
   uint32_t t = 0u;
   for (int bit = 31; bit >= 0; --bit) {
@@ -66,8 +84,8 @@ __device__ __forceinline__ void select_rows(const float* __restrict__ srow, int3
   }
 }
 
-// Same selection for long rows: keys recomputed from the (cached) score row.
-__device__ __forceinline__ void select_rows_long(const float* __restrict__ srow, int32_t* __restrict__ orow, int jd,
+// Same selection for long rows: keys recomputed from the (cached) score rows.
+__device__ __forceinline__ void select_rows_long(const RowScores& srow, int32_t* __restrict__ orow, int jd,
                                                  int need, int lane) {
   uint32_t t = 0u;
   for (int bit = 31; bit >= 0; --bit) {
@@ -75,20 +93,20 @@ __device__ __forceinline__ void select_rows_long(const float* __restrict__ srow,
     int cnt = 0;
     for (int jb = 0; jb < jd; jb += 64) {
       const int j = jb + lane;
-      cnt += wave_count(j < jd && cand_key(srow[j]) >= trial);
+      cnt += wave_count(j < jd && cand_key(srow(j)) >= trial);
     }
     if (cnt >= need) t = trial;
   }
   int greater = 0;
   for (int jb = 0; jb < jd; jb += 64) {
     const int j = jb + lane;
-    greater += wave_count(j < jd && cand_key(srow[j]) > t);
+    greater += wave_count(j < jd && cand_key(srow(j)) > t);
   }
   const int ties = need - greater;
   int count = 0, tie_seen = 0;
   for (int jb = 0; jb < jd; jb += 64) {
     const int j = jb + lane;
-    const uint32_t k = j < jd ? cand_key(srow[j]) : 0u;
+    const uint32_t k = j < jd ? cand_key(srow(j)) : 0u;
     const uint64_t lt = (1ull << lane) - 1ull;
     const uint64_t tm = __builtin_amdgcn_ballot_w64(k == t && j < jd);
     const int tie_rank = tie_seen + (int)__builtin_popcountll(tm & lt);
@@ -100,16 +118,30 @@ __device__ __forceinline__ void select_rows_long(const float* __restrict__ srow,
   }
 }
 
+// Rows are (b, query head, query block), or (b, KV head, query block) for the
+// group-shared selection.
 template <int NPER>
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
-                                                          int32_t* __restrict__ idx, Geometry geo, int nrows) {
+                                                          int32_t* __restrict__ idx, Geometry geo, int nrows,
+                                                          int shared) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerWg + wave;
   if (row >= nrows) return;  // whole wavefront leaves together; no block barriers below
   const int i = row % geo.nqb;
   const int jd = (geo.q_offset + i * kBlock) / kBlock;
   const int k = geo.topk;
-  const float* srow = scores + (size_t)row * geo.nkb;
+  RowScores srow;
+  if (shared) {
+    const int bg = row / geo.nqb;  // b * Hkv + g
+    const int b = bg / geo.hkv, g = bg - b * geo.hkv;
+    srow.s0 = scores + ((size_t)(b * geo.hq + g * geo.group) * geo.nqb + i) * geo.nkb;
+    srow.hstride = (size_t)geo.nqb * geo.nkb;
+    srow.heads = geo.group;
+  } else {
+    srow.s0 = scores + (size_t)row * geo.nkb;
+    srow.hstride = 0;
+    srow.heads = 1;
+  }
   int32_t* orow = idx + (size_t)row * k;
   if (jd + 1 <= k) {
     for (int e = lane; e < k; e += 64) orow[e] = e <= jd ? e : -1;
@@ -124,18 +156,18 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g,
+hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g, bool shared,
                               hipStream_t stream) {
-  const size_t nrows = (size_t)g.batch * g.hq * g.nqb;
+  const size_t nrows = (size_t)g.batch * (shared ? g.hkv : g.hq) * g.nqb;
   if (nrows == 0) return hipSuccess;
   const dim3 grid((unsigned)((nrows + kRowsPerWg - 1) / kRowsPerWg)), block(256);
   const int maxjd = (g.q_offset + (g.nqb - 1) * kBlock) / kBlock;  // largest candidate count
   if (maxjd <= 128)
-    hipLaunchKernelGGL(select_topk_kernel<2>, grid, block, 0, stream, scores, idx, g, (int)nrows);
+    hipLaunchKernelGGL(select_topk_kernel<2>, grid, block, 0, stream, scores, idx, g, (int)nrows, (int)shared);
   else if (maxjd <= 512)
-    hipLaunchKernelGGL(select_topk_kernel<8>, grid, block, 0, stream, scores, idx, g, (int)nrows);
+    hipLaunchKernelGGL(select_topk_kernel<8>, grid, block, 0, stream, scores, idx, g, (int)nrows, (int)shared);
   else
-    hipLaunchKernelGGL(select_topk_kernel<0>, grid, block, 0, stream, scores, idx, g, (int)nrows);
+    hipLaunchKernelGGL(select_topk_kernel<0>, grid, block, 0, stream, scores, idx, g, (int)nrows, (int)shared);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ SSA_OP_BLOCK_SCORES, SSA_OP_SELECT_TOPK, SSA_OP_SPARSE_FWD, SSA_OP_FULL_FWD = ra
 
 EXPORTED_SYMBOLS = (
     "ssa_block_summaries", "ssa_block_scores", "ssa_select_topk", "ssa_block_sparse_attn_fwd",
-    "ssa_full_attn_fwd_dropped_mass", "ssa_workspace_bytes", "ssa_status_string",
+    "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared", "ssa_block_sparse_attn_fwd_shared",
+    "ssa_full_attn_fwd_dropped_mass_shared", "ssa_workspace_bytes", "ssa_status_string",
     "ssa_last_error", "ssa_version",
 )
 
@@ -66,8 +67,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssa_select_topk.argtypes = [sp, vp, vp, vp]
     lib.ssa_block_sparse_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssa_full_attn_fwd_dropped_mass.argtypes = [sp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.ssa_select_topk_shared.argtypes = [sp, vp, vp, vp]
+    lib.ssa_block_sparse_attn_fwd_shared.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssa_full_attn_fwd_dropped_mass_shared.argtypes = [sp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     for fn in ("ssa_block_summaries", "ssa_block_scores", "ssa_select_topk",
-               "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass"):
+               "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared",
+               "ssa_block_sparse_attn_fwd_shared", "ssa_full_attn_fwd_dropped_mass_shared"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ssa_workspace_bytes.argtypes = [sp, ctypes.c_int]
     lib.ssa_workspace_bytes.restype = ctypes.c_size_t
@@ -165,9 +170,23 @@ def ssa_select_topk(shape: Shape, scores: torch.Tensor, idx: Optional[torch.Tens
     return idx
 
 
+def ssa_select_topk_shared(shape: Shape, scores: torch.Tensor, idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Group-shared selection int32 [b, Hkv, nqb, topk] from the mean of each
+    KV group's per-head scores."""
+    _require_gpu(scores, idx)
+    if idx is None:
+        idx = torch.empty((shape.batch, shape.n_kv_heads, n_blocks(shape.seq_q, shape.block), shape.topk),
+                          dtype=torch.int32, device=scores.device)
+    _check("ssa_select_topk_shared", load_library().ssa_select_topk_shared(
+        ctypes.byref(shape), _ptr(scores), _ptr(idx), _stream(scores.device)))
+    return idx
+
+
 def ssa_block_sparse_attn_fwd(shape: Shape, q, k, v, block_idx, workspace: Optional[torch.Tensor] = None,
-                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q])."""
+                              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                              shared: bool = False):
+    """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q]).  ``shared``: block_idx
+    is a group-shared selection [b, Hkv, nqb, topk] (ssa_block_sparse_attn_fwd_shared)."""
     _require_gpu(q, k, v, block_idx, workspace, out, lse)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -177,16 +196,19 @@ def ssa_block_sparse_attn_fwd(shape: Shape, q, k, v, block_idx, workspace: Optio
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("ssa_block_sparse_attn_fwd", load_library().ssa_block_sparse_attn_fwd(
+    name = "ssa_block_sparse_attn_fwd_shared" if shared else "ssa_block_sparse_attn_fwd"
+    _check(name, getattr(load_library(), name)(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(q.device)))
     return out, lse
 
 
 def ssa_full_attn_fwd_dropped_mass(shape: Shape, q, k, v, block_idx, q_block_begin: int = 0,
-                                   q_block_count: Optional[int] = None, out=None, lse=None, dropped=None):
+                                   q_block_count: Optional[int] = None, out=None, lse=None, dropped=None,
+                                   shared: bool = False):
     """(out_full bf16, lse_full fp32, dropped_mass fp32) over query blocks
-    [q_block_begin, q_block_begin + q_block_count)."""
+    [q_block_begin, q_block_begin + q_block_count).  ``shared``: block_idx is a
+    group-shared selection (ssa_full_attn_fwd_dropped_mass_shared)."""
     _require_gpu(q, k, v, block_idx, out, lse, dropped)
     nqb = n_blocks(shape.seq_q, shape.block)
     if q_block_count is None:
@@ -199,7 +221,8 @@ def ssa_full_attn_fwd_dropped_mass(shape: Shape, q, k, v, block_idx, q_block_beg
         lse = torch.empty((b, hq, rows), dtype=torch.float32, device=q.device)
     if dropped is None:
         dropped = torch.empty((b, hq, rows), dtype=torch.float32, device=q.device)
-    _check("ssa_full_attn_fwd_dropped_mass", load_library().ssa_full_attn_fwd_dropped_mass(
+    name = "ssa_full_attn_fwd_dropped_mass_shared" if shared else "ssa_full_attn_fwd_dropped_mass"
+    _check(name, getattr(load_library(), name)(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), int(q_block_begin),
         int(q_block_count), _ptr(out), _ptr(lse), _ptr(dropped), None, 0, _stream(q.device)))
     return out, lse, dropped

@@ -32,7 +32,8 @@
  * Errors.  Arguments are validated on the host before anything is launched:
  *   SSA_ERR_INVALID_ARG (bad pointer, alignment, or inconsistent shape) or
  *   SSA_ERR_UNSUPPORTED (a valid shape this build does not implement: d != 64,
- *   B != 64, causal == 0, topk > 256).  A failed launch returns SSA_ERR_HIP.
+ *   B != 64, causal == 0, topk > 256, a negative scale).  A failed launch
+ *   returns SSA_ERR_HIP.
  *   On error nothing is written.  ssa_last_error() gives a message for the
  *   calling thread's last failure.  Empty problems (batch == 0 or
  *   seq_q == 0) return SSA_OK without launching.
@@ -71,7 +72,8 @@ typedef struct ssa_shape {
   int32_t topk;       /* k: blocks kept per query block, counting the forced diagonal
                          (most recent) block; 1 <= k <= 256 */
   int32_t causal;     /* must be 1 */
-  float scale;        /* softmax and score scale; 0 selects 1/sqrt(d) */
+  float scale;        /* softmax and score scale, >= 0 (negative: SSA_ERR_UNSUPPORTED);
+                         0 selects 1/sqrt(d) */
 } ssa_shape_t;
 
 typedef enum ssa_op {
@@ -162,6 +164,37 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void
                                             void* out_full, float* lse_full, float* dropped_mass,
                                             void* workspace, size_t workspace_bytes,
                                             hipStream_t stream);
+
+/* Group-shared selection: one list per (b, KV head g, query block i) for all
+ * the query heads of the group.  Candidate j is ranked by the group mean
+ *   sbar[j] = fp32( (sum over h in group g, in head order, in fp64, of
+ *                    scores[b,h,i,j]) / G )
+ * with the same rule as ssa_select_topk (diagonal kept; higher score, then
+ * lower index; NaN below -inf; ascending, -1 padded).
+ * [DashAttn] "Etapa 1" (with grouped-query attention the routing of the
+ * query heads that share a KV head is averaged into one shared support).
+ *   scores     fp32 [b,Hq,nqb,nkb]
+ *   block_idx  int32 [b,Hkv,nqb,topk] (output) */
+ssa_status_t ssa_select_topk_shared(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
+                                    hipStream_t stream);
+
+/* ssa_block_sparse_attn_fwd with a group-shared selection: query head h
+ * attends over the list block_idx[b, h/G, i, :] (int32 [b,Hkv,nqb,topk], as
+ * written by ssa_select_topk_shared); same outputs, workspace and errors. */
+ssa_status_t ssa_block_sparse_attn_fwd_shared(const ssa_shape_t* shape, const void* q, const void* k,
+                                              const void* v, const int32_t* block_idx, void* out,
+                                              float* lse, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
+
+/* ssa_full_attn_fwd_dropped_mass with a group-shared selection: the dropped
+ * mass of query head h counts the keys whose block is not in
+ * block_idx[b, h/G, i, :] (int32 [b,Hkv,nqb,topk]); same outputs and errors. */
+ssa_status_t ssa_full_attn_fwd_dropped_mass_shared(const ssa_shape_t* shape, const void* q, const void* k,
+                                                   const void* v, const int32_t* block_idx,
+                                                   int32_t q_block_begin, int32_t q_block_count,
+                                                   void* out_full, float* lse_full, float* dropped_mass,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   hipStream_t stream);
 
 /* Workspace bytes an entry point needs for this shape (0 if none; SIZE_MAX if
  * the shape is invalid). */

@@ -64,6 +64,7 @@ def test_version_and_status_strings(lib):
     (dict(block=32), ssa.SSA_ERR_UNSUPPORTED),
     (dict(causal=0), ssa.SSA_ERR_UNSUPPORTED),
     (dict(topk=257), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(scale=-0.125), ssa.SSA_ERR_UNSUPPORTED),
 ])
 def test_shape_validation(lib, kw, status):
     sh = good_shape(**kw)
@@ -73,6 +74,10 @@ def test_shape_validation(lib, kw, status):
     assert lib.ssa_block_sparse_attn_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == status
     assert lib.ssa_full_attn_fwd_dropped_mass(p, FAKE, FAKE, FAKE, FAKE, 0, 1, FAKE, FAKE, FAKE, None, 0,
                                               None) == status
+    assert lib.ssa_select_topk_shared(p, FAKE, FAKE, None) == status
+    assert lib.ssa_block_sparse_attn_fwd_shared(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == status
+    assert lib.ssa_full_attn_fwd_dropped_mass_shared(p, FAKE, FAKE, FAKE, FAKE, 0, 1, FAKE, FAKE, FAKE, None, 0,
+                                                     None) == status
     assert lib.ssa_last_error()
 
 
@@ -85,6 +90,10 @@ def test_pointer_validation(lib):
     assert b"aligned" in lib.ssa_last_error()
     assert lib.ssa_block_scores(p, FAKE, None, FAKE, 0, FAKE, None) == ssa.SSA_ERR_INVALID_ARG
     assert lib.ssa_select_topk(p, FAKE, None, None) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_select_topk_shared(p, None, FAKE, None) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_block_sparse_attn_fwd_shared(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0,
+                                                None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"block_idx is NULL" in lib.ssa_last_error()
     assert lib.ssa_block_summaries(None, FAKE, FAKE, None) == ssa.SSA_ERR_INVALID_ARG
     # query-block range outside the problem
     assert lib.ssa_full_attn_fwd_dropped_mass(p, FAKE, FAKE, FAKE, FAKE, 3, 2, FAKE, FAKE, FAKE, None, 0,
@@ -120,6 +129,9 @@ def test_empty_problems_launch_nothing(lib):
         assert lib.ssa_block_sparse_attn_fwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ssa.SSA_OK
         assert lib.ssa_full_attn_fwd_dropped_mass(p, FAKE, FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, None, 0,
                                                   None) == ssa.SSA_OK
+        assert lib.ssa_select_topk_shared(p, FAKE, FAKE, None) == ssa.SSA_OK
+        assert lib.ssa_block_sparse_attn_fwd_shared(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                                    None) == ssa.SSA_OK
     sh = good_shape()
     assert lib.ssa_full_attn_fwd_dropped_mass(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, FAKE,
                                               None, 0, None) == ssa.SSA_OK

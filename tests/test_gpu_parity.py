@@ -31,8 +31,9 @@ def say(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def gpu_path(w: W.Workload, q, k, v, dev, full_range=None, with_full=True):
-    """Run summaries -> scores -> top-k -> sparse -> full on the GPU."""
+def gpu_path(w: W.Workload, q, k, v, dev, full_range=None, with_full=True, shared=False):
+    """Run summaries -> scores -> top-k -> sparse -> full on the GPU (``shared``:
+    group-shared selection)."""
     shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     res = {}
@@ -41,12 +42,14 @@ def gpu_path(w: W.Workload, q, k, v, dev, full_range=None, with_full=True):
         res["scores"], res["k_summary"] = ssa.ssa_block_scores(shape, qd, None, ks)
     else:
         res["scores"], res["k_summary"] = ssa.ssa_block_scores(shape, qd, kd)
-    res["idx"] = ssa.ssa_select_topk(shape, res["scores"])
-    res["o"], res["lse"] = ssa.ssa_block_sparse_attn_fwd(shape, qd, kd, vd, res["idx"])
+    select = ssa.ssa_select_topk_shared if shared else ssa.ssa_select_topk
+    res["idx"] = select(shape, res["scores"])
+    res["o"], res["lse"] = ssa.ssa_block_sparse_attn_fwd(shape, qd, kd, vd, res["idx"], shared=shared)
     if with_full:
         nqb = ssa.n_blocks(w.seq_q, w.block)
         b0, cnt = (0, nqb) if full_range is None else full_range
-        res["of"], res["lf"], res["dm"] = ssa.ssa_full_attn_fwd_dropped_mass(shape, qd, kd, vd, res["idx"], b0, cnt)
+        res["of"], res["lf"], res["dm"] = ssa.ssa_full_attn_fwd_dropped_mass(shape, qd, kd, vd, res["idx"], b0, cnt,
+                                                                             shared=shared)
     torch.cuda.synchronize()
     return {k2: v2.cpu() for k2, v2 in res.items()}
 
@@ -55,10 +58,24 @@ def np_inputs(q, k, v):
     return q.double().numpy(), k.double().numpy(), v.double().numpy()
 
 
-def check_small(w: W.Workload, dev, full_range=None):
-    say(w)
+def reference_selection(s_ref, w: W.Workload, shared: bool):
+    """(selection scores, oracle index lists) for per-head or group-shared selection."""
+    if shared:
+        sel_scores = O.shared_block_scores(s_ref, w.n_kv_heads)
+    else:
+        sel_scores = s_ref
+    return sel_scores, O.select_blocks(sel_scores, w.topk, B, q_offset=w.q_offset)
+
+
+def per_head(idx, w: W.Workload, shared: bool):
+    idx = np.asarray(idx)
+    return O.expand_shared(idx, w.n_q_heads) if shared else idx
+
+
+def check_small(w: W.Workload, dev, full_range=None, shared=False):
+    say(f"{w} shared={shared}")
     q, k, v = W.make_inputs(w)
-    g = gpu_path(w, q, k, v, dev, full_range)
+    g = gpu_path(w, q, k, v, dev, full_range, shared=shared)
     qn, kn, vn = np_inputs(q, k, v)
     off = w.q_offset
     ks_ref = O.key_summaries(kn, B)
@@ -68,9 +85,9 @@ def check_small(w: W.Workload, dev, full_range=None):
     assert np.array_equal(np.isneginf(s_gpu), np.isneginf(s_ref))
     fin = np.isfinite(s_ref)
     assert np.all(np.abs(s_gpu[fin] - s_ref[fin]) <= 1e-6 * np.maximum(np.abs(s_ref[fin]), 1e-3))
-    idx_ref = O.select_blocks(s_ref, w.topk, B, q_offset=off)
-    P.check_indices(g["idx"], s_ref, idx_ref, w.topk, B, off)
-    gidx = g["idx"].numpy()
+    sel_scores, idx_ref = reference_selection(s_ref, w, shared)
+    P.check_indices(g["idx"], sel_scores, idx_ref, w.topk, B, off)
+    gidx = per_head(g["idx"].numpy(), w, shared)
     o_ref, lse_ref = O.sparse_attention(qn, kn, vn, gidx, B, q_offset=off)
     P.check_close_outputs(g["o"], o_ref, "O_sparse")
     P.check_abs(g["lse"], lse_ref, P.LSE_ABS, "LSE_sparse")
@@ -198,15 +215,15 @@ def test_empty_problem_writes_nothing(dev):
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-def check_full_size(w: W.Workload, dev, nrows=96, seq_subset=None):
-    say(w)
+def check_full_size(w: W.Workload, dev, nrows=96, seq_subset=None, shared=False):
+    say(f"{w} shared={shared}")
     q, k, v = W.make_inputs(w)
     nqb = ssa.n_blocks(w.seq_q, B)
     if w.full_rows is None:
         fr = (0, nqb)
     else:
         fr = (w.full_rows[0] // B, ssa.n_blocks(w.full_rows[1], B) - w.full_rows[0] // B)
-    g = gpu_path(w, q, k, v, dev, full_range=fr, with_full=True)
+    g = gpu_path(w, q, k, v, dev, full_range=fr, with_full=True, shared=shared)
     bsel = list(range(w.batch)) if seq_subset is None else seq_subset
     qn = q[bsel].double().numpy()
     kn = k[bsel].double().numpy()
@@ -214,10 +231,10 @@ def check_full_size(w: W.Workload, dev, nrows=96, seq_subset=None):
     off = w.q_offset
     assert np.array_equal(P.np64(g["k_summary"][bsel]), O.key_summaries(kn, B))
     s_ref = O.block_scores(qn, kn, B, q_offset=off)
-    idx_ref = O.select_blocks(s_ref, w.topk, B, q_offset=off)
-    ndiff = P.check_indices(g["idx"][bsel], s_ref, idx_ref, w.topk, B, off)
+    sel_scores, idx_ref = reference_selection(s_ref, w, shared)
+    ndiff = P.check_indices(g["idx"][bsel], sel_scores, idx_ref, w.topk, B, off)
     print(f"[case] {w.name}: index rows differing inside the tie band: {ndiff}", flush=True)
-    gidx = g["idx"][bsel].numpy()
+    gidx = per_head(g["idx"][bsel].numpy(), w, shared)
     rng = np.random.default_rng(w.seed)
     rows = P.sample_rows(rng, len(bsel), w.n_q_heads, w.seq_q, nrows)
     o_ref, lse_ref = O.sparse_attention(qn, kn, vn, gidx, B, q_offset=off, rows=rows)
@@ -305,3 +322,51 @@ def test_decode_32k_full_size(dev):
     P.check_abs(g["lse"][sub], lse_ref, P.LSE_ABS, "LSE_decode")
     # every sequence: the forced block is the most recent one
     assert torch.all(g["idx"][..., -1] == (w.seq_kv - 1) // B)
+
+
+# ----------------------------------------------------------------------------- group-shared selection
+
+SHARED_SMALL = [W.TINY_512, SMALL[2], SMALL[4], SMALL[6], SMALL[7], SMALL[8]]
+
+
+@pytest.mark.parametrize("w", SHARED_SMALL, ids=lambda w: w.name)
+def test_small_parity_shared(dev, w):
+    g = check_small(w, dev, shared=True)
+    assert g["idx"].shape[1] == w.n_kv_heads
+
+
+@pytest.mark.parametrize("w", DECODE_SMALL[:3], ids=lambda w: w.name)
+def test_decode_parity_shared(dev, w):
+    check_small(w, dev, shared=True)
+
+
+def test_shared_one_head_per_group_matches_per_head(dev):
+    # with one query head per KV head the shared entry points are the per-head ones
+    w = W.Workload("mha_shared", 2, 4, 4, 512, 512, 64, 64, 3, seed=41)
+    say(w)
+    q, k, v = W.make_inputs(w)
+    a = gpu_path(w, q, k, v, dev)
+    b = gpu_path(w, q, k, v, dev, shared=True)
+    for key in ("idx", "o", "lse", "of", "lf", "dm"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_prefill_8k_shared_full_size(dev):
+    g = check_full_size(W.PREFILL_8K, dev, nrows=64, shared=True)
+    assert torch.all(g["dm"][:, :, : W.PREFILL_8K.topk * B] == 0)
+
+
+def test_decode_32k_shared_full_size(dev):
+    w = W.DECODE_32K
+    say(f"{w} shared=True")
+    q, k, v = W.make_inputs(w)
+    g = gpu_path(w, q, k, v, dev, with_full=False, shared=True)
+    sub = [0, 17, 63]
+    qn, kn, vn = q[sub].double().numpy(), k[sub].double().numpy(), v[sub].double().numpy()
+    ks_ref = O.key_summaries(kn, B)
+    s_ref = O.block_scores(qn, None, B, q_offset=w.q_offset, k_summary=ks_ref)
+    sel_scores, idx_ref = reference_selection(s_ref, w, True)
+    P.check_indices(g["idx"][sub], sel_scores, idx_ref, w.topk, B, w.q_offset)
+    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, per_head(g["idx"][sub].numpy(), w, True), B, q_offset=w.q_offset)
+    P.check_close_outputs(g["o"][sub], o_ref, "O_decode shared")
+    P.check_abs(g["lse"][sub], lse_ref, P.LSE_ABS, "LSE_decode shared")
