@@ -87,7 +87,9 @@ class KernelTimer:
         return self.total[name] / self.count[name]
 
 
-def bench_prefill(args, torch, ssa, W):
+def bench_prefill(args, torch, ssa, W, shared=False):
+    """One step = summaries+scores, top-k, block-sparse forward, full forward
+    with dropped mass; ``shared`` uses the group-shared selection."""
     w = W.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in W.make_inputs(w))
@@ -100,7 +102,9 @@ def bench_prefill(args, torch, ssa, W):
         fcnt = ssa.n_blocks(w.full_rows[1], w.block) - fb0
     scores = torch.empty((w.batch, w.n_q_heads, nqb, nkb), dtype=torch.float32, device=dev)
     ksum = torch.empty((w.batch, w.n_kv_heads, nkb, w.head_dim), dtype=torch.float32, device=dev)
-    idx = torch.empty((w.batch, w.n_q_heads, nqb, w.topk), dtype=torch.int32, device=dev)
+    idx = torch.empty((w.batch, w.n_kv_heads if shared else w.n_q_heads, nqb, w.topk), dtype=torch.int32,
+                      device=dev)
+    select = ssa.ssa_select_topk_shared if shared else ssa.ssa_select_topk
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     rows = min(w.seq_q, (fb0 + fcnt) * w.block) - fb0 * w.block
@@ -111,10 +115,10 @@ def bench_prefill(args, torch, ssa, W):
 
     def step(t):
         t.run("scores", ssa.ssa_block_scores, shape, q, k, summary_out=ksum, scores=scores)
-        t.run("topk", ssa.ssa_select_topk, shape, scores, idx)
-        t.run("sparse_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, out=out, lse=lse)
+        t.run("topk", select, shape, scores, idx)
+        t.run("sparse_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, out=out, lse=lse, shared=shared)
         t.run("full_attn", ssa.ssa_full_attn_fwd_dropped_mass, shape, q, k, v, idx, fb0, fcnt,
-              out=out_f, lse=lse_f, dropped=drop)
+              out=out_f, lse=lse_f, dropped=drop, shared=shared)
 
     for _ in range(args.warmup):
         step(timer)
@@ -173,7 +177,9 @@ def roofline_entry(name, e, flops, bytes_alg):
     return r
 
 
-def bench_decode(args, torch, ssa, W):
+def bench_decode(args, torch, ssa, W, shared=False):
+    """One decode step = scores, top-k, attention over the selected blocks;
+    ``shared`` uses the group-shared selection."""
     w = W.DECODE_32K
     dev = torch.device("cuda:0")
     q0, k0, v0 = W.make_inputs(w)
@@ -186,7 +192,8 @@ def bench_decode(args, torch, ssa, W):
     shape = ssa.make_shape(copies[0][0], w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
     nkb = ssa.n_blocks(w.seq_kv, w.block)
     scores = torch.empty((w.batch, w.n_q_heads, 1, nkb), dtype=torch.float32, device=dev)
-    idx = torch.empty((w.batch, w.n_q_heads, 1, w.topk), dtype=torch.int32, device=dev)
+    idx = torch.empty((w.batch, w.n_kv_heads if shared else w.n_q_heads, 1, w.topk), dtype=torch.int32, device=dev)
+    select = ssa.ssa_select_topk_shared if shared else ssa.ssa_select_topk
     out = torch.empty_like(copies[0][0])
     lse = torch.empty((w.batch, w.n_q_heads, 1), dtype=torch.float32, device=dev)
     ws = torch.empty((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD),), dtype=torch.uint8, device=dev)
@@ -195,8 +202,9 @@ def bench_decode(args, torch, ssa, W):
     def step(t, c):
         q, k, v, ks = copies[c % len(copies)]
         t.run("decode_scores", ssa.ssa_block_scores, shape, q, None, ks, scores=scores)
-        t.run("decode_topk", ssa.ssa_select_topk, shape, scores, idx)
-        t.run("decode_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, workspace=ws, out=out, lse=lse)
+        t.run("decode_topk", select, shape, scores, idx)
+        t.run("decode_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, workspace=ws, out=out, lse=lse,
+              shared=shared)
 
     for i in range(args.warmup):
         step(timer, i)
@@ -213,7 +221,7 @@ def bench_decode(args, torch, ssa, W):
     timer.collect()
     # Algorithmic bytes from the GPU's own selection (identical inputs in every copy):
     # the union over the query heads of each KV group of selected K and V blocks.
-    G = w.n_q_heads // w.n_kv_heads
+    G = 1 if shared else w.n_q_heads // w.n_kv_heads
     sel = torch.zeros((w.batch, w.n_kv_heads, nkb + 1), dtype=torch.bool, device=dev)
     ii = idx.view(w.batch, w.n_kv_heads, G * w.topk).long()
     sel.scatter_(2, torch.where(ii < 0, torch.full_like(ii, nkb), ii), True)
@@ -303,6 +311,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=60)
     ap.add_argument("--decode-copies", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-shared", action="store_true", help="skip the group-shared selection legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--counter-pass", action="store_true",
@@ -326,6 +335,16 @@ def main():
 
     pre = bench_prefill(args, torch, ssa, W)
     dec = None if args.no_decode else bench_decode(args, torch, ssa, W)
+    shared = None
+    if not args.no_shared:
+        # the same steps with the group-shared selection (one list per KV group)
+        sp = bench_prefill(args, torch, ssa, W, shared=True)
+        shared = {"prefill": {"workload": sp["w"].name, "ms_per_step": round(sp["ms_step"], 5),
+                              "tokens_per_s": round(sp["tokens_per_s"], 1), "kernels": sp["kernels"]}}
+        if not args.no_decode:
+            sd = bench_decode(args, torch, ssa, W, shared=True)
+            shared["decode"] = {k2: sd[k2] for k2 in ("workload", "tokens_per_s", "ms_per_step",
+                                                       "union_blocks_per_group", "kernels", "roofline")}
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, W)
     w = pre["w"]
     line = {
@@ -351,6 +370,7 @@ def main():
                        "frac_of_bf16_peak": pre["kernels"]["sparse_attn"]["frac_of_peak"],
                        "traffic": measured_traffic("sparse_attn")},
         "decode": dec,
+        "shared_selection": shared,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

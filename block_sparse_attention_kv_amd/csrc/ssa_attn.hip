@@ -315,11 +315,14 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
 }
 
-// Full causal counterpart with dropped mass: NW query heads of one KV group per
-// workgroup (one per wave) share every tile through a double buffer; tile t+1
-// is requested as soon as every wave has finished tile t-1.
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geometry geo) {
+// NW query heads of one KV group per workgroup (one per wave) walk the same
+// tiles, fetched once into a double buffer shared by the NW waves; tile t+1 is
+// requested as soon as every wave has finished tile t-1.
+//   FULL:  every causal tile of the query block (the full counterpart), with
+//          dropped mass from the tiles missing from each head's own list;
+//   !FULL: the tiles of a group-shared selection (block-sparse forward).
+template <int NW, bool FULL>
+__global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geometry geo) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kTileBytes];
   __shared__ int sList[NW][kMaxTopk];
@@ -347,34 +350,44 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
   __builtin_amdgcn_wave_barrier();
   const float c = geo.scale_log2;
   const int pos0 = geo.q_offset + i * kBlock;
-  const int nt = jd + 1;
+  // tiles walked: 0..jd (full), or the shared list (identical in every wave)
+  const int nt = FULL ? jd + 1 : nsel;
+  auto tile_block = [&](int t) { return FULL ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
   TileOffsets<NW, 0> toff;
   toff.init(lane, wave);
-  tile_load(kbase, geo.seq_kv, sK[0], lane, toff);
-  tile_load(vbase, geo.seq_kv, sV[0], lane, toff);
+  if (nt > 0) {
+    const int j0 = tile_block(0);
+    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK[0], lane, toff);
+    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV[0], lane, toff);
+  }
   int sel_ptr = 0;
   int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
   for (int t = 0; t < nt; ++t) {
+    const int j = tile_block(t);
     wait_vmem<0>();   // this wave's share of tile t landed
     __syncthreads();  // ... every wave's share; and every wave is done with tile t-1
     if (t + 1 < nt) {
-      const size_t off = (size_t)(t + 1) * kBlock * kHeadDim;
-      const int nv = geo.seq_kv - (t + 1) * kBlock;
+      const int jn = tile_block(t + 1);
+      const size_t off = (size_t)jn * kBlock * kHeadDim;
+      const int nv = geo.seq_kv - jn * kBlock;
       tile_load(kbase + off, nv, sK[(t + 1) & 1], lane, toff);
       tile_load(vbase + off, nv, sV[(t + 1) & 1], lane, toff);
     }
-    const bool selected = (nxt == t);
-    if (selected) {
-      ++sel_ptr;
-      nxt = sel_ptr < nsel ? __builtin_amdgcn_readfirstlane(sList[wave][sel_ptr]) : -1;
+    bool selected = true;
+    if (FULL) {
+      selected = (nxt == t);
+      if (selected) {
+        ++sel_ptr;
+        nxt = sel_ptr < nsel ? __builtin_amdgcn_readfirstlane(sList[wave][sel_ptr]) : -1;
+      }
     }
     f32x16 s[2][2];
     tile_scores(sK[t & 1], qop, l32, hl, s);
     u32x4 pk[2][2][2];
-    tile_softmax<true>(s, st, pk, t == jd, selected, t * kBlock, pos0, l32, hl, c);
+    tile_softmax<FULL>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c);
     tile_pv(sV[t & 1], pk, st, lane);
   }
-  unit_epilogue<true>(st, a, geo, bh, i, l32, hl);
+  unit_epilogue<FULL>(st, a, geo, bh, i, l32, hl);
 }
 
 }  // namespace
@@ -382,14 +395,18 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_full_kernel(AttnArgs a, Geome
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream) {
   const size_t units = (size_t)g.batch * g.hq * a.qb_count;
   if (units == 0) return hipSuccess;
-  if (!full) {
+  if (!full && !(a.idx_shared && g.group % 4 == 0)) {
+    // per-head lists (or groups too small to share): one wavefront per unit
     hipLaunchKernelGGL(attn_sparse_kernel, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+  } else if (!full) {
+    // group-shared lists: four heads of a group share every tile
+    hipLaunchKernelGGL((attn_group_kernel<4, false>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
   } else if (g.group % 4 == 0) {
-    hipLaunchKernelGGL(attn_full_kernel<4>, dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_group_kernel<4, true>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
   } else if (g.group % 2 == 0) {
-    hipLaunchKernelGGL(attn_full_kernel<2>, dim3((unsigned)(units / 2)), dim3(128), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_group_kernel<2, true>), dim3((unsigned)(units / 2)), dim3(128), 0, stream, a, g);
   } else {
-    hipLaunchKernelGGL(attn_full_kernel<1>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_group_kernel<1, true>), dim3((unsigned)units), dim3(64), 0, stream, a, g);
   }
   return hipGetLastError();
 }

@@ -43,7 +43,14 @@ struct RowScores {
   __device__ __forceinline__ float operator()(int j) const {
     if (heads == 1) return s0[j];
     double acc = 0.0;
-    for (int h = 0; h < heads; ++h) acc += (double)s0[(size_t)h * hstride + j];
+    for (int h0 = 0; h0 < heads; h0 += 16) {  // 16 loads in flight, then summed in head order
+      float v[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) v[x] = h0 + x < heads ? s0[(size_t)(h0 + x) * hstride + j] : 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        if (h0 + x < heads) acc += (double)v[x];
+    }
     return (float)(acc / heads);
   }
 };
@@ -119,7 +126,7 @@ __device__ __forceinline__ void select_rows_long(const RowScores& srow, int32_t*
 }
 
 // Rows are (b, query head, query block), or (b, KV head, query block) for the
-// group-shared selection.
+// group-shared selection (then each wavefront also averages its row).
 template <int NPER>
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
                                                           int32_t* __restrict__ idx, Geometry geo, int nrows,
@@ -154,12 +161,62 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
   if (lane == 0) orow[k - 1] = jd;
 }
 
+// Group-shared selection with the averaging spread over a workgroup: one
+// workgroup per (b, KV head, query block) row; its 256 threads average the
+// candidates' scores into LDS, then one wavefront selects.
+constexpr int kSharedMaxBlocks = 16384;  // LDS row of averaged scores (64 KB)
+template <int NPER>
+__global__ __launch_bounds__(256) void select_topk_shared_kernel(const float* __restrict__ scores,
+                                                                 int32_t* __restrict__ idx, Geometry geo) {
+  extern __shared__ float smean[];  // [jd]: averaged scores of the candidates
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row = blockIdx.x;
+  const int i = row % geo.nqb;
+  const int bg = row / geo.nqb;
+  const int b = bg / geo.hkv, g = bg - b * geo.hkv;
+  const int jd = (geo.q_offset + i * kBlock) / kBlock;
+  const int k = geo.topk;
+  int32_t* orow = idx + (size_t)row * k;
+  if (jd + 1 <= k) {
+    if (wave == 0)
+      for (int e = lane; e < k; e += 64) orow[e] = e <= jd ? e : -1;
+    return;  // the whole workgroup leaves: no barrier is reached
+  }
+  RowScores src;
+  src.s0 = scores + ((size_t)(b * geo.hq + g * geo.group) * geo.nqb + i) * geo.nkb;
+  src.hstride = (size_t)geo.nqb * geo.nkb;
+  src.heads = geo.group;
+  for (int j = tid; j < jd; j += 256) smean[j] = src(j);
+  __syncthreads();
+  if (wave != 0) return;
+  RowScores srow;
+  srow.s0 = smean;
+  srow.hstride = 0;
+  srow.heads = 1;
+  if (NPER > 0)
+    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane);
+  else
+    select_rows_long(srow, orow, jd, k - 1, lane);
+  if (lane == 0) orow[k - 1] = jd;
+}
+
 }  // namespace
 
 hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g, bool shared,
                               hipStream_t stream) {
   const size_t nrows = (size_t)g.batch * (shared ? g.hkv : g.hq) * g.nqb;
   if (nrows == 0) return hipSuccess;
+  if (shared && g.nkb <= kSharedMaxBlocks) {
+    const int maxjd_s = (g.q_offset + (g.nqb - 1) * kBlock) / kBlock;
+    const size_t lds = (size_t)(maxjd_s > 0 ? maxjd_s : 1) * sizeof(float);
+    if (maxjd_s <= 128)
+      hipLaunchKernelGGL(select_topk_shared_kernel<2>, dim3((unsigned)nrows), dim3(256), lds, stream, scores, idx, g);
+    else if (maxjd_s <= 512)
+      hipLaunchKernelGGL(select_topk_shared_kernel<8>, dim3((unsigned)nrows), dim3(256), lds, stream, scores, idx, g);
+    else
+      hipLaunchKernelGGL(select_topk_shared_kernel<0>, dim3((unsigned)nrows), dim3(256), lds, stream, scores, idx, g);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((nrows + kRowsPerWg - 1) / kRowsPerWg)), block(256);
   const int maxjd = (g.q_offset + (g.nqb - 1) * kBlock) / kBlock;  // largest candidate count
   if (maxjd <= 128)

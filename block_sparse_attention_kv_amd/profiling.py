@@ -7,8 +7,9 @@
          counter runs, scaled by what the same counters read for a plain copy of
          known size (the calibration dispatch in the same run)
 
-Kernel names are matched by substring: attn_full_kernel is the full
-counterpart, attn_sparse_kernel the block-sparse forward,
+Kernel names are matched by substring: attn_group_kernel<NW, true> is the
+full counterpart, attn_group_kernel<NW, false> the block-sparse forward with a
+group-shared selection, attn_sparse_kernel the block-sparse forward,
 attn_decode_partial_kernel the decode gather.
 """
 from __future__ import annotations
@@ -43,8 +44,10 @@ def source_hash(kernel: str) -> str:
 
 
 def classify(name: str):
-    if "attn_full_kernel" in name:
-        return "full_attn"
+    if "attn_group_kernel" in name:
+        # attn_group_kernel<NW, FULL>: demangled "..., true>" / mangled "...Lb1E..."
+        full = ("true>" in name) or ("Lb1E" in name)
+        return "full_attn" if full else "sparse_attn_shared"
     if "attn_sparse_kernel" in name:
         return "sparse_attn"
     if "attn_decode_partial_kernel" in name:
