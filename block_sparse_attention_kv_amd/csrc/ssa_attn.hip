@@ -252,7 +252,8 @@ __device__ __forceinline__ void map_unit(int w, int n_groups, int per_group, int
 // Tile loop of the block-sparse forward.  The LDS buffers arrive as distinct
 // restrict pointers so that, once inlined, the compiler can tell a K read from
 // an in-flight V load (and the tile list from both) and waits only for the
-// buffer it reads.  Pipeline per tile t (K_t, V_t already requested):
+// buffer it reads.  The caller has requested K_0 and V_0.  Pipeline per tile t
+// (K_t, V_t already requested):
 //   wait K_t | S_t | request K_{t+1} | softmax_t | wait V_t | PV_t | request V_{t+1}
 __device__ __attribute__((always_inline)) inline void sparse_tiles(
     uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, const int* __restrict__ sList, int nt,
@@ -260,11 +261,6 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     float c, const bf16x8 qop[2][4], UnitState& st, int lane, int l32, int hl) {
   TileOffsets<1, 0> toff;
   toff.init(lane, 0);
-  if (nt > 0) {
-    const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
-    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sK, lane, toff);
-    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, seq_kv - j0 * kBlock, sV, lane, toff);
-  }
   for (int t = 0; t < nt; ++t) {
     const int j = __builtin_amdgcn_readfirstlane(sList[t]);
     const bool more = t + 1 < nt;
@@ -302,13 +298,24 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   const int jd = (geo.q_offset + i * kBlock) / kBlock;
   const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
 
-  const int irow = a.idx_shared ? gi : bh;  // index row: per query head, or per KV group when shared
-  const int nt = stage_tile_list(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, jd, sList, lane);
+  // index row (per query head, or per KV group when shared) and Q requested
+  // together, so their latencies overlap
+  const int irow = a.idx_shared ? gi : bh;
+  int iv[4];
+  load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
+  const int nt = compact_index_row(iv, geo.topk, jd, sList, lane);
+  if (nt > 0) {  // first tile requested before waiting for Q, so the two latencies overlap
+    TileOffsets<1, 0> toff;
+    toff.init(lane, 0);
+    const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
+    tile_load(a.k + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK, lane, toff);
+    tile_load(a.v + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV, lane, toff);
+  }
   UnitState st;
   init_state(st);
-  wait_vmem<0>();  // Q and the index row are in; from here only tile loads use vmcnt
+  wait_vmem<0>();  // Q, and the first tile; from here only tile loads use vmcnt
   __builtin_amdgcn_wave_barrier();
   sparse_tiles(sK, sV, sList, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd, geo.q_offset + i * kBlock,
                geo.scale_log2, qop, st, lane, l32, hl);
@@ -340,26 +347,30 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
   const uint16_t* kbase = a.k + kvoff;
   const uint16_t* vbase = a.v + kvoff;
 
-  const int irow = a.idx_shared ? gi : bh;  // index row: per query head, or per KV group when shared
-  const int nsel = stage_tile_list(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, jd, sList[wave], lane);
+  // index row (per query head, or per KV group when shared) and Q requested
+  // together, so their latencies overlap
+  const int irow = a.idx_shared ? gi : bh;
+  int iv[4];
+  load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
+  const int nsel = compact_index_row(iv, geo.topk, jd, sList[wave], lane);
+  // tiles walked: 0..jd (full), or the shared list (identical in every wave)
+  const int nt = FULL ? jd + 1 : nsel;
+  auto tile_block = [&](int t) { return FULL ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
+  TileOffsets<NW, 0> toff;
+  toff.init(lane, wave);
+  if (nt > 0) {  // first tile requested before waiting for Q, so the two latencies overlap
+    const int j0 = tile_block(0);
+    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK[0], lane, toff);
+    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV[0], lane, toff);
+  }
   UnitState st;
   init_state(st);
   wait_vmem<0>();
   __builtin_amdgcn_wave_barrier();
   const float c = geo.scale_log2;
   const int pos0 = geo.q_offset + i * kBlock;
-  // tiles walked: 0..jd (full), or the shared list (identical in every wave)
-  const int nt = FULL ? jd + 1 : nsel;
-  auto tile_block = [&](int t) { return FULL ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
-  TileOffsets<NW, 0> toff;
-  toff.init(lane, wave);
-  if (nt > 0) {
-    const int j0 = tile_block(0);
-    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK[0], lane, toff);
-    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV[0], lane, toff);
-  }
   int sel_ptr = 0;
   int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
   for (int t = 0; t < nt; ++t) {

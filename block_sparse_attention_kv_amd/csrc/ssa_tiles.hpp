@@ -67,24 +67,33 @@ __device__ __forceinline__ void wait_lds_reads() {
   asm volatile("" ::: "memory");
 }
 
-// Compact this unit's index list into LDS: the entries before the first -1
-// that name a causal block (j <= jd), in list order.  Returns their count.
-// Whole-wave operation; `lst` has room for kMaxTopk entries.
-__device__ __forceinline__ int stage_tile_list(const int32_t* __restrict__ irow, int topk, int jd, int* lst,
-                                               int lane) {
+// One unit's index row into registers: lane e holds entries e + 64c (c < 4),
+// -1 past topk.
+__device__ __forceinline__ void load_index_row(const int32_t* __restrict__ irow, int topk, int lane, int iv[4]) {
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    iv[c] = e < topk ? irow[e] : -1;
+  }
+}
+
+// Compact an index row (as loaded by load_index_row) into LDS: the entries
+// before the first -1 that name a causal block (j <= jd), in list order.
+// Returns their count.  Whole-wave operation; `lst` has room for kMaxTopk
+// entries.
+__device__ __forceinline__ int compact_index_row(const int iv[4], int topk, int jd, int* lst, int lane) {
   int first_neg = topk;
 #pragma unroll
   for (int c = 0; c < kMaxTopk / 64; ++c) {
     const int e = lane + 64 * c;
-    const int j = e < topk ? irow[e] : 0;
-    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < topk && j < 0);
+    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < topk && iv[c] < 0);
     if (neg != 0ull && first_neg == topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
   }
   int n = 0;
 #pragma unroll
   for (int c = 0; c < kMaxTopk / 64; ++c) {
     const int e = lane + 64 * c;
-    const int j = e < topk ? irow[e] : -1;
+    const int j = iv[c];
     const bool keep = e < first_neg && j >= 0 && j <= jd;
     const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
     if (keep) lst[n + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = j;
