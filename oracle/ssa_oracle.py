@@ -23,6 +23,9 @@ What is computed (all arithmetic in float64 unless a step says it rounds):
                                                                      over the heads sharing a KV head)
   4. softmax attention restricted to the selected blocks            [SSA-summary] 2 "Mecanismo Central" (SA stream)
   5. full causal softmax attention (the counterpart output)         [SSA-summary] "Alineacion Bidireccional"
+  4'. optional early stopping: selected blocks visited in decreasing
+     estimated importance, stopping once a block's marginal mass gain
+     falls below a threshold relative to the accumulated mass       [S2O] "Regla de Parada Temprana"
   6. dropped attention mass: full-softmax probability on keys the
      sparse pattern leaves out                                      [SSA-summary] 1 "Planteamiento del Problema",
                                                                      "Alineacion Bidireccional" (delta(t))
@@ -32,6 +35,10 @@ Readings where the pages leave a step open:
     budget ``topk`` counts the forced diagonal block;
   * group-shared selection (one list per KV group) ranks blocks by the mean
     of the group's per-head block scores;
+  * early stopping visits the diagonal block first, then the other selected
+    blocks by coarse score; a query block stops after the first block whose
+    gain is below tau times the accumulated mass for all of its rows (that
+    block is kept);
   * summaries are held in fp32 and scores are rounded to fp32 before the
     top-k decision (the decision is taken in the precision the scores are
     stored in, on both sides);
@@ -361,6 +368,99 @@ def full_attention_dropped_mass(q, k, v, sel, block: int, scale: Optional[float]
 
 
 # --------------------------------------------------------------------------- the whole path
+
+# --------------------------------------------------------------------------- early stopping
+
+def early_stop_order(sel_row, score_row, jd: int):
+    """Visiting order of one query block's selected blocks under early
+    stopping: the diagonal block first, then the other listed blocks by coarse
+    score (higher first, then lower index, NaN last), i.e. in decreasing
+    estimated importance.
+
+    [S2O] "Regla de Parada Temprana" (candidate blocks processed in descending
+    order of estimated importance) and "Implementacion del Kernel" (a dense
+    pass over the query's own segment initialises the softmax state first)."""
+    listed = [int(j) for j in sel_row if j >= 0]
+    others = sorted((j for j in listed if j != jd), key=lambda j: _rank_key(float(score_row[j]), j))
+    return ([jd] if jd in listed else []) + others
+
+
+def _early_stop_count(gains, tau: float) -> int:
+    """Number of blocks visited: stop after the first block t >= 1 whose gain
+    is below tau times the mass of the blocks before it, for every row."""
+    for t in range(1, len(gains)):
+        if np.all(gains[t] < tau * sum(gains[:t])):
+            return t + 1
+    return len(gains)
+
+
+def early_stop_attention(q, k, v, scores, sel, tau: float, block: int, scale: Optional[float] = None,
+                         q_offset: int = 0, used=None):
+    """Block-sparse attention with early stopping over the selected blocks.
+
+    Query block i visits its blocks in early_stop_order.  For every block
+    after the first, the marginal gain of row r is
+        g_r = sum over the block's keys c <= pos_r of exp(scale * q_r . k_c)
+    and the mass accumulated before it is L_r = the same sum over the blocks
+    visited before it.  When g_r < tau * L_r for every row of the query block,
+    that block is kept and the remaining ones are skipped.  Each row then
+    attends over the keys c <= pos_r of the visited blocks.
+
+    [S2O] "Regla de Parada Temprana" (stop once the marginal gain in attention
+    mass of a processed block falls below a threshold relative to the
+    accumulated mass) and "Implementacion del Kernel".
+
+    ``used`` (int [b, Hq, nqb]) imposes the number of visited blocks instead of
+    the rule.  Returns (O [b,Hq,seq_q,d], LSE [b,Hq,seq_q], used [b,Hq,nqb],
+    ratio [b,Hq,nqb,topk]) where ratio[..., t] = max over the block's rows of
+    g_r / L_r at block t of the order (t >= 1; NaN where there is none)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    scores = _f64(scores)
+    b, hq, seq_q, d = q.shape
+    hkv, seq_kv = k.shape[1], k.shape[2]
+    group = hq // hkv
+    _check_geometry(seq_q, seq_kv, q_offset, block)
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    nqb = n_blocks(seq_q, block)
+    topk = sel.shape[-1]
+    out = np.empty((b, hq, seq_q, d))
+    lse = np.empty((b, hq, seq_q))
+    used_out = np.zeros((b, hq, nqb), dtype=np.int64)
+    ratio = np.full((b, hq, nqb, topk), np.nan)
+    for bi in range(b):
+        for h in range(hq):
+            g = h // group
+            for i in range(nqb):
+                jd = diag_block(i, q_offset, block)
+                order = early_stop_order(sel[bi, h, i], scores[bi, h, i], jd)
+                r0, r1 = i * block, min((i + 1) * block, seq_q)
+                pos = q_offset + np.arange(r0, r1)
+                # per-block logits of the rows, causal keys only (-inf elsewhere)
+                blk_logits = []
+                for j in order:
+                    c = np.arange(j * block, min((j + 1) * block, seq_kv))
+                    lg = scale * (q[bi, h, r0:r1] @ k[bi, g, c].T)
+                    lg[c[None, :] > pos[:, None]] = -np.inf
+                    blk_logits.append((c, lg))
+                mrow = np.max(np.concatenate([lg for _, lg in blk_logits], axis=1), axis=1)
+                gains = [np.exp(lg - mrow[:, None]).sum(axis=1) for _, lg in blk_logits]
+                acc = gains[0].copy() if gains else np.zeros(r1 - r0)
+                for t in range(1, len(order)):
+                    ratio[bi, h, i, t] = float(np.max(gains[t] / acc))
+                    acc = acc + gains[t]
+                n_used = _early_stop_count(gains, tau) if used is None else int(used[bi, h, i])
+                used_out[bi, h, i] = n_used
+                cols = np.concatenate([c for c, _ in blk_logits[:n_used]])
+                lg = np.concatenate([lg for _, lg in blk_logits[:n_used]], axis=1)
+                m = lg.max(axis=1, keepdims=True)
+                w = np.exp(lg - m)
+                z = w.sum(axis=1, keepdims=True)
+                out[bi, h, r0:r1] = (w @ v[bi, g, cols]) / z
+                lse[bi, h, r0:r1] = (m + np.log(z))[:, 0]
+    return out, lse, used_out, ratio
+
 
 def hot_path(q, k, v, block: int, topk: int, scale: Optional[float] = None, q_offset: int = 0,
              k_summary=None, full_row_range: Optional[Tuple[int, int]] = None, with_full: bool = True,

@@ -387,12 +387,102 @@ def check_shared_brute_force(O):
                    key=lambda comb: sorted((-float(np.float32(tot[j] / 3)), j) for j in comb))
         assert list(sel[0, 0, i]) == sorted(list(best) + [i]), (i, sel[0, 0, i], best)
 
+
+def check_early_stop_hand_example(O):
+    # One head, d = 1, B = 1 (each block is one key), scale 1: logits equal
+    # the keys 0, 1, 2, 3.  Query row 3 visits its own block 3 first, then
+    # blocks 2, 0, 1 (coarse scores 5, 4, 1).  Worked by hand:
+    #   block 2: gain e^2 against e^3            ratio e^-1            = 0.3679
+    #   block 0: gain 1 against e^3 + e^2        ratio 1/(e^3 + e^2)   = 0.0367
+    #   block 1: gain e against e^3 + e^2 + 1    ratio e/(e^3 + e^2 + 1) = 0.0992
+    q = np.ones((1, 1, 4, 1))
+    kk = np.array([0.0, 1.0, 2.0, 3.0]).reshape(1, 1, 4, 1)
+    v = np.arange(4.0).reshape(1, 1, 4, 1) * 10.0
+    sc = np.full((1, 1, 4, 4), -np.inf)
+    sc[0, 0, 3, :4] = [4.0, 1.0, 5.0, 0.0]
+    for i in range(3):
+        sc[0, 0, i, : i + 1] = 0.0
+    sel = O.select_blocks(sc, 4, 1)
+    e = math.e
+    _, _, used, ratio = O.early_stop_attention(q, kk, v, sc, sel, 0.3, 1, scale=1.0)
+    np.testing.assert_allclose(ratio[0, 0, 3, 1:], [1 / e, 1 / (e ** 3 + e ** 2), e / (e ** 3 + e ** 2 + 1)], rtol=1e-14)
+    assert used[0, 0, 3] == 3                       # stops after block 0, which is kept
+    o, lse, used, _ = O.early_stop_attention(q, kk, v, sc, sel, 0.5, 1, scale=1.0)
+    assert used[0, 0, 3] == 2                       # stops after block 2
+    w = np.array([e ** 3, e ** 2])
+    np.testing.assert_allclose(o[0, 0, 3, 0], (w * [30.0, 20.0]).sum() / w.sum(), rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0, 3], math.log(w.sum()), rtol=1e-14)
+    _, _, used, _ = O.early_stop_attention(q, kk, v, sc, sel, 0.03, 1, scale=1.0)
+    assert used[0, 0, 3] == 4                       # no ratio below 0.03: every block
+
+
+def check_early_stop_limits(O):
+    q, k, v = rand_qkv(1, 4, 2, 512, 16)
+    s = O.block_scores(q, k, 64)
+    sel = O.select_blocks(s, 4, 64)
+    o_sp, l_sp = O.sparse_attention(q, k, v, sel, 64)
+    # tau = 0 never stops: the plain block-sparse forward
+    o0, l0, used0, _ = O.early_stop_attention(q, k, v, s, sel, 0.0, 64)
+    assert np.array_equal(used0, (sel >= 0).sum(-1))
+    np.testing.assert_allclose(o0, o_sp, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l0, l_sp, rtol=1e-12, atol=1e-12)
+    # tau = inf stops after the first block past the diagonal: the best-scored one
+    oi, li, usedi, _ = O.early_stop_attention(q, k, v, s, sel, np.inf, 64)
+    assert np.array_equal(usedi, np.minimum((sel >= 0).sum(-1), 2))
+    best = sel.copy()
+    for h in range(4):
+        for i in range(8):
+            order = O.early_stop_order(sel[0, h, i], s[0, h, i], i)
+            row = sorted(order[:2])
+            best[0, h, i] = row + [-1] * (4 - len(row))
+    o_b, l_b = O.sparse_attention(q, k, v, best, 64)
+    np.testing.assert_allclose(oi, o_b, rtol=1e-12, atol=1e-12)
+    # monotone: a larger threshold never visits more blocks
+    prev = None
+    for tau in (0.0, 0.01, 0.05, 0.2, 1.0, np.inf):
+        u = O.early_stop_attention(q, k, v, s, sel, tau, 64)[2]
+        if prev is not None:
+            assert np.all(u <= prev)
+        prev = u
+
+
+def check_early_stop_loops(O):
+    # the ratios and decisions recomputed key by key with math.exp
+    q, k, v = rand_qkv(1, 2, 1, 192, 8)
+    s = O.block_scores(q, k, 64)
+    sel = O.select_blocks(s, 3, 64)
+    tau = 0.05
+    _, _, used, ratio = O.early_stop_attention(q, k, v, s, sel, tau, 64)
+    sc = 1 / math.sqrt(8)
+    sc = float(np.float32(sc))
+    for h in range(2):
+        for i in range(3):
+            order = [i] + sorted((int(j) for j in sel[0, h, i] if 0 <= j < i), key=lambda j: (-s[0, h, i, j], j))
+            rows = range(64 * i, 64 * i + 64)
+            gains = []
+            for j in order:
+                gr = []
+                for r in rows:
+                    lg = [sc * sum(q[0, h, r, t] * k[0, 0, c, t] for t in range(8)) for c in range(64 * j, 64 * j + 64) if c <= r]
+                    mx = max(sc * sum(q[0, h, r, t] * k[0, 0, c, t] for t in range(8)) for jj in order
+                             for c in range(64 * jj, 64 * jj + 64) if c <= r)
+                    gr.append(sum(math.exp(x - mx) for x in lg))
+                gains.append(gr)
+            want = len(order)
+            for t in range(1, len(order)):
+                rt = max(gains[t][n] / sum(gains[u][n] for u in range(t)) for n in range(64))
+                assert abs(rt - ratio[0, h, i, t]) <= 1e-12 * max(1.0, rt)
+                if want == len(order) and all(gains[t][n] < tau * sum(gains[u][n] for u in range(t)) for n in range(64)):
+                    want = t + 1
+            assert used[0, h, i] == want
+
 ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_causal,
               check_select_brute_force, check_select_ties_and_decode, check_sparse_vs_sdpa,
               check_sparse_special_cases, check_sparse_brute_force_loops,
               check_full_and_dropped_identities, check_tie_closed_form, check_decode,
               check_shared_hand_example, check_shared_scores_pool_queries, check_shared_reductions,
-              check_shared_brute_force]
+              check_shared_brute_force, check_early_stop_hand_example, check_early_stop_limits,
+              check_early_stop_loops]
 
 
 # ----------------------------------------------------------------------------- the pins
@@ -443,6 +533,9 @@ MUTANTS = {
     "drops_last_selected_block": ("_allowed_keys", None),
     "shared_uses_first_head": ("shared_block_scores", None),
     "shared_sum_not_mean": ("shared_block_scores", None),
+    "early_stop_drops_trigger_block": ("_early_stop_count", None),
+    "early_stop_counts_own_gain": ("_early_stop_count", None),
+    "early_stop_index_order": ("early_stop_order", None),
 }
 
 
@@ -478,9 +571,30 @@ def _mutant_shared_sum(scores, n_kv_heads):
     return _orig_shared(scores, n_kv_heads) * g
 
 
+def _mutant_drop_trigger(gains, tau):
+    for t in range(1, len(gains)):
+        if np.all(gains[t] < tau * sum(gains[:t])):
+            return t
+    return len(gains)
+
+
+def _mutant_own_gain(gains, tau):
+    for t in range(1, len(gains)):
+        if np.all(gains[t] < tau * sum(gains[: t + 1])):
+            return t + 1
+    return len(gains)
+
+
+def _mutant_index_order(sel_row, score_row, jd):
+    listed = sorted(int(j) for j in sel_row if j >= 0)
+    return ([jd] if jd in listed else []) + [j for j in listed if j != jd]
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch, golden_dir):
     attr, fn = MUTANTS[name]
+    fn = {"early_stop_drops_trigger_block": _mutant_drop_trigger, "early_stop_counts_own_gain": _mutant_own_gain,
+          "early_stop_index_order": _mutant_index_order}.get(name, fn)
     if name == "shared_uses_first_head":
         fn = _mutant_shared_first_head
     if name == "shared_sum_not_mean":
