@@ -250,6 +250,45 @@ def bench_decode(args, torch, ssa, W, shared=False):
     }
 
 
+def bench_early_stop(args, torch, ssa, W, taus=(0.05, 1.0)):
+    """Block-sparse forward with early stopping on the bench workload, for a
+    few thresholds: time, blocks visited per query block, and the useful
+    (visited, unmasked) work rate."""
+    w = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.make_inputs(w))
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    scores, _ = ssa.ssa_block_scores(shape, q, k)
+    idx = ssa.ssa_select_topk(shape, scores)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    nqb = ssa.n_blocks(w.seq_q, w.block)
+    used = torch.empty((w.batch, w.n_q_heads, nqb), dtype=torch.int32, device=dev)
+    listed = float((idx >= 0).sum(-1).float().mean())
+    res = {"workload": w.name, "blocks_listed_per_query_block": round(listed, 3), "thresholds": {}}
+    n = max(1, args.steps // 2)
+    for tau in taus:
+        for _ in range(3):
+            ssa.ssa_block_sparse_attn_fwd_early_stop(shape, q, k, v, scores, idx, tau, out, lse, used)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            ssa.ssa_block_sparse_attn_fwd_early_stop(shape, q, k, v, scores, idx, tau, out, lse, used)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        # useful pairs: the diagonal block's causal half plus every other visited block
+        # (every query block of this workload is complete)
+        u = used.double()
+        pairs = float((w.block * (w.block + 1) / 2 + (u - 1).clamp(min=0) * w.block * w.block).sum())
+        tf = 4.0 * w.head_dim * pairs / (ms * 1e-3) / 1e12
+        res["thresholds"][str(tau)] = {"avg_ms": round(ms, 5), "blocks_visited_per_query_block": round(float(u.mean()), 3),
+                                       "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return res
+
+
 def cpu_baseline(args, W):
     """The fp64 oracle, as it stands, on a bounded sample of the prefill workload:
     whole query heads (all rows, all five steps) until ~target seconds elapse."""
@@ -311,7 +350,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=60)
     ap.add_argument("--decode-copies", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-shared", action="store_true", help="skip the group-shared selection legs")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the extra legs (group-shared selection, early stopping)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--counter-pass", action="store_true",
@@ -371,6 +411,7 @@ def main():
                        "traffic": measured_traffic("sparse_attn")},
         "decode": dec,
         "shared_selection": shared,
+        "early_stop": None if args.no_shared else bench_early_stop(args, torch, ssa, W),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

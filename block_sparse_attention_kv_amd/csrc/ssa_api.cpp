@@ -272,6 +272,41 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass_shared(const ssa_shape_t* shape, con
                    dropped_mass, stream, "ssa_full_attn_fwd_dropped_mass_shared");
 }
 
+ssa_status_t ssa_block_sparse_attn_fwd_early_stop(const ssa_shape_t* shape, const void* q, const void* k,
+                                                  const void* v, const float* scores, const int32_t* block_idx,
+                                                  float tau, void* out, float* lse, int32_t* blocks_used,
+                                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  const char* fn = "ssa_block_sparse_attn_fwd_early_stop";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (!(tau >= 0.f)) return fail(SSA_ERR_INVALID_ARG, "%s: tau must be >= 0 (got %g)", fn, (double)tau);
+  if (empty) return SSA_OK;
+  CHECK_PTR(q, 16, fn);
+  CHECK_PTR(k, 16, fn);
+  CHECK_PTR(v, 16, fn);
+  CHECK_PTR(scores, 4, fn);
+  CHECK_PTR(block_idx, 4, fn);
+  CHECK_PTR(out, 16, fn);
+  CHECK_PTR(lse, 4, fn);
+  CHECK_PTR(blocks_used, 4, fn);
+  ssa::AttnArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.idx = block_idx;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.qb_begin = 0;
+  a.qb_count = g.nqb;
+  a.rows_out = g.seq_q;
+  hipError_t e = ssa::launch_attn_early_stop(a, scores, tau, blocks_used, g, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
 size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {
   ssa::Geometry g;
   bool empty;

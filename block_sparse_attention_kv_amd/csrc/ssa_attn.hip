@@ -91,9 +91,12 @@ __device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[
 }
 
 // Online-softmax update for one tile; leaves packed bf16 probabilities in pk.
+// tile_rs (optional) receives this lane's fp32 sum of the tile's
+// probabilities per query block (relative to the updated reference max).
 template <bool FULL>
 __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x4 pk[2][2][2], bool diag,
-                                             bool selected, int key0, int pos0, int l32, int hl, float c) {
+                                             bool selected, int key0, int pos0, int l32, int hl, float c,
+                                             float* tile_rs = nullptr) {
   if (diag) {
     // Causal mask of the tile holding the query rows' own positions: key > pos
     // becomes -inf.  Branch-free sign arithmetic (no compare masks to keep live).
@@ -154,6 +157,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
           rs1 += p1;
         }
     const float rs = rs0 + rs1;
+    if (tile_rs) tile_rs[qb] = rs;
     st.l[qb] += rs;
     if (FULL && !selected) st.ld[qb] += rs;
   }
@@ -322,6 +326,124 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
 }
 
+// Block-sparse forward with early stopping.  One wavefront per unit, as
+// attn_sparse_kernel, but the unit's blocks are visited diagonal first and
+// then by coarse score (higher first, lower index on ties, NaN last); after
+// each block past the first, the unit stops if for every valid row the
+// block's mass is below tau times the mass accumulated before it (the block
+// is kept).  blocks_used[b,h,i] records how many blocks were visited.
+// Method: S2O summary, "Regla de Parada Temprana" and "Implementacion del
+// Kernel" (own segment first, then the prefix in decreasing importance).
+__global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs a, Geometry geo,
+                                                                       const float* __restrict__ scores, float tau,
+                                                                       int32_t* __restrict__ blocks_used) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[kTileBytes];
+  __shared__ int sList[kMaxTopk];
+  __shared__ int sOrder[kMaxTopk];
+  __shared__ uint32_t sKey[kMaxTopk];
+  const int lane = threadIdx.x, hl = lane >> 5, l32 = lane & 31;
+  const int G = geo.group;
+  int gi, u;
+  map_unit(blockIdx.x, geo.batch * geo.hkv, G * a.qb_count, gi, u);
+  const int i = a.qb_begin + a.qb_count - 1 - u / G;
+  const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+  const int h = g * G + (u - (u / G) * G);
+  const int bh = b * geo.hq + h;
+  const int jd = (geo.q_offset + i * kBlock) / kBlock;
+  const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
+  const uint16_t* kbase = a.k + kvoff;
+  const uint16_t* vbase = a.v + kvoff;
+
+  int iv[4];
+  load_index_row(a.idx + ((size_t)bh * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
+  bf16x8 qop[2][4];
+  load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
+  const int n = compact_index_row(iv, geo.topk, jd, sList, lane);
+  // visiting order: the diagonal block, then the rest by (score desc, index asc)
+  const float* srow = scores + ((size_t)bh * geo.nqb + i) * geo.nkb;
+  int has_diag = 0;
+  for (int e = lane; e < n; e += 64) {
+    const int j = sList[e];
+    has_diag |= j == jd;
+    sKey[e] = orderable_score(srow[j]);  // each listed block's score read once
+  }
+  has_diag = __builtin_amdgcn_ballot_w64(has_diag != 0) != 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int e = lane; e < n; e += 64) {
+    const int j = sList[e];
+    if (j == jd) {
+      sOrder[0] = j;
+      continue;
+    }
+    const uint32_t kj = sKey[e];
+    int rank = 0;
+    for (int f = 0; f < n; ++f) {
+      const int jf = sList[f];
+      const uint32_t kf = sKey[f];
+      rank += (jf != jd && (kf > kj || (kf == kj && jf < j))) ? 1 : 0;
+    }
+    sOrder[has_diag + rank] = j;
+  }
+  const int nt = n;
+  TileOffsets<1, 0> toff;
+  toff.init(lane, 0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (nt > 0) {
+    const int j0 = __builtin_amdgcn_readfirstlane(sOrder[0]);
+    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK, lane, toff);
+    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV, lane, toff);
+  }
+  UnitState st;
+  init_state(st);
+  wait_vmem<0>();  // Q and the first tile
+  __builtin_amdgcn_wave_barrier();
+  const float c = geo.scale_log2;
+  const int pos0 = geo.q_offset + i * kBlock;
+  int used = 0;
+  for (int t = 0; t < nt; ++t) {
+    const int j = __builtin_amdgcn_readfirstlane(sOrder[t]);
+    const bool more = t + 1 < nt;
+    const int jn = more ? __builtin_amdgcn_readfirstlane(sOrder[t + 1]) : 0;
+    wait_vmem<8>();  // K_t landed (V_t may still be in flight)
+    f32x16 s[2][2];
+    tile_scores(sK, qop, l32, hl, s);
+    wait_lds_reads();
+    if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sK, lane, toff);
+    u32x4 pk[2][2][2];
+    float trs[2];
+    tile_softmax<false>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c, trs);
+    // stop after this tile if every valid row gained less than tau times its earlier mass
+    bool stop = false;
+    if (t > 0) {
+      bool keep_going = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float gain = sum_xor32(trs[qb]);
+        const float before = sum_xor32(st.l[qb] - trs[qb]);
+        const bool valid = i * kBlock + 32 * qb + l32 < geo.seq_q;
+        keep_going |= valid && !(gain < tau * before);
+      }
+      stop = __builtin_amdgcn_ballot_w64(keep_going) == 0ull;
+    }
+    if (more && !stop)
+      wait_vmem<8>();  // V_t landed (K_{t+1} may still be in flight)
+    else
+      wait_vmem<0>();
+    tile_pv(sV, pk, st, lane);
+    wait_lds_reads();
+    used = t + 1;
+    if (stop) break;
+    if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sV, lane, toff);
+  }
+  unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
+  if (lane == 0) blocks_used[(size_t)bh * geo.nqb + i] = used;
+}
+
 // NW query heads of one KV group per workgroup (one per wave) walk the same
 // tiles, fetched once into a double buffer shared by the NW waves; tile t+1 is
 // requested as soon as every wave has finished tile t-1.
@@ -402,6 +524,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
 }
 
 }  // namespace
+
+hipError_t launch_attn_early_stop(const AttnArgs& a, const float* scores, float tau, int32_t* blocks_used,
+                                  const Geometry& g, hipStream_t stream) {
+  const size_t units = (size_t)g.batch * g.hq * a.qb_count;
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_sparse_early_stop_kernel, dim3((unsigned)units), dim3(64), 0, stream, a, g, scores, tau,
+                     blocks_used);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream) {
   const size_t units = (size_t)g.batch * g.hq * a.qb_count;

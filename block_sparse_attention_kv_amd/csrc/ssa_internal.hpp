@@ -70,6 +70,8 @@ hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float
 hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g, bool shared,
                               hipStream_t stream);
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream);
+hipError_t launch_attn_early_stop(const AttnArgs& a, const float* scores, float tau, int32_t* blocks_used,
+                                  const Geometry& g, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometry& g,
                               hipStream_t stream);
 

@@ -23,7 +23,8 @@ SSA_OP_BLOCK_SCORES, SSA_OP_SELECT_TOPK, SSA_OP_SPARSE_FWD, SSA_OP_FULL_FWD = ra
 EXPORTED_SYMBOLS = (
     "ssa_block_summaries", "ssa_block_scores", "ssa_select_topk", "ssa_block_sparse_attn_fwd",
     "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared", "ssa_block_sparse_attn_fwd_shared",
-    "ssa_full_attn_fwd_dropped_mass_shared", "ssa_workspace_bytes", "ssa_status_string",
+    "ssa_full_attn_fwd_dropped_mass_shared", "ssa_block_sparse_attn_fwd_early_stop", "ssa_workspace_bytes",
+    "ssa_status_string",
     "ssa_last_error", "ssa_version",
 )
 
@@ -70,9 +71,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssa_select_topk_shared.argtypes = [sp, vp, vp, vp]
     lib.ssa_block_sparse_attn_fwd_shared.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssa_full_attn_fwd_dropped_mass_shared.argtypes = [sp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.ssa_block_sparse_attn_fwd_early_stop.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                                         sz, vp]
     for fn in ("ssa_block_summaries", "ssa_block_scores", "ssa_select_topk",
                "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared",
-               "ssa_block_sparse_attn_fwd_shared", "ssa_full_attn_fwd_dropped_mass_shared"):
+               "ssa_block_sparse_attn_fwd_shared", "ssa_full_attn_fwd_dropped_mass_shared",
+               "ssa_block_sparse_attn_fwd_early_stop"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ssa_workspace_bytes.argtypes = [sp, ctypes.c_int]
     lib.ssa_workspace_bytes.restype = ctypes.c_size_t
@@ -226,6 +230,23 @@ def ssa_full_attn_fwd_dropped_mass(shape: Shape, q, k, v, block_idx, q_block_beg
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), int(q_block_begin),
         int(q_block_count), _ptr(out), _ptr(lse), _ptr(dropped), None, 0, _stream(q.device)))
     return out, lse, dropped
+
+
+def ssa_block_sparse_attn_fwd_early_stop(shape: Shape, q, k, v, scores, block_idx, tau: float, out=None, lse=None,
+                                         blocks_used=None):
+    """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q], blocks_used int32 [b, Hq, nqb])."""
+    _require_gpu(q, k, v, scores, block_idx, out, lse, blocks_used)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if blocks_used is None:
+        blocks_used = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block)),
+                                  dtype=torch.int32, device=q.device)
+    _check("ssa_block_sparse_attn_fwd_early_stop", load_library().ssa_block_sparse_attn_fwd_early_stop(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(scores), _ptr(block_idx), float(tau), _ptr(out),
+        _ptr(lse), _ptr(blocks_used), None, 0, _stream(q.device)))
+    return out, lse, blocks_used
 
 
 def default_scale(head_dim: int) -> float:

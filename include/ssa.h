@@ -196,6 +196,32 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass_shared(const ssa_shape_t* shape, con
                                                    void* workspace, size_t workspace_bytes,
                                                    hipStream_t stream);
 
+/* Block-sparse attention forward with early stopping over the selected
+ * blocks.  Query block i visits the blocks of block_idx[b,h,i,:] in
+ * decreasing estimated importance: its diagonal block first, then the others
+ * by scores[b,h,i,j] (higher first, lower index on ties, NaN last).  After
+ * each block past the first, if every row r of the block (r < seq_q) has
+ *   gain_r < tau * before_r,
+ * where gain_r is the softmax mass (sum of exp(scale * q_r . k_c) over the
+ * block's keys c <= q_offset + r) and before_r the same mass over the blocks
+ * visited before it, the block is kept and the remaining ones are skipped.
+ * Rows then attend over the keys of the visited blocks (out, lse as in
+ * ssa_block_sparse_attn_fwd) and blocks_used[b,h,i] counts them.  tau = 0
+ * never stops; larger tau stops sooner.  The decision is taken in fp32.
+ * [S2O] "Regla de Parada Temprana" (stop once the marginal gain in attention
+ * mass of a processed block falls below a threshold relative to the
+ * accumulated mass; blocks processed in descending estimated importance) and
+ * "Implementacion del Kernel" (the query's own segment first).
+ *   scores       fp32 [b,Hq,nqb,nkb] (as written by ssa_block_scores)
+ *   block_idx    int32 [b,Hq,nqb,topk] (as written by ssa_select_topk)
+ *   tau          >= 0 (else SSA_ERR_INVALID_ARG)
+ *   out, lse     as ssa_block_sparse_attn_fwd;  blocks_used int32 [b,Hq,nqb] (output)
+ * No workspace is needed (workspace may be NULL). */
+ssa_status_t ssa_block_sparse_attn_fwd_early_stop(const ssa_shape_t* shape, const void* q, const void* k,
+                                                  const void* v, const float* scores, const int32_t* block_idx,
+                                                  float tau, void* out, float* lse, int32_t* blocks_used,
+                                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes an entry point needs for this shape (0 if none; SIZE_MAX if
  * the shape is invalid). */
 size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op);

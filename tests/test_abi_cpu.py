@@ -78,6 +78,8 @@ def test_shape_validation(lib, kw, status):
     assert lib.ssa_block_sparse_attn_fwd_shared(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == status
     assert lib.ssa_full_attn_fwd_dropped_mass_shared(p, FAKE, FAKE, FAKE, FAKE, 0, 1, FAKE, FAKE, FAKE, None, 0,
                                                      None) == status
+    assert lib.ssa_block_sparse_attn_fwd_early_stop(p, FAKE, FAKE, FAKE, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, None,
+                                                    0, None) == status
     assert lib.ssa_last_error()
 
 
@@ -98,6 +100,17 @@ def test_pointer_validation(lib):
     # query-block range outside the problem
     assert lib.ssa_full_attn_fwd_dropped_mass(p, FAKE, FAKE, FAKE, FAKE, 3, 2, FAKE, FAKE, FAKE, None, 0,
                                               None) == ssa.SSA_ERR_INVALID_ARG
+
+
+def test_early_stop_threshold_validation(lib):
+    p = ctypes.byref(good_shape())
+    for tau in (-0.5, float("nan")):
+        assert lib.ssa_block_sparse_attn_fwd_early_stop(p, FAKE, FAKE, FAKE, FAKE, FAKE, tau, FAKE, FAKE, FAKE, None,
+                                                        0, None) == ssa.SSA_ERR_INVALID_ARG
+        assert b"tau" in lib.ssa_last_error()
+    assert lib.ssa_block_sparse_attn_fwd_early_stop(p, FAKE, FAKE, FAKE, None, FAKE, 0.1, FAKE, FAKE, FAKE, None,
+                                                    0, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"scores is NULL" in lib.ssa_last_error()
 
 
 def test_decode_workspace(lib):

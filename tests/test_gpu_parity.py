@@ -370,3 +370,65 @@ def test_decode_32k_shared_full_size(dev):
     o_ref, lse_ref = O.sparse_attention(qn, kn, vn, per_head(g["idx"][sub].numpy(), w, True), B, q_offset=w.q_offset)
     P.check_close_outputs(g["o"][sub], o_ref, "O_decode shared")
     P.check_abs(g["lse"][sub], lse_ref, P.LSE_ABS, "LSE_decode shared")
+
+
+# ----------------------------------------------------------------------------- early stopping
+
+def check_early_stop(w: W.Workload, taus, dev, heads=None):
+    """GPU early stopping vs the oracle.  The oracle orders the blocks with the
+    GPU's own (checked) scores and index lists; the number of visited blocks
+    must match except where the deciding ratio lies within 1e-3 of tau, and
+    the outputs must match the oracle evaluated with the GPU's counts."""
+    q, k, v = W.make_inputs(w)
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    scores, _ = ssa.ssa_block_scores(shape, qd, kd)
+    idx = ssa.ssa_select_topk(shape, scores)
+    o_all, l_all = ssa.ssa_block_sparse_attn_fwd(shape, qd, kd, vd, idx)
+    hs = list(range(w.n_q_heads)) if heads is None else heads
+    G = w.n_q_heads // w.n_kv_heads
+    qn = q[:, hs].double().numpy()
+    kn, vn = k.double().numpy(), v.double().numpy()
+    # the oracle takes K/V per query head here (head h -> its KV head)
+    kn = np.stack([kn[:, h // G] for h in hs], axis=1)
+    vn = np.stack([vn[:, h // G] for h in hs], axis=1)
+    s_g = P.np64(scores.cpu())[:, hs]
+    i_g = idx.cpu().numpy()[:, hs]
+    for tau in taus:
+        say(f"{w.name} early stop tau={tau}")
+        o, lse, used = ssa.ssa_block_sparse_attn_fwd_early_stop(shape, qd, kd, vd, scores, idx, tau)
+        torch.cuda.synchronize()
+        used_g = used.cpu().numpy()[:, hs]
+        _, _, used_ref, ratio = O.early_stop_attention(qn, kn, vn, s_g, i_g, tau, B, q_offset=w.q_offset)
+        for bi, hh, i in np.argwhere(used_g != used_ref):
+            t = min(used_g[bi, hh, i], used_ref[bi, hh, i]) - 1      # the decision the two sides took differently
+            r = ratio[bi, hh, i, t]
+            assert abs(r - tau) <= 1e-3 * tau, (w.name, tau, (bi, hh, i), used_g[bi, hh, i], used_ref[bi, hh, i], r)
+        o_ref, lse_ref, _, _ = O.early_stop_attention(qn, kn, vn, s_g, i_g, tau, B, q_offset=w.q_offset,
+                                                       used=used_g)
+        P.check_close_outputs(o[:, hs].cpu(), o_ref, f"O early stop tau={tau}")
+        P.check_abs(lse[:, hs].cpu(), lse_ref, P.LSE_ABS, f"LSE early stop tau={tau}")
+        if tau == 0.0:
+            assert np.array_equal(used_g, (i_g >= 0).sum(-1))
+            P.check_close_outputs(o.cpu(), o_all.cpu(), "tau=0 vs block-sparse forward")
+        if tau >= 1.0:  # the rule must actually stop somewhere on these inputs
+            assert used_g.sum() < (i_g >= 0).sum()
+        print(f"[case] {w.name} tau={tau}: mean blocks visited {used_g.mean():.2f} of {(i_g >= 0).sum(-1).mean():.2f}",
+              flush=True)
+
+
+EARLY_STOP = [
+    (W.Workload("es_gqa8_2k", 1, 8, 2, 2048, 2048, 64, 64, 8, seed=51), [0.0, 0.05, 0.2, 1.0]),
+    (W.Workload("es_ragged_1000", 2, 4, 2, 1000, 1000, 64, 64, 5, seed=52), [0.0, 0.1, 2.0]),
+    (W.Workload("es_planted_2k", 1, 8, 2, 2048, 2048, 64, 64, 6, seed=53, variant="planted"), [0.02, 0.3, 1.0]),
+    (W.Workload("es_chunked", 1, 4, 2, 192, 320, 64, 64, 3, seed=54), [0.1, 1e30]),
+]
+
+
+@pytest.mark.parametrize("case", EARLY_STOP, ids=lambda c: c[0].name)
+def test_early_stop_parity(dev, case):
+    check_early_stop(case[0], case[1], dev)
+
+
+def test_early_stop_prefill_8k(dev):
+    check_early_stop(W.PREFILL_8K, [0.05, 1.0], dev, heads=[0, 17])
