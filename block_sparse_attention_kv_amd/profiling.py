@@ -9,8 +9,8 @@
 
 Kernel names are matched by substring: attn_group_kernel<NW, true> is the
 full counterpart, attn_group_kernel<NW, false> the block-sparse forward with a
-group-shared selection, attn_sparse_kernel the block-sparse forward,
-attn_decode_partial_kernel the decode gather.
+group-shared selection, attn_sparse_kernel the block-sparse forward, attn_sparse_early_stop_kernel its
+early-stopping variant, attn_decode_partial_kernel the decode gather.
 """
 from __future__ import annotations
 
@@ -48,6 +48,8 @@ def classify(name: str):
         # attn_group_kernel<NW, FULL>: demangled "..., true>" / mangled "...Lb1E..."
         full = ("true>" in name) or ("Lb1E" in name)
         return "full_attn" if full else "sparse_attn_shared"
+    if "attn_sparse_early_stop_kernel" in name:
+        return "sparse_attn_early_stop"
     if "attn_sparse_kernel" in name:
         return "sparse_attn"
     if "attn_decode_partial_kernel" in name:
@@ -60,6 +62,8 @@ def classify(name: str):
         return "decode_scores"
     if "block_summaries_kernel" in name:
         return "block_summaries"
+    if "select_topk_shared_kernel" in name:
+        return "select_topk_shared"
     if "select_topk_kernel" in name:
         return "select_topk"
     if "copyBuffer" in name:
