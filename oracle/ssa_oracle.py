@@ -29,6 +29,11 @@ What is computed (all arithmetic in float64 unless a step says it rounds):
   6. dropped attention mass: full-softmax probability on keys the
      sparse pattern leaves out                                      [SSA-summary] 1 "Planteamiento del Problema",
                                                                      "Alineacion Bidireccional" (delta(t))
+  7. gradients of steps 4 and 5 with respect to Q, K, V for a given
+     output gradient (chain rule through the masked softmax)       [SSA-summary] 1 "Planteamiento del Problema"
+                                                                     (dropped keys get no gradient in the sparse
+                                                                     stream), 2 "Mecanismo Central" (the full
+                                                                     stream reaches every token)
 
 Readings where the pages leave a step open:
   * selection is per query block (block-mean query), per query head; the
@@ -39,6 +44,9 @@ Readings where the pages leave a step open:
     blocks by coarse score; a query block stops after the first block whose
     gain is below tau times the accumulated mass for all of its rows (that
     block is kept);
+  * the backward takes the output gradient as given (the alignment losses
+    that would produce it have no stated functional form); only O carries
+    gradient (not LSE or the dropped mass);
   * summaries are held in fp32 and scores are rounded to fp32 before the
     top-k decision (the decision is taken in the precision the scores are
     stored in, on both sides);
@@ -365,6 +373,82 @@ def full_attention_dropped_mass(q, k, v, sel, block: int, scale: Optional[float]
                 dropped = (~selected)[None, :] & ~future
                 delta[bi, h, r0 - lo:r1 - lo] = np.where(dropped, np.exp(logits - row_lse), 0.0).sum(axis=1)
     return out, lse, delta
+
+
+# --------------------------------------------------------------------------- backward
+
+def _block_backward(qb, kc, vc, dob, allowed, scale):
+    """Gradients of L = sum(dob * o) for the query rows qb [n, d] of one query
+    block, where row r's output o_r is softmax attention over the keys kc
+    [m, d] / values vc [m, d] that ``allowed`` [n, m] marks for it.  With P the
+    masked softmax probabilities:
+        dV  = P^T dO
+        dP  = dO V^T
+        dS  = P * (dP - rowsum(P * dP))      (the softmax Jacobian applied to dP)
+        dQ  = scale * dS K
+        dK  = scale * dS^T Q
+    A row with no allowed key has no output and gets zero gradients.
+    Returns (dq [n, d], dk [m, d], dv [m, d])."""
+    logits = np.where(allowed, scale * (qb @ kc.T), -np.inf)
+    live = allowed.any(axis=1, keepdims=True)
+    m = np.where(live, logits.max(axis=1, keepdims=True), 0.0)
+    w = np.where(allowed, np.exp(logits - m), 0.0)
+    p = w / np.where(live, w.sum(axis=1, keepdims=True), 1.0)
+    dv = p.T @ dob
+    dp = dob @ vc.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return scale * (ds @ kc), scale * (ds.T @ qb), dv
+
+
+def attention_backward(q, k, v, dout, sel, block: int, scale: Optional[float] = None, q_offset: int = 0,
+                       full: bool = False, row_range: Optional[Tuple[int, int]] = None):
+    """Gradients of the scalar sum(dout * O) with respect to Q, K and V, where
+    O is the block-sparse attention of sparse_attention (``full`` False: row r
+    of query block i sees keys c <= its position whose block is in sel[b,h,i])
+    or the full causal attention of full_attention_dropped_mass (``full`` True;
+    sel unused).  Keys outside a row's set get no gradient from that row.
+    [SSA-summary] 1 "Planteamiento del Problema" (the sparse stream gives
+    unselected keys zero gradient and normalises over the selected subset
+    only) and 2 "Mecanismo Central" (the full stream passes gradient to every
+    token); the formulas are the chain rule through softmax attention.
+
+    ``row_range`` = (lo, hi) (lo a multiple of the block size) restricts the
+    outputs to query rows [lo, hi); dout then holds just those rows.
+    Returns dq [b,Hq,hi-lo,d], dk and dv [b,Hkv,seq_kv,d] (float64); the
+    gradient of a query head's rows lands on its KV head (GQA: summed over the
+    group)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    b, hq, seq_q, d = q.shape
+    hkv, seq_kv = k.shape[1], k.shape[2]
+    group = hq // hkv
+    _check_geometry(seq_q, seq_kv, q_offset, block)
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    lo, hi = (0, seq_q) if row_range is None else row_range
+    if dout.shape != (b, hq, hi - lo, d):
+        raise ValueError("dout must cover the rows of row_range")
+    dq = np.zeros((b, hq, hi - lo, d))
+    dk = np.zeros((b, hkv, seq_kv, d))
+    dv = np.zeros((b, hkv, seq_kv, d))
+    for bi in range(b):
+        for h in range(hq):
+            g = h // group
+            for i in range(lo // block, n_blocks(hi, block)):
+                r0, r1 = max(i * block, lo), min((i + 1) * block, hi)
+                last = q_offset + r1 - 1
+                if full:
+                    cols = np.arange(last + 1)
+                else:
+                    cols = _allowed_keys(sel[bi, h, i], last, block, seq_kv)
+                pos = q_offset + np.arange(r0, r1)
+                allowed = cols[None, :] <= pos[:, None]
+                gq, gk, gv = _block_backward(q[bi, h, r0:r1], k[bi, g, cols], v[bi, g, cols],
+                                             dout[bi, h, r0 - lo:r1 - lo], allowed, scale)
+                dq[bi, h, r0 - lo:r1 - lo] = gq
+                np.add.at(dk[bi, g], cols, gk)
+                np.add.at(dv[bi, g], cols, gv)
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------- the whole path

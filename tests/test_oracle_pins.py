@@ -476,13 +476,114 @@ def check_early_stop_loops(O):
                     want = t + 1
             assert used[0, h, i] == want
 
+# ----------------------------------------------------------------------------- backward
+
+def _loss(O, q, kk, v, dout, idx, B, sc, q_off, full, row_range=None):
+    """sum(dout * O) from the oracle's own forward (the scalar the gradients are of)."""
+    if full:
+        o, _, _ = O.full_attention_dropped_mass(q, kk, v, idx, B, scale=sc, q_offset=q_off, row_range=row_range)
+    else:
+        o, _ = O.sparse_attention(q, kk, v, idx, B, scale=sc, q_offset=q_off)
+    return float((o * dout).sum())
+
+
+def check_backward_finite_differences(O):
+    # central differences of the forward loss, element by element, on tiny inputs
+    rng = np.random.default_rng(11)
+    for (n_q, q_off, B, k, full, rr) in [(10, 0, 4, 2, False, None),    # ragged last block
+                                          (10, 0, 4, 2, True, None),
+                                          (8, 8, 4, 2, False, None),      # a chunk at q_offset 8
+                                          (12, 0, 4, 1, True, (4, 12))]:  # full on a row slice
+        n_kv, d = n_q + q_off, 3
+        q = rng.standard_normal((1, 2, n_q, d))
+        kk = rng.standard_normal((1, 1, n_kv, d))
+        v = rng.standard_normal((1, 1, n_kv, d))
+        lo, hi = (0, n_q) if rr is None else rr
+        dout = rng.standard_normal((1, 2, hi - lo, d))
+        sc = 0.6
+        idx = O.select_blocks(O.block_scores(q, kk, B, scale=sc, q_offset=q_off), k, B, q_offset=q_off)
+        dq, dk, dv = O.attention_backward(q, kk, v, dout, idx, B, scale=sc, q_offset=q_off, full=full,
+                                          row_range=rr)
+        eps = 1e-5
+        for name, x, g in (("q", q, dq), ("k", kk, dk), ("v", v, dv)):
+            fd = np.zeros_like(x)
+            for ix in np.ndindex(x.shape):
+                x0 = x[ix]
+                x[ix] = x0 + eps
+                lp = _loss(O, q, kk, v, dout, idx, B, sc, q_off, full, rr)
+                x[ix] = x0 - eps
+                lm = _loss(O, q, kk, v, dout, idx, B, sc, q_off, full, rr)
+                x[ix] = x0
+                fd[ix] = (lp - lm) / (2 * eps)
+            if name == "q":
+                fd = fd[:, :, lo:hi]
+            np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=f"d{name} full={full} off={q_off}")
+
+
+def check_backward_autograd(O):
+    # torch autograd through float64 SDPA with the same boolean mask (GQA)
+    b, hq, hkv, n, d, B, k = 2, 4, 2, 40, 8, 8, 3
+    q, kk, v = rand_qkv(b, hq, hkv, n, d)
+    dout = bf16_values((b, hq, n, d))
+    sc = float(np.float32(1 / math.sqrt(d)))
+    idx = O.select_blocks(O.block_scores(q, kk, B), k, B)
+    for full in (False, True):
+        mask = tr.causal_mask(n, n, 0) if full else tr.block_mask_from_idx(idx, n, n, B, 0)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, kk, v))
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=sc, enable_gqa=True)
+        (o * torch.tensor(dout)).sum().backward()
+        dq, dk, dv = O.attention_backward(q, kk, v, dout, idx, B, full=full)
+        np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def check_backward_identities(O):
+    b, hq, hkv, n, d, B, k = 1, 4, 2, 96, 8, 16, 2
+    q, kk, v = rand_qkv(b, hq, hkv, n, d)
+    dout = bf16_values((b, hq, n, d))
+    idx = O.select_blocks(O.block_scores(q, kk, B), k, B)
+    for full in (False, True):
+        dq, dk, dv = O.attention_backward(q, kk, v, dout, idx, B, full=full)
+        # each row's softmax Jacobian annihilates constants: the key gradients of a group sum to zero
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-11)
+        # each row's probabilities sum to one: the value gradients sum to the group's output gradients
+        np.testing.assert_allclose(dv.sum(axis=2), dout.reshape(b, hkv, hq // hkv, n, d).sum(axis=(2, 3)),
+                                   rtol=1e-11, atol=1e-11)
+        # row 0 attends to its own key only: its output is v_0 whatever q_0 is
+        np.testing.assert_allclose(dq[:, :, 0], 0.0, atol=1e-14)
+        # GQA: the same as one KV head per query head, summed over each group
+        g = hq // hkv
+        dq1, dk1, dv1 = O.attention_backward(q, np.repeat(kk, g, axis=1), np.repeat(v, g, axis=1), dout, idx, B,
+                                             full=full)
+        np.testing.assert_allclose(dq1, dq, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dk1.reshape(b, hkv, g, n, d).sum(axis=2), dk, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dv1.reshape(b, hkv, g, n, d).sum(axis=2), dv, rtol=1e-11, atol=1e-12)
+    # every block selected: the sparse gradients are the full ones
+    idx_all = O.select_blocks(O.block_scores(q, kk, B), n // B, B)
+    for a_, b_ in zip(O.attention_backward(q, kk, v, dout, idx_all, B),
+                      O.attention_backward(q, kk, v, dout, idx_all, B, full=True)):
+        np.testing.assert_allclose(a_, b_, rtol=1e-12, atol=1e-13)
+    # the sparse stream passes no gradient to keys outside a row's blocks
+    idx_diag = O.select_blocks(O.block_scores(q, kk, B), 1, B)
+    _, dkd, dvd = O.attention_backward(q, kk, v, dout, idx_diag, B)
+    _, _, dvf = O.attention_backward(q, kk, v, dout, idx_diag, B, full=True)
+    for j in range(n // B):   # k == 1: block j only sees itself, so its keys only get block j's gradient
+        rows = slice(j * B, (j + 1) * B)
+        np.testing.assert_allclose(dvd[:, :, rows].sum(axis=2),
+                                   dout[:, :, rows].reshape(b, hkv, hq // hkv, B, d).sum(axis=(2, 3)),
+                                   rtol=1e-11, atol=1e-11)
+    assert not np.allclose(dvd, dvf)
+
+
 ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_causal,
               check_select_brute_force, check_select_ties_and_decode, check_sparse_vs_sdpa,
               check_sparse_special_cases, check_sparse_brute_force_loops,
               check_full_and_dropped_identities, check_tie_closed_form, check_decode,
               check_shared_hand_example, check_shared_scores_pool_queries, check_shared_reductions,
               check_shared_brute_force, check_early_stop_hand_example, check_early_stop_limits,
-              check_early_stop_loops]
+              check_early_stop_loops, check_backward_finite_differences, check_backward_autograd,
+              check_backward_identities]
 
 
 # ----------------------------------------------------------------------------- the pins
@@ -536,6 +637,9 @@ MUTANTS = {
     "early_stop_drops_trigger_block": ("_early_stop_count", None),
     "early_stop_counts_own_gain": ("_early_stop_count", None),
     "early_stop_index_order": ("early_stop_order", None),
+    "bwd_no_softmax_correction": ("_block_backward", None),
+    "bwd_dk_unscaled": ("_block_backward", None),
+    "bwd_dv_unnormalised": ("_block_backward", None),
 }
 
 
@@ -590,6 +694,20 @@ def _mutant_index_order(sel_row, score_row, jd):
     return ([jd] if jd in listed else []) + [j for j in listed if j != jd]
 
 
+def _mutant_bwd(kind):
+    def f(qb, kc, vc, dob, allowed, scale):
+        logits = np.where(allowed, scale * (qb @ kc.T), -np.inf)
+        m = logits.max(axis=1, keepdims=True)
+        w = np.where(allowed, np.exp(logits - m), 0.0)
+        p = w / w.sum(axis=1, keepdims=True)
+        dv = (w if kind == "unnormalised" else p).T @ dob
+        dp = dob @ vc.T
+        ds = p * dp if kind == "no_correction" else p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dk = (ds.T @ qb) if kind == "unscaled" else scale * (ds.T @ qb)
+        return scale * (ds @ kc), dk, dv
+    return f
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch, golden_dir):
     attr, fn = MUTANTS[name]
@@ -603,5 +721,8 @@ def test_mutant_is_caught(name, monkeypatch, golden_dir):
         fn = _mutant_block_means
     if name == "drops_last_selected_block":
         fn = _mutant_allowed
+    if name.startswith("bwd_"):
+        fn = _mutant_bwd({"bwd_no_softmax_correction": "no_correction", "bwd_dk_unscaled": "unscaled",
+                          "bwd_dv_unnormalised": "unnormalised"}[name])
     monkeypatch.setattr(ssa_oracle, attr, fn)
     assert _any_pin_fails(golden_dir), f"no pin catches mutant {name}"
