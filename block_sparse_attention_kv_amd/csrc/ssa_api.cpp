@@ -222,9 +222,96 @@ ssa_status_t full_impl(const ssa_shape_t* shape, const void* q, const void* k, c
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
 
+ssa_status_t bwd_impl(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
+                      const int32_t* block_idx, bool shared, bool full, int32_t q_block_begin, int32_t q_block_count,
+                      const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream, const char* fn) {
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (!full) {
+    q_block_begin = 0;
+    q_block_count = g.nqb;
+  }
+  if (q_block_begin < 0 || q_block_count < 0 || (int64_t)q_block_begin + q_block_count > g.nqb)
+    return fail(SSA_ERR_INVALID_ARG, "%s: query block range [%d, %d) outside [0, %d)", fn, q_block_begin,
+                q_block_begin + q_block_count, g.nqb);
+  if (!full && g.group > 32)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: more than 32 query heads per KV head", fn);
+  if (empty || q_block_count == 0) return SSA_OK;
+  CHECK_PTR(q, 16, fn);
+  CHECK_PTR(k, 16, fn);
+  CHECK_PTR(v, 16, fn);
+  if (!full) CHECK_PTR(block_idx, 4, fn);
+  CHECK_PTR(out, 16, fn);
+  CHECK_PTR(lse, 4, fn);
+  CHECK_PTR(dout, 16, fn);
+  CHECK_PTR(dq, 16, fn);
+  CHECK_PTR(dk, 16, fn);
+  CHECK_PTR(dv, 16, fn);
+  ssa::BwdChunks ch;
+  size_t off[4], need;
+  ssa::bwd_plan(g, full, q_block_begin, q_block_count, &ch, off, &need);
+  const uint64_t grid = (uint64_t)g.batch * g.hkv * g.nkb * ch.max_count();
+  if (grid > 0x7fffffffull) return fail(SSA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  if (workspace_bytes < need)
+    return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+  CHECK_PTR(workspace, 256, fn);
+  ssa::BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)out;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.idx = block_idx;
+  a.idx_shared = shared ? 1 : 0;
+  a.full = full ? 1 : 0;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  uint8_t* ws = (uint8_t*)workspace;
+  a.lse2 = (float*)(ws + off[0]);
+  a.delta = (float*)(ws + off[1]);
+  a.mask = full ? nullptr : (uint32_t*)(ws + off[2]);
+  a.part = (float*)(ws + off[3]);
+  a.qb_begin = q_block_begin;
+  a.qb_count = q_block_count;
+  const int64_t end_row = (int64_t)(q_block_begin + q_block_count) * ssa::kBlock;
+  a.rows_out = (int)((end_row < g.seq_q ? end_row : g.seq_q) - (int64_t)q_block_begin * ssa::kBlock);
+  a.chunks = ch;
+  hipError_t e = ssa::launch_attn_backward(a, g, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
 }  // namespace
 
 extern "C" {
+
+ssa_status_t ssa_block_sparse_attn_bwd(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
+                                       const int32_t* block_idx, const void* out, const float* lse,
+                                       const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(shape, q, k, v, block_idx, false, false, 0, 0, out, lse, dout, dq, dk, dv, workspace,
+                  workspace_bytes, stream, "ssa_block_sparse_attn_bwd");
+}
+
+ssa_status_t ssa_block_sparse_attn_bwd_shared(const ssa_shape_t* shape, const void* q, const void* k,
+                                              const void* v, const int32_t* block_idx, const void* out,
+                                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(shape, q, k, v, block_idx, true, false, 0, 0, out, lse, dout, dq, dk, dv, workspace,
+                  workspace_bytes, stream, "ssa_block_sparse_attn_bwd_shared");
+}
+
+ssa_status_t ssa_full_attn_bwd(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
+                               int32_t q_block_begin, int32_t q_block_count, const void* out_full,
+                               const float* lse_full, const void* dout_full, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(shape, q, k, v, nullptr, false, true, q_block_begin, q_block_count, out_full, lse_full, dout_full,
+                  dq, dk, dv, workspace, workspace_bytes, stream, "ssa_full_attn_bwd");
+}
 
 ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
                              hipStream_t stream) {
@@ -313,6 +400,12 @@ size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {
   if (make_geometry(shape, &g, &empty, "ssa_workspace_bytes") != SSA_OK) return SIZE_MAX;
   if (empty) return 0;
   if (op == SSA_OP_SPARSE_FWD && g.seq_q == 1) return ssa::decode_workspace_bytes(g.batch, g.hq, g.hkv);
+  if (op == SSA_OP_SPARSE_BWD || op == SSA_OP_FULL_BWD) {
+    ssa::BwdChunks ch;
+    size_t off[4], need;
+    ssa::bwd_plan(g, op == SSA_OP_FULL_BWD, 0, g.nqb, &ch, off, &need);
+    return need;
+  }
   return 0;
 }
 

@@ -168,33 +168,14 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
 // 8*ap .. 8*ap+7 hold.  The V^T operand for d block db is two transposing
 // reads of 4 keys x 16 d columns per 16-lane group.
 __device__ __forceinline__ void tile_pv(const uint8_t* sV, const u32x4 pk[2][2][2], UnitState& st, int lane) {
-  const int grp = lane >> 4, s16 = lane & 15;
-  const int tq = s16 >> 2, qq = s16 & 3;
-  const int hh = grp >> 1, gd = grp & 1;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     // the four V^T operands of this 32-key half, read before its MFMAs
     bf16x8 vop[2][2];
 #pragma unroll
-    for (int ap = 0; ap < 2; ++ap) {
+    for (int ap = 0; ap < 2; ++ap)
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        uint32_t w[4];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int row = 32 * kb + 16 * ap + 8 * rr + 4 * hh + tq;
-          const int chunk = 4 * db + 2 * gd + (qq >> 1);
-          const uint32_t off = swz<0>(row, chunk) + 8 * (qq & 1);
-          const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)to_lds((void*)(sV + off)));
-          const u32x2 tw = __builtin_bit_cast(u32x2, t);
-          w[2 * rr] = tw[0];
-          w[2 * rr + 1] = tw[1];
-        }
-        u32x4 va;
-        va[0] = w[0]; va[1] = w[1]; va[2] = w[2]; va[3] = w[3];
-        vop[ap][db] = as_bf16x8(va);
-      }
-    }
+      for (int db = 0; db < 2; ++db) vop[ap][db] = read_tile_tr(sV, 32 * kb + 16 * ap, db, lane);
 #pragma unroll
     for (int ap = 0; ap < 2; ++ap)
 #pragma unroll

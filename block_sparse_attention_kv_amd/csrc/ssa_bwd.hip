@@ -1,0 +1,510 @@
+// Backward kernels (gfx950) of the block-sparse forward and of the full causal
+// counterpart: given dO, O and the forward's LSE, the gradients dQ, dK, dV of
+// the attention output.
+//
+// With P = exp(scale * Q K^T - LSE) on the keys a row attends to (0 elsewhere)
+// and D = rowsum(dO * O):
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
+//   dQ = scale * dS K,   dK = scale * dS^T Q.
+// Method: SSA summary (gist.science 2511.20102), 1 "Planteamiento del
+// Problema" (the sparse stream gives keys outside the selected blocks no
+// gradient and normalises over the selected subset) and 2 "Mecanismo Central"
+// (the full stream passes gradient to every token); the formulas are the chain
+// rule through the softmax.
+//
+// Work is split two ways, so that no gradient is accumulated with atomics and
+// the result is bitwise reproducible:
+//   * dQ kernel: one workgroup (2 waves, 32 query rows each) per unit
+//     (b, query head, query block), walking the unit's key blocks like the
+//     forward; it also writes the per-row LSE (log2 units) and D that the
+//     key-side kernel reads.  Per tile, transposed as in the forward (a lane
+//     owns one query column):  S^T = K Q^T,  dP^T = V dO^T  (Q, dO in
+//     registers), then dQ^T += K^T dS^T with K^T read transposed from LDS.
+//   * dK/dV kernel: one workgroup (2 waves, 32 keys each) per work item
+//     (b, KV head, key block j, chunk of at most R query blocks); it walks the
+//     (query head, query block) pairs of the chunk whose list holds j, in
+//     (query block, head) order.  Per pair, untransposed (a lane owns one key
+//     column):  S = Q K^T,  dP = dO V^T  (K, V in registers), then
+//     dV += P^T dO and dK += dS^T Q with dO, Q read transposed from LDS.
+//     Each item writes an fp32 partial; a reduce kernel sums the chunks of a
+//     key block in chunk order and rounds to bf16.
+// The (query head, query block) pairs of a key block come from a bitmask
+// mask[b, g, j, i] (bit hh: head g*G+hh lists j for query block i), built
+// from the index rows with atomic ORs (order-independent).
+#include <algorithm>
+
+#include "ssa_common.hpp"
+#include "ssa_internal.hpp"
+#include "ssa_tiles.hpp"
+
+namespace ssa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxPairs = kBwdMaxChunk * 32;  // query blocks per item x heads per group (sparse)
+
+// ---------------------------------------------------------------------------- index inversion
+
+__global__ __launch_bounds__(256) void bwd_fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) p[e] = 0u;
+}
+
+// One wavefront per index row (b, query head or KV group, query block i): the
+// row's entries before its first -1 that name a causal block j <= diag(i) set
+// the bits of their query heads in mask[b, g, j, i].
+__global__ __launch_bounds__(64) void bwd_mask_kernel(const int32_t* __restrict__ idx, uint32_t* __restrict__ mask,
+                                                      Geometry geo, int shared) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;  // (b, head or group, i)
+  const int i = row % geo.nqb;
+  const int bh = row / geo.nqb;
+  const int G = geo.group;
+  int gi, bits;
+  if (shared) {
+    gi = bh;
+    bits = G >= 32 ? -1 : (int)((1u << G) - 1u);
+  } else {
+    const int b = bh / geo.hq, h = bh - b * geo.hq;
+    gi = b * geo.hkv + h / G;
+    bits = (int)(1u << (h % G));
+  }
+  const int jd = (geo.q_offset + i * kBlock) / kBlock;
+  int iv[kMaxTopk / 64];
+  load_index_row(idx + (size_t)row * geo.topk, geo.topk, lane, iv);
+  int first_neg = geo.topk;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < geo.topk && iv[c] < 0);
+    if (neg != 0ull && first_neg == geo.topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
+  }
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const int j = iv[c];
+    if (e < first_neg && j >= 0 && j <= jd)
+      atomicOr(mask + ((size_t)gi * geo.nkb + j) * geo.nqb + i, (uint32_t)bits);
+  }
+}
+
+// ---------------------------------------------------------------------------- dQ
+
+// Four 16-byte pieces of one bf16 row as MFMA operand k-slots: piece ks holds
+// columns 16*ks + 8*hl .. +7 (zeros for a row that does not exist).
+__device__ __forceinline__ void load_row_op(const uint16_t* rowp, bool valid, int hl, bf16x8 op[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (valid) v = *reinterpret_cast<const u32x4*>(rowp + 16 * ks + 8 * hl);
+    op[ks] = as_bf16x8(v);
+  }
+}
+
+__device__ __forceinline__ float dot_row_ops(const bf16x8 a[4], const bf16x8 b[4]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc = fmaf((float)a[ks][t], (float)b[ks][t], acc);
+  return acc;
+}
+
+__global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry geo) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kTileBytes];
+  __shared__ int sList[2][kMaxTopk];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = geo.group;
+  const int u = blockIdx.x;  // (b, h, i) with the longest query blocks first
+  const int bh = u % (geo.batch * geo.hq);
+  const int i = a.qb_begin + a.qb_count - 1 - u / (geo.batch * geo.hq);
+  const int b = bh / geo.hq, h = bh - b * geo.hq;
+  const int gi = b * geo.hkv + h / G;
+  const int jd = (geo.q_offset + i * kBlock) / kBlock;
+  const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
+  const uint16_t* kbase = a.k + kvoff;
+  const uint16_t* vbase = a.v + kvoff;
+
+  const int row = i * kBlock + 32 * wave + l32;  // this lane's query row
+  const bool vrow = row < geo.seq_q;
+  const int orow = row - a.qb_begin * kBlock;    // its row in the slice-shaped tensors
+  int nt = jd + 1;
+  if (!a.full) {
+    const int irow = a.idx_shared ? gi : bh;
+    int iv[kMaxTopk / 64];
+    load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
+    nt = compact_index_row(iv, geo.topk, jd, sList[wave], lane);
+  }
+  bf16x8 qop[4], dop[4], oop[4];
+  load_row_op(a.q + ((size_t)bh * geo.seq_q + (vrow ? row : 0)) * kHeadDim, vrow, hl, qop);
+  const size_t srow = (size_t)bh * a.rows_out + (vrow ? orow : 0);
+  load_row_op(a.dout + srow * kHeadDim, vrow, hl, dop);
+  load_row_op(a.o + srow * kHeadDim, vrow, hl, oop);
+  const float lse = vrow ? a.lse[srow] : 0.f;
+  auto tile_block = [&](int t) { return a.full ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
+  TileOffsets<2, 0> toff;
+  toff.init(lane, wave);
+  if (nt > 0) {
+    const int j0 = tile_block(0);
+    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK[0], lane, toff);
+    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV[0], lane, toff);
+  }
+  // per-row constants: LSE in log2 units (+inf where the row has no keys or
+  // does not exist, so that every P is 0) and D = dO . O
+  const float dsum = sum_xor32(dot_row_ops(dop, oop));
+  const float lse2 = (vrow && lse > -__builtin_inff()) ? lse * kLog2e : __builtin_inff();
+  if (hl == 0) {
+    const size_t prow = (size_t)bh * (a.qb_count * kBlock) + (row - a.qb_begin * kBlock);
+    a.lse2[prow] = lse2;
+    a.delta[prow] = vrow ? dsum : 0.f;
+  }
+  f32x16 dq[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+  const float c = geo.scale_log2;
+  const int pos = geo.q_offset + row;
+  for (int t = 0; t < nt; ++t) {
+    const int j = tile_block(t);
+    wait_vmem<0>();   // this wave's share of tile t (and, at t = 0, the row loads)
+    __syncthreads();  // every wave's share; every wave is done with tile t-1
+    if (t + 1 < nt) {
+      const int jn = tile_block(t + 1);
+      const size_t off = (size_t)jn * kBlock * kHeadDim;
+      const int nv = geo.seq_kv - jn * kBlock;
+      tile_load(kbase + off, nv, sK[(t + 1) & 1], lane, toff);
+      tile_load(vbase + off, nv, sV[(t + 1) & 1], lane, toff);
+    }
+    const uint8_t* tK = sK[t & 1];
+    const uint8_t* tV = sV[t & 1];
+    const bool diag = j == jd;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 ka[4], va[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ka[ks] = *reinterpret_cast<const bf16x8*>(tK + swz<0>(32 * kb + l32, 2 * ks + hl));
+        va[ks] = *reinterpret_cast<const bf16x8*>(tV + swz<0>(32 * kb + l32, 2 * ks + hl));
+      }
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = mfma32(ka[ks], qop[ks], s);    // S^T: rows keys, columns queries
+        dp = mfma32(va[ks], dop[ks], dp);  // dP^T
+      }
+      // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * c - LSE2), future keys 0
+      u32x4 pds[2];
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float d2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int r = 8 * ap + 2 * e + x;
+            float p = fast_exp2(fmaf(s[r], c, -lse2));
+            if (diag) {
+              const int key = j * kBlock + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+              p = key > pos ? 0.f : p;
+            }
+            d2[x] = p * (dp[r] - dsum);
+          }
+          pds[ap][e] = pack_bf16x2(d2[0], d2[1]);
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          dq[db] = mfma32(read_tile_tr(tK, 32 * kb + 16 * ap, db, lane), as_bf16x8(pds[ap]), dq[db]);
+    }
+  }
+  if (vrow) {
+    uint16_t* qp = a.dq + ((size_t)bh * a.rows_out + orow) * kHeadDim;
+    const float sc = geo.scale;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dq[db][4 * rg] * sc, dq[db][4 * rg + 1] * sc);
+        w[1] = pack_bf16x2(dq[db][4 * rg + 2] * sc, dq[db][4 * rg + 3] * sc);
+        *reinterpret_cast<u32x2*>(qp + 32 * db + 8 * rg + 4 * hl) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------- dK / dV
+
+// One dword per lane of a 64-float row, direct to LDS.
+__device__ __forceinline__ void dma_row64(const float* g, uint32_t lds_base, int lane) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"((uint32_t)lane * 4u), "s"(g), "s"(lds_base)
+      : "memory", "m0");
+}
+
+__global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometry geo) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sO[2][kTileBytes];  // dO tiles
+  __shared__ __attribute__((aligned(256))) float sL[2][kBlock];          // LSE (log2 units)
+  __shared__ __attribute__((aligned(256))) float sD[2][kBlock];          // D
+  __shared__ int sPairs[kMaxPairs];
+  __shared__ int sNPairs;
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = geo.group;
+  const BwdChunks ch = a.chunks;
+  const int ngroups = geo.batch * geo.hkv;
+  const int x = blockIdx.x;
+  const int gi = x % ngroups;
+  const int rest = x / ngroups;
+  const int j = rest % geo.nkb;
+  const int cidx = rest / geo.nkb;
+  const int nch = ch.count(j);
+  if (cidx >= nch) return;
+  const int i0 = ch.first_block(j) + cidx * ch.R;
+  const int i1 = min(i0 + ch.R, ch.hi);
+  const size_t item = (size_t)gi * ch.items_per_group + ch.prefix(j) + cidx;
+  const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+
+  // the chunk's (query block, head) pairs, in (query block, head) order
+  int npairs;
+  if (a.full) {
+    npairs = (i1 - i0) * G;
+  } else {
+    if (wave == 0) {
+      const int ii = i0 + lane;
+      const uint32_t bits = ii < i1 ? a.mask[((size_t)gi * geo.nkb + j) * geo.nqb + ii] : 0u;
+      const int cnt = __builtin_popcount(bits);
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      int pos = incl - cnt;
+      uint32_t m = bits;
+      while (m) {
+        const int hh = __builtin_ctz(m);
+        m &= m - 1u;
+        sPairs[pos++] = (lane << 8) | hh;
+      }
+      if (lane == 63) sNPairs = incl;
+    }
+    __syncthreads();
+    npairs = sNPairs;
+  }
+  auto pair_of = [&](int p, int& ii, int& hh) {
+    if (a.full) {
+      ii = i0 + p / G;
+      hh = p - (p / G) * G;
+    } else {
+      const int e = __builtin_amdgcn_readfirstlane(sPairs[p]);
+      ii = i0 + (e >> 8);
+      hh = e & 255;
+    }
+  };
+
+  // this wave's 32 keys as MFMA B operands (rows past seq_kv re-read a valid
+  // row; such keys lie in the future of every query and are masked)
+  const int key = j * kBlock + 32 * wave + l32;
+  const int krow = min(key, geo.seq_kv - 1);
+  bf16x8 kop[4], vop[4];
+  load_row_op(a.k + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, kop);
+  load_row_op(a.v + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, vop);
+
+  TileOffsets<2, 0> toff;
+  toff.init(lane, wave);
+  const size_t rows_pad = (size_t)a.qb_count * kBlock;
+  auto issue = [&](int p, int buf) {
+    int ii, hh;
+    pair_of(p, ii, hh);
+    const int bh = b * geo.hq + g * G + hh;
+    const int nv = geo.seq_q - ii * kBlock;
+    tile_load(a.q + ((size_t)bh * geo.seq_q + (size_t)ii * kBlock) * kHeadDim, nv, sQ[buf], lane, toff);
+    const int orow0 = (ii - a.qb_begin) * kBlock;
+    tile_load(a.dout + ((size_t)bh * a.rows_out + orow0) * kHeadDim, a.rows_out - orow0, sO[buf], lane, toff);
+    const size_t prow = (size_t)bh * rows_pad + orow0;
+    if (wave == 0)
+      dma_row64(a.lse2 + prow, lds_addr(sL[buf]), lane);
+    else
+      dma_row64(a.delta + prow, lds_addr(sD[buf]), lane);
+  };
+  if (npairs > 0) issue(0, 0);
+
+  f32x16 dk[2], dv[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.f;
+      dv[db][r] = 0.f;
+    }
+  const float c = geo.scale_log2;
+  for (int p = 0; p < npairs; ++p) {
+    int ii, hh;
+    pair_of(p, ii, hh);
+    wait_vmem<0>();   // this wave's share of pair p (and, at p = 0, K and V)
+    __syncthreads();  // every wave's share; every wave is done with pair p-1
+    if (p + 1 < npairs) issue(p + 1, (p + 1) & 1);
+    const uint8_t* tQ = sQ[p & 1];
+    const uint8_t* tO = sO[p & 1];
+    const float* tL = sL[p & 1];
+    const float* tD = sD[p & 1];
+    const bool diag = j == (geo.q_offset + ii * kBlock) / kBlock;
+    const int kpos = key - (geo.q_offset + ii * kBlock);  // key position relative to the block's first row
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      bf16x8 qa[4], oa[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qa[ks] = *reinterpret_cast<const bf16x8*>(tQ + swz<0>(32 * qb + l32, 2 * ks + hl));
+        oa[ks] = *reinterpret_cast<const bf16x8*>(tO + swz<0>(32 * qb + l32, 2 * ks + hl));
+      }
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = mfma32(qa[ks], kop[ks], s);    // S: rows queries, columns keys
+        dp = mfma32(oa[ks], vop[ks], dp);  // dP
+      }
+      u32x4 pp[2], pds[2];
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap) {
+#pragma unroll
+        for (int rg2 = 0; rg2 < 2; ++rg2) {
+          const int m0 = 32 * qb + 16 * ap + 8 * rg2 + 4 * hl;  // query rows m0 .. m0+3
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(tL + m0);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(tD + m0);
+          float pv[4], dv4[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = 8 * ap + 4 * rg2 + x;
+            float p = fast_exp2(fmaf(s[r], c, -l4[x]));
+            if (diag) p = kpos > m0 + x ? 0.f : p;
+            pv[x] = p;
+            dv4[x] = p * (dp[r] - d4[x]);
+          }
+          pp[ap][2 * rg2] = pack_bf16x2(pv[0], pv[1]);
+          pp[ap][2 * rg2 + 1] = pack_bf16x2(pv[2], pv[3]);
+          pds[ap][2 * rg2] = pack_bf16x2(dv4[0], dv4[1]);
+          pds[ap][2 * rg2 + 1] = pack_bf16x2(dv4[2], dv4[3]);
+        }
+      }
+      // dV += P^T dO,  dK += dS^T Q   (contraction over this half's 32 queries)
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          dv[db] = mfma32(as_bf16x8(pp[ap]), read_tile_tr(tO, 32 * qb + 16 * ap, db, lane), dv[db]);
+          dk[db] = mfma32(as_bf16x8(pds[ap]), read_tile_tr(tQ, 32 * qb + 16 * ap, db, lane), dk[db]);
+        }
+    }
+  }
+  // partial sums of this item: [2][64 keys][64 d] fp32 (dK unscaled)
+  float* pk = a.part + item * (2 * kBlock * kHeadDim);
+  float* pv = pk + kBlock * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3);
+      pk[kr * kHeadDim + 32 * db + l32] = dk[db][r];
+      pv[kr * kHeadDim + 32 * db + l32] = dv[db][r];
+    }
+}
+
+// Sum the chunk partials of each key block in chunk order: dK = scale * sum,
+// dV = sum, rounded to bf16.  One thread per 4 columns of a key row.
+__global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometry geo) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t per_group = (size_t)geo.seq_kv * (kHeadDim / 4);
+  if (t >= (size_t)geo.batch * geo.hkv * per_group) return;
+  const int gi = (int)(t / per_group);
+  const int rem = (int)(t - (size_t)gi * per_group);
+  const int key = rem / (kHeadDim / 4);
+  const int c4 = rem - key * (kHeadDim / 4);
+  const int j = key / kBlock, kr = key - j * kBlock;
+  const BwdChunks ch = a.chunks;
+  const int n = ch.count(j);
+  const float* base = a.part + ((size_t)gi * ch.items_per_group + ch.prefix(j)) * (2 * kBlock * kHeadDim) +
+                      kr * kHeadDim + 4 * c4;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < n; ++e) {
+    const float* pe = base + (size_t)e * (2 * kBlock * kHeadDim);
+    sk += *reinterpret_cast<const f32x4*>(pe);
+    sv += *reinterpret_cast<const f32x4*>(pe + kBlock * kHeadDim);
+  }
+  const size_t o = ((size_t)gi * geo.seq_kv + key) * kHeadDim + 4 * c4;
+  u32x2 wk, wv;
+  wk[0] = pack_bf16x2(sk[0] * geo.scale, sk[1] * geo.scale);
+  wk[1] = pack_bf16x2(sk[2] * geo.scale, sk[3] * geo.scale);
+  wv[0] = pack_bf16x2(sv[0], sv[1]);
+  wv[1] = pack_bf16x2(sv[2], sv[3]);
+  *reinterpret_cast<u32x2*>(a.dk + o) = wk;
+  *reinterpret_cast<u32x2*>(a.dv + o) = wv;
+}
+
+}  // namespace
+
+void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdChunks* ch, size_t off[4],
+              size_t* total) {
+  BwdChunks c;
+  c.lo = qb_begin;
+  c.hi = qb_begin + qb_count;
+  c.qoffb = g.q_offset / kBlock;
+  // chunk length from the problem's query-block count only, so that a slice
+  // never needs more items than the whole range
+  c.R = std::max(4, std::min(kBwdMaxChunk, g.nqb / 8));
+  c.items_per_group = c.prefix(g.nkb);
+  *ch = c;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)g.batch * g.hq * qb_count * kBlock;
+  size_t o = 0;
+  off[0] = o;
+  o += up(rows * sizeof(float));
+  off[1] = o;
+  o += up(rows * sizeof(float));
+  off[2] = o;
+  if (!full) o += up((size_t)g.batch * g.hkv * g.nkb * g.nqb * sizeof(uint32_t));
+  off[3] = o;
+  o += up((size_t)g.batch * g.hkv * c.items_per_group * 2 * kBlock * kHeadDim * sizeof(float));
+  *total = o;
+}
+
+hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t stream) {
+  const size_t units = (size_t)g.batch * g.hq * a.qb_count;
+  if (units == 0) return hipSuccess;
+  if (!a.full) {
+    const size_t words = (size_t)g.batch * g.hkv * g.nkb * g.nqb;
+    const unsigned zb = (unsigned)std::min<size_t>((words + 255) / 256, 4096);
+    hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3(zb), dim3(256), 0, stream, a.mask, words);
+    const size_t rows = (size_t)g.batch * (a.idx_shared ? g.hkv : g.hq) * g.nqb;
+    hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)rows), dim3(64), 0, stream, a.idx, a.mask, g,
+                       a.idx_shared);
+  }
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)units), dim3(128), 0, stream, a, g);
+  const size_t items_grid = (size_t)g.batch * g.hkv * g.nkb * a.chunks.max_count();
+  if (items_grid > 0)
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)items_grid), dim3(128), 0, stream, a, g);
+  const size_t threads = (size_t)g.batch * g.hkv * g.seq_kv * (kHeadDim / 4);
+  if (threads > 0)
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, g);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

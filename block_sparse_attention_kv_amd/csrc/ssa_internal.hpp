@@ -61,6 +61,65 @@ inline size_t decode_workspace_bytes(int batch, int hq, int hkv) {
   return (size_t)batch * hq * decode_pieces(batch, hkv) * kPartialFloats * sizeof(float);
 }
 
+// Backward work items: the dK/dV of key block j are summed over the query
+// blocks i in [lo, hi) whose diagonal block is >= j, cut into chunks of at most
+// R query blocks; count(j) chunks for key block j, numbered prefix(j) ..
+// prefix(j) + count(j) - 1 within each (batch, KV head) group.
+constexpr int kBwdMaxChunk = 64;
+
+struct BwdChunks {
+  int lo, hi;   // query blocks handled
+  int qoffb;    // q_offset / B: query block i's diagonal key block is qoffb + i
+  int R;        // query blocks per chunk (<= kBwdMaxChunk)
+  long long items_per_group;
+
+  __host__ __device__ int first_block(int j) const { return j - qoffb > lo ? j - qoffb : lo; }
+  __host__ __device__ int count(int j) const {
+    const int n = hi - first_block(j);
+    return n > 0 ? (n + R - 1) / R : 0;
+  }
+  __host__ __device__ int max_count() const { return (hi - lo + R - 1) / R; }
+  // sum_{m=1..x} ceil(m / R)
+  __host__ __device__ long long ceil_sum(long long x) const {
+    if (x <= 0) return 0;
+    const long long q = x / R, s = x - q * R;
+    return (long long)R * q * (q + 1) / 2 + s * (q + 1);
+  }
+  // sum of count(j') for j' < j
+  __host__ __device__ long long prefix(int j) const {
+    const long long t = (long long)lo + qoffb;
+    const long long c0 = max_count();
+    if (j <= t + 1) return (long long)j * c0;
+    return (t + 1) * c0 + ceil_sum(hi - lo - 1) - ceil_sum((long long)hi + qoffb - j);
+  }
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;     // forward output, rows_out rows per (b, h)
+  const uint16_t* dout;  // its gradient, same layout
+  const float* lse;      // forward LSE (natural log), rows_out per (b, h)
+  const int32_t* idx;    // sparse only
+  int idx_shared;
+  int full;
+  uint16_t* dq;  // rows_out rows per (b, h)
+  uint16_t* dk;  // [b, Hkv, seq_kv, d]
+  uint16_t* dv;
+  float* lse2;     // workspace: per-row LSE in log2 units, qb_count*B rows per (b, h)
+  float* delta;    // workspace: per-row dO . O, same layout
+  uint32_t* mask;  // workspace (sparse): [b, Hkv, nkb, nqb] head bits
+  float* part;     // workspace: per-item [2][B][d] fp32 partial dK, dV
+  int qb_begin, qb_count, rows_out;
+  BwdChunks chunks;
+};
+
+// Chunking and workspace layout of a backward call (byte offsets of lse2,
+// delta, mask, part; total bytes).
+void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdChunks* ch, size_t off[4],
+              size_t* total);
+
 hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geometry& g,
                                   hipStream_t stream);
 hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, float* scores,
@@ -72,6 +131,7 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry&
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream);
 hipError_t launch_attn_early_stop(const AttnArgs& a, const float* scores, float tau, int32_t* blocks_used,
                                   const Geometry& g, hipStream_t stream);
+hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometry& g,
                               hipStream_t stream);
 

@@ -132,6 +132,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
 }
 
+// Transposed MFMA operand from a swizzle-kind-0 tile (64 rows x 64 bf16):
+// lane l receives column 32*cb + l%32 of the tile rows
+//   row0 + 8*(t/4) + 4*(l/32) + t%4,   t = 0..7 (its 8 k-slots),
+// i.e. the row order of the accumulator registers 8*ap .. 8*ap+7 when
+// row0 = 32*kb + 16*ap.  Two transposing reads (4 rows x 16 columns per
+// 16-lane group each).
+__device__ __forceinline__ bf16x8 read_tile_tr(const uint8_t* tile, int row0, int cb, int lane) {
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int tq = s16 >> 2, qq = s16 & 3;
+  const int hh = grp >> 1, gd = grp & 1;
+  uint32_t w[4];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = row0 + 8 * rr + 4 * hh + tq;
+    const int chunk = 4 * cb + 2 * gd + (qq >> 1);
+    const uint32_t off = swz<0>(row, chunk) + 8 * (qq & 1);
+    const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)to_lds((void*)(tile + off)));
+    const u32x2 tw = __builtin_bit_cast(u32x2, t);
+    w[2 * rr] = tw[0];
+    w[2 * rr + 1] = tw[1];
+  }
+  u32x4 va;
+  va[0] = w[0]; va[1] = w[1]; va[2] = w[2]; va[3] = w[3];
+  return as_bf16x8(va);
+}
+
 // Per-lane byte offset (within a tile) of the 16 bytes this lane fetches for
 // slice c (rows 8c..8c+7): chunk q of row r is stored at swz(r, q).  Rows at or
 // past `nvalid` re-read row 0 of the tile (always present); their contents

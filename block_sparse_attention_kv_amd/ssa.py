@@ -18,12 +18,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssa.so")
 
 SSA_OK, SSA_ERR_INVALID_ARG, SSA_ERR_UNSUPPORTED, SSA_ERR_HIP, SSA_ERR_WORKSPACE = range(5)
-SSA_OP_BLOCK_SCORES, SSA_OP_SELECT_TOPK, SSA_OP_SPARSE_FWD, SSA_OP_FULL_FWD = range(4)
+SSA_OP_BLOCK_SCORES, SSA_OP_SELECT_TOPK, SSA_OP_SPARSE_FWD, SSA_OP_FULL_FWD, SSA_OP_SPARSE_BWD, SSA_OP_FULL_BWD = range(6)
 
 EXPORTED_SYMBOLS = (
     "ssa_block_summaries", "ssa_block_scores", "ssa_select_topk", "ssa_block_sparse_attn_fwd",
     "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared", "ssa_block_sparse_attn_fwd_shared",
-    "ssa_full_attn_fwd_dropped_mass_shared", "ssa_block_sparse_attn_fwd_early_stop", "ssa_workspace_bytes",
+    "ssa_full_attn_fwd_dropped_mass_shared", "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
+    "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_workspace_bytes",
     "ssa_status_string",
     "ssa_last_error", "ssa_version",
 )
@@ -73,10 +74,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssa_full_attn_fwd_dropped_mass_shared.argtypes = [sp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.ssa_block_sparse_attn_fwd_early_stop.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                                          sz, vp]
+    lib.ssa_block_sparse_attn_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssa_block_sparse_attn_bwd_shared.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssa_full_attn_bwd.argtypes = [sp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("ssa_block_summaries", "ssa_block_scores", "ssa_select_topk",
                "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared",
                "ssa_block_sparse_attn_fwd_shared", "ssa_full_attn_fwd_dropped_mass_shared",
-               "ssa_block_sparse_attn_fwd_early_stop"):
+               "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
+               "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ssa_workspace_bytes.argtypes = [sp, ctypes.c_int]
     lib.ssa_workspace_bytes.restype = ctypes.c_size_t
@@ -247,6 +252,52 @@ def ssa_block_sparse_attn_fwd_early_stop(shape: Shape, q, k, v, scores, block_id
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(scores), _ptr(block_idx), float(tau), _ptr(out),
         _ptr(lse), _ptr(blocks_used), None, 0, _stream(q.device)))
     return out, lse, blocks_used
+
+
+def _bwd_outputs(shape: Shape, q, rows: int, dq, dk, dv, workspace, op: int):
+    b, hq, hkv, d = shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    if dq is None:
+        dq = torch.empty((b, hq, rows, d), dtype=torch.bfloat16, device=q.device)
+    if dk is None:
+        dk = torch.empty((b, hkv, shape.seq_kv, d), dtype=torch.bfloat16, device=q.device)
+    if dv is None:
+        dv = torch.empty((b, hkv, shape.seq_kv, d), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = torch.empty((max(1, ssa_workspace_bytes(shape, op)),), dtype=torch.uint8, device=q.device)
+    return dq, dk, dv, workspace, workspace.numel() * workspace.element_size()
+
+
+def ssa_block_sparse_attn_bwd(shape: Shape, q, k, v, block_idx, out, lse, dout, dq=None, dk=None, dv=None,
+                              workspace: Optional[torch.Tensor] = None, shared: bool = False):
+    """(dq bf16 [b, Hq, seq_q, d], dk, dv bf16 [b, Hkv, seq_kv, d]): gradients of
+    sum(dout * out) for the block-sparse forward that produced out and lse.
+    ``shared``: block_idx is a group-shared selection (ssa_block_sparse_attn_bwd_shared)."""
+    _require_gpu(q, k, v, block_idx, out, lse, dout, dq, dk, dv, workspace)
+    dq, dk, dv, workspace, ws_bytes = _bwd_outputs(shape, q, shape.seq_q, dq, dk, dv, workspace, SSA_OP_SPARSE_BWD)
+    name = "ssa_block_sparse_attn_bwd_shared" if shared else "ssa_block_sparse_attn_bwd"
+    _check(name, getattr(load_library(), name)(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(dout),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(q.device)))
+    return dq, dk, dv
+
+
+def ssa_full_attn_bwd(shape: Shape, q, k, v, out_full, lse_full, dout_full, q_block_begin: int = 0,
+                      q_block_count: Optional[int] = None, dq=None, dk=None, dv=None,
+                      workspace: Optional[torch.Tensor] = None):
+    """(dq bf16 [b, Hq, rows, d], dk, dv bf16 [b, Hkv, seq_kv, d]): gradients of
+    sum(dout_full * out_full) for the full causal forward over query blocks
+    [q_block_begin, q_block_begin + q_block_count)."""
+    _require_gpu(q, k, v, out_full, lse_full, dout_full, dq, dk, dv, workspace)
+    nqb = n_blocks(shape.seq_q, shape.block)
+    if q_block_count is None:
+        q_block_count = nqb - q_block_begin
+    rows = max(0, min(shape.seq_q, (q_block_begin + q_block_count) * shape.block) - q_block_begin * shape.block)
+    dq, dk, dv, workspace, ws_bytes = _bwd_outputs(shape, q, rows, dq, dk, dv, workspace, SSA_OP_FULL_BWD)
+    _check("ssa_full_attn_bwd", load_library().ssa_full_attn_bwd(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), int(q_block_begin), int(q_block_count), _ptr(out_full),
+        _ptr(lse_full), _ptr(dout_full), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+        _stream(q.device)))
+    return dq, dk, dv
 
 
 def default_scale(head_dim: int) -> float:

@@ -116,3 +116,15 @@ def make_inputs(w: Workload, device: str | torch.device = "cpu"):
         out.append(t.to(torch.bfloat16).contiguous().to(device))
     return tuple(out)
 
+
+
+def make_output_grad(w: Workload, rows: Optional[Tuple[int, int]] = None, device: str | torch.device = "cpu"):
+    """Seeded synthetic gradient of the attention output, bf16
+    [b, Hq, hi - lo, d] for query rows [lo, hi) (default: every row), drawn
+    from its own generator (seed + 500000) so the forward inputs are unchanged.
+    Row r of the full tensor holds the same values whatever the range."""
+    lo, hi = (0, w.seq_q) if rows is None else rows
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 500000)
+    full = torch.randn((w.batch, w.n_q_heads, w.seq_q, w.head_dim), generator=g, dtype=torch.float32)
+    return full[:, :, lo:hi].to(torch.bfloat16).contiguous().to(device)

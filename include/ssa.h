@@ -80,7 +80,9 @@ typedef enum ssa_op {
   SSA_OP_BLOCK_SCORES = 0,
   SSA_OP_SELECT_TOPK = 1,
   SSA_OP_SPARSE_FWD = 2,
-  SSA_OP_FULL_FWD = 3
+  SSA_OP_FULL_FWD = 3,
+  SSA_OP_SPARSE_BWD = 4, /* ssa_block_sparse_attn_bwd and its _shared variant */
+  SSA_OP_FULL_BWD = 5    /* ssa_full_attn_bwd (any query block range) */
 } ssa_op_t;
 
 /* Key-block summaries: k_summary[b,g,j,:] = fp32 rounding of the mean of the
@@ -221,6 +223,55 @@ ssa_status_t ssa_block_sparse_attn_fwd_early_stop(const ssa_shape_t* shape, cons
                                                   const void* v, const float* scores, const int32_t* block_idx,
                                                   float tau, void* out, float* lse, int32_t* blocks_used,
                                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of the block-sparse forward: for the scalar L = sum(dout * out),
+ * with P = exp(scale * q_r . k_c - lse_r) on the keys c that row r attends to
+ * in ssa_block_sparse_attn_fwd (block_idx as there) and D_r = dout_r . out_r,
+ *   dv[b,g,c,:] = sum over rows r of heads in group g of P_rc dout_r
+ *   dk[b,g,c,:] = scale * sum_r dS_rc q_r,  dq[b,h,r,:] = scale * sum_c dS_rc k_c,
+ *   dS_rc = P_rc (dout_r . v_c - D_r)
+ * (keys outside a row's blocks get nothing from it); fp32 accumulation, bf16
+ * outputs.  out and lse must be what the forward wrote for these inputs.
+ * [SSA-summary] 1 "Planteamiento del Problema" (the sparse stream gives
+ * unselected tokens zero gradient and normalises over the selected subset
+ * only) and 2 "Mecanismo Central" (the sparse stream is trained directly).
+ *   q, k, v, block_idx, out, lse  as ssa_block_sparse_attn_fwd (inputs)
+ *   dout  bf16 [b,Hq,seq_q,d];  dq bf16 [b,Hq,seq_q,d] (output)
+ *   dk, dv  bf16 [b,Hkv,seq_kv,d] (outputs; every row written, zero for keys
+ *           no row attends to)
+ *   workspace  >= ssa_workspace_bytes(shape, SSA_OP_SPARSE_BWD) bytes,
+ *              256-byte aligned (else SSA_ERR_WORKSPACE / SSA_ERR_INVALID_ARG)
+ * More than 32 query heads per KV head: SSA_ERR_UNSUPPORTED.  Results are
+ * bitwise reproducible (no atomics on gradients). */
+ssa_status_t ssa_block_sparse_attn_bwd(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
+                                       const int32_t* block_idx, const void* out, const float* lse,
+                                       const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/* ssa_block_sparse_attn_bwd for a group-shared selection (block_idx int32
+ * [b,Hkv,nqb,topk] as for ssa_block_sparse_attn_fwd_shared); same outputs,
+ * workspace and errors. */
+ssa_status_t ssa_block_sparse_attn_bwd_shared(const ssa_shape_t* shape, const void* q, const void* k,
+                                              const void* v, const int32_t* block_idx, const void* out,
+                                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of the full causal counterpart on query blocks
+ * [q_block_begin, q_block_begin + q_block_count): the gradients of
+ * L = sum(dout_full * out_full) over those rows (P over every key c <= the
+ * row's position; otherwise as ssa_block_sparse_attn_bwd).
+ * [SSA-summary] 2 "Mecanismo Central" (the full stream passes gradient to
+ * every token) and "Alineacion Bidireccional" (the counterpart output is
+ * trained through the alignment objective).
+ *   out_full, lse_full  as written by ssa_full_attn_fwd_dropped_mass for the same range
+ *   dout_full, dq  bf16 [b,Hq,rows_out,d] (rows_out as for the forward)
+ *   dk, dv  bf16 [b,Hkv,seq_kv,d] (outputs; every row written)
+ *   workspace  >= ssa_workspace_bytes(shape, SSA_OP_FULL_BWD) bytes, 256-byte aligned
+ * An empty range (q_block_count == 0) writes nothing. */
+ssa_status_t ssa_full_attn_bwd(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
+                               int32_t q_block_begin, int32_t q_block_count, const void* out_full,
+                               const float* lse_full, const void* dout_full, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes an entry point needs for this shape (0 if none; SIZE_MAX if
  * the shape is invalid). */

@@ -4,6 +4,13 @@ Tolerances (bf16 inputs, fp32 accumulation):
   outputs O      max |diff| <= 2e-2 and ||diff||_2 / ||ref||_2 <= 5e-3
   LSE            max |diff| <= 1e-3
   dropped mass   max |diff| <= 1e-3
+  gradients      max |diff| <= 2e-2 * max |ref| and ||diff||_2 / ||ref||_2 <= 1e-2
+                 (dQ, dK, dV are sums of products with one bf16-rounded factor, P
+                 or dS (relative error <= 2^-9 each), rounded once more to bf16,
+                 and D is taken from the bf16 forward output: about three bf16
+                 roundings against the output's one, hence twice O's rel-L2 bound;
+                 their scale varies with how many rows reach a key, so the
+                 element bound is relative to the tensor's largest entry)
   block indices  identical, except rows whose (k-1)-th and k-th best candidate
                  scores tie within 1e-5 relative; there every swapped block
                  must itself lie inside that tie band.
@@ -38,6 +45,25 @@ def check_close_outputs(got, ref, what="O"):
     assert max_abs <= O_MAX_ABS, f"{what}: max abs {max_abs:.3e} > {O_MAX_ABS}"
     assert rel <= O_REL_L2, f"{what}: rel-L2 {rel:.3e} > {O_REL_L2}"
     return max_abs, rel
+
+
+GRAD_MAX_REL = 2e-2
+GRAD_REL_L2 = 1e-2
+
+
+def check_grad(got, ref, what="grad"):
+    got, ref = np64(got), np64(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    if ref.size == 0:
+        return 0.0, 0.0
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    diff = got - ref
+    max_rel = float(np.abs(diff).max()) / scale
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-30))
+    assert max_rel <= GRAD_MAX_REL, f"{what}: max |diff| / max |ref| = {max_rel:.3e} > {GRAD_MAX_REL}"
+    assert rel <= GRAD_REL_L2, f"{what}: rel-L2 {rel:.3e} > {GRAD_REL_L2}"
+    return max_rel, rel
 
 
 def check_abs(got, ref, tol, what):

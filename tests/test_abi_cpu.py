@@ -80,6 +80,10 @@ def test_shape_validation(lib, kw, status):
                                                      None) == status
     assert lib.ssa_block_sparse_attn_fwd_early_stop(p, FAKE, FAKE, FAKE, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, None,
                                                     0, None) == status
+    for fn in (lib.ssa_block_sparse_attn_bwd, lib.ssa_block_sparse_attn_bwd_shared):
+        assert fn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == status
+    assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                 None) == status
     assert lib.ssa_last_error()
 
 
@@ -133,6 +137,33 @@ def test_decode_workspace(lib):
                                          None) == ssa.SSA_ERR_UNSUPPORTED
 
 
+def test_backward_workspace_and_validation(lib):
+    sh = good_shape()            # b=1, Hq=4, Hkv=2, 256 rows: 4 query / key blocks, chunks of 4 query blocks
+    p = ctypes.byref(sh)
+    rows = 4 * 4 * 64 * 4        # per-row LSE / D arrays: 4 heads x 4 query blocks x 64 rows, fp32
+    parts = 2 * 4 * 2 * 64 * 64 * 4   # 2 KV heads x 4 items x (dK, dV) 64 x 64 fp32
+    need = lib.ssa_workspace_bytes(p, ssa.SSA_OP_SPARSE_BWD)
+    assert need == 2 * rows + 256 + parts           # + the 2 x 4 x 4 head-bit words, padded to 256 bytes
+    assert lib.ssa_workspace_bytes(p, ssa.SSA_OP_FULL_BWD) == 2 * rows + parts
+    args = (FAKE,) * 10
+    assert lib.ssa_block_sparse_attn_bwd(p, *args, FAKE, need - 1, None) == ssa.SSA_ERR_WORKSPACE
+    assert lib.ssa_block_sparse_attn_bwd(p, *args, ctypes.c_void_p(0x10080), need, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"workspace" in lib.ssa_last_error()
+    assert lib.ssa_block_sparse_attn_bwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, need,
+                                         None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"dout is NULL" in lib.ssa_last_error()
+    assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 3, 2, *((FAKE,) * 7), need, None) == ssa.SSA_ERR_INVALID_ARG
+    # a slice never needs more workspace than the whole range
+    assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 2, 2, *((FAKE,) * 6), None, need, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"workspace is NULL" in lib.ssa_last_error()
+    # group-shared / per-head masks hold 32 heads per KV head at most
+    wide = good_shape(n_q_heads=64, n_kv_heads=1)
+    assert lib.ssa_block_sparse_attn_bwd(ctypes.byref(wide), *args, FAKE, 1 << 40, None) == ssa.SSA_ERR_UNSUPPORTED
+    # the long-sequence chunking stays within 64 query blocks per work item
+    long = good_shape(n_q_heads=32, n_kv_heads=2, seq_q=32768, seq_kv=32768, topk=16)
+    assert lib.ssa_workspace_bytes(ctypes.byref(long), ssa.SSA_OP_SPARSE_BWD) < 1 << 30
+
+
 def test_empty_problems_launch_nothing(lib):
     # batch 0 or no query rows: SSA_OK with no HIP call (works without a GPU)
     for sh in (good_shape(batch=0), good_shape(seq_q=0, seq_kv=0)):
@@ -145,6 +176,8 @@ def test_empty_problems_launch_nothing(lib):
         assert lib.ssa_select_topk_shared(p, FAKE, FAKE, None) == ssa.SSA_OK
         assert lib.ssa_block_sparse_attn_fwd_shared(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
                                                     None) == ssa.SSA_OK
+        assert lib.ssa_block_sparse_attn_bwd(p, *((FAKE,) * 11), 0, None) == ssa.SSA_OK
+        assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 0, 0, *((FAKE,) * 7), 0, None) == ssa.SSA_OK
     sh = good_shape()
     assert lib.ssa_full_attn_fwd_dropped_mass(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, 2, 0, FAKE, FAKE, FAKE,
                                               None, 0, None) == ssa.SSA_OK
