@@ -289,6 +289,59 @@ def bench_early_stop(args, torch, ssa, W, taus=(0.05, 1.0)):
     return res
 
 
+def bench_backward(args, torch, ssa, W):
+    """Backward of the block-sparse forward and of the full counterpart on the
+    bench workload, for a synthetic output gradient: time per call (all its
+    kernels) and the useful rate, counting 5 products of 2*d flops per
+    attended (query row, key) pair (score recomputation, dP, dV, dQ, dK)."""
+    w = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.make_inputs(w))
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    nqb = ssa.n_blocks(w.seq_q, w.block)
+    if w.full_rows is None:
+        fb0, fcnt = 0, nqb
+    else:
+        fb0 = w.full_rows[0] // w.block
+        fcnt = ssa.n_blocks(w.full_rows[1], w.block) - fb0
+    rows = (fb0 * w.block, min(w.seq_q, (fb0 + fcnt) * w.block))
+    scores, _ = ssa.ssa_block_scores(shape, q, k)
+    idx = ssa.ssa_select_topk(shape, scores)
+    o, lse = ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx)
+    of, lf, _ = ssa.ssa_full_attn_fwd_dropped_mass(shape, q, k, v, idx, fb0, fcnt)
+    dout = W.make_output_grad(w, device=dev)
+    dout_f = W.make_output_grad(w, rows, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq_f = torch.empty_like(dout_f)
+    ws = torch.empty((max(ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_BWD),
+                          ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_FULL_BWD)),), dtype=torch.uint8, device=dev)
+    calls = {
+        "sparse": lambda: ssa.ssa_block_sparse_attn_bwd(shape, q, k, v, idx, o, lse, dout, dq, dk, dv, ws),
+        "full": lambda: ssa.ssa_full_attn_bwd(shape, q, k, v, of, lf, dout_f, fb0, fcnt, dq_f, dk, dv, ws),
+    }
+    pairs = {"sparse": w.batch * w.n_q_heads * sparse_useful_pairs(nqb, w.topk, w.block),
+             "full": w.batch * w.n_q_heads * full_useful_pairs(*rows)}
+    res = {"workload": w.name, "flops_per_pair": 10 * w.head_dim}
+    n = max(1, args.steps // 2)
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        gf = 10.0 * w.head_dim * pairs[name] / 1e9
+        tf = gf / (ms * 1e-3) / 1e3
+        res[name] = {"avg_ms": round(ms, 5), "gflop_per_call": round(gf, 3), "tflops": round(tf, 2),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return res
+
+
 def cpu_baseline(args, W):
     """The fp64 oracle, as it stands, on a bounded sample of the prefill workload:
     whole query heads (all rows, all five steps) until ~target seconds elapse."""
@@ -352,6 +405,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the extra legs (group-shared selection, early stopping)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--counter-pass", action="store_true",
@@ -412,6 +466,7 @@ def main():
         "decode": dec,
         "shared_selection": shared,
         "early_stop": None if args.no_shared else bench_early_stop(args, torch, ssa, W),
+        "backward": None if args.no_backward else bench_backward(args, torch, ssa, W),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -250,11 +250,12 @@ ssa_status_t bwd_impl(const ssa_shape_t* shape, const void* q, const void* k, co
   CHECK_PTR(dq, 16, fn);
   CHECK_PTR(dk, 16, fn);
   CHECK_PTR(dv, 16, fn);
-  ssa::BwdChunks ch;
-  size_t off[4], need;
-  ssa::bwd_plan(g, full, q_block_begin, q_block_count, &ch, off, &need);
-  const uint64_t grid = (uint64_t)g.batch * g.hkv * g.nkb * ch.max_count();
-  if (grid > 0x7fffffffull) return fail(SSA_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  ssa::BwdPlan plan;
+  size_t off[7], need;
+  ssa::bwd_plan(g, full, q_block_begin, q_block_count, &plan, off, &need);
+  const uint64_t grid = (uint64_t)g.batch * g.hkv * (uint64_t)plan.max_items;
+  if (grid > 0x7fffffffull || plan.max_items == 0x7fffffff)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: problem too large", fn);
   if (workspace_bytes < need)
     return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
   CHECK_PTR(workspace, 256, fn);
@@ -275,12 +276,15 @@ ssa_status_t bwd_impl(const ssa_shape_t* shape, const void* q, const void* k, co
   a.lse2 = (float*)(ws + off[0]);
   a.delta = (float*)(ws + off[1]);
   a.mask = full ? nullptr : (uint32_t*)(ws + off[2]);
-  a.part = (float*)(ws + off[3]);
+  a.pairs = full ? nullptr : (int*)(ws + off[3]);
+  a.item_base = (int*)(ws + off[4]);
+  a.item_key = (int*)(ws + off[5]);
+  a.part = (float*)(ws + off[6]);
   a.qb_begin = q_block_begin;
   a.qb_count = q_block_count;
   const int64_t end_row = (int64_t)(q_block_begin + q_block_count) * ssa::kBlock;
   a.rows_out = (int)((end_row < g.seq_q ? end_row : g.seq_q) - (int64_t)q_block_begin * ssa::kBlock);
-  a.chunks = ch;
+  a.plan = plan;
   hipError_t e = ssa::launch_attn_backward(a, g, stream);
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
@@ -401,9 +405,9 @@ size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {
   if (empty) return 0;
   if (op == SSA_OP_SPARSE_FWD && g.seq_q == 1) return ssa::decode_workspace_bytes(g.batch, g.hq, g.hkv);
   if (op == SSA_OP_SPARSE_BWD || op == SSA_OP_FULL_BWD) {
-    ssa::BwdChunks ch;
-    size_t off[4], need;
-    ssa::bwd_plan(g, op == SSA_OP_FULL_BWD, 0, g.nqb, &ch, off, &need);
+    ssa::BwdPlan plan;
+    size_t off[7], need;
+    ssa::bwd_plan(g, op == SSA_OP_FULL_BWD, 0, g.nqb, &plan, off, &need);
     return need;
   }
   return 0;

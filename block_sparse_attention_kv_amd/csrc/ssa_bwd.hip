@@ -20,18 +20,21 @@
 //     key-side kernel reads.  Per tile, transposed as in the forward (a lane
 //     owns one query column):  S^T = K Q^T,  dP^T = V dO^T  (Q, dO in
 //     registers), then dQ^T += K^T dS^T with K^T read transposed from LDS.
-//   * dK/dV kernel: one workgroup (2 waves, 32 keys each) per work item
-//     (b, KV head, key block j, chunk of at most R query blocks); it walks the
-//     (query head, query block) pairs of the chunk whose list holds j, in
-//     (query block, head) order.  Per pair, untransposed (a lane owns one key
-//     column):  S = Q K^T,  dP = dO V^T  (K, V in registers), then
-//     dV += P^T dO and dK += dS^T Q with dO, Q read transposed from LDS.
-//     Each item writes an fp32 partial; a reduce kernel sums the chunks of a
-//     key block in chunk order and rounds to bf16.
-// The (query head, query block) pairs of a key block come from a bitmask
-// mask[b, g, j, i] (bit hh: head g*G+hh lists j for query block i), built
-// from the index rows with atomic ORs (order-independent).
+//   * dK/dV kernel: one workgroup (2 waves, 32 keys each) per work item: at
+//     most P consecutive (query head, query block) pairs, in (query block,
+//     head) order, of the pairs whose list holds key block j.  Per pair,
+//     untransposed (a lane owns one key column):  S = Q K^T,  dP = dO V^T
+//     (K, V in registers), then dV += P^T dO and dK += dS^T Q with dO, Q read
+//     transposed from LDS.  Each item writes an fp32 partial; a reduce kernel
+//     sums the items of a key block in item order and rounds to bf16.
+// Both tile loops run a three-buffer ring: the tiles of step t+2 are requested
+// while step t is computed.
+// The pairs of a key block come from a bitmask mask[b, g, j, i] (bit hh: head
+// g*G+hh lists j for query block i) built from the index rows with atomic
+// ORs (order-independent); the pairs of each key block are then counted from
+// the bits, so the item boundaries do not depend on timing.
 #include <algorithm>
+#include <type_traits>
 
 #include "ssa_common.hpp"
 #include "ssa_internal.hpp"
@@ -41,7 +44,9 @@ namespace ssa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxPairs = kBwdMaxChunk * 32;  // query blocks per item x heads per group (sparse)
+constexpr int kSparsePairs = 64;   // pairs per work item, block-sparse backward
+constexpr int kFullPairs = 128;    // pairs per work item, full backward
+constexpr int kRing = 3;           // tile buffers per loop
 
 // ---------------------------------------------------------------------------- index inversion
 
@@ -109,18 +114,38 @@ __device__ __forceinline__ float dot_row_ops(const bf16x8 a[4], const bf16x8 b[4
   return acc;
 }
 
+// Workgroup id -> (KV group gi = b*Hkv + g, unit index within the group, 0 =
+// heaviest), dealt so that a KV group's units stay on a fixed subset of the 8
+// XCDs when the counts allow (its K and V then stay in that L2).
+__device__ __forceinline__ void map_unit_bwd(int w, int n_groups, int per_group, int& gi, int& u) {
+  const int n = n_groups * per_group;
+  if ((n & 7) == 0 && n_groups <= 8 && (8 % n_groups) == 0) {
+    const int x = w & 7, k = w >> 3, xpg = 8 / n_groups;
+    gi = x / xpg;
+    u = k * xpg + (x - gi * xpg);
+  } else if ((n & 7) == 0 && (n_groups & 7) == 0) {
+    const int x = w & 7, k = w >> 3, gpx = n_groups >> 3;
+    gi = x + 8 * (k % gpx);
+    u = k / gpx;
+  } else {
+    gi = w % n_groups;
+    u = w / n_groups;
+  }
+}
+
 __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry geo) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[kRing][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[kRing][kTileBytes];
   __shared__ int sList[2][kMaxTopk];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = geo.group;
-  const int u = blockIdx.x;  // (b, h, i) with the longest query blocks first
-  const int bh = u % (geo.batch * geo.hq);
-  const int i = a.qb_begin + a.qb_count - 1 - u / (geo.batch * geo.hq);
-  const int b = bh / geo.hq, h = bh - b * geo.hq;
-  const int gi = b * geo.hkv + h / G;
+  int gi, u;
+  map_unit_bwd(blockIdx.x, geo.batch * geo.hkv, G * a.qb_count, gi, u);
+  const int i = a.qb_begin + a.qb_count - 1 - u / G;  // longest rows first
+  const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+  const int h = g * G + (u - (u / G) * G);
+  const int bh = b * geo.hq + h;
   const int jd = (geo.q_offset + i * kBlock) / kBlock;
   const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
   const uint16_t* kbase = a.k + kvoff;
@@ -145,11 +170,22 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
   auto tile_block = [&](int t) { return a.full ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
   TileOffsets<2, 0> toff;
   toff.init(lane, wave);
-  if (nt > 0) {
-    const int j0 = tile_block(0);
-    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK[0], lane, toff);
-    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV[0], lane, toff);
-  }
+  // requests of tile t into ring buffer BUF (a compile-time index, so that
+  // every LDS address below is a fixed per-lane offset plus an immediate)
+  auto issue = [&](auto BUF, int t) {
+    constexpr int buf = decltype(BUF)::value;
+    const int jn = tile_block(t);
+    const size_t off = (size_t)jn * kBlock * kHeadDim;
+    const int nv = geo.seq_kv - jn * kBlock;
+    tile_load(kbase + off, nv, sK[buf], lane, toff);
+    tile_load(vbase + off, nv, sV[buf], lane, toff);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  static_assert(kRing == 3, "the tile loop is unrolled over a three-buffer ring");
+  if (nt > 0) issue(B0{}, 0);
+  if (nt > 1) issue(B1{}, 1);
   // per-row constants: LSE in log2 units (+inf where the row has no keys or
   // does not exist, so that every P is 0) and D = dO . O
   const float dsum = sum_xor32(dot_row_ops(dop, oop));
@@ -166,20 +202,20 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
   const float c = geo.scale_log2;
   const int pos = geo.q_offset + row;
-  for (int t = 0; t < nt; ++t) {
+  auto step = [&](auto BUF, int t) {
+    constexpr int buf = decltype(BUF)::value;
     const int j = tile_block(t);
-    wait_vmem<0>();   // this wave's share of tile t (and, at t = 0, the row loads)
+    // this wave's share of tile t landed (tile t+1's 8 requests may be in flight)
+    if (t + 1 < nt)
+      wait_vmem<8>();
+    else
+      wait_vmem<0>();
     __syncthreads();  // every wave's share; every wave is done with tile t-1
-    if (t + 1 < nt) {
-      const int jn = tile_block(t + 1);
-      const size_t off = (size_t)jn * kBlock * kHeadDim;
-      const int nv = geo.seq_kv - jn * kBlock;
-      tile_load(kbase + off, nv, sK[(t + 1) & 1], lane, toff);
-      tile_load(vbase + off, nv, sV[(t + 1) & 1], lane, toff);
-    }
-    const uint8_t* tK = sK[t & 1];
-    const uint8_t* tV = sV[t & 1];
+    if (t + 2 < nt) issue(std::integral_constant<int, (buf + 2) % kRing>{}, t + 2);
+    const uint8_t* tK = sK[buf];
+    const uint8_t* tV = sV[buf];
     const bool diag = j == jd;
+    int qrel = pos - j * kBlock;  // query position relative to the tile's first key
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       bf16x8 ka[4], va[4];
@@ -199,7 +235,17 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
         s = mfma32(ka[ks], qop[ks], s);    // S^T: rows keys, columns queries
         dp = mfma32(va[ks], dop[ks], dp);  // dP^T
       }
-      // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * c - LSE2), future keys 0
+      if (diag) {
+        // the tile holding the rows' own positions: a key after the query gets -inf
+        asm volatile("" : "+v"(qrel));  // keep the mask inside this branch
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const uint32_t neg_inf_if_future = (uint32_t)((qrel - kr) >> 31) & 0xFF800000u;
+          s[r] += __uint_as_float(neg_inf_if_future);
+        }
+      }
+      // dS^T = P^T * (dP^T - D), P^T = exp2(S^T * c - LSE2)
       u32x4 pds[2];
 #pragma unroll
       for (int ap = 0; ap < 2; ++ap)
@@ -209,11 +255,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             const int r = 8 * ap + 2 * e + x;
-            float p = fast_exp2(fmaf(s[r], c, -lse2));
-            if (diag) {
-              const int key = j * kBlock + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-              p = key > pos ? 0.f : p;
-            }
+            const float p = fast_exp2(fmaf(s[r], c, -lse2));
             d2[x] = p * (dp[r] - dsum);
           }
           pds[ap][e] = pack_bf16x2(d2[0], d2[1]);
@@ -225,6 +267,11 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
         for (int db = 0; db < 2; ++db)
           dq[db] = mfma32(read_tile_tr(tK, 32 * kb + 16 * ap, db, lane), as_bf16x8(pds[ap]), dq[db]);
     }
+  };
+  for (int t0 = 0; t0 < nt; t0 += kRing) {
+    step(B0{}, t0);
+    if (t0 + 1 < nt) step(B1{}, t0 + 1);
+    if (t0 + 2 < nt) step(B2{}, t0 + 2);
   }
   if (vrow) {
     uint16_t* qp = a.dq + ((size_t)bh * a.rows_out + orow) * kHeadDim;
@@ -253,64 +300,116 @@ __device__ __forceinline__ void dma_row64(const float* g, uint32_t lds_base, int
       : "memory", "m0");
 }
 
+// pairs[gi, j] = number of head bits of key block j over its query blocks
+// (one wavefront per (group, key block)).
+__global__ __launch_bounds__(64) void bwd_count_kernel(BwdArgs a, Geometry geo) {
+  const int lane = threadIdx.x;
+  const int gi = blockIdx.x / geo.nkb, j = blockIdx.x - gi * geo.nkb;
+  const BwdPlan pl = a.plan;
+  const uint32_t* m = a.mask + ((size_t)gi * geo.nkb + j) * geo.nqb;
+  int cnt = 0;
+  for (int i = pl.first_block(j) + lane; i < pl.hi; i += 64) cnt += __builtin_popcount(m[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) a.pairs[blockIdx.x] = cnt;
+}
+
+// Exclusive scan over key blocks of each group's item counts:
+// item_base[gi, j] = first item of key block j, item_base[gi, nkb] = total;
+// item_key[gi, e] = key block of item e.
+__global__ __launch_bounds__(256) void bwd_items_kernel(BwdArgs a, Geometry geo) {
+  __shared__ int sTot[256];
+  const int gi = blockIdx.x, tid = threadIdx.x;
+  const BwdPlan pl = a.plan;
+  const int per = (geo.nkb + 255) / 256;
+  const int j0 = min(geo.nkb, tid * per), j1 = min(geo.nkb, j0 + per);
+  auto items = [&](int j) {
+    const int np = a.full ? geo.group * pl.n_blocks(j) : a.pairs[(size_t)gi * geo.nkb + j];
+    return (np + pl.P - 1) / pl.P;
+  };
+  int tot = 0;
+  for (int j = j0; j < j1; ++j) tot += items(j);
+  sTot[tid] = tot;
+  __syncthreads();
+  int base = 0;
+  for (int t = 0; t < tid; ++t) base += sTot[t];
+  int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
+  int* ik = a.item_key + (size_t)gi * pl.max_items;
+  for (int j = j0; j < j1; ++j) {
+    ib[j] = base;
+    const int n = items(j);
+    for (int e = 0; e < n && base + e < pl.max_items; ++e) ik[base + e] = j;  // never exceeds the bound
+    base += n;
+  }
+  if (tid == 255) ib[geo.nkb] = base;
+}
+
 __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometry geo) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sQ[2][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sO[2][kTileBytes];  // dO tiles
-  __shared__ __attribute__((aligned(256))) float sL[2][kBlock];          // LSE (log2 units)
-  __shared__ __attribute__((aligned(256))) float sD[2][kBlock];          // D
-  __shared__ int sPairs[kMaxPairs];
-  __shared__ int sNPairs;
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[kRing][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sO[kRing][kTileBytes];  // dO tiles
+  __shared__ __attribute__((aligned(256))) float sL[kRing][kBlock];          // LSE (log2 units)
+  __shared__ __attribute__((aligned(256))) float sD[kRing][kBlock];          // D
+  __shared__ int sPairs[kSparsePairs];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = geo.group;
-  const BwdChunks ch = a.chunks;
+  const BwdPlan pl = a.plan;
   const int ngroups = geo.batch * geo.hkv;
-  const int x = blockIdx.x;
-  const int gi = x % ngroups;
-  const int rest = x / ngroups;
-  const int j = rest % geo.nkb;
-  const int cidx = rest / geo.nkb;
-  const int nch = ch.count(j);
-  if (cidx >= nch) return;
-  const int i0 = ch.first_block(j) + cidx * ch.R;
-  const int i1 = min(i0 + ch.R, ch.hi);
-  const size_t item = (size_t)gi * ch.items_per_group + ch.prefix(j) + cidx;
+  const int gi = blockIdx.x % ngroups;
+  const int nslots = gridDim.x / ngroups;
+  const int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
+  const int* item_key = a.item_key + (size_t)gi * pl.max_items;
+  const int total = __builtin_amdgcn_readfirstlane(min(ib[geo.nkb], pl.max_items));
   const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+  TileOffsets<2, 0> toff;
+  toff.init(lane, wave);
+  const size_t rows_pad = (size_t)a.qb_count * kBlock;
+  const float c = geo.scale_log2;
+  // items in key-block order, dealt round-robin to this group's workgroups
+  for (int li = blockIdx.x / ngroups; li < total; li += nslots) {
+  const int j = __builtin_amdgcn_readfirstlane(item_key[li]);
+  const int p_lo = (li - ib[j]) * pl.P;
+  const int pairs_j = a.full ? G * pl.n_blocks(j) : a.pairs[(size_t)gi * geo.nkb + j];
+  const int npairs = __builtin_amdgcn_readfirstlane(min(pl.P, pairs_j - p_lo));
+  const int ifirst = pl.first_block(j);
+  __syncthreads();  // both waves are done with the previous item's buffers and pair list
 
-  // the chunk's (query block, head) pairs, in (query block, head) order
-  int npairs;
-  if (a.full) {
-    npairs = (i1 - i0) * G;
-  } else {
+  if (!a.full) {
+    // this item's pairs: numbers p_lo .. p_lo + npairs - 1 of key block j, in
+    // (query block, head) order, from the head bits of query blocks ifirst..
     if (wave == 0) {
-      const int ii = i0 + lane;
-      const uint32_t bits = ii < i1 ? a.mask[((size_t)gi * geo.nkb + j) * geo.nqb + ii] : 0u;
-      const int cnt = __builtin_popcount(bits);
-      int incl = cnt;
+      int before = 0;  // pairs of the query blocks already passed
+      for (int i0 = ifirst; i0 < pl.hi && before < p_lo + npairs; i0 += 64) {
+        const int ii = i0 + lane;
+        const uint32_t bits = ii < pl.hi ? a.mask[((size_t)gi * geo.nkb + j) * geo.nqb + ii] : 0u;
+        const int cnt = __builtin_popcount(bits);
+        int incl = cnt;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        int pos = before + incl - cnt;
+        uint32_t m = bits;
+        while (m) {
+          const int hh = __builtin_ctz(m);
+          m &= m - 1u;
+          if (pos >= p_lo && pos < p_lo + npairs) sPairs[pos - p_lo] = (ii << 8) | hh;
+          ++pos;
+        }
+        before += __shfl(incl, 63, 64);
       }
-      int pos = incl - cnt;
-      uint32_t m = bits;
-      while (m) {
-        const int hh = __builtin_ctz(m);
-        m &= m - 1u;
-        sPairs[pos++] = (lane << 8) | hh;
-      }
-      if (lane == 63) sNPairs = incl;
     }
     __syncthreads();
-    npairs = sNPairs;
   }
   auto pair_of = [&](int p, int& ii, int& hh) {
     if (a.full) {
-      ii = i0 + p / G;
-      hh = p - (p / G) * G;
+      const int q = p_lo + p;
+      ii = ifirst + q / G;
+      hh = q - (q / G) * G;
     } else {
       const int e = __builtin_amdgcn_readfirstlane(sPairs[p]);
-      ii = i0 + (e >> 8);
+      ii = e >> 8;
       hh = e & 255;
     }
   };
@@ -323,10 +422,10 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
   load_row_op(a.k + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, kop);
   load_row_op(a.v + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, vop);
 
-  TileOffsets<2, 0> toff;
-  toff.init(lane, wave);
-  const size_t rows_pad = (size_t)a.qb_count * kBlock;
-  auto issue = [&](int p, int buf) {
+  // requests of pair p into ring buffer BUF (a compile-time index, so that
+  // every LDS address below is a fixed per-lane offset plus an immediate)
+  auto issue = [&](auto BUF, int p) {
+    constexpr int buf = decltype(BUF)::value;
     int ii, hh;
     pair_of(p, ii, hh);
     const int bh = b * geo.hq + g * G + hh;
@@ -340,7 +439,12 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
     else
       dma_row64(a.delta + prow, lds_addr(sD[buf]), lane);
   };
-  if (npairs > 0) issue(0, 0);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  static_assert(kRing == 3, "the pair loop is unrolled over a three-buffer ring");
+  if (npairs > 0) issue(B0{}, 0);
+  if (npairs > 1) issue(B1{}, 1);
 
   f32x16 dk[2], dv[2];
 #pragma unroll
@@ -350,19 +454,23 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
       dk[db][r] = 0.f;
       dv[db][r] = 0.f;
     }
-  const float c = geo.scale_log2;
-  for (int p = 0; p < npairs; ++p) {
+  auto step = [&](auto BUF, int p) {
+    constexpr int buf = decltype(BUF)::value;
     int ii, hh;
     pair_of(p, ii, hh);
-    wait_vmem<0>();   // this wave's share of pair p (and, at p = 0, K and V)
+    // this wave's share of pair p landed (pair p+1's 9 requests may be in flight)
+    if (p + 1 < npairs)
+      wait_vmem<9>();
+    else
+      wait_vmem<0>();
     __syncthreads();  // every wave's share; every wave is done with pair p-1
-    if (p + 1 < npairs) issue(p + 1, (p + 1) & 1);
-    const uint8_t* tQ = sQ[p & 1];
-    const uint8_t* tO = sO[p & 1];
-    const float* tL = sL[p & 1];
-    const float* tD = sD[p & 1];
+    if (p + 2 < npairs) issue(std::integral_constant<int, (buf + 2) % kRing>{}, p + 2);
+    const uint8_t* tQ = sQ[buf];
+    const uint8_t* tO = sO[buf];
+    const float* tL = sL[buf];
+    const float* tD = sD[buf];
     const bool diag = j == (geo.q_offset + ii * kBlock) / kBlock;
-    const int kpos = key - (geo.q_offset + ii * kBlock);  // key position relative to the block's first row
+    int kpos = key - (geo.q_offset + ii * kBlock);  // key position relative to the block's first row
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       bf16x8 qa[4], oa[4];
@@ -382,6 +490,16 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
         s = mfma32(qa[ks], kop[ks], s);    // S: rows queries, columns keys
         dp = mfma32(oa[ks], vop[ks], dp);  // dP
       }
+      if (diag) {
+        // the key-query block on the diagonal: a key after the query's position gets -inf
+        asm volatile("" : "+v"(kpos));  // keep the mask inside this branch
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 32 * qb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const uint32_t neg_inf_if_future = (uint32_t)((m - kpos) >> 31) & 0xFF800000u;
+          s[r] += __uint_as_float(neg_inf_if_future);
+        }
+      }
       u32x4 pp[2], pds[2];
 #pragma unroll
       for (int ap = 0; ap < 2; ++ap) {
@@ -394,8 +512,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = 8 * ap + 4 * rg2 + x;
-            float p = fast_exp2(fmaf(s[r], c, -l4[x]));
-            if (diag) p = kpos > m0 + x ? 0.f : p;
+            const float p = fast_exp2(fmaf(s[r], c, -l4[x]));
             pv[x] = p;
             dv4[x] = p * (dp[r] - d4[x]);
           }
@@ -414,9 +531,14 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
           dk[db] = mfma32(as_bf16x8(pds[ap]), read_tile_tr(tQ, 32 * qb + 16 * ap, db, lane), dk[db]);
         }
     }
+  };
+  for (int p0 = 0; p0 < npairs; p0 += kRing) {
+    step(B0{}, p0);
+    if (p0 + 1 < npairs) step(B1{}, p0 + 1);
+    if (p0 + 2 < npairs) step(B2{}, p0 + 2);
   }
   // partial sums of this item: [2][64 keys][64 d] fp32 (dK unscaled)
-  float* pk = a.part + item * (2 * kBlock * kHeadDim);
+  float* pk = a.part + ((size_t)gi * pl.max_items + li) * (2 * kBlock * kHeadDim);
   float* pv = pk + kBlock * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 2; ++db)
@@ -426,9 +548,10 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
       pk[kr * kHeadDim + 32 * db + l32] = dk[db][r];
       pv[kr * kHeadDim + 32 * db + l32] = dv[db][r];
     }
+  }
 }
 
-// Sum the chunk partials of each key block in chunk order: dK = scale * sum,
+// Sum the item partials of each key block in item order: dK = scale * sum,
 // dV = sum, rounded to bf16.  One thread per 4 columns of a key row.
 __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometry geo) {
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -439,9 +562,9 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometr
   const int key = rem / (kHeadDim / 4);
   const int c4 = rem - key * (kHeadDim / 4);
   const int j = key / kBlock, kr = key - j * kBlock;
-  const BwdChunks ch = a.chunks;
-  const int n = ch.count(j);
-  const float* base = a.part + ((size_t)gi * ch.items_per_group + ch.prefix(j)) * (2 * kBlock * kHeadDim) +
+  const int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
+  const int n = min(ib[j + 1], a.plan.max_items) - ib[j];
+  const float* base = a.part + ((size_t)gi * a.plan.max_items + ib[j]) * (2 * kBlock * kHeadDim) +
                       kr * kHeadDim + 4 * c4;
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
   for (int e = 0; e < n; ++e) {
@@ -461,47 +584,66 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometr
 
 }  // namespace
 
-void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdChunks* ch, size_t off[4],
+void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan* plan, size_t off[7],
               size_t* total) {
-  BwdChunks c;
-  c.lo = qb_begin;
-  c.hi = qb_begin + qb_count;
-  c.qoffb = g.q_offset / kBlock;
-  // chunk length from the problem's query-block count only, so that a slice
-  // never needs more items than the whole range
-  c.R = std::max(4, std::min(kBwdMaxChunk, g.nqb / 8));
-  c.items_per_group = c.prefix(g.nkb);
-  *ch = c;
+  BwdPlan p;
+  p.lo = qb_begin;
+  p.hi = qb_begin + qb_count;
+  p.qoffb = g.q_offset / kBlock;
+  p.P = full ? kFullPairs : kSparsePairs;
+  long long items = 0;  // every (head, query block) pair present
+  for (int j = 0; j < g.nkb; ++j) items += ((long long)g.group * p.n_blocks(j) + p.P - 1) / p.P;
+  if (!full) {
+    // a list names at most min(topk, diag + 1) distinct blocks, so a group has
+    // at most G * sum_i min(topk, diag(i) + 1) pairs; cutting each key block's
+    // pairs into items of P adds at most one partial item per key block
+    long long pairs = 0;
+    for (int i = p.lo; i < p.hi; ++i) pairs += std::min<long long>(g.topk, (long long)p.qoffb + i + 1);
+    items = std::min(items, (g.group * pairs + p.P - 1) / p.P + g.nkb);
+  }
+  p.max_items = (int)std::min<long long>(items, 0x7fffffff);
+  *plan = p;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)g.batch * g.hq * qb_count * kBlock;
+  const size_t ngroups = (size_t)g.batch * g.hkv;
   size_t o = 0;
   off[0] = o;
   o += up(rows * sizeof(float));
   off[1] = o;
   o += up(rows * sizeof(float));
   off[2] = o;
-  if (!full) o += up((size_t)g.batch * g.hkv * g.nkb * g.nqb * sizeof(uint32_t));
+  if (!full) o += ngroups * g.nkb * g.nqb * sizeof(uint32_t);
   off[3] = o;
-  o += up((size_t)g.batch * g.hkv * c.items_per_group * 2 * kBlock * kHeadDim * sizeof(float));
+  if (!full) o += ngroups * g.nkb * sizeof(int);
+  o = up(o);
+  off[4] = o;
+  o += up(ngroups * (g.nkb + 1) * sizeof(int));
+  off[5] = o;
+  o += up(ngroups * (size_t)p.max_items * sizeof(int));
+  off[6] = o;
+  o += up(ngroups * (size_t)p.max_items * 2 * kBlock * kHeadDim * sizeof(float));
   *total = o;
 }
 
 hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t stream) {
   const size_t units = (size_t)g.batch * g.hq * a.qb_count;
   if (units == 0) return hipSuccess;
+  const size_t ngroups = (size_t)g.batch * g.hkv;
   if (!a.full) {
-    const size_t words = (size_t)g.batch * g.hkv * g.nkb * g.nqb;
+    const size_t words = ngroups * g.nkb * g.nqb;
     const unsigned zb = (unsigned)std::min<size_t>((words + 255) / 256, 4096);
     hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3(zb), dim3(256), 0, stream, a.mask, words);
     const size_t rows = (size_t)g.batch * (a.idx_shared ? g.hkv : g.hq) * g.nqb;
-    hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)rows), dim3(64), 0, stream, a.idx, a.mask, g,
-                       a.idx_shared);
+    hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)rows), dim3(64), 0, stream, a.idx, a.mask, g, a.idx_shared);
+    hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)(ngroups * g.nkb)), dim3(64), 0, stream, a, g);
   }
+  hipLaunchKernelGGL(bwd_items_kernel, dim3((unsigned)ngroups), dim3(256), 0, stream, a, g);
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)units), dim3(128), 0, stream, a, g);
-  const size_t items_grid = (size_t)g.batch * g.hkv * g.nkb * a.chunks.max_count();
-  if (items_grid > 0)
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)items_grid), dim3(128), 0, stream, a, g);
-  const size_t threads = (size_t)g.batch * g.hkv * g.seq_kv * (kHeadDim / 4);
+  // enough workgroups to fill the chip a few times over; each walks its
+  // group's items with a stride
+  const size_t slots = std::max<size_t>(1, std::min<size_t>((size_t)a.plan.max_items, 2048 / ngroups));
+  hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)(ngroups * slots)), dim3(128), 0, stream, a, g);
+  const size_t threads = ngroups * g.seq_kv * (kHeadDim / 4);
   if (threads > 0)
     hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, g);
   return hipGetLastError();

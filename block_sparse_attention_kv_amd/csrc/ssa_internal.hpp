@@ -61,36 +61,20 @@ inline size_t decode_workspace_bytes(int batch, int hq, int hkv) {
   return (size_t)batch * hq * decode_pieces(batch, hkv) * kPartialFloats * sizeof(float);
 }
 
-// Backward work items: the dK/dV of key block j are summed over the query
-// blocks i in [lo, hi) whose diagonal block is >= j, cut into chunks of at most
-// R query blocks; count(j) chunks for key block j, numbered prefix(j) ..
-// prefix(j) + count(j) - 1 within each (batch, KV head) group.
-constexpr int kBwdMaxChunk = 64;
-
-struct BwdChunks {
-  int lo, hi;   // query blocks handled
-  int qoffb;    // q_offset / B: query block i's diagonal key block is qoffb + i
-  int R;        // query blocks per chunk (<= kBwdMaxChunk)
-  long long items_per_group;
+// Backward work items: the (query head, query block) pairs that attend to key
+// block j -- query blocks i in [lo, hi) with diagonal block qoffb + i >= j, in
+// (query block, head) order -- are cut into items of at most P pairs; items
+// are numbered per (batch, KV head) group in key-block order.
+struct BwdPlan {
+  int lo, hi;     // query blocks handled
+  int qoffb;      // q_offset / B (floor): query block i's diagonal key block is qoffb + i
+  int P;          // pairs per item
+  int max_items;  // items of one group when every pair is present (bound)
 
   __host__ __device__ int first_block(int j) const { return j - qoffb > lo ? j - qoffb : lo; }
-  __host__ __device__ int count(int j) const {
+  __host__ __device__ int n_blocks(int j) const {
     const int n = hi - first_block(j);
-    return n > 0 ? (n + R - 1) / R : 0;
-  }
-  __host__ __device__ int max_count() const { return (hi - lo + R - 1) / R; }
-  // sum_{m=1..x} ceil(m / R)
-  __host__ __device__ long long ceil_sum(long long x) const {
-    if (x <= 0) return 0;
-    const long long q = x / R, s = x - q * R;
-    return (long long)R * q * (q + 1) / 2 + s * (q + 1);
-  }
-  // sum of count(j') for j' < j
-  __host__ __device__ long long prefix(int j) const {
-    const long long t = (long long)lo + qoffb;
-    const long long c0 = max_count();
-    if (j <= t + 1) return (long long)j * c0;
-    return (t + 1) * c0 + ceil_sum(hi - lo - 1) - ceil_sum((long long)hi + qoffb - j);
+    return n > 0 ? n : 0;
   }
 };
 
@@ -107,17 +91,20 @@ struct BwdArgs {
   uint16_t* dq;  // rows_out rows per (b, h)
   uint16_t* dk;  // [b, Hkv, seq_kv, d]
   uint16_t* dv;
-  float* lse2;     // workspace: per-row LSE in log2 units, qb_count*B rows per (b, h)
-  float* delta;    // workspace: per-row dO . O, same layout
-  uint32_t* mask;  // workspace (sparse): [b, Hkv, nkb, nqb] head bits
-  float* part;     // workspace: per-item [2][B][d] fp32 partial dK, dV
+  float* lse2;        // workspace: per-row LSE in log2 units, qb_count*B rows per (b, h)
+  float* delta;       // workspace: per-row dO . O, same layout
+  uint32_t* mask;     // workspace (sparse): [b*Hkv, nkb, nqb] head bits
+  int* pairs;         // workspace (sparse): [b*Hkv, nkb] pairs per key block
+  int* item_base;     // workspace: [b*Hkv, nkb + 1] first item of each key block
+  int* item_key;      // workspace: [b*Hkv, max_items] key block of each item
+  float* part;        // workspace: [b*Hkv, max_items][2][B][d] fp32 partial dK, dV
   int qb_begin, qb_count, rows_out;
-  BwdChunks chunks;
+  BwdPlan plan;
 };
 
-// Chunking and workspace layout of a backward call (byte offsets of lse2,
-// delta, mask, part; total bytes).
-void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdChunks* ch, size_t off[4],
+// Work-item plan and workspace layout of a backward call (byte offsets of
+// lse2, delta, mask, pairs, item_base, item_key, part; total bytes).
+void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan* plan, size_t off[7],
               size_t* total);
 
 hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geometry& g,

@@ -48,6 +48,18 @@ def classify(name: str):
         # attn_group_kernel<NW, FULL>: demangled "..., true>" / mangled "...Lb1E..."
         full = ("true>" in name) or ("Lb1E" in name)
         return "full_attn" if full else "sparse_attn_shared"
+    if "attn_bwd_dkv_kernel" in name:
+        return "bwd_dkv"
+    if "attn_bwd_dq_kernel" in name:
+        return "bwd_dq"
+    if "attn_bwd_reduce_kernel" in name:
+        return "bwd_reduce"
+    if "bwd_mask_kernel" in name:
+        return "bwd_mask"
+    if "bwd_items_kernel" in name:
+        return "bwd_items"
+    if "bwd_fill_zero_kernel" in name:
+        return "bwd_clear"
     if "attn_sparse_early_stop_kernel" in name:
         return "sparse_attn_early_stop"
     if "attn_sparse_kernel" in name:

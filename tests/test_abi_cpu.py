@@ -138,13 +138,14 @@ def test_decode_workspace(lib):
 
 
 def test_backward_workspace_and_validation(lib):
-    sh = good_shape()            # b=1, Hq=4, Hkv=2, 256 rows: 4 query / key blocks, chunks of 4 query blocks
+    sh = good_shape()            # b=1, Hq=4, Hkv=2, 256 rows: 4 query / key blocks
     p = ctypes.byref(sh)
     rows = 4 * 4 * 64 * 4        # per-row LSE / D arrays: 4 heads x 4 query blocks x 64 rows, fp32
-    parts = 2 * 4 * 2 * 64 * 64 * 4   # 2 KV heads x 4 items x (dK, dV) 64 x 64 fp32
+    parts = 2 * 4 * 2 * 64 * 64 * 4   # 2 KV heads x 4 items (one per key block) x (dK, dV) 64 x 64 fp32
     need = lib.ssa_workspace_bytes(p, ssa.SSA_OP_SPARSE_BWD)
-    assert need == 2 * rows + 256 + parts           # + the 2 x 4 x 4 head-bit words, padded to 256 bytes
-    assert lib.ssa_workspace_bytes(p, ssa.SSA_OP_FULL_BWD) == 2 * rows + parts
+    # + head bits and pair counts, item starts, item key blocks: each under 256 bytes, padded to 256
+    assert need == 2 * rows + 3 * 256 + parts
+    assert lib.ssa_workspace_bytes(p, ssa.SSA_OP_FULL_BWD) == 2 * rows + 2 * 256 + parts
     args = (FAKE,) * 10
     assert lib.ssa_block_sparse_attn_bwd(p, *args, FAKE, need - 1, None) == ssa.SSA_ERR_WORKSPACE
     assert lib.ssa_block_sparse_attn_bwd(p, *args, ctypes.c_void_p(0x10080), need, None) == ssa.SSA_ERR_INVALID_ARG
