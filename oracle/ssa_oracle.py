@@ -29,6 +29,9 @@ What is computed (all arithmetic in float64 unless a step says it rounds):
   6. dropped attention mass: full-softmax probability on keys the
      sparse pattern leaves out                                      [SSA-summary] 1 "Planteamiento del Problema",
                                                                      "Alineacion Bidireccional" (delta(t))
+  3''. optional DashAttention stages: chunk summaries from a learned
+     query, alpha-entmax routing averaged over a KV group, and softmax
+     with a prior bias sigma * ln(w) over the routed blocks           [DashAttn] "Etapa 0", "Etapa 1", "Etapa 2"
   7. gradients of steps 4 and 5 with respect to Q, K, V for a given
      output gradient (chain rule through the masked softmax)       [SSA-summary] 1 "Planteamiento del Problema"
                                                                      (dropped keys get no gradient in the sparse
@@ -44,6 +47,11 @@ Readings where the pages leave a step open:
     blocks by coarse score; a query block stops after the first block whose
     gain is below tau times the accumulated mass for all of its rows (that
     block is kept);
+  * DashAttention routing is per query block (block-mean query scores, as
+    in step 2), over the blocks before the diagonal; the diagonal block is
+    always kept with bias 0; the prior is g proportional to w ** sigma, i.e.
+    a logit bias sigma * ln(w); the list is capped at ``topk`` blocks by
+    weight (diagonal kept);
   * the backward takes the output gradient as given (the alignment losses
     that would produce it have no stated functional form); only O carries
     gradient (not LSE or the dropped mass);
@@ -373,6 +381,186 @@ def full_attention_dropped_mass(q, k, v, sel, block: int, scale: Optional[float]
                 dropped = (~selected)[None, :] & ~future
                 delta[bi, h, r0 - lo:r1 - lo] = np.where(dropped, np.exp(logits - row_lse), 0.0).sum(axis=1)
     return out, lse, delta
+
+
+# --------------------------------------------------------------------------- DashAttention stages
+
+def learned_key_summaries(k, qbar, block: int, scale: Optional[float] = None) -> np.ndarray:
+    """Chunk summaries from a learned query: for KV head g and chunk j, the
+    softmax-weighted average of the chunk's key rows,
+        kbar[b,g,j] = sum_c softmax_c(scale * qbar[g] . k_c) k_c   (rows c < seq_kv of chunk j),
+    rounded to fp32.  qbar == 0 gives the plain block mean (step 1).
+    [DashAttn] "Etapa 0" (a learned query attends to the keys of each chunk by
+    local scaled dot-product attention; zero-initialised it is the uniform
+    average; a finished chunk's summary is cached).
+    qbar: [Hkv, d].  Returns float64 [b, Hkv, nkb, d]."""
+    k, qbar = _f64(k), _f64(qbar)
+    b, hkv, n, d = k.shape
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    nb = n_blocks(n, block)
+    out = np.empty((b, hkv, nb, d))
+    for bi in range(b):
+        for g in range(hkv):
+            for j in range(nb):
+                rows = k[bi, g, j * block: min((j + 1) * block, n)]
+                logits = scale * (rows @ qbar[g])
+                w = np.exp(logits - logits.max())
+                out[bi, g, j] = (w / w.sum()) @ rows
+    return round_f32(out)
+
+
+def entmax(z, alpha: float) -> np.ndarray:
+    """alpha-entmax of a score vector (1 < alpha <= 2):
+        p_j = max(0, (alpha - 1) z_j - tau) ** (1 / (alpha - 1)),
+    with the threshold tau fixed by sum_j p_j = 1 (-inf scores get 0).  The sum
+    decreases in tau, and tau lies in [max - 1, max - n**(1 - alpha)] for the
+    scaled scores, so it is found by bisection in float64; the result is then
+    normalised.  alpha = 2 is sparsemax; alpha -> 1 tends to softmax.
+    [DashAttn] "Etapa 1" (routing by alpha-entmax: a sparse probability vector
+    whose support size follows from the scores)."""
+    z = _f64(z)
+    if not 1.0 < alpha <= 2.0:
+        raise ValueError("alpha must be in (1, 2]")
+    out = np.zeros_like(z)
+    fin = np.isfinite(z)
+    if not fin.any():
+        return out
+    zt = (alpha - 1.0) * z[fin]
+    inv = 1.0 / (alpha - 1.0)
+    lo, hi = zt.max() - 1.0, zt.max() - len(zt) ** (1.0 - alpha)
+
+    def total(tau):
+        return (np.maximum(zt - tau, 0.0) ** inv).sum()
+
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if total(mid) >= 1.0:
+            lo = mid
+        else:
+            hi = mid
+    p = np.maximum(zt - lo, 0.0) ** inv
+    out[fin] = p / p.sum()
+    return out
+
+
+def entmax_routing(scores, n_kv_heads: int, alpha: float, gamma: float, block: int,
+                   q_offset: int = 0) -> np.ndarray:
+    """Routing weights of each (b, KV head g, query block i): for every query
+    head h of the group, w_h = alpha-entmax(gamma * scores[b,h,i,j]) over the
+    earlier blocks j < diag(i); the group's weights are the mean of its heads'.
+    The diagonal block is not routed (it has its own branch).
+    [DashAttn] "Etapa 1" (entmax routing of the chunk logits; with GQA the
+    probabilities of the heads sharing a KV head are averaged into one sparse
+    support) and "Etapa 2" (near-diagonal chunks kept apart).
+    Returns float64 [b, Hkv, nqb, nkb] (0 outside the support and from the
+    diagonal on)."""
+    s = _f64(scores)
+    b, hq, nqb, nkb = s.shape
+    group = hq // n_kv_heads
+    out = np.zeros((b, n_kv_heads, nqb, nkb))
+    for bi in range(b):
+        for g in range(n_kv_heads):
+            for i in range(nqb):
+                jd = diag_block(i, q_offset, block)
+                if jd == 0:
+                    continue
+                acc = np.zeros(jd)
+                for hh in range(group):
+                    acc = acc + entmax(gamma * s[bi, g * group + hh, i, :jd], alpha)
+                out[bi, g, i, :jd] = acc / group
+    return out
+
+
+def routing_support(weights, topk: int, block: int, q_offset: int = 0) -> np.ndarray:
+    """Block lists from routing weights: the diagonal block plus every earlier
+    block of positive weight; past ``topk`` blocks, the diagonal plus the
+    topk - 1 largest weights (lower index on ties).  Ascending, -1 padded.
+    [DashAttn] "Etapa 2" (attention restricted to the chunks the routing
+    selected plus the diagonal branch; the kernel walks the active chunks).
+    Returns int64 [b, Hkv, nqb, topk]."""
+    w = _f64(weights)
+    b, hkv, nqb, nkb = w.shape
+    out = np.full((b, hkv, nqb, topk), -1, dtype=np.int64)
+    for bi in range(b):
+        for g in range(hkv):
+            for i in range(nqb):
+                jd = diag_block(i, q_offset, block)
+                live = [j for j in range(jd) if w[bi, g, i, j] > 0]
+                live = sorted(live, key=lambda j: (-w[bi, g, i, j], j))[: topk - 1]
+                chosen = sorted(live + [jd])
+                out[bi, g, i, : len(chosen)] = chosen
+    return out
+
+
+def prior_bias(weights, sel, sigma: float, block: int, q_offset: int = 0) -> np.ndarray:
+    """Logit bias of each listed block: sigma * ln(w) for a routed block, 0 for
+    the diagonal block (and for padding).  Adding it to the logits is the
+    softmax taken relative to the prior g proportional to w ** sigma (zero where
+    w is zero): sigma = 0 is the plain softmax over the listed blocks.
+    [DashAttn] "Etapa 2" (softmax with the reference distribution replaced by a
+    prior built from the routing weights, zero where they are zero; sigma sets
+    how strongly the prior counts; the routing bias is added to the logits).
+    Returns float64, the shape of sel."""
+    w = _f64(weights)
+    sel = np.asarray(sel)
+    out = np.zeros(sel.shape)
+    b, hkv, nqb, topk = sel.shape
+    for bi in range(b):
+        for g in range(hkv):
+            for i in range(nqb):
+                jd = diag_block(i, q_offset, block)
+                for e in range(topk):
+                    j = int(sel[bi, g, i, e])
+                    if j >= 0 and j != jd:
+                        out[bi, g, i, e] = sigma * math.log(w[bi, g, i, j])
+    return out
+
+
+def prior_attention(q, k, v, sel, bias, block: int, scale: Optional[float] = None, q_offset: int = 0):
+    """Softmax attention over the keys of the listed blocks (causal), each
+    logit shifted by its block's bias:
+        logit_rc = scale * q_r . k_c + bias[b, g, i, e]   for c in block sel[b,g,i,e].
+    sel and bias are per KV group [b, Hkv, nqb, topk].  Returns (O, LSE), LSE
+    the natural log-sum-exp of the shifted logits.
+    [DashAttn] "Etapa 2" (prior-induced sparse softmax over the selected
+    chunks)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    sel, bias = np.asarray(sel), _f64(bias)
+    b, hq, seq_q, d = q.shape
+    hkv, seq_kv = k.shape[1], k.shape[2]
+    group = hq // hkv
+    _check_geometry(seq_q, seq_kv, q_offset, block)
+    if scale is None:
+        scale = default_scale(d)
+    scale = float(np.float32(scale))
+    out = np.empty((b, hq, seq_q, d))
+    lse = np.empty((b, hq, seq_q))
+    for bi in range(b):
+        for h in range(hq):
+            g = h // group
+            for i in range(n_blocks(seq_q, block)):
+                r0, r1 = i * block, min((i + 1) * block, seq_q)
+                last = q_offset + r1 - 1
+                cols, shift = [], []
+                for e, j in enumerate(sel[bi, g, i]):
+                    if j < 0:
+                        continue
+                    c = _allowed_keys([j], last, block, seq_kv)
+                    cols.append(c)
+                    shift.append(np.full(len(c), bias[bi, g, i, e]))
+                cols = np.concatenate(cols) if cols else np.zeros(0, dtype=np.int64)
+                shift = np.concatenate(shift) if shift else np.zeros(0)
+                logits = scale * (q[bi, h, r0:r1] @ k[bi, g, cols].T) + shift[None, :]
+                pos = q_offset + np.arange(r0, r1)
+                logits[cols[None, :] > pos[:, None]] = -np.inf
+                m = logits.max(axis=1, keepdims=True)
+                w = np.exp(logits - m)
+                z = w.sum(axis=1, keepdims=True)
+                out[bi, h, r0:r1] = (w @ v[bi, g, cols]) / z
+                lse[bi, h, r0:r1] = (m + np.log(z))[:, 0]
+    return out, lse
 
 
 # --------------------------------------------------------------------------- backward

@@ -576,6 +576,148 @@ def check_backward_identities(O):
     assert not np.allclose(dvd, dvf)
 
 
+# ----------------------------------------------------------------------------- DashAttention stages
+
+def check_entmax_hand_example(O):
+    # sparsemax of (0, 0.5, 1): support {0.5, 1}, tau = 0.25
+    np.testing.assert_allclose(O.entmax(np.array([0.0, 0.5, 1.0]), 2.0), [0.0, 0.25, 0.75], atol=1e-14)
+    # 1.5-entmax of (0, 1): halved scores (0, 0.5), both in the support, tau the smaller root of
+    # (0.5 - tau)^2 + tau^2 = 1, i.e. tau = (1 - sqrt 7) / 4
+    r7 = math.sqrt(7.0)
+    np.testing.assert_allclose(O.entmax(np.array([0.0, 1.0]), 1.5), [(4 - r7) / 8, (4 + r7) / 8], atol=1e-14)
+    # -inf scores take no mass; a single finite score takes all of it
+    np.testing.assert_allclose(O.entmax(np.array([-np.inf, 3.0, -np.inf]), 1.5), [0.0, 1.0, 0.0], atol=0)
+
+
+def _sparsemax_sorted(z):
+    zs = np.sort(z)[::-1]
+    css = np.cumsum(zs)
+    k = np.arange(1, len(z) + 1)
+    kmax = k[1 + k * zs > css].max()
+    tau = (css[kmax - 1] - 1) / kmax
+    return np.maximum(z - tau, 0)
+
+
+def _entmax15_sorted(z):
+    # exact 1.5-entmax: with the support of size k (largest scaled scores), tau solves
+    # sum (zt - tau)^2 = 1, tau = mean - sqrt((1 - ss) / k); the support is the largest
+    # k whose smallest member stays above its tau
+    zt = np.sort(z / 2)[::-1]
+    best = None
+    for k in range(1, len(z) + 1):
+        top = zt[:k]
+        mean = top.mean()
+        ss = ((top - mean) ** 2).sum()
+        if ss > 1:
+            break
+        tau = mean - math.sqrt((1 - ss) / k)
+        if top[-1] > tau:
+            best = tau
+    return np.maximum(z / 2 - best, 0) ** 2
+
+
+def check_entmax_closed_forms(O):
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 5, 17, 64):
+        for scale in (0.1, 1.0, 4.0):
+            z = rng.standard_normal(n) * scale
+            np.testing.assert_allclose(O.entmax(z, 2.0), _sparsemax_sorted(z), atol=1e-12)
+            np.testing.assert_allclose(O.entmax(z, 1.5), _entmax15_sorted(z), atol=1e-12)
+            for alpha in (1.2, 1.5, 1.8, 2.0):
+                p = O.entmax(z, alpha)
+                assert abs(p.sum() - 1) < 1e-12 and np.all(p >= 0)
+                np.testing.assert_allclose(O.entmax(z + 3.25, alpha), p, atol=1e-12)   # shift invariance
+                # optimality: p^(alpha-1) = (alpha-1) z - tau on the support, (alpha-1) z <= tau off it
+                sup = p > 0
+                taus = (alpha - 1) * z[sup] - p[sup] ** (alpha - 1)
+                assert np.ptp(taus) < 1e-9
+                assert np.all((alpha - 1) * z[~sup] <= taus[0] + 1e-12)
+
+
+def check_learned_summaries(O):
+    b, hkv, n, d, B = 2, 2, 200, 8, 64          # ragged last chunk (8 rows)
+    kk = bf16_values((b, hkv, n, d))
+    qbar = bf16_values((hkv, d), scale=2.0)
+    # zero query: the plain block mean
+    np.testing.assert_array_equal(O.learned_key_summaries(kk, np.zeros((hkv, d)), B), O.key_summaries(kk, B))
+    # library: one-row SDPA of qbar over each chunk's keys (keys as values)
+    got = O.learned_key_summaries(kk, qbar, B, scale=0.5)
+    for j in range(-(-n // B)):
+        rows = tr.t64(kk[:, :, j * B: (j + 1) * B])
+        qq = tr.t64(np.broadcast_to(qbar[None, :, None, :], (b, hkv, 1, d)).copy())
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, rows, rows, scale=0.5)[:, :, 0].numpy()
+        np.testing.assert_allclose(got[:, :, j], ref, rtol=1e-6, atol=1e-7)   # got is fp32-rounded
+
+
+def check_entmax_routing(O):
+    rng = np.random.default_rng(6)
+    b, hq, hkv, nqb, B = 1, 4, 2, 6, 16
+    s = rng.standard_normal((b, hq, nqb, nqb))
+    for i in range(nqb):
+        s[:, :, i, i + 1:] = -np.inf
+    for alpha, gamma in ((1.5, 2.0), (2.0, 0.7)):
+        w = O.entmax_routing(s, hkv, alpha, gamma, B)
+        for g in range(hkv):
+            for i in range(nqb):
+                assert np.all(w[0, g, i, i:] == 0)                 # nothing routed from the diagonal on
+                if i == 0:
+                    continue
+                ref = sum(O.entmax(gamma * s[0, g * 2 + hh, i, :i], alpha) for hh in range(2)) / 2
+                np.testing.assert_allclose(w[0, g, i, :i], ref, atol=1e-15)
+                assert abs(w[0, g, i].sum() - 1) < 1e-12
+    # one head per KV head: the per-head entmax itself
+    w1 = O.entmax_routing(s, hq, 1.5, 1.0, B)
+    np.testing.assert_allclose(w1[0, 3, 5, :5], O.entmax(s[0, 3, 5, :5], 1.5), atol=1e-15)
+
+
+def check_routing_support_and_bias(O):
+    w = np.zeros((1, 1, 2, 5))
+    w[0, 0, 1] = [0.5, 0.0, 0.3, 0.2, 0.0]                        # query block 1 of a 4-block offset
+    sel = O.routing_support(w, 3, 16, q_offset=64)                  # diag(1) = 5 // ... = (64 + 16) // 16 = 5
+    assert list(sel[0, 0, 1]) == [0, 2, 5]
+    assert list(O.routing_support(w, 8, 16, q_offset=64)[0, 0, 1]) == [0, 2, 3, 5, -1, -1, -1, -1]
+    assert list(sel[0, 0, 0]) == [4, -1, -1]                        # no weight: the diagonal only
+    bias = O.prior_bias(w, sel, 0.5, 16, q_offset=64)
+    np.testing.assert_allclose(bias[0, 0, 1], [0.5 * math.log(0.5), 0.5 * math.log(0.3), 0.0], atol=1e-15)
+    assert np.all(bias[0, 0, 0] == 0)
+
+
+def check_prior_attention(O):
+    b, hq, hkv, n, d, B, k = 1, 4, 2, 192, 8, 32, 3
+    q, kk, v = rand_qkv(b, hq, hkv, n, d)
+    rng = np.random.default_rng(7)
+    s = O.block_scores(q, kk, B)
+    w = O.entmax_routing(s, hkv, 1.5, 4.0, B)
+    sel = O.routing_support(w, k, B)
+    sc = float(np.float32(1 / math.sqrt(d)))
+    # sigma = 0: the plain block-sparse softmax over the listed blocks
+    o0, l0 = O.prior_attention(q, kk, v, sel, O.prior_bias(w, sel, 0.0, B), B)
+    o_ref, l_ref = O.sparse_attention(q, kk, v, O.expand_shared(sel, hq), B)
+    np.testing.assert_allclose(o0, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l0, l_ref, rtol=1e-12, atol=1e-13)
+    # library: SDPA with an additive float mask (bias on listed causal keys, -inf elsewhere)
+    bias = O.prior_bias(w, sel, 0.7, B)
+    o1, l1 = O.prior_attention(q, kk, v, sel, bias, B)
+    mask = np.full((b, hq, n, n), -np.inf)
+    for h in range(hq):
+        for i in range(n // B):
+            for e, j in enumerate(sel[0, h // 2, i]):
+                if j >= 0:
+                    mask[0, h, i * B:(i + 1) * B, j * B:(j + 1) * B] = bias[0, h // 2, i, e]
+    mask = np.where(np.tril(np.ones((n, n), dtype=bool))[None, None], mask, -np.inf)
+    tm = torch.tensor(mask)
+    ref = torch.nn.functional.scaled_dot_product_attention(tr.t64(q), tr.t64(kk), tr.t64(v), attn_mask=tm, scale=sc,
+                                                           enable_gqa=True).numpy()
+    np.testing.assert_allclose(o1, ref, rtol=1e-11, atol=1e-12)
+    logits = torch.matmul(tr.t64(q), tr.t64(np.repeat(kk, 2, axis=1)).transpose(-1, -2)) * sc + tm
+    np.testing.assert_allclose(l1, torch.logsumexp(logits, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+    # one constant added to every bias of a query block (diagonal included) leaves O and shifts LSE
+    o2, l2 = O.prior_attention(q, kk, v, sel, bias + 1.5 * (sel >= 0), B)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1 + 1.5, rtol=1e-12, atol=1e-12)
+    del rng
+
+
 ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_causal,
               check_select_brute_force, check_select_ties_and_decode, check_sparse_vs_sdpa,
               check_sparse_special_cases, check_sparse_brute_force_loops,
@@ -583,7 +725,9 @@ ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_
               check_shared_hand_example, check_shared_scores_pool_queries, check_shared_reductions,
               check_shared_brute_force, check_early_stop_hand_example, check_early_stop_limits,
               check_early_stop_loops, check_backward_finite_differences, check_backward_autograd,
-              check_backward_identities]
+              check_backward_identities, check_entmax_hand_example, check_entmax_closed_forms,
+              check_learned_summaries, check_entmax_routing, check_routing_support_and_bias,
+              check_prior_attention]
 
 
 # ----------------------------------------------------------------------------- the pins
@@ -640,6 +784,10 @@ MUTANTS = {
     "bwd_no_softmax_correction": ("_block_backward", None),
     "bwd_dk_unscaled": ("_block_backward", None),
     "bwd_dv_unnormalised": ("_block_backward", None),
+    "entmax_linear_for_any_alpha": ("entmax", None),
+    "routing_includes_diagonal": ("entmax_routing", None),
+    "prior_bias_ignores_sigma": ("prior_bias", None),
+    "summaries_ignore_learned_query": ("learned_key_summaries", None),
 }
 
 
@@ -708,6 +856,37 @@ def _mutant_bwd(kind):
     return f
 
 
+_orig_entmax = ssa_oracle.entmax
+_orig_routing = ssa_oracle.entmax_routing
+_orig_prior_bias = ssa_oracle.prior_bias
+
+
+def _mutant_entmax_linear(z, alpha):
+    return _orig_entmax(z, 2.0)
+
+
+def _mutant_routing_diag(scores, n_kv_heads, alpha, gamma, block, q_offset=0):
+    s = np.asarray(scores, dtype=np.float64)
+    b, hq, nqb, nkb = s.shape
+    group = hq // n_kv_heads
+    out = np.zeros((b, n_kv_heads, nqb, nkb))
+    for bi in range(b):
+        for g in range(n_kv_heads):
+            for i in range(nqb):
+                jd = ssa_oracle.diag_block(i, q_offset, block)
+                acc = sum(_orig_entmax(gamma * s[bi, g * group + hh, i, :jd + 1], alpha) for hh in range(group))
+                out[bi, g, i, :jd + 1] = acc / group
+    return out
+
+
+def _mutant_bias_no_sigma(weights, sel, sigma, block, q_offset=0):
+    return _orig_prior_bias(weights, sel, 1.0, block, q_offset)
+
+
+def _mutant_summaries_mean(k, qbar, block, scale=None):
+    return ssa_oracle.key_summaries(k, block)
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch, golden_dir):
     attr, fn = MUTANTS[name]
@@ -721,6 +900,9 @@ def test_mutant_is_caught(name, monkeypatch, golden_dir):
         fn = _mutant_block_means
     if name == "drops_last_selected_block":
         fn = _mutant_allowed
+    fn = {"entmax_linear_for_any_alpha": _mutant_entmax_linear, "routing_includes_diagonal": _mutant_routing_diag,
+          "prior_bias_ignores_sigma": _mutant_bias_no_sigma,
+          "summaries_ignore_learned_query": _mutant_summaries_mean}.get(name, fn)
     if name.startswith("bwd_"):
         fn = _mutant_bwd({"bwd_no_softmax_correction": "no_correction", "bwd_dk_unscaled": "unscaled",
                           "bwd_dv_unnormalised": "unnormalised"}[name])
