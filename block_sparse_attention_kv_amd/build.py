@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssa.so")
-SOURCES = ["ssa_api.cpp", "ssa_scores.hip", "ssa_topk.hip", "ssa_attn.hip", "ssa_decode.hip", "ssa_bwd.hip"]
+SOURCES = ["ssa_api.cpp", "ssa_scores.hip", "ssa_topk.hip", "ssa_attn.hip", "ssa_decode.hip", "ssa_bwd.hip", "ssa_route.hip"]
 ARCH = os.environ.get("SSA_OFFLOAD_ARCH", "gfx950")
 
 CXXFLAGS = [

@@ -102,6 +102,43 @@ ssa_status_t ssa_block_summaries(const ssa_shape_t* shape, const void* k, float*
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
 
+ssa_status_t ssa_block_summaries_learned(const ssa_shape_t* shape, const void* k, const float* qbar,
+                                         float* k_summary, hipStream_t stream) {
+  const char* fn = "ssa_block_summaries_learned";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (g.batch == 0 || g.seq_kv == 0) return SSA_OK;
+  CHECK_PTR(k, 16, fn);
+  CHECK_PTR(qbar, 4, fn);
+  CHECK_PTR(k_summary, 16, fn);
+  hipError_t e = ssa::launch_learned_summaries((const uint16_t*)k, qbar, k_summary, g, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
+ssa_status_t ssa_entmax_route(const ssa_shape_t* shape, const float* scores, float alpha, float gamma, float sigma,
+                              int32_t* block_idx, float* block_bias, float* weights, hipStream_t stream) {
+  const char* fn = "ssa_entmax_route";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (!(alpha > 1.f && alpha <= 2.f))
+    return fail(alpha == alpha ? SSA_ERR_UNSUPPORTED : SSA_ERR_INVALID_ARG, "%s: alpha must be in (1, 2] (got %g)", fn,
+                (double)alpha);
+  if (!(gamma >= 0.f) || !isfinite(gamma) || !(sigma >= 0.f) || !isfinite(sigma))
+    return fail(SSA_ERR_INVALID_ARG, "%s: gamma and sigma must be finite and >= 0", fn);
+  if (g.nkb > 2048) return fail(SSA_ERR_UNSUPPORTED, "%s: more than 2048 key blocks", fn);
+  if (empty) return SSA_OK;
+  CHECK_PTR(scores, 4, fn);
+  CHECK_PTR(block_idx, 4, fn);
+  CHECK_PTR(block_bias, 4, fn);
+  if (weights) CHECK_PTR(weights, 4, fn);
+  hipError_t e = ssa::launch_entmax_route(scores, alpha, gamma, sigma, block_idx, block_bias, weights, g, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
 ssa_status_t ssa_block_scores(const ssa_shape_t* shape, const void* q, const void* k, float* k_summary,
                               int summary_is_input, float* scores, hipStream_t stream) {
   const char* fn = "ssa_block_scores";
@@ -146,12 +183,16 @@ ssa_status_t select_topk_impl(const ssa_shape_t* shape, const float* scores, int
 
 ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
                              const int32_t* block_idx, bool shared, void* out, float* lse, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream, const char* fn) {
+                             size_t workspace_bytes, hipStream_t stream, const char* fn,
+                             const float* block_bias = nullptr, bool biased = false) {
   ssa::Geometry g;
   bool empty;
   ssa_status_t st = make_geometry(shape, &g, &empty, fn);
   if (st != SSA_OK) return st;
+  if (biased && g.seq_q == 1)
+    return fail(SSA_ERR_UNSUPPORTED, "%s: decode (seq_q == 1) with a block bias is not implemented", fn);
   if (empty) return SSA_OK;
+  if (biased) CHECK_PTR(block_bias, 4, fn);
   CHECK_PTR(q, 16, fn);
   CHECK_PTR(k, 16, fn);
   CHECK_PTR(v, 16, fn);
@@ -164,6 +205,7 @@ ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void
   a.v = (const uint16_t*)v;
   a.idx = block_idx;
   a.idx_shared = shared ? 1 : 0;
+  a.bias = biased ? block_bias : nullptr;
   a.out = (uint16_t*)out;
   a.lse = lse;
   a.qb_begin = 0;
@@ -339,6 +381,14 @@ ssa_status_t ssa_block_sparse_attn_fwd_shared(const ssa_shape_t* shape, const vo
                                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return sparse_fwd_impl(shape, q, k, v, block_idx, true, out, lse, workspace, workspace_bytes, stream,
                          "ssa_block_sparse_attn_fwd_shared");
+}
+
+ssa_status_t ssa_block_sparse_attn_fwd_biased(const ssa_shape_t* shape, const void* q, const void* k,
+                                              const void* v, const int32_t* block_idx, const float* block_bias,
+                                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  return sparse_fwd_impl(shape, q, k, v, block_idx, true, out, lse, workspace, workspace_bytes, stream,
+                         "ssa_block_sparse_attn_fwd_biased", block_bias, true);
 }
 
 ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void* q, const void* k,

@@ -32,6 +32,8 @@
 namespace ssa {
 namespace {
 
+constexpr float kLog2eF = 1.4426950408889634f;
+
 struct UnitState {
   f32x16 o[2][2];  // O^T accumulators [d block][query block]
   float m[2];      // reference max (log2 units) per owned query column
@@ -93,10 +95,11 @@ __device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[
 // Online-softmax update for one tile; leaves packed bf16 probabilities in pk.
 // tile_rs (optional) receives this lane's fp32 sum of the tile's
 // probabilities per query block (relative to the updated reference max).
-template <bool FULL>
+// With BIAS, b2 (log2 units) is added to every logit of the tile.
+template <bool FULL, bool BIAS = false>
 __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x4 pk[2][2][2], bool diag,
                                              bool selected, int key0, int pos0, int l32, int hl, float c,
-                                             float* tile_rs = nullptr) {
+                                             float* tile_rs = nullptr, float b2 = 0.f) {
   if (diag) {
     // Causal mask of the tile holding the query rows' own positions: key > pos
     // becomes -inf.  Branch-free sign arithmetic (no compare masks to keep live).
@@ -123,7 +126,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[1][qb][r]), s[1][qb][r + 1]);
     mx = max_xor32(mx);
-    mt[qb] = mx * c;
+    mt[qb] = BIAS ? fmaf(mx, c, b2) : mx * c;
     grow |= !(mt[qb] <= st.m[qb] + kRescaleSlack);
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
@@ -142,7 +145,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float nm = -st.m[qb];
+    const float nm = BIAS ? b2 - st.m[qb] : -st.m[qb];
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -240,10 +243,11 @@ __device__ __forceinline__ void map_unit(int w, int n_groups, int per_group, int
 // buffer it reads.  The caller has requested K_0 and V_0.  Pipeline per tile t
 // (K_t, V_t already requested):
 //   wait K_t | S_t | request K_{t+1} | softmax_t | wait V_t | PV_t | request V_{t+1}
+template <bool BIAS>
 __device__ __attribute__((always_inline)) inline void sparse_tiles(
-    uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, const int* __restrict__ sList, int nt,
-    const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int seq_kv, int jd, int pos0,
-    float c, const bf16x8 qop[2][4], UnitState& st, int lane, int l32, int hl) {
+    uint8_t* __restrict__ sK, uint8_t* __restrict__ sV, const int* __restrict__ sList,
+    const float* __restrict__ sBias, int nt, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
+    int seq_kv, int jd, int pos0, float c, const bf16x8 qop[2][4], UnitState& st, int lane, int l32, int hl) {
   TileOffsets<1, 0> toff;
   toff.init(lane, 0);
   for (int t = 0; t < nt; ++t) {
@@ -256,7 +260,8 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     wait_lds_reads();
     if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sK, lane, toff);
     u32x4 pk[2][2][2];
-    tile_softmax<false>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c);
+    const float b2 = BIAS ? sBias[t] * kLog2eF : 0.f;
+    tile_softmax<false, BIAS>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c, nullptr, b2);
     if (more)
       wait_vmem<8>();  // V_t landed (K_{t+1} may still be in flight)
     else
@@ -268,10 +273,13 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
 }
 
 // Block-sparse forward: one wavefront per unit, private K and V buffers.
+// BIAS: each listed block's logits are shifted by its entry of a.bias.
+template <bool BIAS>
 __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry geo) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[kTileBytes];
   __shared__ int sList[kMaxTopk];
+  __shared__ float sBias[BIAS ? kMaxTopk : 1];
   const int lane = threadIdx.x, hl = lane >> 5, l32 = lane & 31;
   const int G = geo.group;
   int gi, u;
@@ -288,9 +296,12 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   const int irow = a.idx_shared ? gi : bh;
   int iv[4];
   load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
+  float bv[4];
+  if (BIAS) load_value_row(a.bias + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, bv);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
-  const int nt = compact_index_row(iv, geo.topk, jd, sList, lane);
+  const int nt = BIAS ? compact_index_row(iv, bv, geo.topk, jd, sList, sBias, lane)
+                      : compact_index_row(iv, geo.topk, jd, sList, lane);
   if (nt > 0) {  // first tile requested before waiting for Q, so the two latencies overlap
     TileOffsets<1, 0> toff;
     toff.init(lane, 0);
@@ -302,8 +313,8 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   init_state(st);
   wait_vmem<0>();  // Q, and the first tile; from here only tile loads use vmcnt
   __builtin_amdgcn_wave_barrier();
-  sparse_tiles(sK, sV, sList, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd, geo.q_offset + i * kBlock,
-               geo.scale_log2, qop, st, lane, l32, hl);
+  sparse_tiles<BIAS>(sK, sV, sList, sBias, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd,
+                     geo.q_offset + i * kBlock, geo.scale_log2, qop, st, lane, l32, hl);
   unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
 }
 
@@ -431,11 +442,14 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
 //   FULL:  every causal tile of the query block (the full counterpart), with
 //          dropped mass from the tiles missing from each head's own list;
 //   !FULL: the tiles of a group-shared selection (block-sparse forward).
-template <int NW, bool FULL>
+// BIAS (with !FULL): each listed block's logits are shifted by its entry of
+// a.bias.
+template <int NW, bool FULL, bool BIAS = false>
 __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geometry geo) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kTileBytes];
   __shared__ int sList[NW][kMaxTopk];
+  __shared__ float sBias[BIAS ? NW : 1][BIAS ? kMaxTopk : 1];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = geo.group, GS = G / NW;
@@ -455,9 +469,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
   const int irow = a.idx_shared ? gi : bh;
   int iv[4];
   load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
+  float bv[4];
+  if (BIAS) load_value_row(a.bias + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, bv);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
-  const int nsel = compact_index_row(iv, geo.topk, jd, sList[wave], lane);
+  const int nsel = BIAS ? compact_index_row(iv, bv, geo.topk, jd, sList[wave], sBias[BIAS ? wave : 0], lane)
+                        : compact_index_row(iv, geo.topk, jd, sList[wave], lane);
   // tiles walked: 0..jd (full), or the shared list (identical in every wave)
   const int nt = FULL ? jd + 1 : nsel;
   auto tile_block = [&](int t) { return FULL ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
@@ -498,7 +515,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
     f32x16 s[2][2];
     tile_scores(sK[t & 1], qop, l32, hl, s);
     u32x4 pk[2][2][2];
-    tile_softmax<FULL>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c);
+    const float b2 = BIAS ? sBias[BIAS ? wave : 0][BIAS ? t : 0] * kLog2eF : 0.f;
+    tile_softmax<FULL, BIAS>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c, nullptr, b2);
     tile_pv(sV[t & 1], pk, st, lane);
   }
   unit_epilogue<FULL>(st, a, geo, bh, i, l32, hl);
@@ -518,12 +536,20 @@ hipError_t launch_attn_early_stop(const AttnArgs& a, const float* scores, float 
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream) {
   const size_t units = (size_t)g.batch * g.hq * a.qb_count;
   if (units == 0) return hipSuccess;
+  const bool bias = !full && a.bias != nullptr;
   if (!full && !(a.idx_shared && g.group % 4 == 0)) {
     // per-head lists (or groups too small to share): one wavefront per unit
-    hipLaunchKernelGGL(attn_sparse_kernel, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+    if (bias)
+      hipLaunchKernelGGL(attn_sparse_kernel<true>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+    else
+      hipLaunchKernelGGL(attn_sparse_kernel<false>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
   } else if (!full) {
     // group-shared lists: four heads of a group share every tile
-    hipLaunchKernelGGL((attn_group_kernel<4, false>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
+    if (bias)
+      hipLaunchKernelGGL((attn_group_kernel<4, false, true>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a,
+                         g);
+    else
+      hipLaunchKernelGGL((attn_group_kernel<4, false>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
   } else if (g.group % 4 == 0) {
     hipLaunchKernelGGL((attn_group_kernel<4, true>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
   } else if (g.group % 2 == 0) {

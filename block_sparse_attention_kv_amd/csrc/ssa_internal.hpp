@@ -26,6 +26,7 @@ struct AttnArgs {
   const uint16_t* v;
   const int32_t* idx;
   int idx_shared;    // 1: one index row per (b, KV head, query block), else per query head
+  const float* bias; // optional logit bias per index entry (same layout as idx; natural-log units)
   uint16_t* out;
   float* lse;
   float* dropped;    // full mode only
@@ -109,6 +110,10 @@ void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan*
 
 hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geometry& g,
                                   hipStream_t stream);
+hipError_t launch_learned_summaries(const uint16_t* k, const float* qbar, float* k_summary, const Geometry& g,
+                                   hipStream_t stream);
+hipError_t launch_entmax_route(const float* scores, float alpha, float gamma, float sigma, int32_t* idx,
+                               float* bias, float* weights, const Geometry& g, hipStream_t stream);
 hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, float* scores,
                                  const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float* scores,

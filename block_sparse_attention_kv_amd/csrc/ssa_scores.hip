@@ -67,6 +67,56 @@ __global__ __launch_bounds__(64) void block_summaries_kernel(const uint16_t* __r
   }
 }
 
+// Chunk summaries from a learned query (one fp32 vector per KV head): the
+// softmax(scale * qbar . k_c)-weighted average of the block's key rows, in
+// fp64, rounded once to fp32.  One wavefront per (b, g, j): lane r scores row
+// r, then lane d sums column d over the rows.  qbar = 0 reproduces the mean.
+// DashAttention summary, "Etapa 0" (a learned query attends to each chunk's
+// keys by local scaled dot-product attention).
+__global__ __launch_bounds__(64) void learned_summaries_kernel(const uint16_t* __restrict__ k,
+                                                               const float* __restrict__ qbar,
+                                                               float* __restrict__ ksum, Geometry geo) {
+  const int lane = threadIdx.x;
+  const size_t bgj = blockIdx.x;
+  const size_t bg = bgj / (size_t)geo.nkb;
+  const int j = (int)(bgj - bg * (size_t)geo.nkb);
+  const int g = (int)(bg % (size_t)geo.hkv);
+  const int r0 = j * kBlock;
+  const int nrows = min(kBlock, geo.seq_kv - r0);
+  const uint16_t* base = k + (bg * (size_t)geo.seq_kv + r0) * kHeadDim;
+  const float* qv = qbar + (size_t)g * kHeadDim;
+  // row logits (lane = row)
+  double logit = -__builtin_inf();
+  if (lane < nrows) {
+    double acc = 0.0;
+    const u32x4* rp = reinterpret_cast<const u32x4*>(base + (size_t)lane * kHeadDim);
+#pragma unroll
+    for (int c = 0; c < kHeadDim / 8; ++c) {
+      const u32x4 v = rp[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += (double)qv[8 * c + 2 * e] * (double)bf16_to_f32((uint16_t)(v[e] & 0xffffu));
+        acc += (double)qv[8 * c + 2 * e + 1] * (double)bf16_to_f32((uint16_t)(v[e] >> 16));
+      }
+    }
+    logit = (double)geo.scale * acc;
+  }
+  double mx = logit;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+  const double w = lane < nrows ? exp(logit - mx) : 0.0;
+  double wsum = w;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
+  // weighted column sums (lane = column)
+  double col = 0.0;
+  for (int r = 0; r < nrows; ++r) {
+    const double wr = __shfl(w, r, 64);
+    col += wr * (double)bf16_to_f32(base[(size_t)r * kHeadDim + lane]);
+  }
+  ksum[bgj * kHeadDim + lane] = (float)(col / wsum);
+}
+
 constexpr int kScoreQb = 4;     // query blocks per workgroup (prefill): one per wavefront
 constexpr int kScoreKTile = 64;  // key blocks staged per pass (decode)
 constexpr int kKbStride = 65;    // padded LDS row (floats) -> conflict-free row-per-lane reads
@@ -195,6 +245,14 @@ hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geo
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL(block_summaries_kernel, dim3((unsigned)nblk), dim3(64), 0, stream, k,
                      k_summary, g.seq_kv, g.nkb);
+  return hipGetLastError();
+}
+
+hipError_t launch_learned_summaries(const uint16_t* k, const float* qbar, float* k_summary, const Geometry& g,
+                                   hipStream_t stream) {
+  const size_t nblk = (size_t)g.batch * g.hkv * g.nkb;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(learned_summaries_kernel, dim3((unsigned)nblk), dim3(64), 0, stream, k, qbar, k_summary, g);
   return hipGetLastError();
 }
 

@@ -77,6 +77,15 @@ __device__ __forceinline__ void load_index_row(const int32_t* __restrict__ irow,
   }
 }
 
+// A per-entry fp32 row laid out like load_index_row's (0 past topk).
+__device__ __forceinline__ void load_value_row(const float* __restrict__ vrow, int topk, int lane, float v[4]) {
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    v[c] = e < topk ? vrow[e] : 0.f;
+  }
+}
+
 // Compact an index row (as loaded by load_index_row) into LDS: the entries
 // before the first -1 that name a causal block (j <= jd), in list order.
 // Returns their count.  Whole-wave operation; `lst` has room for kMaxTopk
@@ -97,6 +106,34 @@ __device__ __forceinline__ int compact_index_row(const int iv[4], int topk, int 
     const bool keep = e < first_neg && j >= 0 && j <= jd;
     const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
     if (keep) lst[n + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = j;
+    n += (int)__builtin_popcountll(m);
+  }
+  return n;
+}
+
+// compact_index_row that also carries a per-entry value (bv, loaded like iv)
+// into vlst at the same positions.
+__device__ __forceinline__ int compact_index_row(const int iv[4], const float bv[4], int topk, int jd, int* lst,
+                                                 float* vlst, int lane) {
+  int first_neg = topk;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < topk && iv[c] < 0);
+    if (neg != 0ull && first_neg == topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
+  }
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    const int j = iv[c];
+    const bool keep = e < first_neg && j >= 0 && j <= jd;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+    if (keep) {
+      const int pos = n + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+      lst[pos] = j;
+      vlst[pos] = bv[c];
+    }
     n += (int)__builtin_popcountll(m);
   }
   return n;

@@ -20,6 +20,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -45,9 +46,18 @@ def source_hash(kernel: str) -> str:
 
 def classify(name: str):
     if "attn_group_kernel" in name:
-        # attn_group_kernel<NW, FULL>: demangled "..., true>" / mangled "...Lb1E..."
-        full = ("true>" in name) or ("Lb1E" in name)
-        return "full_attn" if full else "sparse_attn_shared"
+        # attn_group_kernel<NW, FULL, BIAS>: demangled "<4, true, false>", mangled "ILi4ELb1ELb0E"
+        m = re.search(r"attn_group_kernel<\s*\d+,\s*(true|false)(?:,\s*(true|false))?", name)
+        if m:
+            full, bias = m.group(1) == "true", m.group(2) == "true"
+        else:
+            m = re.search(r"attn_group_kernelILi\d+ELb([01])E(?:Lb([01])E)?", name)
+            full, bias = (m.group(1) == "1", m.group(2) == "1") if m else (False, False)
+        if full:
+            return "full_attn"
+        return "sparse_attn_biased" if bias else "sparse_attn_shared"
+    if "attn_sparse_kernel" in name and ("<true>" in name or "ILb1E" in name):
+        return "sparse_attn_biased"
     if "attn_bwd_dkv_kernel" in name:
         return "bwd_dkv"
     if "attn_bwd_dq_kernel" in name:
@@ -74,6 +84,10 @@ def classify(name: str):
         return "decode_scores"
     if "block_summaries_kernel" in name:
         return "block_summaries"
+    if "learned_summaries_kernel" in name:
+        return "learned_summaries"
+    if "entmax_route_kernel" in name:
+        return "entmax_route"
     if "select_topk_shared_kernel" in name:
         return "select_topk_shared"
     if "select_topk_kernel" in name:

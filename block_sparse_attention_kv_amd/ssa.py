@@ -24,7 +24,8 @@ EXPORTED_SYMBOLS = (
     "ssa_block_summaries", "ssa_block_scores", "ssa_select_topk", "ssa_block_sparse_attn_fwd",
     "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared", "ssa_block_sparse_attn_fwd_shared",
     "ssa_full_attn_fwd_dropped_mass_shared", "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
-    "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_workspace_bytes",
+    "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_block_summaries_learned", "ssa_entmax_route",
+    "ssa_block_sparse_attn_fwd_biased", "ssa_workspace_bytes",
     "ssa_status_string",
     "ssa_last_error", "ssa_version",
 )
@@ -77,11 +78,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssa_block_sparse_attn_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssa_block_sparse_attn_bwd_shared.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssa_full_attn_bwd.argtypes = [sp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    f32 = ctypes.c_float
+    lib.ssa_block_summaries_learned.argtypes = [sp, vp, vp, vp, vp]
+    lib.ssa_entmax_route.argtypes = [sp, vp, f32, f32, f32, vp, vp, vp, vp]
+    lib.ssa_block_sparse_attn_fwd_biased.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("ssa_block_summaries", "ssa_block_scores", "ssa_select_topk",
                "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared",
                "ssa_block_sparse_attn_fwd_shared", "ssa_full_attn_fwd_dropped_mass_shared",
                "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
-               "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd"):
+               "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_block_summaries_learned",
+               "ssa_entmax_route", "ssa_block_sparse_attn_fwd_biased"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ssa_workspace_bytes.argtypes = [sp, ctypes.c_int]
     lib.ssa_workspace_bytes.restype = ctypes.c_size_t
@@ -145,6 +151,55 @@ def ssa_block_summaries(k: torch.Tensor, *, block: int = 64) -> torch.Tensor:
     _check("ssa_block_summaries", load_library().ssa_block_summaries(
         ctypes.byref(shape), _ptr(k), _ptr(ks), _stream(k.device)))
     return ks
+
+
+def ssa_block_summaries_learned(k: torch.Tensor, qbar: torch.Tensor, *, block: int = 64, scale: float = 0.0,
+                                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunk summaries fp32 [b, Hkv, nkb, d] from a learned query qbar fp32
+    [Hkv, d] (softmax-weighted key average per block; scale 0 = 1/sqrt(d))."""
+    _require_gpu(k, qbar, out)
+    b, hkv, n, d = k.shape
+    shape = Shape(batch=b, n_q_heads=hkv, n_kv_heads=hkv, seq_q=n, seq_kv=n, q_offset=0,
+                  head_dim=d, block=block, topk=1, causal=1, scale=float(scale))
+    if out is None:
+        out = torch.empty((b, hkv, n_blocks(n, block), d), dtype=torch.float32, device=k.device)
+    _check("ssa_block_summaries_learned", load_library().ssa_block_summaries_learned(
+        ctypes.byref(shape), _ptr(k), _ptr(qbar), _ptr(out), _stream(k.device)))
+    return out
+
+
+def ssa_entmax_route(shape: Shape, scores: torch.Tensor, alpha: float, gamma: float, sigma: float,
+                     idx=None, bias=None, weights=None, with_weights: bool = True):
+    """(block_idx int32 [b, Hkv, nqb, topk], block_bias fp32 [b, Hkv, nqb, topk],
+    weights fp32 [b, Hkv, nqb, nkb] or None): alpha-entmax routing averaged over
+    each KV group."""
+    _require_gpu(scores, idx, bias, weights)
+    b, hkv = shape.batch, shape.n_kv_heads
+    nqb, nkb = n_blocks(shape.seq_q, shape.block), n_blocks(shape.seq_kv, shape.block)
+    if idx is None:
+        idx = torch.empty((b, hkv, nqb, shape.topk), dtype=torch.int32, device=scores.device)
+    if bias is None:
+        bias = torch.empty((b, hkv, nqb, shape.topk), dtype=torch.float32, device=scores.device)
+    if weights is None and with_weights:
+        weights = torch.empty((b, hkv, nqb, nkb), dtype=torch.float32, device=scores.device)
+    _check("ssa_entmax_route", load_library().ssa_entmax_route(
+        ctypes.byref(shape), _ptr(scores), float(alpha), float(gamma), float(sigma), _ptr(idx), _ptr(bias),
+        _ptr(weights), _stream(scores.device)))
+    return idx, bias, weights
+
+
+def ssa_block_sparse_attn_fwd_biased(shape: Shape, q, k, v, block_idx, block_bias, out=None, lse=None):
+    """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q]) of the block-sparse
+    forward over group-shared lists with a per-block logit bias."""
+    _require_gpu(q, k, v, block_idx, block_bias, out, lse)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check("ssa_block_sparse_attn_fwd_biased", load_library().ssa_block_sparse_attn_fwd_biased(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(block_bias), _ptr(out), _ptr(lse),
+        None, 0, _stream(q.device)))
+    return out, lse
 
 
 def ssa_block_scores(shape: Shape, q: torch.Tensor, k: Optional[torch.Tensor] = None,

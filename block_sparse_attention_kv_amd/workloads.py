@@ -128,3 +128,12 @@ def make_output_grad(w: Workload, rows: Optional[Tuple[int, int]] = None, device
     g.manual_seed(w.seed + 500000)
     full = torch.randn((w.batch, w.n_q_heads, w.seq_q, w.head_dim), generator=g, dtype=torch.float32)
     return full[:, :, lo:hi].to(torch.bfloat16).contiguous().to(device)
+
+
+def make_learned_query(w: Workload, scale: float = 1.0, device: str | torch.device = "cpu"):
+    """Seeded synthetic learned chunk query, fp32 [Hkv, d]: N(0, scale^2),
+    drawn from its own generator (seed + 700000); it stands in for the trained
+    vector of a chunk-summary stage (there are no trained weights here)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 700000)
+    return (torch.randn((w.n_kv_heads, w.head_dim), generator=g, dtype=torch.float32) * scale).to(device)

@@ -273,6 +273,59 @@ ssa_status_t ssa_full_attn_bwd(const ssa_shape_t* shape, const void* q, const vo
                                const float* lse_full, const void* dout_full, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Chunk summaries from a learned query: for KV head g and key block j,
+ *   k_summary[b,g,j,:] = fp32 rounding of sum_c softmax_c(scale * qbar[g] . k_c) k_c
+ * over the rows c < seq_kv of block j (computed in fp64).  qbar == 0 gives the
+ * plain mean of ssa_block_summaries.  Feed the result to ssa_block_scores
+ * with summary_is_input = 1.
+ * [DashAttn] "Etapa 0" (a learned query attends to each chunk's keys by local
+ * scaled dot-product attention; zero-initialised it is the uniform average;
+ * a finished chunk's summary is cached).
+ *   k          bf16 [b,Hkv,seq_kv,d]
+ *   qbar       fp32 [Hkv,d] (one learned query per KV head)
+ *   k_summary  fp32 [b,Hkv,nkb,d]  (output) */
+ssa_status_t ssa_block_summaries_learned(const ssa_shape_t* shape, const void* k, const float* qbar,
+                                         float* k_summary, hipStream_t stream);
+
+/* alpha-entmax routing with a group-shared support.  For each (b, KV head g,
+ * query block i) and each query head h of the group,
+ *   w_h = alpha-entmax(gamma * scores[b,h,i,j]) over j < diag(i),
+ *   alpha-entmax(z)_j = max(0, (alpha-1) z_j - tau)^(1/(alpha-1)), tau such that sum_j = 1,
+ * and the group's weights are wbar = mean_h w_h (fp32; tau by bisection in
+ * fp32).  block_idx lists diag(i) plus every j with wbar_j > 0 -- past topk
+ * blocks, the topk-1 largest wbar (lower index on ties) -- ascending, -1
+ * padded; block_bias holds sigma * ln(wbar_j) for each listed j != diag(i)
+ * and 0 for diag(i) and padding.  Non-finite scores take no weight.
+ * [DashAttn] "Etapa 1" (entmax routing instead of a fixed top-k: the support
+ * size follows from the scores; with GQA the probabilities of the heads
+ * sharing a KV head are averaged into one support) and "Etapa 2" (the
+ * routing weights become a prior on the token softmax, zero where they are
+ * zero, of strength sigma; near-diagonal chunks have their own branch).
+ *   scores      fp32 [b,Hq,nqb,nkb] (ssa_block_scores)
+ *   alpha       in (1, 2] (NaN: SSA_ERR_INVALID_ARG; otherwise outside: SSA_ERR_UNSUPPORTED)
+ *   gamma, sigma  finite, >= 0 (else SSA_ERR_INVALID_ARG)
+ *   block_idx   int32 [b,Hkv,nqb,topk] (output);  block_bias fp32 [b,Hkv,nqb,topk] (output)
+ *   weights     fp32 [b,Hkv,nqb,nkb] (optional output, NULL to skip: wbar, 0 from diag(i) on)
+ * More than 2048 key blocks: SSA_ERR_UNSUPPORTED. */
+ssa_status_t ssa_entmax_route(const ssa_shape_t* shape, const float* scores, float alpha, float gamma, float sigma,
+                              int32_t* block_idx, float* block_bias, float* weights, hipStream_t stream);
+
+/* Block-sparse attention forward with a per-block logit bias and a
+ * group-shared selection: row r of query head h, query block i attends to the
+ * keys c <= q_offset + r of the blocks listed in block_idx[b, h/G, i, :], with
+ * logits scale * q_r . k_c + block_bias[b, h/G, i, e] for c in the e-th listed
+ * block (out, lse as ssa_block_sparse_attn_fwd; lse includes the bias).  With
+ * the output of ssa_entmax_route this is the softmax taken relative to the
+ * prior g proportional to wbar^sigma.
+ * [DashAttn] "Etapa 2" (prior-induced sparse softmax: a FlashAttention-style
+ * loop over the active chunks adding the routing bias to the logits).
+ *   block_idx   int32 [b,Hkv,nqb,topk];  block_bias fp32 [b,Hkv,nqb,topk]
+ * Prefill only: seq_q == 1 returns SSA_ERR_UNSUPPORTED.  No workspace. */
+ssa_status_t ssa_block_sparse_attn_fwd_biased(const ssa_shape_t* shape, const void* q, const void* k,
+                                              const void* v, const int32_t* block_idx, const float* block_bias,
+                                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
+
 /* Workspace bytes an entry point needs for this shape (0 if none; SIZE_MAX if
  * the shape is invalid). */
 size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op);

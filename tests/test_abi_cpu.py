@@ -80,6 +80,10 @@ def test_shape_validation(lib, kw, status):
                                                      None) == status
     assert lib.ssa_block_sparse_attn_fwd_early_stop(p, FAKE, FAKE, FAKE, FAKE, FAKE, 0.01, FAKE, FAKE, FAKE, None,
                                                     0, None) == status
+    assert lib.ssa_block_summaries_learned(p, FAKE, FAKE, FAKE, None) == status
+    assert lib.ssa_entmax_route(p, FAKE, ctypes.c_float(1.5), ctypes.c_float(1.0), ctypes.c_float(1.0), FAKE, FAKE,
+                                None, None) == status
+    assert lib.ssa_block_sparse_attn_fwd_biased(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == status
     for fn in (lib.ssa_block_sparse_attn_bwd, lib.ssa_block_sparse_attn_bwd_shared):
         assert fn(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == status
     assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
@@ -163,6 +167,31 @@ def test_backward_workspace_and_validation(lib):
     # the long-sequence chunking stays within 64 query blocks per work item
     long = good_shape(n_q_heads=32, n_kv_heads=2, seq_q=32768, seq_kv=32768, topk=16)
     assert lib.ssa_workspace_bytes(ctypes.byref(long), ssa.SSA_OP_SPARSE_BWD) < 1 << 30
+
+
+def test_dash_route_validation(lib):
+    p = ctypes.byref(good_shape())
+    f = ctypes.c_float
+    args = (FAKE, FAKE, None, None)
+    for alpha, st in ((1.0, ssa.SSA_ERR_UNSUPPORTED), (2.5, ssa.SSA_ERR_UNSUPPORTED),
+                      (float("nan"), ssa.SSA_ERR_INVALID_ARG)):
+        assert lib.ssa_entmax_route(p, FAKE, f(alpha), f(1.0), f(1.0), *args) == st
+        assert b"alpha" in lib.ssa_last_error()
+    for gamma, sigma in ((-1.0, 1.0), (1.0, -0.5), (float("inf"), 1.0), (1.0, float("nan"))):
+        assert lib.ssa_entmax_route(p, FAKE, f(1.5), f(gamma), f(sigma), *args) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_entmax_route(p, FAKE, f(1.5), f(1.0), f(1.0), FAKE, None, None, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"block_bias is NULL" in lib.ssa_last_error()
+    long = good_shape(seq_q=64 * 2049, seq_kv=64 * 2049)
+    assert lib.ssa_entmax_route(ctypes.byref(long), FAKE, f(1.5), f(1.0), f(1.0), FAKE, FAKE, None,
+                                None) == ssa.SSA_ERR_UNSUPPORTED
+    # the biased forward: prefill only, bias required
+    dec = good_shape(seq_q=1, seq_kv=300, q_offset=299)
+    assert lib.ssa_block_sparse_attn_fwd_biased(ctypes.byref(dec), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                                None) == ssa.SSA_ERR_UNSUPPORTED
+    assert lib.ssa_block_sparse_attn_fwd_biased(p, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0,
+                                                None) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_block_summaries_learned(p, FAKE, None, FAKE, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"qbar is NULL" in lib.ssa_last_error()
 
 
 def test_empty_problems_launch_nothing(lib):
