@@ -342,6 +342,57 @@ def bench_backward(args, torch, ssa, W):
     return res
 
 
+def bench_dash(args, torch, ssa, W, alpha=1.5, gamma=800.0, sigma=1.0, cap=64):
+    """DashAttention-style stages on the bench workload with a synthetic learned
+    query: learned-query summaries, scores against them, alpha-entmax routing
+    (group-shared support, capped at ``cap`` blocks), prior-biased block-sparse
+    forward.  Time per stage (HIP events), list length, useful attention rate."""
+    w = W.BY_NAME[args.workload].scaled(topk=cap)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.make_inputs(w))
+    qbar = W.make_learned_query(w, device=dev)
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    nqb, nkb = ssa.n_blocks(w.seq_q, w.block), ssa.n_blocks(w.seq_kv, w.block)
+    ks = torch.empty((w.batch, w.n_kv_heads, nkb, w.head_dim), dtype=torch.float32, device=dev)
+    scores = torch.empty((w.batch, w.n_q_heads, nqb, nkb), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.batch, w.n_kv_heads, nqb, w.topk), dtype=torch.int32, device=dev)
+    bias = torch.empty((w.batch, w.n_kv_heads, nqb, w.topk), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    timer = KernelTimer(torch)
+
+    def step(t):
+        t.run("summaries", ssa.ssa_block_summaries_learned, k, qbar, out=ks)
+        t.run("scores", ssa.ssa_block_scores, shape, q, None, ks, scores=scores)
+        t.run("route", ssa.ssa_entmax_route, shape, scores, alpha, gamma, sigma, idx, bias, None, False)
+        t.run("attn", ssa.ssa_block_sparse_attn_fwd_biased, shape, q, k, v, idx, bias, out, lse)
+
+    for _ in range(3):
+        step(timer)
+    torch.cuda.synchronize()
+    timer.pending.clear()
+    n = max(1, args.steps // 2)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step(timer)
+    e1.record()
+    torch.cuda.synchronize()
+    timer.collect()
+    ms = e0.elapsed_time(e1) / n
+    # useful pairs: every listed block whole, the diagonal block's causal half
+    listed = (idx >= 0).sum(-1).double()                       # [b, Hkv, nqb]
+    pairs = float(((listed - 1) * w.block * w.block + w.block * (w.block + 1) / 2).sum()) * (w.n_q_heads // w.n_kv_heads)
+    attn_ms = timer.avg_ms("attn")
+    tf = 4.0 * w.head_dim * pairs / (attn_ms * 1e-3) / 1e12
+    return {"workload": w.name, "alpha": alpha, "gamma": gamma, "sigma": sigma, "list_cap": cap,
+            "blocks_listed_per_query_block": round(float(listed.mean()), 3), "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(w.batch * w.seq_q / (ms * 1e-3), 1),
+            "kernels_ms": {kk: round(timer.avg_ms(kk), 5) for kk in ("summaries", "scores", "route", "attn")},
+            "attn_tflops": round(tf, 2), "attn_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_baseline(args, W):
     """The fp64 oracle, as it stands, on a bounded sample of the prefill workload:
     whole query heads (all rows, all five steps) until ~target seconds elapse."""
@@ -404,7 +455,7 @@ def main():
     ap.add_argument("--decode-copies", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-shared", action="store_true",
-                    help="skip the extra legs (group-shared selection, early stopping)")
+                    help="skip the extra legs (group-shared selection, early stopping, DashAttention stages)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -467,6 +518,7 @@ def main():
         "shared_selection": shared,
         "early_stop": None if args.no_shared else bench_early_stop(args, torch, ssa, W),
         "backward": None if args.no_backward else bench_backward(args, torch, ssa, W),
+        "dash": None if args.no_shared else bench_dash(args, torch, ssa, W),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

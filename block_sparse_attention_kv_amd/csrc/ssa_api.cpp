@@ -129,7 +129,7 @@ ssa_status_t ssa_entmax_route(const ssa_shape_t* shape, const float* scores, flo
                 (double)alpha);
   if (!(gamma >= 0.f) || !isfinite(gamma) || !(sigma >= 0.f) || !isfinite(sigma))
     return fail(SSA_ERR_INVALID_ARG, "%s: gamma and sigma must be finite and >= 0", fn);
-  if (g.nkb > 2048) return fail(SSA_ERR_UNSUPPORTED, "%s: more than 2048 key blocks", fn);
+  if (g.nkb > 1024) return fail(SSA_ERR_UNSUPPORTED, "%s: more than 1024 key blocks", fn);
   if (empty) return SSA_OK;
   CHECK_PTR(scores, 4, fn);
   CHECK_PTR(block_idx, 4, fn);

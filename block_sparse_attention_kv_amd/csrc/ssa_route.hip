@@ -6,9 +6,9 @@
 // diagonal block plus every block of positive weight (past topk blocks: the
 // topk-1 largest weights, lower index on ties), ascending, with a logit bias
 // sigma * ln(w) per routed block (0 for the diagonal).
-// tau is found by bisection on [max - 1, max] of the scaled scores (the mass
-// decreases in tau: at least 1 at the lower end, 0 at the upper), one
-// wavefront per head with shuffle reductions; the weights are then normalised.
+// tau is found by Newton's method from max - 1 (the mass is convex and
+// decreasing in tau, so the iterates rise monotonically to the root), one
+// wavefront per head with DPP reductions; the weights are then normalised.
 // Method: DashAttention summary, "Etapa 1" (entmax routing of the chunk
 // logits; with grouped-query attention the probabilities of the heads sharing
 // a KV head are averaged into one sparse support) and "Etapa 2" (prior bias
@@ -20,8 +20,30 @@
 namespace ssa {
 namespace {
 
-constexpr int kRouteWaves = 4;
-constexpr int kBisectSteps = 30;
+constexpr int kRouteWaves = 8;
+constexpr int kNewtonSteps = 32;  // cap; a handful of steps reach fp32 resolution
+
+// Whole-wave sum / max on the VALU: DPP within rows of 16 lanes (quad
+// permutes, then the half-row and row mirrors), then the 16- and 32-lane
+// swaps; every lane ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return sum_xor32(sum_xor16(x));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return max_xor32(max_xor16(x));
+}
 
 __device__ __forceinline__ float entmax_pow(float x, float inv, int kind) {
   // x >= 0; kind 2: alpha = 2 (power 1), kind 1: alpha = 1.5 (power 2), else general
@@ -30,9 +52,16 @@ __device__ __forceinline__ float entmax_pow(float x, float inv, int kind) {
   return x > 0.f ? __builtin_amdgcn_exp2f(inv * __builtin_amdgcn_logf(x)) : 0.f;
 }
 
+// d/dx of x^inv for x >= 0 (0 at x = 0).
+__device__ __forceinline__ float entmax_dpow(float x, float inv, int kind) {
+  if (kind == 2) return x > 0.f ? 1.f : 0.f;
+  if (kind == 1) return 2.f * x;
+  return x > 0.f ? inv * __builtin_amdgcn_exp2f((inv - 1.f) * __builtin_amdgcn_logf(x)) : 0.f;
+}
+
 // Dynamic LDS: per wave, the scaled scores of its current head (n floats) and
 // the sum of its heads' weights (n floats).
-__global__ __launch_bounds__(256) void entmax_route_kernel(const float* __restrict__ scores, float alpha, float gamma,
+__global__ __launch_bounds__(64 * kRouteWaves) void entmax_route_kernel(const float* __restrict__ scores, float alpha, float gamma,
                                                            float sigma, int32_t* __restrict__ idx,
                                                            float* __restrict__ bias, float* __restrict__ weights,
                                                            Geometry geo, int npad) {
@@ -69,32 +98,37 @@ __global__ __launch_bounds__(256) void entmax_route_kernel(const float* __restri
       mx = fmaxf(mx, v);
       nfin += fin ? 1 : 0;
     }
-    mx = wave_max(mx);
+    mx = wave_max_dpp(mx);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) nfin += __shfl_xor(nfin, o, 64);
     if (nfin == 0) continue;
-    float lo = mx - 1.f;  // the largest score alone already gives mass 1
-    float hi = mx;        // nothing above the largest score: mass 0
-    for (int it = 0; it < kBisectSteps; ++it) {
-      const float mid = 0.5f * (lo + hi);
-      float f = 0.f;
-      for (int j = lane; j < n; j += 64) f += entmax_pow(fmaxf(zt[j] - mid, 0.f), inv, kind);
-      f = wave_sum(f);
-      if (f >= 1.f)
-        lo = mid;
-      else
-        hi = mid;
+    // Newton from below: the mass f(tau) = sum max(0, zt - tau)^inv is convex
+    // and decreasing (inv >= 1), so from tau0 = max - 1 (f >= 1) each step
+    // lands at or below the root; stop when tau no longer increases.
+    float lo = mx - 1.f;
+    for (int it = 0; it < kNewtonSteps; ++it) {
+      float f = 0.f, df = 0.f;
+      for (int j = lane; j < n; j += 64) {
+        const float x = fmaxf(zt[j] - lo, 0.f);
+        f += entmax_pow(x, inv, kind);
+        df += entmax_dpow(x, inv, kind);
+      }
+      f = wave_sum_dpp(f);
+      df = wave_sum_dpp(df);
+      const float nxt = lo + (f - 1.f) / df;
+      if (!(nxt > lo)) break;
+      lo = nxt;
     }
     float tot = 0.f;
     for (int j = lane; j < n; j += 64) tot += entmax_pow(fmaxf(zt[j] - lo, 0.f), inv, kind);
-    tot = wave_sum(tot);
+    tot = wave_sum_dpp(tot);
     const float rs = 1.f / tot;
     for (int j = lane; j < n; j += 64) acc[j] += entmax_pow(fmaxf(zt[j] - lo, 0.f), inv, kind) * rs;
   }
   __syncthreads();
-  // group mean into wave 0's accumulator: ((w0 + w1) + w2) + w3, over G
+  // group mean into wave 0's accumulator: (((w0 + w1) + w2) + ...), over G
   const float rg = 1.f / (float)G;
-  for (int j = tid; j < n; j += 256) {
+  for (int j = tid; j < n; j += 64 * kRouteWaves) {
     float s = lds[npad + j];
     for (int w = 1; w < kRouteWaves; ++w) s += lds[(size_t)w * 2 * npad + npad + j];
     lds[npad + j] = s * rg;
@@ -104,11 +138,11 @@ __global__ __launch_bounds__(256) void entmax_route_kernel(const float* __restri
   float* wbar = lds + npad;
   const size_t row = ((size_t)gi * geo.nqb + i);
   if (weights) {
-    for (int j = tid; j < geo.nkb; j += 256) weights[row * geo.nkb + j] = j < n ? wbar[j] : 0.f;
+    for (int j = tid; j < geo.nkb; j += 64 * kRouteWaves) weights[row * geo.nkb + j] = j < n ? wbar[j] : 0.f;
   }
   // support size, then (if it exceeds topk - 1) the rank of each block by weight
   int cnt = 0;
-  for (int j = tid; j < n; j += 256) cnt += wbar[j] > 0.f ? 1 : 0;
+  for (int j = tid; j < n; j += 64 * kRouteWaves) cnt += wbar[j] > 0.f ? 1 : 0;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
   if (lane == 0) atomicAdd(&sCount, cnt);  // integer sum: order-independent
@@ -116,7 +150,7 @@ __global__ __launch_bounds__(256) void entmax_route_kernel(const float* __restri
   const int nsup = sCount;
   const int keep = geo.topk - 1;
   float* flag = lds;  // wave 0's score buffer, reused: 1 = block kept
-  for (int j = tid; j < n; j += 256) {
+  for (int j = tid; j < n; j += 64 * kRouteWaves) {
     const float wj = wbar[j];
     bool kept = wj > 0.f;
     if (kept && nsup > keep) {
@@ -161,7 +195,8 @@ hipError_t launch_entmax_route(const float* scores, float alpha, float gamma, fl
   if (rows == 0) return hipSuccess;
   const int npad = (g.nkb + 63) & ~63;
   const size_t lds = (size_t)kRouteWaves * 2 * npad * sizeof(float);
-  hipLaunchKernelGGL(entmax_route_kernel, dim3((unsigned)rows), dim3(256), lds, stream, scores, alpha, gamma, sigma,
+  hipLaunchKernelGGL(entmax_route_kernel, dim3((unsigned)rows), dim3(64 * kRouteWaves), lds, stream, scores, alpha,
+                     gamma, sigma,
                      idx, bias, weights, g, npad);
   return hipGetLastError();
 }

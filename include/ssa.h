@@ -306,7 +306,7 @@ ssa_status_t ssa_block_summaries_learned(const ssa_shape_t* shape, const void* k
  *   gamma, sigma  finite, >= 0 (else SSA_ERR_INVALID_ARG)
  *   block_idx   int32 [b,Hkv,nqb,topk] (output);  block_bias fp32 [b,Hkv,nqb,topk] (output)
  *   weights     fp32 [b,Hkv,nqb,nkb] (optional output, NULL to skip: wbar, 0 from diag(i) on)
- * More than 2048 key blocks: SSA_ERR_UNSUPPORTED. */
+ * More than 1024 key blocks (65536 keys): SSA_ERR_UNSUPPORTED. */
 ssa_status_t ssa_entmax_route(const ssa_shape_t* shape, const float* scores, float alpha, float gamma, float sigma,
                               int32_t* block_idx, float* block_bias, float* weights, hipStream_t stream);
 

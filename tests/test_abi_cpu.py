@@ -181,7 +181,7 @@ def test_dash_route_validation(lib):
         assert lib.ssa_entmax_route(p, FAKE, f(1.5), f(gamma), f(sigma), *args) == ssa.SSA_ERR_INVALID_ARG
     assert lib.ssa_entmax_route(p, FAKE, f(1.5), f(1.0), f(1.0), FAKE, None, None, None) == ssa.SSA_ERR_INVALID_ARG
     assert b"block_bias is NULL" in lib.ssa_last_error()
-    long = good_shape(seq_q=64 * 2049, seq_kv=64 * 2049)
+    long = good_shape(seq_q=64 * 1025, seq_kv=64 * 1025)
     assert lib.ssa_entmax_route(ctypes.byref(long), FAKE, f(1.5), f(1.0), f(1.0), FAKE, FAKE, None,
                                 None) == ssa.SSA_ERR_UNSUPPORTED
     # the biased forward: prefill only, bias required
