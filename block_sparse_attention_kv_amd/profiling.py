@@ -66,6 +66,8 @@ def classify(name: str):
         return "bwd_reduce"
     if "bwd_mask_kernel" in name:
         return "bwd_mask"
+    if "bwd_count_kernel" in name:
+        return "bwd_count"
     if "bwd_items_kernel" in name:
         return "bwd_items"
     if "bwd_fill_zero_kernel" in name:
