@@ -189,8 +189,6 @@ ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void
   bool empty;
   ssa_status_t st = make_geometry(shape, &g, &empty, fn);
   if (st != SSA_OK) return st;
-  if (biased && g.seq_q == 1)
-    return fail(SSA_ERR_UNSUPPORTED, "%s: decode (seq_q == 1) with a block bias is not implemented", fn);
   if (empty) return SSA_OK;
   if (biased) CHECK_PTR(block_bias, 4, fn);
   CHECK_PTR(q, 16, fn);

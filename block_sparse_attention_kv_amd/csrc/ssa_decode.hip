@@ -8,6 +8,8 @@
 // balanced whatever the selection.  A wavefront streams exactly its union
 // blocks from HBM through a ring of LDS slots filled by direct-to-LDS loads,
 // keeping kRing-1 blocks in flight while it computes.
+// With a group-shared list and a per-block bias (prior-biased softmax), the
+// block's logits are shifted by its bias.
 // Every union block is applied to all query heads of the group at once with
 // bf16 MFMAs (16 heads per 16x16x32 tile): heads that did not select the block
 // see it masked.  Each wavefront writes one partial online-softmax state
@@ -56,7 +58,7 @@ template <int NHB>  // 16-head blocks per KV group: 1 (G <= 16) or 2 (G <= 32)
 __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, float* __restrict__ ws,
                                                                     Geometry geo, int npieces) {
   __shared__ __attribute__((aligned(1024))) uint8_t sKV[kRing][2][kTileBytes];
-  extern __shared__ uint32_t sDyn[];  // bitmap[nw] | prefix[nw] | list[cap] | heads[cap]
+  extern __shared__ uint32_t sDyn[];  // bitmap[nw] | prefix[nw] | list[cap] | heads[cap] | bias[cap]
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int bg = blockIdx.x / npieces;
@@ -70,6 +72,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   int* prefix = reinterpret_cast<int*>(sDyn + nw);
   int* sBlk = reinterpret_cast<int*>(sDyn + 2 * nw);
   uint32_t* sHm = sDyn + 2 * nw + cap;
+  float* sBias = reinterpret_cast<float*>(sDyn + 2 * nw + 2 * cap);  // group-shared lists with a bias only
   // the group's index rows: one per query head, or one shared row
   const int32_t* gidx = a.idx + (size_t)(a.idx_shared ? bg : head0) * geo.topk;
   const uint32_t all_heads = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
       const int r = prefix[j >> 5] + __builtin_popcount(bitmap[j >> 5] & ((1u << (j & 31)) - 1u));
       sBlk[r] = j;
       atomicOr(&sHm[r], a.idx_shared ? all_heads : 1u << (e / geo.topk));
+      if (a.bias) sBias[r] = a.bias[(size_t)bg * geo.topk + e];  // shared row: one entry per block
     }
   }
   wave_sync_lds();
@@ -165,6 +169,10 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
     }
     const int j = __builtin_amdgcn_readfirstlane(sBlk[u0 + n]);
     const uint32_t hm = __builtin_amdgcn_readfirstlane(sHm[u0 + n]);
+    // logit shift of this block (log2 units), 0 without a bias
+    const float b2 =
+        a.bias ? __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sBias[u0 + n]))) * 1.4426950408889634f
+               : 0.f;
     wait_block(min(kRing - 1, nmine - 1 - n));
     const uint8_t* sK = sKV[slot][0];
     const uint8_t* sV = sKV[slot][1];
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
       mx = sel ? mx : -__builtin_inff();
       mx = max_xor16(mx);
       mx = max_xor32(mx);
-      const float mt = mx * c;
+      const float mt = fmaf(mx, c, b2);  // == mx * c without a bias
       if (!(mt <= m[hb] + kRescaleSlack)) {  // per-lane: its head's reference max moves
         const float mn = fmaxf(m[hb], mt);
         const float alpha = fast_exp2(m[hb] - mn);
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
           for (int r = 0; r < 4; ++r) o[hb][db][r] *= alpha;
       }
       // unselected head: p = exp2(-inf) = 0; selected head: exponent relative to its reference max
-      const float nm = !sel ? -__builtin_inff() : -m[hb];
+      const float nm = !sel ? -__builtin_inff() : b2 - m[hb];
       float rs = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -324,7 +332,8 @@ hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometr
   const int npieces = decode_pieces(g.batch, g.hkv);
   const size_t nwg = (size_t)g.batch * g.hkv * npieces;
   if (nwg == 0) return hipSuccess;
-  const size_t dyn = (2 * (size_t)((g.nkb + 31) / 32) + 2 * (size_t)g.group * g.topk) * sizeof(uint32_t);
+  const size_t dyn =
+      (2 * (size_t)((g.nkb + 31) / 32) + 2 * (size_t)g.group * g.topk + (size_t)g.topk) * sizeof(uint32_t);
   if (g.group <= 16)
     hipLaunchKernelGGL(attn_decode_partial_kernel<1>, dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace, g,
                        npieces);

@@ -188,17 +188,23 @@ def ssa_entmax_route(shape: Shape, scores: torch.Tensor, alpha: float, gamma: fl
     return idx, bias, weights
 
 
-def ssa_block_sparse_attn_fwd_biased(shape: Shape, q, k, v, block_idx, block_bias, out=None, lse=None):
+def ssa_block_sparse_attn_fwd_biased(shape: Shape, q, k, v, block_idx, block_bias, out=None, lse=None,
+                                     workspace: Optional[torch.Tensor] = None):
     """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q]) of the block-sparse
-    forward over group-shared lists with a per-block logit bias."""
-    _require_gpu(q, k, v, block_idx, block_bias, out, lse)
+    forward over group-shared lists with a per-block logit bias (decode uses a
+    workspace, allocated here when not given)."""
+    _require_gpu(q, k, v, block_idx, block_bias, out, lse, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    need = ssa_workspace_bytes(shape, SSA_OP_SPARSE_FWD)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ssa_block_sparse_attn_fwd_biased", load_library().ssa_block_sparse_attn_fwd_biased(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(block_bias), _ptr(out), _ptr(lse),
-        None, 0, _stream(q.device)))
+        _ptr(workspace), ws_bytes, _stream(q.device)))
     return out, lse
 
 

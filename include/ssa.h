@@ -320,7 +320,8 @@ ssa_status_t ssa_entmax_route(const ssa_shape_t* shape, const float* scores, flo
  * [DashAttn] "Etapa 2" (prior-induced sparse softmax: a FlashAttention-style
  * loop over the active chunks adding the routing bias to the logits).
  *   block_idx   int32 [b,Hkv,nqb,topk];  block_bias fp32 [b,Hkv,nqb,topk]
- * Prefill only: seq_q == 1 returns SSA_ERR_UNSUPPORTED.  No workspace. */
+ * Decode (seq_q == 1) needs ssa_workspace_bytes(shape, SSA_OP_SPARSE_FWD)
+ * bytes of workspace, as ssa_block_sparse_attn_fwd; prefill needs none. */
 ssa_status_t ssa_block_sparse_attn_fwd_biased(const ssa_shape_t* shape, const void* q, const void* k,
                                               const void* v, const int32_t* block_idx, const float* block_bias,
                                               void* out, float* lse, void* workspace, size_t workspace_bytes,

@@ -184,10 +184,10 @@ def test_dash_route_validation(lib):
     long = good_shape(seq_q=64 * 1025, seq_kv=64 * 1025)
     assert lib.ssa_entmax_route(ctypes.byref(long), FAKE, f(1.5), f(1.0), f(1.0), FAKE, FAKE, None,
                                 None) == ssa.SSA_ERR_UNSUPPORTED
-    # the biased forward: prefill only, bias required
+    # the biased forward: decode needs the decode workspace; the bias is required
     dec = good_shape(seq_q=1, seq_kv=300, q_offset=299)
     assert lib.ssa_block_sparse_attn_fwd_biased(ctypes.byref(dec), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
-                                                None) == ssa.SSA_ERR_UNSUPPORTED
+                                                None) == ssa.SSA_ERR_WORKSPACE
     assert lib.ssa_block_sparse_attn_fwd_biased(p, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0,
                                                 None) == ssa.SSA_ERR_INVALID_ARG
     assert lib.ssa_block_summaries_learned(p, FAKE, None, FAKE, None) == ssa.SSA_ERR_INVALID_ARG

@@ -130,6 +130,10 @@ CASES = [
     (W.Workload("dash_sigma0", 1, 8, 1, 768, 768, 64, 64, 12, seed=46), 1.5, 200.0, 0.0),
     (W.Workload("dash_chunked", 1, 8, 2, 320, 640, 64, 64, 8, seed=47), 1.5, 300.0, 1.0),
     (W.Workload("dash_g3", 1, 6, 2, 640, 640, 64, 64, 10, seed=48), 2.0, 100.0, 1.0),
+    # decode: one query token per sequence against a cache (ragged last block)
+    (W.Workload("dash_decode_4133", 4, 32, 2, 1, 4133, 64, 64, 17, seed=52), 1.5, 800.0, 1.0),
+    (W.Workload("dash_decode_g8_cap", 3, 16, 2, 1, 2048, 64, 64, 6, seed=53), 2.0, 400.0, 0.5),
+    (W.Workload("dash_decode_32k", 8, 32, 2, 1, 32768, 64, 64, 64, seed=54), 1.5, 800.0, 1.0),
 ]
 
 
