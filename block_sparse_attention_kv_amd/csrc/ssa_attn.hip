@@ -293,6 +293,12 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
 
   // index row (per query head, or per KV group when shared) and Q requested
   // together, so their latencies overlap
+  // The diagonal block ends every valid (ascending) list, so its tile is
+  // requested before the list is read, and visited first.
+  TileOffsets<1, 0> toff;
+  toff.init(lane, 0);
+  tile_load(a.k + kvoff + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sK, lane, toff);
+  tile_load(a.v + kvoff + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sV, lane, toff);
   const int irow = a.idx_shared ? gi : bh;
   int iv[4];
   load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
@@ -300,19 +306,47 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   if (BIAS) load_value_row(a.bias + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, bv);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
-  const int nt = BIAS ? compact_index_row(iv, bv, geo.topk, jd, sList, sBias, lane)
-                      : compact_index_row(iv, geo.topk, jd, sList, lane);
-  if (nt > 0) {  // first tile requested before waiting for Q, so the two latencies overlap
-    TileOffsets<1, 0> toff;
-    toff.init(lane, 0);
-    const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
-    tile_load(a.k + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK, lane, toff);
-    tile_load(a.v + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV, lane, toff);
+  int nt = BIAS ? compact_index_row(iv, bv, geo.topk, jd, sList, sBias, lane)
+                : compact_index_row(iv, geo.topk, jd, sList, lane);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool has_diag = nt > 0 && __builtin_amdgcn_readfirstlane(sList[nt - 1]) == jd;
+  if (has_diag) {
+    // rotate: diagonal first, then the others in list order
+    int jv[kMaxTopk / 64];
+    float bw[kMaxTopk / 64];
+#pragma unroll
+    for (int cc = 0; cc < kMaxTopk / 64; ++cc) {
+      const int e = lane + 64 * cc;
+      jv[cc] = e < nt ? sList[(e + nt - 1) % nt] : 0;
+      if (BIAS) bw[cc] = e < nt ? sBias[(e + nt - 1) % nt] : 0.f;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int cc = 0; cc < kMaxTopk / 64; ++cc) {
+      const int e = lane + 64 * cc;
+      if (e < nt) {
+        sList[e] = jv[cc];
+        if (BIAS) sBias[e] = bw[cc];
+      }
+    }
   }
   UnitState st;
   init_state(st);
-  wait_vmem<0>();  // Q, and the first tile; from here only tile loads use vmcnt
+  wait_vmem<0>();  // Q, the list, and the diagonal tile
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (!has_diag && nt > 0) {  // a list without its diagonal: the prefetched tile is not used
+    const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
+    tile_load(a.k + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK, lane, toff);
+    tile_load(a.v + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV, lane, toff);
+    wait_vmem<0>();
+    __builtin_amdgcn_wave_barrier();
+  }
   sparse_tiles<BIAS>(sK, sV, sList, sBias, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd,
                      geo.q_offset + i * kBlock, geo.scale_log2, qop, st, lane, l32, hl);
   unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
