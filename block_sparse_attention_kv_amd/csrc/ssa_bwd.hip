@@ -20,9 +20,10 @@
 //     key-side kernel reads.  Per tile, transposed as in the forward (a lane
 //     owns one query column):  S^T = K Q^T,  dP^T = V dO^T  (Q, dO in
 //     registers), then dQ^T += K^T dS^T with K^T read transposed from LDS.
-//   * dK/dV kernel: one workgroup (2 waves, 32 keys each) per work item: at
-//     most P consecutive (query head, query block) pairs, in (query block,
-//     head) order, of the pairs whose list holds key block j.  Per pair,
+//   * dK/dV kernel: workgroups of 2 waves (32 keys each) walk the work items
+//     of their (batch, KV head) group with a stride; an item is at most P
+//     consecutive (query head, query block) pairs, in (query block, head)
+//     order, of the pairs whose list holds key block j.  Per pair,
 //     untransposed (a lane owns one key column):  S = Q K^T,  dP = dO V^T
 //     (K, V in registers), then dV += P^T dO and dK += dS^T Q with dO, Q read
 //     transposed from LDS.  Each item writes an fp32 partial; a reduce kernel
