@@ -81,6 +81,8 @@ SMALL = [
     W.Workload("bwd_chunked", 1, 4, 2, 192, 320, 64, 64, 3, seed=25),
     W.Workload("bwd_planted_1k", 1, 32, 2, 1024, 1024, 64, 64, 4, seed=26, variant="planted"),
     W.Workload("bwd_gqa16_2k", 1, 32, 2, 2048, 2048, 64, 64, 16, seed=27),
+    W.Workload("bwd_mha_topk256", 1, 2, 2, 4096, 4096, 64, 64, 256, seed=32),   # every block selected
+    W.Workload("bwd_g32", 1, 32, 1, 1024, 1024, 64, 64, 8, seed=33),            # 32 heads on one KV head
 ]
 
 
@@ -93,7 +95,7 @@ def test_sparse_backward_small(dev, w):
     compare(outs[0], ref, w.name)
 
 
-@pytest.mark.parametrize("w", [SMALL[1], SMALL[2], SMALL[5], SMALL[7]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SMALL[1], SMALL[2], SMALL[5], SMALL[7], SMALL[9]], ids=lambda w: w.name)
 def test_shared_backward_small(dev, w):
     say(f"shared-selection backward {w}")
     (q, k, v, dout), gidx, outs = sparse_bwd_gpu(w, dev, shared=True)
@@ -119,6 +121,16 @@ def test_full_backward_small(dev, case):
     ref = O.attention_backward(q.double().numpy(), k.double().numpy(), v.double().numpy(), dout.double().numpy(),
                                None, B, q_offset=w.q_offset, full=True, row_range=rows)
     compare(got, ref, w.name + " full")
+
+
+def test_sparse_backward_with_every_block_equals_full(dev):
+    """topk >= number of blocks: the block-sparse gradients are the full ones."""
+    w = SMALL[8]
+    say(f"sparse == full backward {w.name}")
+    (q, k, v, dout), gidx, outs = sparse_bwd_gpu(w, dev)
+    _, _, full = full_bwd_gpu(w, dev, (0, ssa.n_blocks(w.seq_q, B)))
+    for name, a, b in zip(("dQ", "dK", "dV"), outs[0], full):
+        P.check_grad(a, b.double().numpy(), f"sparse vs full {name}")
 
 
 def test_backward_is_deterministic(dev):
