@@ -381,6 +381,12 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
   const uint16_t* kbase = a.k + kvoff;
   const uint16_t* vbase = a.v + kvoff;
 
+  // the diagonal block is visited first whenever it is listed (as it is on
+  // every valid list): its tile is requested before the list is read
+  TileOffsets<1, 0> toff;
+  toff.init(lane, 0);
+  tile_load(kbase + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sK, lane, toff);
+  tile_load(vbase + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sV, lane, toff);
   int iv[4];
   load_index_row(a.idx + ((size_t)bh * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
   bf16x8 qop[2][4];
@@ -414,20 +420,20 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
     sOrder[has_diag + rank] = j;
   }
   const int nt = n;
-  TileOffsets<1, 0> toff;
-  toff.init(lane, 0);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (nt > 0) {
+  UnitState st;
+  init_state(st);
+  wait_vmem<0>();  // Q, the scores and the diagonal tile
+  __builtin_amdgcn_wave_barrier();
+  if (!has_diag && nt > 0) {  // a list without its diagonal: its first block replaces the prefetched tile
     const int j0 = __builtin_amdgcn_readfirstlane(sOrder[0]);
     tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK, lane, toff);
     tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV, lane, toff);
+    wait_vmem<0>();
+    __builtin_amdgcn_wave_barrier();
   }
-  UnitState st;
-  init_state(st);
-  wait_vmem<0>();  // Q and the first tile
-  __builtin_amdgcn_wave_barrier();
   const float c = geo.scale_log2;
   const int pos0 = geo.q_offset + i * kBlock;
   int used = 0;
