@@ -14,19 +14,22 @@ namespace ssa {
 namespace {
 
 // Sum the rows [0, nrows) of a 64-wide bf16 block in fp64.  Lane layout: lane
-// covers columns 8*(lane%8) .. +8 of rows lane/8, lane/8 + 8, ...; all eight
-// loads are issued before any is used.  The eight row groups are then folded
-// together, so lanes 0..7 end with the column sums.
-__device__ __forceinline__ void pool_rows_f64(const uint16_t* __restrict__ base, int nrows,
-                                              int lane, double acc[8]) {
+// covers columns 8*(lane%8) .. +8 of rows lane/8, lane/8 + 8, ...; the eight
+// loads (pool_load_rows) are all issued before any is used.  The eight row
+// groups are then folded together (pool_sum_rows), so lanes 0..7 end with the
+// column sums.
+__device__ __forceinline__ void pool_load_rows(const uint16_t* __restrict__ base, int nrows, int lane,
+                                               u32x4 (&v)[8]) {
   const int c8 = lane & 7, rg = lane >> 3;
-  u32x4 v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int r = rg + 8 * k;
     v[k] = *reinterpret_cast<const u32x4*>(base + (size_t)(r < nrows ? r : 0) * kHeadDim + c8 * 8);
     if (r >= nrows) v[k] = u32x4{0u, 0u, 0u, 0u};
   }
+}
+
+__device__ __forceinline__ void pool_sum_rows(const u32x4 (&v)[8], double acc[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 #pragma unroll
@@ -42,6 +45,13 @@ __device__ __forceinline__ void pool_rows_f64(const uint16_t* __restrict__ base,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
   }
+}
+
+__device__ __forceinline__ void pool_rows_f64(const uint16_t* __restrict__ base, int nrows, int lane,
+                                              double acc[8]) {
+  u32x4 v[8];
+  pool_load_rows(base, nrows, lane, v);
+  pool_sum_rows(v, acc);
 }
 
 __global__ __launch_bounds__(64) void block_summaries_kernel(const uint16_t* __restrict__ k,
@@ -117,123 +127,176 @@ __global__ __launch_bounds__(64) void learned_summaries_kernel(const uint16_t* _
   ksum[bgj * kHeadDim + lane] = (float)(col / wsum);
 }
 
-constexpr int kScoreQb = 4;     // query blocks per workgroup (prefill): one per wavefront
-constexpr int kScoreKTile = 64;  // key blocks staged per pass (decode)
-constexpr int kKbStride = 65;    // padded LDS row (floats) -> conflict-free row-per-lane reads
+// Scores are small fp64 matrix products, done with the fp64 matrix
+// instruction 16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16] and
+// holds C[l/16 + 4r][l%16], r = 0..3.  Lane l's k-slot covers
+// d = 16 (l/16) + s over the 16 steps s, so each lane reads 16 consecutive
+// values of a row.  Products and sums are fp64; each score is rounded once to
+// fp32.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// One workgroup of four wavefronts per (b, h, 4 query blocks, 256 key
-// blocks).  Each wavefront pools one query block (Q is read once per 256 key
-// blocks: once overall up to 16k tokens); then each thread scores one key
-// block's summary (read straight from global memory, L2-resident) against
-// the pooled blocks.
-__global__ __launch_bounds__(256) void prefill_scores_kernel(const uint16_t* __restrict__ q,
-                                                             const float* __restrict__ ksum,
-                                                             float* __restrict__ scores,
-                                                             Geometry geo) {
-  __shared__ double sQ[kScoreQb][kHeadDim];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ntile = (geo.nqb + kScoreQb - 1) / kScoreQb;
-  const int bh = blockIdx.x / ntile;
-  const int j = blockIdx.y * 256 + tid;
-  const int i0 = (blockIdx.x - bh * ntile) * kScoreQb;
-  const int b = bh / geo.hq, h = bh - b * geo.hq, g = h / geo.group;
-  const int nq = min(kScoreQb, geo.nqb - i0);
+__device__ __forceinline__ f64x4 mfma_dot64(const double (&a)[16], const double (&b)[16], f64x4 acc) {
+#pragma unroll
+  for (int st = 0; st < 16; ++st) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[st], b[st], acc, 0, 0, 0);
+  return acc;
+}
 
-  const int jd0 = geo.q_offset / kBlock + i0;  // diagonal block of the first query block
-  float* srow = scores + ((size_t)bh * geo.nqb + i0) * geo.nkb;
-  if ((int)blockIdx.y * 256 > jd0 + nq - 1) {  // every key block here is past the diagonal
-    if (j < geo.nkb)
-      for (int qi = 0; qi < nq; ++qi) srow[(size_t)qi * geo.nkb + j] = -__builtin_inff();
-    return;
-  }
-  if (wave < nq) {
-    const int r0 = (i0 + wave) * kBlock;
-    const int nrows = min(kBlock, geo.seq_q - r0);
-    double acc[8];
-    pool_rows_f64(q + ((size_t)bh * geo.seq_q + r0) * kHeadDim, nrows, lane, acc);
-    if (lane < 8) {
+// B operand: 16 consecutive fp32 values of a summary row, as fp64.
+__device__ __forceinline__ void load_row16_f64(const float* __restrict__ p, double (&out)[16]) {
+  const float4* r = reinterpret_cast<const float4*>(p);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sQ[wave][lane * 8 + e] = (double)(float)(acc[e] / nrows);
-    }
-  }
-  __syncthreads();
-
-  const float* kb = ksum + (size_t)(b * geo.hkv + g) * geo.nkb * kHeadDim;
-  const double scale = (double)geo.scale;
-  if (j < geo.nkb) {
-    float out[kScoreQb];
-#pragma unroll
-    for (int qi = 0; qi < kScoreQb; ++qi) out[qi] = -__builtin_inff();
-    if (j <= jd0 + nq - 1) {
-      const float4* kr = reinterpret_cast<const float4*>(kb + (size_t)j * kHeadDim);
-      float4 kv[16];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) kv[x] = kr[x];
-      double acc[kScoreQb] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float kk[4] = {kv[x].x, kv[x].y, kv[x].z, kv[x].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double kd = (double)kk[e];
-#pragma unroll
-          for (int qi = 0; qi < kScoreQb; ++qi) acc[qi] = fma(sQ[qi][4 * x + e], kd, acc[qi]);
-        }
-      }
-#pragma unroll
-      for (int qi = 0; qi < kScoreQb; ++qi)
-        if (j <= jd0 + qi) out[qi] = (float)(scale * acc[qi]);
-    }
-#pragma unroll
-    for (int qi = 0; qi < kScoreQb; ++qi)
-      if (qi < nq) srow[(size_t)qi * geo.nkb + j] = out[qi];
+  for (int c = 0; c < 4; ++c) {
+    const float4 v = r[c];
+    out[4 * c] = v.x;
+    out[4 * c + 1] = v.y;
+    out[4 * c + 2] = v.z;
+    out[4 * c + 3] = v.w;
   }
 }
 
-// Decode (one query row per (b, h)): one workgroup per (b, KV head, pass of
-// kScoreKTile key blocks) scores every query head of the group against the
-// staged summaries, so each summary is read from HBM once.
-constexpr int kMaxGroupScores = 64;
-__global__ __launch_bounds__(256) void decode_scores_kernel(const uint16_t* __restrict__ q,
-                                                            const float* __restrict__ ksum,
-                                                            float* __restrict__ scores,
-                                                            Geometry geo) {
-  extern __shared__ float sQ[];  // [G][kHeadDim]: the group's query rows (bf16 values, exact in fp32)
-  __shared__ float sKb[kScoreKTile * kKbStride];
-  const int tid = threadIdx.x;
-  const int npass = (geo.nkb + kScoreKTile - 1) / kScoreKTile;
-  const int bg = blockIdx.x / npass;
-  const int jc = (blockIdx.x - bg * npass) * kScoreKTile;
-  const int b = bg / geo.hkv, g = bg - b * geo.hkv;
-  const int G = geo.group;
-  const int nj = min(kScoreKTile, geo.nkb - jc);
-  const uint16_t* qg = q + (size_t)(b * geo.hq + g * G) * kHeadDim;  // seq_q == 1
-  for (int e = tid; e < G * kHeadDim; e += 256) sQ[e] = bf16_to_f32(qg[e]);
-  const float* kb = ksum + ((size_t)bg * geo.nkb + jc) * kHeadDim;
-  for (int e = tid; e < nj * 16; e += 256) {
-    const int jj = e >> 4, c4 = e & 15;
-    const float4 v = reinterpret_cast<const float4*>(kb + (size_t)jj * kHeadDim)[c4];
-    float* d = &sKb[jj * kKbStride + c4 * 4];
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+constexpr int kScoreQt = 16;    // query blocks per workgroup (prefill): the matrix row tile
+constexpr int kScoreWaves = 8;  // wavefronts per workgroup (prefill)
+constexpr int kScoreQStride = kHeadDim + 2;  // padded LDS row of the pooled queries (doubles)
+
+// Prefill: one workgroup of eight wavefronts per (b, h, 16 query blocks).
+// Each wavefront pools two of the query blocks into LDS (Q is read once);
+// then the wavefronts take the 16-block column tiles of the summaries in
+// turn (summaries are L2-resident) and write 16 x 16 scores per tile.
+// Tiles wholly past the last diagonal are filled with -inf without a product.
+__global__ __launch_bounds__(64 * kScoreWaves) void prefill_scores_kernel(const uint16_t* __restrict__ q,
+                                                                          const float* __restrict__ ksum,
+                                                                          float* __restrict__ scores,
+                                                                          Geometry geo) {
+  __shared__ double sQ[kScoreQt * kScoreQStride];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntile = (geo.nqb + kScoreQt - 1) / kScoreQt;
+  const int bh = blockIdx.x / ntile;
+  const int i0 = (blockIdx.x - bh * ntile) * kScoreQt;
+  const int b = bh / geo.hq, h = bh - b * geo.hq, g = h / geo.group;
+  const int nq = min(kScoreQt, geo.nqb - i0);
+  // both query blocks' loads are in flight before either is summed
+  constexpr int kPer = kScoreQt / kScoreWaves;
+  u32x4 qv[kPer][8];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int qi = wave + kScoreWaves * u;
+    const int r0 = (i0 + min(qi, nq - 1)) * kBlock;
+    pool_load_rows(q + ((size_t)bh * geo.seq_q + r0) * kHeadDim, qi < nq ? min(kBlock, geo.seq_q - r0) : 0, lane,
+                   qv[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int qi = wave + kScoreWaves * u;
+    const int nrows = qi < nq ? min(kBlock, geo.seq_q - (i0 + qi) * kBlock) : 1;
+    double acc[8];
+    pool_sum_rows(qv[u], acc);
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sQ[qi * kScoreQStride + lane * 8 + e] = qi < nq ? (double)(float)(acc[e] / nrows) : 0.0;
+    }
   }
   __syncthreads();
+
+  const int col = lane & 15, ks = lane >> 4;
+  double qa[16];
+#pragma unroll
+  for (int st = 0; st < 16; ++st) qa[st] = sQ[col * kScoreQStride + 16 * ks + st];
+  const int jd0 = geo.q_offset / kBlock + i0;       // diagonal block of the first query block
+  const int nt_live = (jd0 + nq - 1) / 16 + 1;      // tiles holding a block on or before a diagonal
+  const int nt = (geo.nkb + 15) / 16;
+  const float* kb = ksum + (size_t)(b * geo.hkv + g) * geo.nkb * kHeadDim + 16 * ks;
+  float* srow = scores + ((size_t)bh * geo.nqb + i0) * geo.nkb;
+  const double scale = (double)geo.scale;
+  for (int t = wave; t < nt; t += kScoreWaves) {
+    const int j = 16 * t + col;
+    if (t < nt_live) {
+      double kv[16];
+      load_row16_f64(kb + (size_t)min(j, geo.nkb - 1) * kHeadDim, kv);
+      const f64x4 c = mfma_dot64(qa, kv, f64x4{0.0, 0.0, 0.0, 0.0});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = ks + 4 * r;
+        if (qi < nq && j < geo.nkb)
+          srow[(size_t)qi * geo.nkb + j] = j <= jd0 + qi ? (float)(scale * c[r]) : -__builtin_inff();
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = ks + 4 * r;
+        if (qi < nq && j < geo.nkb) srow[(size_t)qi * geo.nkb + j] = -__builtin_inff();
+      }
+    }
+  }
+}
+
+// Decode (one query row per (b, h)): one wavefront per (b, KV head, 32 key
+// blocks) scores every query head of the group, so each summary is read from
+// HBM once: the group's [G x d] query rows times [d x 32] summaries, in 16-row
+// tiles of heads.  No LDS: the query rows come straight from memory.
+constexpr int kMaxGroupScores = 64;
+constexpr int kDscTiles = 2;  // 16-block column tiles per wavefront
+constexpr int kDscBlocks = 16 * kDscTiles;
+__global__ __launch_bounds__(64) void decode_scores_kernel(const uint16_t* __restrict__ q,
+                                                           const float* __restrict__ ksum,
+                                                           float* __restrict__ scores, Geometry geo) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, ks = lane >> 4;
+  const int npass = (geo.nkb + kDscBlocks - 1) / kDscBlocks;
+  const int bg = blockIdx.x / npass;
+  const int j0 = (blockIdx.x - bg * npass) * kDscBlocks;
+  const int b = bg / geo.hkv, g = bg - b * geo.hkv;
+  const int G = geo.group;
+  const uint16_t* qg = q + (size_t)(b * geo.hq + g * G) * kHeadDim + 16 * ks;  // seq_q == 1
+  // first row tile of the query heads: issued before the summaries
+  uint4 qv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  if (col < G) {
+    const uint4* qr = reinterpret_cast<const uint4*>(qg + (size_t)col * kHeadDim);
+    qv[0] = qr[0];
+    qv[1] = qr[1];
+  }
+  // B operand: summaries of key blocks j0 + 16 t + col (rows past the end
+  // read the last block; their scores are not stored)
+  double kb[kDscTiles][16];
+#pragma unroll
+  for (int t = 0; t < kDscTiles; ++t)
+    load_row16_f64(ksum + ((size_t)bg * geo.nkb + min(j0 + 16 * t + col, geo.nkb - 1)) * kHeadDim + 16 * ks, kb[t]);
   const int jd = geo.q_offset / kBlock;
   const double scale = (double)geo.scale;
-  for (int e = tid; e < G * kScoreKTile; e += 256) {
-    const int hh = e >> 6, jj = e & 63;
-    if (jj >= nj) continue;
-    const int j = jc + jj;
-    float out;
-    if (j > jd) {
-      out = -__builtin_inff();
-    } else {
-      double acc = 0.0;
-#pragma unroll 16
-      for (int d = 0; d < kHeadDim; ++d)
-        acc = fma((double)sQ[hh * kHeadDim + d], (double)sKb[jj * kKbStride + d], acc);
-      out = (float)(scale * acc);
+  for (int h0 = 0; h0 < G; h0 += 16) {
+    if (h0 > 0) {
+      qv[0] = qv[1] = make_uint4(0, 0, 0, 0);
+      if (h0 + col < G) {
+        const uint4* qr = reinterpret_cast<const uint4*>(qg + (size_t)(h0 + col) * kHeadDim);
+        qv[0] = qr[0];
+        qv[1] = qr[1];
+      }
     }
-    scores[(size_t)(b * geo.hq + g * G + hh) * geo.nkb + j] = out;
+    double qa[16];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t w[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qa[8 * u + 2 * e] = (double)__uint_as_float(w[e] << 16);
+        qa[8 * u + 2 * e + 1] = (double)__uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+    f64x4 acc[kDscTiles];
+#pragma unroll
+    for (int t = 0; t < kDscTiles; ++t) acc[t] = mfma_dot64(qa, kb[t], f64x4{0.0, 0.0, 0.0, 0.0});
+#pragma unroll
+    for (int t = 0; t < kDscTiles; ++t) {
+      const int j = j0 + 16 * t + col;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = h0 + ks + 4 * r;
+        if (hh < G && j < geo.nkb)
+          scores[(size_t)(b * geo.hq + g * G + hh) * geo.nkb + j] =
+              j <= jd ? (float)(scale * acc[t][r]) : -__builtin_inff();
+      }
+    }
   }
 }
 
@@ -258,20 +321,19 @@ hipError_t launch_learned_summaries(const uint16_t* k, const float* qbar, float*
 
 hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, float* scores,
                                  const Geometry& g, hipStream_t stream) {
-  const size_t nwg = (size_t)g.batch * g.hq * ((g.nqb + kScoreQb - 1) / kScoreQb);
+  const size_t nwg = (size_t)g.batch * g.hq * ((g.nqb + kScoreQt - 1) / kScoreQt);
   if (nwg == 0 || g.nkb == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_scores_kernel, dim3((unsigned)nwg, (unsigned)((g.nkb + 255) / 256)), dim3(256), 0,
-                     stream, q, k_summary, scores, g);
+  hipLaunchKernelGGL(prefill_scores_kernel, dim3((unsigned)nwg), dim3(64 * kScoreWaves), 0, stream, q, k_summary,
+                     scores, g);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float* scores,
                                 const Geometry& g, hipStream_t stream) {
   if (g.group > kMaxGroupScores) return hipErrorInvalidValue;
-  const size_t nwg = (size_t)g.batch * g.hkv * ((g.nkb + kScoreKTile - 1) / kScoreKTile);
+  const size_t nwg = (size_t)g.batch * g.hkv * ((g.nkb + kDscBlocks - 1) / kDscBlocks);
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_scores_kernel, dim3((unsigned)nwg), dim3(256),
-                     (size_t)g.group * kHeadDim * sizeof(float), stream, q, k_summary, scores, g);
+  hipLaunchKernelGGL(decode_scores_kernel, dim3((unsigned)nwg), dim3(64), 0, stream, q, k_summary, scores, g);
   return hipGetLastError();
 }
 
