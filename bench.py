@@ -87,6 +87,41 @@ class KernelTimer:
         return self.total[name] / self.count[name]
 
 
+class PlainRunner:
+    """Same interface as KernelTimer, no events: the step timing runs through
+    this, since an event record between kernels costs a few microseconds of
+    GPU time by itself."""
+
+    def run(self, name, fn, *args, **kw):
+        return fn(*args, **kw)
+
+
+def timed_steps(torch, step, n):
+    """(ms per step, wall seconds) of ``n`` back-to-back plain steps, bracketed
+    by synchronisations."""
+    plain = PlainRunner()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(n):
+        step(plain, i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n, time.perf_counter() - t0
+
+
+def kernel_pass(torch, timer, step, n):
+    """Per-call HIP-event durations over ``n`` further steps."""
+    torch.cuda.synchronize()
+    timer.pending.clear()
+    for i in range(n):
+        step(timer, i)
+    torch.cuda.synchronize()
+    timer.collect()
+
+
 def bench_prefill(args, torch, ssa, W, shared=False):
     """One step = summaries+scores, top-k, block-sparse forward, full forward
     with dropped mass; ``shared`` uses the group-shared selection."""
@@ -113,29 +148,18 @@ def bench_prefill(args, torch, ssa, W, shared=False):
     drop = torch.empty_like(lse_f)
     timer = KernelTimer(torch)
 
-    def step(t):
+    def step(t, i=0):
         t.run("scores", ssa.ssa_block_scores, shape, q, k, summary_out=ksum, scores=scores)
         t.run("topk", select, shape, scores, idx)
         t.run("sparse_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, out=out, lse=lse, shared=shared)
         t.run("full_attn", ssa.ssa_full_attn_fwd_dropped_mass, shape, q, k, v, idx, fb0, fcnt,
               out=out_f, lse=lse_f, dropped=drop, shared=shared)
 
-    for _ in range(args.warmup):
-        step(timer)
-    torch.cuda.synchronize()
-    timer.pending.clear()
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_start.record()
-    for _ in range(args.steps):
-        step(timer)
-    e_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = e_start.elapsed_time(e_end) / args.steps
-    timer.collect()
+    plain = PlainRunner()
+    for i in range(args.warmup):
+        step(plain, i)
+    ms_step, wall = timed_steps(torch, step, args.steps)
+    kernel_pass(torch, timer, step, args.steps)
 
     pairs_sp = w.batch * w.n_q_heads * sparse_useful_pairs(nqb, w.topk, w.block)
     pairs_full = w.batch * w.n_q_heads * full_useful_pairs(fb0 * w.block, fb0 * w.block + rows)
@@ -206,19 +230,11 @@ def bench_decode(args, torch, ssa, W, shared=False):
         t.run("decode_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, workspace=ws, out=out, lse=lse,
               shared=shared)
 
+    plain = PlainRunner()
     for i in range(args.warmup):
-        step(timer, i)
-    torch.cuda.synchronize()
-    timer.pending.clear()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.decode_steps):
-        step(timer, i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.decode_steps
-    timer.collect()
+        step(plain, i)
+    ms_step, _ = timed_steps(torch, step, args.decode_steps)
+    kernel_pass(torch, timer, step, args.decode_steps)
     # Algorithmic bytes from the GPU's own selection (identical inputs in every copy):
     # the union over the query heads of each KV group of selected K and V blocks.
     G = 1 if shared else w.n_q_heads // w.n_kv_heads
@@ -361,26 +377,18 @@ def bench_dash(args, torch, ssa, W, alpha=1.5, gamma=800.0, sigma=1.0, cap=64):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     timer = KernelTimer(torch)
 
-    def step(t):
+    def step(t, i=0):
         t.run("summaries", ssa.ssa_block_summaries_learned, k, qbar, out=ks)
         t.run("scores", ssa.ssa_block_scores, shape, q, None, ks, scores=scores)
         t.run("route", ssa.ssa_entmax_route, shape, scores, alpha, gamma, sigma, idx, bias, None, False)
         t.run("attn", ssa.ssa_block_sparse_attn_fwd_biased, shape, q, k, v, idx, bias, out, lse)
 
-    for _ in range(3):
-        step(timer)
-    torch.cuda.synchronize()
-    timer.pending.clear()
+    plain = PlainRunner()
+    for i in range(3):
+        step(plain, i)
     n = max(1, args.steps // 2)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(n):
-        step(timer)
-    e1.record()
-    torch.cuda.synchronize()
-    timer.collect()
-    ms = e0.elapsed_time(e1) / n
+    ms, _ = timed_steps(torch, step, n)
+    kernel_pass(torch, timer, step, n)
     # useful pairs: every listed block whole, the diagonal block's causal half
     listed = (idx >= 0).sum(-1).double()                       # [b, Hkv, nqb]
     pairs = float(((listed - 1) * w.block * w.block + w.block * (w.block + 1) / 2).sum()) * (w.n_q_heads // w.n_kv_heads)
