@@ -43,10 +43,12 @@ struct RowScores {
   __device__ __forceinline__ float operator()(int j) const {
     if (heads == 1) return s0[j];
     double acc = 0.0;
-    for (int h0 = 0; h0 < heads; h0 += 16) {  // 16 loads in flight, then summed in head order
+    for (int h0 = 0; h0 < heads; h0 += 16) {
+      // 16 unconditional loads (past the last head: the last head again), all
+      // in flight before the first is summed; then the sum in head order
       float v[16];
 #pragma unroll
-      for (int x = 0; x < 16; ++x) v[x] = h0 + x < heads ? s0[(size_t)(h0 + x) * hstride + j] : 0.f;
+      for (int x = 0; x < 16; ++x) v[x] = s0[(size_t)min(h0 + x, heads - 1) * hstride + j];
 #pragma unroll
       for (int x = 0; x < 16; ++x)
         if (h0 + x < heads) acc += (double)v[x];
@@ -59,12 +61,17 @@ struct RowScores {
 template <int NPER>
 __device__ __forceinline__ void select_rows(const RowScores& srow, int32_t* __restrict__ orow, int jd,
                                             int need, int lane) {
-  uint32_t key[NPER];
+  // every score is requested before the first is used (rows past the
+  // candidates read candidate 0 and are dropped)
+  float sv[NPER];
 #pragma unroll
   for (int c = 0; c < NPER; ++c) {
     const int j = lane + 64 * c;
-    key[c] = j < jd ? cand_key(srow(j)) : 0u;
+    sv[c] = srow(j < jd ? j : 0);
   }
+  uint32_t key[NPER];
+#pragma unroll
+  for (int c = 0; c < NPER; ++c) key[c] = lane + 64 * c < jd ? cand_key(sv[c]) : 0u;
   uint32_t t = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t trial = t | (1u << bit);
@@ -127,18 +134,17 @@ __device__ __forceinline__ void select_rows_long(const RowScores& srow, int32_t*
 
 // Rows are (b, query head, query block), or (b, KV head, query block) for the
 // group-shared selection (then each wavefront also averages its row).
-template <int NPER>
+template <int NPER, bool SHARED>
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
-                                                          int32_t* __restrict__ idx, Geometry geo, int nrows,
-                                                          int shared) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                                          int32_t* __restrict__ idx, Geometry geo, int nrows) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerWg + wave;
   if (row >= nrows) return;  // whole wavefront leaves together; no block barriers below
   const int i = row % geo.nqb;
   const int jd = (geo.q_offset + i * kBlock) / kBlock;
   const int k = geo.topk;
   RowScores srow;
-  if (shared) {
+  if (SHARED) {
     const int bg = row / geo.nqb;  // b * Hkv + g
     const int b = bg / geo.hkv, g = bg - b * geo.hkv;
     srow.s0 = scores + ((size_t)(b * geo.hq + g * geo.group) * geo.nqb + i) * geo.nkb;
@@ -169,7 +175,7 @@ template <int NPER>
 __global__ __launch_bounds__(256) void select_topk_shared_kernel(const float* __restrict__ scores,
                                                                  int32_t* __restrict__ idx, Geometry geo) {
   extern __shared__ float smean[];  // [jd]: averaged scores of the candidates
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int row = blockIdx.x;
   const int i = row % geo.nqb;
   const int bg = row / geo.nqb;
@@ -219,12 +225,14 @@ hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry&
   }
   const dim3 grid((unsigned)((nrows + kRowsPerWg - 1) / kRowsPerWg)), block(256);
   const int maxjd = (g.q_offset + (g.nqb - 1) * kBlock) / kBlock;  // largest candidate count
-  if (maxjd <= 128)
-    hipLaunchKernelGGL(select_topk_kernel<2>, grid, block, 0, stream, scores, idx, g, (int)nrows, (int)shared);
+  if (shared)  // rows longer than the LDS row of the workgroup variant
+    hipLaunchKernelGGL((select_topk_kernel<0, true>), grid, block, 0, stream, scores, idx, g, (int)nrows);
+  else if (maxjd <= 128)
+    hipLaunchKernelGGL((select_topk_kernel<2, false>), grid, block, 0, stream, scores, idx, g, (int)nrows);
   else if (maxjd <= 512)
-    hipLaunchKernelGGL(select_topk_kernel<8>, grid, block, 0, stream, scores, idx, g, (int)nrows, (int)shared);
+    hipLaunchKernelGGL((select_topk_kernel<8, false>), grid, block, 0, stream, scores, idx, g, (int)nrows);
   else
-    hipLaunchKernelGGL(select_topk_kernel<0>, grid, block, 0, stream, scores, idx, g, (int)nrows, (int)shared);
+    hipLaunchKernelGGL((select_topk_kernel<0, false>), grid, block, 0, stream, scores, idx, g, (int)nrows);
   return hipGetLastError();
 }
 
