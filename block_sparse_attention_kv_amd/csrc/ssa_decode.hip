@@ -54,7 +54,9 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NHB>  // 16-head blocks per KV group: 1 (G <= 16) or 2 (G <= 32)
+// NHB: 16-head blocks per KV group, 1 (G <= 16) or 2 (G <= 32).  LPER: index
+// entries of the group per lane (64 * LPER >= the group's entry count).
+template <int NHB, int LPER>
 __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, float* __restrict__ ws,
                                                                     Geometry geo, int npieces) {
   __shared__ __attribute__((aligned(1024))) uint8_t sKV[kRing][2][kTileBytes];
@@ -78,13 +80,24 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   const uint32_t all_heads = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
 
   // Union of the group's selected blocks: bitmap, ranks, ascending list and
-  // the heads that selected each listed block.
+  // the heads that selected each listed block.  Entry e = lane + 64 t of the
+  // group's index rows is held in register t; every entry (and its bias) is
+  // requested before the first is used.
+  int jv[LPER];
+  float bv[LPER];
+#pragma unroll
+  for (int t = 0; t < LPER; ++t) jv[t] = gidx[min(lane + 64 * t, cap - 1)];
+  if (a.bias) {
+#pragma unroll
+    for (int t = 0; t < LPER; ++t) bv[t] = a.bias[(size_t)bg * geo.topk + min(lane + 64 * t, cap - 1)];
+  }
   for (int w = lane; w < nw; w += 64) bitmap[w] = 0u;
   for (int e = lane; e < cap; e += 64) sHm[e] = 0u;
   wave_sync_lds();
-  for (int e = lane; e < cap; e += 64) {
-    const int j = gidx[e];
-    if (j >= 0 && j < geo.nkb) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+#pragma unroll
+  for (int t = 0; t < LPER; ++t) {
+    const int j = jv[t];
+    if (lane + 64 * t < cap && j >= 0 && j < geo.nkb) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
   }
   wave_sync_lds();
   int nu = 0;
@@ -101,13 +114,15 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
     nu += __shfl(incl, 63, 64);
   }
   wave_sync_lds();
-  for (int e = lane; e < cap; e += 64) {
-    const int j = gidx[e];
-    if (j >= 0 && j < geo.nkb) {
+#pragma unroll
+  for (int t = 0; t < LPER; ++t) {
+    const int e = lane + 64 * t;
+    const int j = jv[t];
+    if (e < cap && j >= 0 && j < geo.nkb) {
       const int r = prefix[j >> 5] + __builtin_popcount(bitmap[j >> 5] & ((1u << (j & 31)) - 1u));
       sBlk[r] = j;
       atomicOr(&sHm[r], a.idx_shared ? all_heads : 1u << (e / geo.topk));
-      if (a.bias) sBias[r] = a.bias[(size_t)bg * geo.topk + e];  // shared row: one entry per block
+      if (a.bias) sBias[r] = bv[t];  // shared row: one entry per block
     }
   }
   wave_sync_lds();
@@ -309,15 +324,36 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(const float* __
   const int lane = threadIdx.x;
   const size_t bh = blockIdx.x;
   const float* part = ws + bh * npieces * kPartialFloats;
-  float M = -__builtin_inff();
-  for (int c = 0; c < npieces; ++c) M = fmaxf(M, part[c * kPartialFloats]);
+  // the first slices' outputs are requested before the maximum is formed
+  constexpr int kChunk = 8;
+  float ov[kChunk];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u) ov[u] = part[min(u, npieces - 1) * kPartialFloats + 2 + lane];
+  // lane c < npieces holds slice c's reference max and sum (npieces <= 64)
+  const int cl = lane < npieces ? lane : npieces - 1;
+  float mc = part[cl * kPartialFloats];
+  const float lc = part[cl * kPartialFloats + 1];
+  if (lane >= npieces) mc = -__builtin_inff();
+  float M = mc;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float fc = mc == -__builtin_inff() ? 0.f : fast_exp2(mc - M);
+  // slices in order: L = sum l_c f_c, O = sum o_c f_c (empty slices weigh 0)
   float L = 0.f, O = 0.f;
-  for (int c = 0; c < npieces; ++c) {
-    const float mc = part[c * kPartialFloats];
-    if (mc == -__builtin_inff()) continue;
-    const float f = fast_exp2(mc - M);
-    L += part[c * kPartialFloats + 1] * f;
-    O += part[c * kPartialFloats + 2 + lane] * f;
+  for (int c0 = 0; c0 < npieces; c0 += kChunk) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) ov[u] = part[min(c0 + u, npieces - 1) * kPartialFloats + 2 + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int c = c0 + u;
+      if (c < npieces) {
+        const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fc), c));
+        L += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lc), c)) * f;
+        O += ov[u] * f;
+      }
+    }
   }
   const float v = O / L;
   const __bf16 bv = (__bf16)v;
@@ -334,12 +370,21 @@ hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometr
   if (nwg == 0) return hipSuccess;
   const size_t dyn =
       (2 * (size_t)((g.nkb + 31) / 32) + 2 * (size_t)g.group * g.topk + (size_t)g.topk) * sizeof(uint32_t);
-  if (g.group <= 16)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<1>, dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace, g,
-                       npieces);
+  const int cap = a.idx_shared ? g.topk : g.group * g.topk;  // index entries per group
+  if (cap > kDecodeMaxList) return hipErrorInvalidValue;
+  const bool short_list = cap <= 64 * 8;
+  if (g.group <= 16 && short_list)
+    hipLaunchKernelGGL((attn_decode_partial_kernel<1, 8>), dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace,
+                       g, npieces);
+  else if (g.group <= 16)
+    hipLaunchKernelGGL((attn_decode_partial_kernel<1, kDecodeMaxList / 64>), dim3((unsigned)nwg), dim3(64), dyn,
+                       stream, a, workspace, g, npieces);
+  else if (g.group <= 32 && short_list)
+    hipLaunchKernelGGL((attn_decode_partial_kernel<2, 8>), dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace,
+                       g, npieces);
   else if (g.group <= 32)
-    hipLaunchKernelGGL(attn_decode_partial_kernel<2>, dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace, g,
-                       npieces);
+    hipLaunchKernelGGL((attn_decode_partial_kernel<2, kDecodeMaxList / 64>), dim3((unsigned)nwg), dim3(64), dyn,
+                       stream, a, workspace, g, npieces);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
