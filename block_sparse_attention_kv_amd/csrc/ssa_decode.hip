@@ -29,6 +29,7 @@ namespace ssa {
 namespace {
 
 constexpr int kRing = kDecodeRing;  // K/V block slots per wavefront (kRing - 1 in flight while computing)
+constexpr int kListChunk = 8;       // index entries per lane read at once
 static_assert(kRing >= 2 && (kRing - 1) * 16 <= 63, "in-flight block loads must fit the vmcnt counter");
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -54,9 +55,22 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// NHB: 16-head blocks per KV group, 1 (G <= 16) or 2 (G <= 32).  LPER: index
-// entries of the group per lane (64 * LPER >= the group's entry count).
-template <int NHB, int LPER>
+// Chunk ch of a group's index entries (and, with a bias row, their biases):
+// entry 64 * kListChunk * ch + lane + 64 t into register t, all requested
+// before any is used (entries past the end read the last one).
+__device__ __forceinline__ void load_list_chunk(const int32_t* __restrict__ gidx, const float* __restrict__ brow,
+                                                int cap, int ch, int lane, int (&jv)[kListChunk],
+                                                float (&bv)[kListChunk]) {
+#pragma unroll
+  for (int t = 0; t < kListChunk; ++t) jv[t] = gidx[min(64 * kListChunk * ch + lane + 64 * t, cap - 1)];
+  if (brow) {
+#pragma unroll
+    for (int t = 0; t < kListChunk; ++t) bv[t] = brow[min(64 * kListChunk * ch + lane + 64 * t, cap - 1)];
+  }
+}
+
+// NHB: 16-head blocks per KV group, 1 (G <= 16) or 2 (G <= 32).
+template <int NHB>
 __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, float* __restrict__ ws,
                                                                     Geometry geo, int npieces) {
   __shared__ __attribute__((aligned(1024))) uint8_t sKV[kRing][2][kTileBytes];
@@ -80,24 +94,40 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   const uint32_t all_heads = G >= 32 ? 0xffffffffu : ((1u << G) - 1u);
 
   // Union of the group's selected blocks: bitmap, ranks, ascending list and
-  // the heads that selected each listed block.  Entry e = lane + 64 t of the
-  // group's index rows is held in register t; every entry (and its bias) is
-  // requested before the first is used.
-  int jv[LPER];
-  float bv[LPER];
+  // the heads that selected each listed block.  The group's index entries are
+  // read in chunks of 64 * kListChunk: entry e = 64 * kListChunk * ch +
+  // lane + 64 t of chunk ch is held in register t, and a chunk's entries (and
+  // their biases) are all requested before the first is used.  A list of one
+  // chunk is read once for both passes.
+  const int nchunk = (cap + 64 * kListChunk - 1) / (64 * kListChunk);
+  const float* brow = a.bias ? a.bias + (size_t)bg * geo.topk : nullptr;  // shared rows only
+  int jv[kListChunk];
+  float bv[kListChunk];
+  load_list_chunk(gidx, brow, cap, 0, lane, jv, bv);
+  // Q^T as the B operand (requested after the index entries, so that waiting
+  // for those leaves it in flight): column = head 16*hb + l16, k-slots = d 32*ks + 8*g4 .. +8.
+  bf16x8 qop[NHB][2];
 #pragma unroll
-  for (int t = 0; t < LPER; ++t) jv[t] = gidx[min(lane + 64 * t, cap - 1)];
-  if (a.bias) {
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int hh = 16 * hb + l16;
 #pragma unroll
-    for (int t = 0; t < LPER; ++t) bv[t] = a.bias[(size_t)bg * geo.topk + min(lane + 64 * t, cap - 1)];
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hh < G) v = *reinterpret_cast<const u32x4*>(a.q + (size_t)(head0 + hh) * kHeadDim + 32 * ks + 8 * g4);
+      qop[hb][ks] = as_bf16x8(v);
+    }
   }
   for (int w = lane; w < nw; w += 64) bitmap[w] = 0u;
   for (int e = lane; e < cap; e += 64) sHm[e] = 0u;
   wave_sync_lds();
+  for (int ch = 0; ch < nchunk; ++ch) {
+    if (ch > 0) load_list_chunk(gidx, brow, cap, ch, lane, jv, bv);
 #pragma unroll
-  for (int t = 0; t < LPER; ++t) {
-    const int j = jv[t];
-    if (lane + 64 * t < cap && j >= 0 && j < geo.nkb) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+    for (int t = 0; t < kListChunk; ++t) {
+      const int j = jv[t];
+      if (64 * kListChunk * ch + lane + 64 * t < cap && j >= 0 && j < geo.nkb)
+        atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+    }
   }
   wave_sync_lds();
   int nu = 0;
@@ -114,33 +144,24 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
     nu += __shfl(incl, 63, 64);
   }
   wave_sync_lds();
+  for (int ch = 0; ch < nchunk; ++ch) {
+    if (nchunk > 1) load_list_chunk(gidx, brow, cap, ch, lane, jv, bv);
 #pragma unroll
-  for (int t = 0; t < LPER; ++t) {
-    const int e = lane + 64 * t;
-    const int j = jv[t];
-    if (e < cap && j >= 0 && j < geo.nkb) {
-      const int r = prefix[j >> 5] + __builtin_popcount(bitmap[j >> 5] & ((1u << (j & 31)) - 1u));
-      sBlk[r] = j;
-      atomicOr(&sHm[r], a.idx_shared ? all_heads : 1u << (e / geo.topk));
-      if (a.bias) sBias[r] = bv[t];  // shared row: one entry per block
+    for (int t = 0; t < kListChunk; ++t) {
+      const int e = 64 * kListChunk * ch + lane + 64 * t;
+      const int j = jv[t];
+      if (e < cap && j >= 0 && j < geo.nkb) {
+        const int r = prefix[j >> 5] + __builtin_popcount(bitmap[j >> 5] & ((1u << (j & 31)) - 1u));
+        sBlk[r] = j;
+        atomicOr(&sHm[r], a.idx_shared ? all_heads : 1u << (e / geo.topk));
+        if (brow) sBias[r] = bv[t];  // shared row: one entry per block
+      }
     }
   }
   wave_sync_lds();
   const int u0 = (int)(((int64_t)nu * piece) / npieces);
   const int u1 = (int)(((int64_t)nu * (piece + 1)) / npieces);
 
-  // Q^T as the B operand: column = head 16*hb + l16, k-slots = d 32*ks + 8*g4 .. +8.
-  bf16x8 qop[NHB][2];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const int hh = 16 * hb + l16;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hh < G) v = *reinterpret_cast<const u32x4*>(a.q + (size_t)(head0 + hh) * kHeadDim + 32 * ks + 8 * g4);
-      qop[hb][ks] = as_bf16x8(v);
-    }
-  }
   f32x4 o[NHB][4];
   float m[NHB], l[NHB];
 #pragma unroll
@@ -158,8 +179,8 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   const size_t kvoff = (size_t)bg * geo.seq_kv * kHeadDim;
-  const uint16_t* kbase = a.k + kvoff;
-  const uint16_t* vbase = a.v + kvoff;
+  const uint16_t* kbase = uniform_ptr(a.k + kvoff);
+  const uint16_t* vbase = uniform_ptr(a.v + kvoff);
   const float c = geo.scale_log2;
   const int pos = geo.q_offset;  // absolute position of the query token
 
@@ -370,21 +391,12 @@ hipError_t launch_attn_decode(const AttnArgs& a, float* workspace, const Geometr
   if (nwg == 0) return hipSuccess;
   const size_t dyn =
       (2 * (size_t)((g.nkb + 31) / 32) + 2 * (size_t)g.group * g.topk + (size_t)g.topk) * sizeof(uint32_t);
-  const int cap = a.idx_shared ? g.topk : g.group * g.topk;  // index entries per group
-  if (cap > kDecodeMaxList) return hipErrorInvalidValue;
-  const bool short_list = cap <= 64 * 8;
-  if (g.group <= 16 && short_list)
-    hipLaunchKernelGGL((attn_decode_partial_kernel<1, 8>), dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace,
-                       g, npieces);
-  else if (g.group <= 16)
-    hipLaunchKernelGGL((attn_decode_partial_kernel<1, kDecodeMaxList / 64>), dim3((unsigned)nwg), dim3(64), dyn,
-                       stream, a, workspace, g, npieces);
-  else if (g.group <= 32 && short_list)
-    hipLaunchKernelGGL((attn_decode_partial_kernel<2, 8>), dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace,
-                       g, npieces);
+  if (g.group <= 16)
+    hipLaunchKernelGGL(attn_decode_partial_kernel<1>, dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace, g,
+                       npieces);
   else if (g.group <= 32)
-    hipLaunchKernelGGL((attn_decode_partial_kernel<2, kDecodeMaxList / 64>), dim3((unsigned)nwg), dim3(64), dyn,
-                       stream, a, workspace, g, npieces);
+    hipLaunchKernelGGL(attn_decode_partial_kernel<2>, dim3((unsigned)nwg), dim3(64), dyn, stream, a, workspace, g,
+                       npieces);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();

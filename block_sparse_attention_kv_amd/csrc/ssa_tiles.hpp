@@ -165,6 +165,16 @@ __device__ __forceinline__ void dma_1k_ragged(const uint16_t* gtile, uint32_t vo
       : "memory", "m0");
 }
 
+// A wave-uniform global pointer, placed in scalar registers (the DMA
+// instructions take their base address from an SGPR pair).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
 }

@@ -152,6 +152,8 @@ DECODE_SMALL = [
     W.Workload("decode_one_key", 2, 4, 4, 1, 1, 64, 64, 3, seed=33),
     W.Workload("decode_65", 1, 6, 2, 1, 65, 64, 64, 1, seed=34),
     W.Workload("decode_long_scan", 1, 2, 1, 1, 64 * 700, 64, 64, 9, seed=35),   # > 512 candidate blocks
+    W.Workload("decode_long_list", 2, 32, 2, 1, 64 * 300 - 17, 64, 64, 40, seed=36),  # 16 x 40 = 640 entries per group
+    W.Workload("decode_g32_list", 1, 64, 2, 1, 64 * 90, 64, 64, 48, seed=37),  # 32 heads per group, 1536 entries
 ]
 
 
