@@ -6,6 +6,10 @@
       -> HBM bytes per dispatch of the attention kernels from FETCH_SIZE / WRITE_SIZE
          counter runs, scaled by what the same counters read for a plain copy of
          known size (the calibration dispatch in the same run)
+  python -m block_sparse_attention_kv_amd.profiling mfma <counter_dir> [--title T] [--command C]
+      -> markdown table of matrix-core utilisation per kernel from one counter run
+         (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+         SQ_INSTS_MFMA, SQ_INSTS_VALU)
 
 Kernel names are matched by substring: attn_group_kernel<NW, true> is the
 full counterpart, attn_group_kernel<NW, false> the block-sparse forward with a
@@ -167,6 +171,61 @@ def traffic(fetch_dir: str, write_dir: str, out_json: str, command: str = ""):
     return res
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU")
+SIMD_NUM = 256 * 4  # compute units x SIMDs per compute unit
+XCD_NUM = 8         # GRBM_GUI_ACTIVE comes summed over the accelerator dies
+
+
+def _counters_per_dispatch(d: str):
+    """kernel class -> dispatch id -> (counter -> summed value, duration ns)."""
+    per = defaultdict(dict)
+    for fpath in _csvs(d, "*counter_collection.csv"):
+        with open(fpath) as f:
+            for r in csv.DictReader(f):
+                cls = classify(r.get("Kernel_Name", ""))
+                if cls is None:
+                    continue
+                ent = per[cls].setdefault(r.get("Dispatch_Id"), [defaultdict(float), 0.0])
+                ent[0][r.get("Counter_Name")] += float(r.get("Counter_Value", 0))
+                ent[1] = float(r.get("End_Timestamp", 0)) - float(r.get("Start_Timestamp", 0))
+    return per
+
+
+def mfma_markdown(d: str, title: str = "", command: str = "") -> str:
+    """Per kernel, averaged over its dispatches: matrix-core busy fraction
+    (busy cycles summed over the SIMDs / (active cycles of one die x SIMDs)),
+    the clock the dispatch ran at (active cycles of one die / duration),
+    executed bf16 matrix flops (MOPS x 512), matrix instructions, and vector
+    instructions issued per matrix instruction."""
+    per = _counters_per_dispatch(d)
+    out = [f"# {title}".rstrip(), ""]
+    if command:
+        out += ["Command:", "", "```", command, "```", ""]
+    out += ["| kernel | dispatches | matrix-core busy % | clock GHz | executed bf16 GFLOP | MFMA instr (M) | "
+            "VALU instr per MFMA instr |",
+            "|---|---|---|---|---|---|---|"]
+    for cls in sorted(per):
+        util, clk, gflop, nmf, ratio = [], [], [], [], []
+        for ctr, dur in per[cls].values():
+            if not all(c in ctr for c in MFMA_COUNTERS) or ctr["SQ_INSTS_MFMA"] <= 0:
+                continue
+            gui = ctr["GRBM_GUI_ACTIVE"] / XCD_NUM
+            if gui <= 0 or dur <= 0:
+                continue
+            util.append(100.0 * ctr["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM))
+            clk.append(gui / dur)
+            gflop.append(ctr["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9)
+            nmf.append(ctr["SQ_INSTS_MFMA"] / 1e6)
+            ratio.append(ctr["SQ_INSTS_VALU"] / ctr["SQ_INSTS_MFMA"])
+        if not util:
+            continue
+        avg = lambda v: sum(v) / len(v)
+        out.append(f"| {cls} | {len(util)} | {avg(util):.1f} | {avg(clk):.2f} | {avg(gflop):.2f} | {avg(nmf):.3f} | "
+                   f"{avg(ratio):.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -179,9 +238,15 @@ def main(argv=None):
     t.add_argument("write_dir")
     t.add_argument("--out", required=True)
     t.add_argument("--command", default="")
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--title", default="")
+    m.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.dir, a.title, a.command))
+    elif a.cmd == "mfma":
+        sys.stdout.write(mfma_markdown(a.dir, a.title, a.command))
     else:
         print(json.dumps(traffic(a.fetch_dir, a.write_dir, a.out, a.command), indent=1))
 
