@@ -315,37 +315,44 @@ __global__ __launch_bounds__(64) void bwd_count_kernel(BwdArgs a, Geometry geo) 
   if (lane == 0) a.pairs[blockIdx.x] = cnt;
 }
 
-// Exclusive scan over key blocks of each group's item counts:
-// item_base[gi, j] = first item of key block j, item_base[gi, nkb] = total;
-// item_key[gi, e] = key block of item e.
+// Exclusive scan over key units of each group's item counts:
+// item_base[gi, u] = first item of key unit u, item_base[gi, nku] = total;
+// item_key[gi, e] = key unit of item e.
 __global__ __launch_bounds__(256) void bwd_items_kernel(BwdArgs a, Geometry geo) {
   __shared__ int sTot[256];
   const int gi = blockIdx.x, tid = threadIdx.x;
   const BwdPlan pl = a.plan;
-  const int per = (geo.nkb + 255) / 256;
-  const int j0 = min(geo.nkb, tid * per), j1 = min(geo.nkb, j0 + per);
-  auto items = [&](int j) {
+  const int nku = (geo.nkb + pl.kpb - 1) / pl.kpb;
+  const int per = (nku + 255) / 256;
+  const int u0 = min(nku, tid * per), u1 = min(nku, u0 + per);
+  auto items = [&](int u) {
+    const int j = u * pl.kpb;  // the unit's first key block
     const int np = a.full ? geo.group * pl.n_blocks(j) : a.pairs[(size_t)gi * geo.nkb + j];
     return (np + pl.P - 1) / pl.P;
   };
   int tot = 0;
-  for (int j = j0; j < j1; ++j) tot += items(j);
+  for (int u = u0; u < u1; ++u) tot += items(u);
   sTot[tid] = tot;
   __syncthreads();
   int base = 0;
   for (int t = 0; t < tid; ++t) base += sTot[t];
   int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
   int* ik = a.item_key + (size_t)gi * pl.max_items;
-  for (int j = j0; j < j1; ++j) {
-    ib[j] = base;
-    const int n = items(j);
-    for (int e = 0; e < n && base + e < pl.max_items; ++e) ik[base + e] = j;  // never exceeds the bound
+  for (int u = u0; u < u1; ++u) {
+    ib[u] = base;
+    const int n = items(u);
+    for (int e = 0; e < n && base + e < pl.max_items; ++e) ik[base + e] = u;  // never exceeds the bound
     base += n;
   }
-  if (tid == 255) ib[geo.nkb] = base;
+  if (tid == 255) ib[nku] = base;
 }
 
-__global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometry geo) {
+// KPB key blocks per work item (1: block-sparse, 2: full), two waves of 32
+// keys per block; the waves share every pair's Q and dO tiles.
+template <int KPB>
+__global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometry geo) {
+  constexpr int NW = 2 * KPB;                      // waves
+  constexpr int kLoadsPerPair = 2 * (8 / NW) + 1;  // per wave: its Q and dO tile slices and one row
   __shared__ __attribute__((aligned(1024))) uint8_t sQ[kRing][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sO[kRing][kTileBytes];  // dO tiles
   __shared__ __attribute__((aligned(256))) float sL[kRing][kBlock];          // LSE (log2 units)
@@ -360,20 +367,25 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
   const int nslots = gridDim.x / ngroups;
   const int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
   const int* item_key = a.item_key + (size_t)gi * pl.max_items;
-  const int total = __builtin_amdgcn_readfirstlane(min(ib[geo.nkb], pl.max_items));
+  const int nku = (geo.nkb + KPB - 1) / KPB;
+  const int total = __builtin_amdgcn_readfirstlane(min(ib[nku], pl.max_items));
   const int b = gi / geo.hkv, g = gi - b * geo.hkv;
-  TileOffsets<2, 0> toff;
+  const int kblk = wave >> 1, kw = wave & 1;  // this wave's key block within the unit, and 32-key half
+  TileOffsets<NW, 0> toff;
   toff.init(lane, wave);
   const size_t rows_pad = (size_t)a.qb_count * kBlock;
   const float c = geo.scale_log2;
-  // items in key-block order, dealt round-robin to this group's workgroups
+  // items in key-unit order, dealt round-robin to this group's workgroups
   for (int li = blockIdx.x / ngroups; li < total; li += nslots) {
-  const int j = __builtin_amdgcn_readfirstlane(item_key[li]);
-  const int p_lo = (li - ib[j]) * pl.P;
-  const int pairs_j = a.full ? G * pl.n_blocks(j) : a.pairs[(size_t)gi * geo.nkb + j];
+  const int ku = __builtin_amdgcn_readfirstlane(item_key[li]);
+  const int j0 = ku * KPB;        // the unit's first key block: its pairs are the item's
+  const int j = j0 + kblk;        // this wave's key block
+  const bool kvalid = j < geo.nkb;
+  const int p_lo = (li - ib[ku]) * pl.P;
+  const int pairs_j = a.full ? G * pl.n_blocks(j0) : a.pairs[(size_t)gi * geo.nkb + j0];
   const int npairs = __builtin_amdgcn_readfirstlane(min(pl.P, pairs_j - p_lo));
-  const int ifirst = pl.first_block(j);
-  __syncthreads();  // both waves are done with the previous item's buffers and pair list
+  const int ifirst = pl.first_block(j0);
+  __syncthreads();  // every wave is done with the previous item's buffers and pair list
 
   if (!a.full) {
     // this item's pairs: numbers p_lo .. p_lo + npairs - 1 of key block j, in
@@ -382,7 +394,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
       int before = 0;  // pairs of the query blocks already passed
       for (int i0 = ifirst; i0 < pl.hi && before < p_lo + npairs; i0 += 64) {
         const int ii = i0 + lane;
-        const uint32_t bits = ii < pl.hi ? a.mask[((size_t)gi * geo.nkb + j) * geo.nqb + ii] : 0u;
+        const uint32_t bits = ii < pl.hi ? a.mask[((size_t)gi * geo.nkb + j0) * geo.nqb + ii] : 0u;
         const int cnt = __builtin_popcount(bits);
         int incl = cnt;
 #pragma unroll
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
 
   // this wave's 32 keys as MFMA B operands (rows past seq_kv re-read a valid
   // row; such keys lie in the future of every query and are masked)
-  const int key = j * kBlock + 32 * wave + l32;
+  const int key = j * kBlock + 32 * kw + l32;
   const int krow = min(key, geo.seq_kv - 1);
   bf16x8 kop[4], vop[4];
   load_row_op(a.k + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, kop);
@@ -435,7 +447,9 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
     const int orow0 = (ii - a.qb_begin) * kBlock;
     tile_load(a.dout + ((size_t)bh * a.rows_out + orow0) * kHeadDim, a.rows_out - orow0, sO[buf], lane, toff);
     const size_t prow = (size_t)bh * rows_pad + orow0;
-    if (wave == 0)
+    // every wave requests one row (with four waves each row twice, same bytes),
+    // so that all waves count the same loads per pair
+    if (kw == 0)
       dma_row64(a.lse2 + prow, lds_addr(sL[buf]), lane);
     else
       dma_row64(a.delta + prow, lds_addr(sD[buf]), lane);
@@ -459,9 +473,9 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
     constexpr int buf = decltype(BUF)::value;
     int ii, hh;
     pair_of(p, ii, hh);
-    // this wave's share of pair p landed (pair p+1's 9 requests may be in flight)
+    // this wave's share of pair p landed (pair p+1's requests may be in flight)
     if (p + 1 < npairs)
-      wait_vmem<9>();
+      wait_vmem<kLoadsPerPair>();
     else
       wait_vmem<0>();
     __syncthreads();  // every wave's share; every wave is done with pair p-1
@@ -470,7 +484,10 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
     const uint8_t* tO = sO[buf];
     const float* tL = sL[buf];
     const float* tD = sD[buf];
-    const bool diag = j == (geo.q_offset + ii * kBlock) / kBlock;
+    const int dblk = (geo.q_offset + ii * kBlock) / kBlock;  // the query block's diagonal key block
+    // a later block of the unit may lie wholly in this query block's future
+    if (!kvalid || j > dblk) return;
+    const bool diag = j == dblk;
     int kpos = key - (geo.q_offset + ii * kBlock);  // key position relative to the block's first row
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -538,14 +555,15 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometr
     if (p0 + 1 < npairs) step(B1{}, p0 + 1);
     if (p0 + 2 < npairs) step(B2{}, p0 + 2);
   }
-  // partial sums of this item: [2][64 keys][64 d] fp32 (dK unscaled)
-  float* pk = a.part + ((size_t)gi * pl.max_items + li) * (2 * kBlock * kHeadDim);
+  // partial sums of this item's block kblk: [2][64 keys][64 d] fp32 (dK unscaled)
+  if (!kvalid) continue;
+  float* pk = a.part + (((size_t)gi * pl.max_items + li) * KPB + kblk) * (2 * kBlock * kHeadDim);
   float* pv = pk + kBlock * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = 32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3);
+      const int kr = 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
       pk[kr * kHeadDim + 32 * db + l32] = dk[db][r];
       pv[kr * kHeadDim + 32 * db + l32] = dv[db][r];
     }
@@ -563,13 +581,16 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometr
   const int key = rem / (kHeadDim / 4);
   const int c4 = rem - key * (kHeadDim / 4);
   const int j = key / kBlock, kr = key - j * kBlock;
+  const int kpb = a.plan.kpb;
+  const int ku = j / kpb, kblk = j - ku * kpb;  // key unit of block j, and j's place in it
   const int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
-  const int n = min(ib[j + 1], a.plan.max_items) - ib[j];
-  const float* base = a.part + ((size_t)gi * a.plan.max_items + ib[j]) * (2 * kBlock * kHeadDim) +
-                      kr * kHeadDim + 4 * c4;
+  const int n = min(ib[ku + 1], a.plan.max_items) - ib[ku];
+  const size_t item_floats = (size_t)kpb * 2 * kBlock * kHeadDim;
+  const float* base = a.part + ((size_t)gi * a.plan.max_items + ib[ku]) * item_floats +
+                      (size_t)kblk * 2 * kBlock * kHeadDim + kr * kHeadDim + 4 * c4;
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
   for (int e = 0; e < n; ++e) {
-    const float* pe = base + (size_t)e * (2 * kBlock * kHeadDim);
+    const float* pe = base + (size_t)e * item_floats;
     sk += *reinterpret_cast<const f32x4*>(pe);
     sv += *reinterpret_cast<const f32x4*>(pe + kBlock * kHeadDim);
   }
@@ -592,8 +613,9 @@ void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan*
   p.hi = qb_begin + qb_count;
   p.qoffb = g.q_offset / kBlock;
   p.P = full ? kFullPairs : kSparsePairs;
+  p.kpb = full ? 2 : 1;
   long long items = 0;  // every (head, query block) pair present
-  for (int j = 0; j < g.nkb; ++j) items += ((long long)g.group * p.n_blocks(j) + p.P - 1) / p.P;
+  for (int j = 0; j < g.nkb; j += p.kpb) items += ((long long)g.group * p.n_blocks(j) + p.P - 1) / p.P;
   if (!full) {
     // a list names at most min(topk, diag + 1) distinct blocks, so a group has
     // at most G * sum_i min(topk, diag(i) + 1) pairs; cutting each key block's
@@ -622,7 +644,7 @@ void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan*
   off[5] = o;
   o += up(ngroups * (size_t)p.max_items * sizeof(int));
   off[6] = o;
-  o += up(ngroups * (size_t)p.max_items * 2 * kBlock * kHeadDim * sizeof(float));
+  o += up(ngroups * (size_t)p.max_items * p.kpb * 2 * kBlock * kHeadDim * sizeof(float));
   *total = o;
 }
 
@@ -643,7 +665,10 @@ hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t
   // enough workgroups to fill the chip a few times over; each walks its
   // group's items with a stride
   const size_t slots = std::max<size_t>(1, std::min<size_t>((size_t)a.plan.max_items, 2048 / ngroups));
-  hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)(ngroups * slots)), dim3(128), 0, stream, a, g);
+  if (a.plan.kpb == 2)
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)(ngroups * slots)), dim3(256), 0, stream, a, g);
+  else
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, dim3((unsigned)(ngroups * slots)), dim3(128), 0, stream, a, g);
   const size_t threads = ngroups * g.seq_kv * (kHeadDim / 4);
   if (threads > 0)
     hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, g);

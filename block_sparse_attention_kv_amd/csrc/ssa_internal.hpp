@@ -62,14 +62,17 @@ inline size_t decode_workspace_bytes(int batch, int hq, int hkv) {
   return (size_t)batch * hq * decode_pieces(batch, hkv) * kPartialFloats * sizeof(float);
 }
 
-// Backward work items: the (query head, query block) pairs that attend to key
-// block j -- query blocks i in [lo, hi) with diagonal block qoffb + i >= j, in
-// (query block, head) order -- are cut into items of at most P pairs; items
-// are numbered per (batch, KV head) group in key-block order.
+// Backward work items: key blocks are taken kpb at a time (a key unit); the
+// (query head, query block) pairs that attend to the unit's first block j --
+// query blocks i in [lo, hi) with diagonal block qoffb + i >= j, in (query
+// block, head) order -- are cut into items of at most P pairs; items are
+// numbered per (batch, KV head) group in key-unit order.  The unit's later
+// blocks see a subset of those pairs (the rest lie wholly in their future).
 struct BwdPlan {
   int lo, hi;     // query blocks handled
   int qoffb;      // q_offset / B (floor): query block i's diagonal key block is qoffb + i
   int P;          // pairs per item
+  int kpb;        // key blocks per key unit (1: block-sparse, 2: full)
   int max_items;  // items of one group when every pair is present (bound)
 
   __host__ __device__ int first_block(int j) const { return j - qoffb > lo ? j - qoffb : lo; }
@@ -96,9 +99,9 @@ struct BwdArgs {
   float* delta;       // workspace: per-row dO . O, same layout
   uint32_t* mask;     // workspace (sparse): [b*Hkv, nkb, nqb] head bits
   int* pairs;         // workspace (sparse): [b*Hkv, nkb] pairs per key block
-  int* item_base;     // workspace: [b*Hkv, nkb + 1] first item of each key block
-  int* item_key;      // workspace: [b*Hkv, max_items] key block of each item
-  float* part;        // workspace: [b*Hkv, max_items][2][B][d] fp32 partial dK, dV
+  int* item_base;     // workspace: [b*Hkv, nkb + 1] first item of each key unit
+  int* item_key;      // workspace: [b*Hkv, max_items] key unit of each item
+  float* part;        // workspace: [b*Hkv, max_items][kpb][2][B][d] fp32 partial dK, dV
   int qb_begin, qb_count, rows_out;
   BwdPlan plan;
 };
