@@ -9,8 +9,9 @@ token against a 32768-entry cache, 16+1 blocks) is measured in the same run
 and reported under "decode".
 
 Prints ONE JSON line.  ``value`` is tokens/s of the whole step (inputs already
-resident in HBM); per-kernel timings come from HIP events recorded on the
-stream the kernels run on, averaged over the timed steps.
+resident in HBM), from the timed steps, which run with no event between their
+kernels; per-kernel timings come from HIP events recorded around each call on
+the stream the kernels run on, averaged over as many further steps.
 """
 from __future__ import annotations
 
