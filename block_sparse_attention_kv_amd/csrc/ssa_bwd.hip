@@ -20,14 +20,17 @@
 //     key-side kernel reads.  Per tile, transposed as in the forward (a lane
 //     owns one query column):  S^T = K Q^T,  dP^T = V dO^T  (Q, dO in
 //     registers), then dQ^T += K^T dS^T with K^T read transposed from LDS.
-//   * dK/dV kernel: workgroups of 2 waves (32 keys each) walk the work items
-//     of their (batch, KV head) group with a stride; an item is at most P
-//     consecutive (query head, query block) pairs, in (query block, head)
-//     order, of the pairs whose list holds key block j.  Per pair,
-//     untransposed (a lane owns one key column):  S = Q K^T,  dP = dO V^T
-//     (K, V in registers), then dV += P^T dO and dK += dS^T Q with dO, Q read
-//     transposed from LDS.  Each item writes an fp32 partial; a reduce kernel
-//     sums the items of a key block in item order and rounds to bf16.
+//   * dK/dV kernel: workgroups walk the work items of their (batch, KV head)
+//     group with a stride; an item is at most P consecutive (query head,
+//     query block) pairs, in (query block, head) order, of the pairs whose
+//     list holds key block j (block-sparse: 2 waves of 32 keys on block j), or
+//     of every pair of key block j (full: 4 waves on blocks j and j+1, which
+//     share each pair's tiles; block j+1 skips the pairs wholly in its
+//     future).  Per pair, untransposed (a lane owns one key column):
+//     S = Q K^T,  dP = dO V^T (K, V in registers), then dV += P^T dO and
+//     dK += dS^T Q with dO, Q read transposed from LDS.  Each item writes an
+//     fp32 partial per key block; a reduce kernel sums the items of a key
+//     block in item order and rounds to bf16.
 // Both tile loops run a three-buffer ring: the tiles of step t+2 are requested
 // while step t is computed.
 // The pairs of a key block come from a bitmask mask[b, g, j, i] (bit hh: head

@@ -2,8 +2,10 @@
 //
 // Summaries: the mean of each 64-row key block, summed exactly in fp64 and
 // rounded once to fp32.  Scores: fp32 rounding of scale * qbar . kbar, with
-// the dot product accumulated in fp64 from the fp32 summaries, so the top-k
-// decision downstream is taken on correctly rounded fp32 scores.
+// the dot product of exact fp64 products summed in fp64 (on the fp64 matrix
+// instruction), so the top-k decision downstream is taken on fp32 scores
+// that are correctly rounded except within about 2^-50 relative of a
+// rounding boundary.
 // Method: SSA guide (mauroscia.it), "Block-sparse attention e Receptive Field";
 // DashAttention summary, "Etapa 0" (mean summary, cached once complete) and
 // "Etapa 1" (query-vs-summary routing logits).
