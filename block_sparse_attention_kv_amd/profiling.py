@@ -107,6 +107,37 @@ def _csvs(d: str, pattern: str):
     return sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
 
 
+def _bench_line(path: str):
+    """The JSON line bench.py printed (the last line of the log that parses)."""
+    line = None
+    with open(path) as f:
+        for raw in f:
+            raw = raw.strip()
+            if raw.startswith("{"):
+                try:
+                    line = json.loads(raw)
+                except ValueError:
+                    pass
+    return line
+
+
+def bench_comparison(path: str) -> str:
+    """Markdown rows: the same run's HIP-event averages from bench.py for the
+    kernels the trace also times."""
+    b = _bench_line(path)
+    if not b:
+        return ""
+    rows = [("sparse_attn", b["kernels"]["sparse_attn"]["avg_ms"]), ("full_attn", b["kernels"]["full_attn"]["avg_ms"])]
+    if b.get("decode"):
+        rows.append(("decode_attn (decode_attn + decode_combine)", b["decode"]["kernels"]["decode_attn"]["avg_ms"]))
+    out = ["", "The same run's bench.py HIP-event averages (prefill_8k, decode_32k; each event pair brackets one",
+           "call). The trace rows above also count the group-shared legs' calls of the same kernels, and its",
+           "decode_attn row mixes the per-head and the group-shared decode.", "",
+           "| call | avg us |", "|---|---|"]
+    out += [f"| {n} | {ms * 1e3:.2f} |" for n, ms in rows]
+    return "\n".join(out) + "\n"
+
+
 def stats_markdown(d: str, title: str = "", command: str = "") -> str:
     files = _csvs(d, "*kernel_stats.csv")
     if not files:
@@ -233,6 +264,7 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--title", default="")
     s.add_argument("--command", default="")
+    s.add_argument("--bench-log", default="", help="output of the profiled bench.py run, for its own timings")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -245,6 +277,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.dir, a.title, a.command))
+        if a.bench_log:
+            sys.stdout.write(bench_comparison(a.bench_log))
     elif a.cmd == "mfma":
         sys.stdout.write(mfma_markdown(a.dir, a.title, a.command))
     else:
