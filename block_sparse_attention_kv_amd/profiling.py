@@ -6,6 +6,8 @@
       -> HBM bytes per dispatch of the attention kernels from FETCH_SIZE / WRITE_SIZE
          counter runs, scaled by what the same counters read for a plain copy of
          known size (the calibration dispatch in the same run)
+  python -m block_sparse_attention_kv_amd.profiling waits <counter_dir> [--title T] [--command C]
+      -> markdown table of where the waves' cycles go per kernel (SQ cycle counters)
   python -m block_sparse_attention_kv_amd.profiling mfma <counter_dir> [--title T] [--command C]
       -> markdown table of matrix-core utilisation per kernel from one counter run
          (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16,
@@ -257,6 +259,37 @@ def mfma_markdown(d: str, title: str = "", command: str = "") -> str:
     return "\n".join(out) + "\n"
 
 
+WAIT_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                 "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY")
+
+
+def waits_markdown(d: str, title: str = "", command: str = "") -> str:
+    """Where the waves' time goes, per kernel: each SQ cycle counter as a
+    fraction of SQ_WAVE_CYCLES (all in the same quad-cycle units), averaged
+    over the kernel's dispatches."""
+    per = _counters_per_dispatch(d)
+    out = [f"# {title}".rstrip(), ""]
+    if command:
+        out += ["Command:", "", "```", command, "```", ""]
+    out += ["Fractions of the waves' cycles (SQ_WAVE_CYCLES):", "",
+            "| kernel | dispatches | executing any | executing VALU | executing LDS | waiting on a dependency "
+            "(SQ_WAIT_ANY) | ready, waiting to issue (SQ_WAIT_INST_ANY) |",
+            "|---|---|---|---|---|---|---|"]
+    for cls in sorted(per):
+        fr = defaultdict(list)
+        for ctr, _dur in per[cls].values():
+            if not all(c in ctr for c in WAIT_COUNTERS) or ctr["SQ_WAVE_CYCLES"] <= 0:
+                continue
+            for c in WAIT_COUNTERS[1:]:
+                fr[c].append(ctr[c] / ctr["SQ_WAVE_CYCLES"])
+        if not fr:
+            continue
+        avg = lambda v: sum(v) / len(v)
+        out.append(f"| {cls} | {len(fr['SQ_WAIT_ANY'])} | " +
+                   " | ".join(f"{avg(fr[c]):.3f}" for c in WAIT_COUNTERS[1:]) + " |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -270,6 +303,10 @@ def main(argv=None):
     t.add_argument("write_dir")
     t.add_argument("--out", required=True)
     t.add_argument("--command", default="")
+    w = sub.add_parser("waits")
+    w.add_argument("dir")
+    w.add_argument("--title", default="")
+    w.add_argument("--command", default="")
     m = sub.add_parser("mfma")
     m.add_argument("dir")
     m.add_argument("--title", default="")
@@ -281,6 +318,8 @@ def main(argv=None):
             sys.stdout.write(bench_comparison(a.bench_log))
     elif a.cmd == "mfma":
         sys.stdout.write(mfma_markdown(a.dir, a.title, a.command))
+    elif a.cmd == "waits":
+        sys.stdout.write(waits_markdown(a.dir, a.title, a.command))
     else:
         print(json.dumps(traffic(a.fetch_dir, a.write_dir, a.out, a.command), indent=1))
 
