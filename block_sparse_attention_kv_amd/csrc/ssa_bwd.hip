@@ -352,14 +352,16 @@ __global__ __launch_bounds__(256) void bwd_items_kernel(BwdArgs a, Geometry geo)
 
 // KPB key blocks per work item (1: block-sparse, 2: full), two waves of 32
 // keys per block; the waves share every pair's Q and dO tiles.
-template <int KPB>
+// R: pair buffers in the ring (3: the pair after next is requested while a
+// pair is computed; 2: the next one, for less LDS and more workgroups per CU).
+template <int KPB, int R = kRing>
 __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, Geometry geo) {
   constexpr int NW = 2 * KPB;                      // waves
   constexpr int kLoadsPerPair = 2 * (8 / NW) + 1;  // per wave: its Q and dO tile slices and one row
-  __shared__ __attribute__((aligned(1024))) uint8_t sQ[kRing][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sO[kRing][kTileBytes];  // dO tiles
-  __shared__ __attribute__((aligned(256))) float sL[kRing][kBlock];          // LSE (log2 units)
-  __shared__ __attribute__((aligned(256))) float sD[kRing][kBlock];          // D
+  __shared__ __attribute__((aligned(1024))) uint8_t sQ[R][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sO[R][kTileBytes];  // dO tiles
+  __shared__ __attribute__((aligned(256))) float sL[R][kBlock];          // LSE (log2 units)
+  __shared__ __attribute__((aligned(256))) float sD[R][kBlock];          // D
   __shared__ int sPairs[kSparsePairs];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -459,10 +461,9 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
-  static_assert(kRing == 3, "the pair loop is unrolled over a three-buffer ring");
+  static_assert(R == 2 || R == 3, "the pair loop is unrolled over a two- or three-buffer ring");
   if (npairs > 0) issue(B0{}, 0);
-  if (npairs > 1) issue(B1{}, 1);
+  if (R == 3 && npairs > 1) issue(B1{}, 1);
 
   f32x16 dk[2], dv[2];
 #pragma unroll
@@ -476,13 +477,14 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
     constexpr int buf = decltype(BUF)::value;
     int ii, hh;
     pair_of(p, ii, hh);
-    // this wave's share of pair p landed (pair p+1's requests may be in flight)
-    if (p + 1 < npairs)
+    // this wave's share of pair p landed (with three buffers pair p+1's
+    // requests may still be in flight)
+    if (R == 3 && p + 1 < npairs)
       wait_vmem<kLoadsPerPair>();
     else
       wait_vmem<0>();
     __syncthreads();  // every wave's share; every wave is done with pair p-1
-    if (p + 2 < npairs) issue(std::integral_constant<int, (buf + 2) % kRing>{}, p + 2);
+    if (p + R - 1 < npairs) issue(std::integral_constant<int, (buf + R - 1) % R>{}, p + R - 1);
     const uint8_t* tQ = sQ[buf];
     const uint8_t* tO = sO[buf];
     const float* tL = sL[buf];
@@ -553,10 +555,10 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
         }
     }
   };
-  for (int p0 = 0; p0 < npairs; p0 += kRing) {
+  for (int p0 = 0; p0 < npairs; p0 += R) {
     step(B0{}, p0);
     if (p0 + 1 < npairs) step(B1{}, p0 + 1);
-    if (p0 + 2 < npairs) step(B2{}, p0 + 2);
+    if (R == 3 && p0 + 2 < npairs) step(std::integral_constant<int, 2 % R>{}, p0 + 2);
   }
   // partial sums of this item's block kblk: [2][64 keys][64 d] fp32 (dK unscaled)
   if (!kvalid) continue;
@@ -671,7 +673,7 @@ hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t
   if (a.plan.kpb == 2)
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)(ngroups * slots)), dim3(256), 0, stream, a, g);
   else
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, dim3((unsigned)(ngroups * slots)), dim3(128), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<1, 2>), dim3((unsigned)(ngroups * slots)), dim3(128), 0, stream, a, g);
   const size_t threads = ngroups * g.seq_kv * (kHeadDim / 4);
   if (threads > 0)
     hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, g);
