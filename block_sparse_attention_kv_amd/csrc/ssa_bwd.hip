@@ -50,7 +50,8 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSparsePairs = 64;   // pairs per work item, block-sparse backward
 constexpr int kFullPairs = 128;    // pairs per work item, full backward
-constexpr int kRing = 3;           // tile buffers per loop
+constexpr int kRing = 3;           // tile buffers per loop (full dK/dV)
+constexpr int kDqRing = 2;         // K/V tile buffers of the dQ loop
 
 // ---------------------------------------------------------------------------- index inversion
 
@@ -137,9 +138,12 @@ __device__ __forceinline__ void map_unit_bwd(int w, int n_groups, int per_group,
   }
 }
 
+// R: K/V tile buffers in the ring (3: the tile after next is requested while a
+// tile is computed; 2: the next one, for less LDS and more workgroups per CU).
+template <int R>
 __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry geo) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sK[kRing][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV[kRing][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[R][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[R][kTileBytes];
   __shared__ int sList[2][kMaxTopk];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,10 +190,9 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  using B2 = std::integral_constant<int, 2>;
-  static_assert(kRing == 3, "the tile loop is unrolled over a three-buffer ring");
+  static_assert(R == 2 || R == 3, "the tile loop is unrolled over a two- or three-buffer ring");
   if (nt > 0) issue(B0{}, 0);
-  if (nt > 1) issue(B1{}, 1);
+  if (R == 3 && nt > 1) issue(B1{}, 1);
   // per-row constants: LSE in log2 units (+inf where the row has no keys or
   // does not exist, so that every P is 0) and D = dO . O
   const float dsum = sum_xor32(dot_row_ops(dop, oop));
@@ -209,13 +212,14 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
   auto step = [&](auto BUF, int t) {
     constexpr int buf = decltype(BUF)::value;
     const int j = tile_block(t);
-    // this wave's share of tile t landed (tile t+1's 8 requests may be in flight)
-    if (t + 1 < nt)
+    // this wave's share of tile t landed (with three buffers tile t+1's 8
+    // requests may still be in flight)
+    if (R == 3 && t + 1 < nt)
       wait_vmem<8>();
     else
       wait_vmem<0>();
     __syncthreads();  // every wave's share; every wave is done with tile t-1
-    if (t + 2 < nt) issue(std::integral_constant<int, (buf + 2) % kRing>{}, t + 2);
+    if (t + R - 1 < nt) issue(std::integral_constant<int, (buf + R - 1) % R>{}, t + R - 1);
     const uint8_t* tK = sK[buf];
     const uint8_t* tV = sV[buf];
     const bool diag = j == jd;
@@ -272,10 +276,10 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
           dq[db] = mfma32(read_tile_tr(tK, 32 * kb + 16 * ap, db, lane), as_bf16x8(pds[ap]), dq[db]);
     }
   };
-  for (int t0 = 0; t0 < nt; t0 += kRing) {
+  for (int t0 = 0; t0 < nt; t0 += R) {
     step(B0{}, t0);
     if (t0 + 1 < nt) step(B1{}, t0 + 1);
-    if (t0 + 2 < nt) step(B2{}, t0 + 2);
+    if (R == 3 && t0 + 2 < nt) step(std::integral_constant<int, 2 % R>{}, t0 + 2);
   }
   if (vrow) {
     uint16_t* qp = a.dq + ((size_t)bh * a.rows_out + orow) * kHeadDim;
@@ -666,7 +670,7 @@ hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t
     hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)(ngroups * g.nkb)), dim3(64), 0, stream, a, g);
   }
   hipLaunchKernelGGL(bwd_items_kernel, dim3((unsigned)ngroups), dim3(256), 0, stream, a, g);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)units), dim3(128), 0, stream, a, g);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing>), dim3((unsigned)units), dim3(128), 0, stream, a, g);
   // enough workgroups to fill the chip a few times over; each walks its
   // group's items with a stride
   const size_t slots = std::max<size_t>(1, std::min<size_t>((size_t)a.plan.max_items, 2048 / ngroups));
