@@ -184,12 +184,15 @@ def bench_prefill(args, torch, ssa, W, shared=False):
                      gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
         kernels[name] = e
     dominant = max(kernels, key=lambda n: kernels[n]["avg_ms"])
-    roof = roofline_entry(dominant, kernels[dominant], flops, bytes_alg)
+    roof = roofline_entry(dominant, kernels[dominant], flops, bytes_alg, shared)
     return dict(w=w, ms_step=ms_step, wall=wall, kernels=kernels, roofline=roof, dominant=dominant,
                 tokens_per_s=w.batch * w.seq_q / (ms_step * 1e-3))
 
 
-def roofline_entry(name, e, flops, bytes_alg):
+def roofline_entry(name, e, flops, bytes_alg, shared=False):
+    """Roofline object of one kernel.  The committed counter summary was taken
+    on the per-head selection: the group-shared sparse forward is another
+    kernel, so it gets no traffic figure."""
     if e["bound"] == "mfma":
         ach = e["tflops"]
         r = {"kernel": name, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -198,7 +201,8 @@ def roofline_entry(name, e, flops, bytes_alg):
         ach = e["gbs"]
         r = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_per_launch": bytes_alg[name]}
-    r["traffic"] = measured_traffic(name) if name in ("full_attn", "sparse_attn") else None
+    counted = name == "full_attn" or (name == "sparse_attn" and not shared)
+    r["traffic"] = measured_traffic(name) if counted else None
     return r
 
 
@@ -262,7 +266,9 @@ def bench_decode(args, torch, ssa, W, shared=False):
         "kernels": kern,
         "roofline": {"kernel": "decode_attn", "bound": "hbm", "achieved": kern["decode_attn"]["gbs"],
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kern["decode_attn"]["frac_of_peak"],
-                     "algorithmic_per_launch": attn_bytes, "traffic": measured_traffic("decode_attn")},
+                     "algorithmic_per_launch": attn_bytes,
+                     # counters were taken on the per-head selection (a different union)
+                     "traffic": None if shared else measured_traffic("decode_attn")},
         "cache_copies_rotated": len(copies), "steps": args.decode_steps,
     }
 
