@@ -133,10 +133,39 @@ def bench_comparison(path: str) -> str:
     if b.get("decode"):
         rows.append(("decode_attn (decode_attn + decode_combine)", b["decode"]["kernels"]["decode_attn"]["avg_ms"]))
     out = ["", "The same run's bench.py HIP-event averages (prefill_8k, decode_32k; each event pair brackets one",
-           "call). The trace rows above also count the group-shared legs' calls of the same kernels, and its",
-           "decode_attn row mixes the per-head and the group-shared decode.", "",
+           "call). Unless the run skipped the extra legs (--no-shared --no-backward), the trace rows",
+           "above also count the group-shared legs' calls of the same kernels, which run at the same",
+           "launch shapes.", "",
            "| call | avg us |", "|---|---|"]
     out += [f"| {n} | {ms * 1e3:.2f} |" for n, ms in rows]
+    return "\n".join(out) + "\n"
+
+
+SHAPE_KERNELS = ("sparse_attn", "sparse_attn_shared", "full_attn", "decode_attn", "decode_combine", "bwd_dq",
+                 "bwd_dkv")
+
+
+def shape_markdown(d: str) -> str:
+    """Per kernel and launch shape (workgroups x threads per workgroup), from
+    the per-dispatch trace: a kernel launched at different sizes (the sparse
+    and the full dK/dV backward) gets a row per size."""
+    files = _csvs(d, "*kernel_trace.csv")
+    if not files:
+        return ""
+    per = defaultdict(list)
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            cls = classify(r.get("Kernel_Name", ""))
+            if cls not in SHAPE_KERNELS:
+                continue
+            wg = int(r.get("Workgroup_Size_X", 1) or 1)
+            grid = int(r.get("Grid_Size_X", 0) or 0)
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per[(cls, grid // max(wg, 1), wg)].append(dur)
+    out = ["", "Per launch shape (workgroups x threads per workgroup):", "",
+           "| kernel | workgroups x threads | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (cls, nwg, wg), v in sorted(per.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
+        out.append(f"| {cls} | {nwg} x {wg} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -159,7 +188,7 @@ def stats_markdown(d: str, title: str = "", command: str = "") -> str:
         mn = float(r.get("MinNs", 0)) / 1e3
         mx = float(r.get("MaxNs", 0)) / 1e3
         out.append(f"| {short} | {r.get('Calls')} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {float(r.get('Percentage', 0)):.2f} |")
-    return "\n".join(out) + "\n"
+    return "\n".join(out) + "\n" + shape_markdown(d)
 
 
 def _counter_per_kernel(d: str, counter: str):
