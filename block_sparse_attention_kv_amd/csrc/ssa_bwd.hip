@@ -31,8 +31,10 @@
 //     dK += dS^T Q with dO, Q read transposed from LDS.  Each item writes an
 //     fp32 partial per key block; a reduce kernel sums the items of a key
 //     block in item order and rounds to bf16.
-// Both tile loops run a three-buffer ring: the tiles of step t+2 are requested
-// while step t is computed.
+// The tile loops stream through rings of LDS buffers.  The dQ loop and the
+// block-sparse dK/dV loop use two: the next step's tiles are requested while
+// a step is computed, and the smaller LDS footprint lets more workgroups
+// share a CU.  The full dK/dV loop uses three (requests two steps ahead).
 // The pairs of a key block come from a bitmask mask[b, g, j, i] (bit hh: head
 // g*G+hh lists j for query block i) built from the index rows with atomic
 // ORs (order-independent); the pairs of each key block are then counted from
