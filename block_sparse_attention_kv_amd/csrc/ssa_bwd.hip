@@ -569,15 +569,32 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
   // partial sums of this item's block kblk: [2][64 keys][64 d] fp32 (dK unscaled)
   if (!kvalid) continue;
   float* pk = a.part + (((size_t)gi * pl.max_items + li) * KPB + kblk) * (2 * kBlock * kHeadDim);
-  float* pv = pk + kBlock * kHeadDim;
+  if constexpr (KPB == 1) {
+    // this lane's offset, opaque so that the 32 per-register offsets are
+    // formed here rather than hoisted out of the item loop, where they are
+    // spilled (measured: 4% faster for this kernel, 3% slower for KPB = 2)
+    pk = const_cast<float*>(uniform_ptr(pk));
+    int lo = 4 * hl * kHeadDim + l32;
+    asm volatile("" : "+v"(lo));
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
-      pk[kr * kHeadDim + 32 * db + l32] = dk[db][r];
-      pv[kr * kHeadDim + 32 * db + l32] = dv[db][r];
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int o = lo + (32 * kw + 8 * (r >> 2) + (r & 3)) * kHeadDim + 32 * db;
+        pk[o] = dk[db][r];
+        pk[kBlock * kHeadDim + o] = dv[db][r];
+      }
+  } else {
+    float* pv = pk + kBlock * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 32 * kw + 8 * (r >> 2) + 4 * hl + (r & 3);
+        pk[kr * kHeadDim + 32 * db + l32] = dk[db][r];
+        pv[kr * kHeadDim + 32 * db + l32] = dv[db][r];
+      }
+  }
   }
 }
 
