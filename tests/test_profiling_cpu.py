@@ -1,0 +1,125 @@
+"""Host logic of the rocprofv3 summaries (block_sparse_attention_kv_amd.profiling)
+on small synthetic CSV directories: kernel-name classification, the trace
+tables, the copy-calibrated HBM traffic, and the matrix-core busy fraction."""
+import csv
+import json
+import os
+
+import pytest
+
+from block_sparse_attention_kv_amd import profiling as P
+
+SPARSE = "ssa::(anonymous namespace)::attn_sparse_kernel<false>(ssa::AttnArgs, ssa::Geometry)"
+FULL = "void ssa::(anonymous namespace)::attn_group_kernel<4, true, false>(ssa::AttnArgs, ssa::Geometry)"
+DKV = "void ssa::(anonymous namespace)::attn_bwd_dkv_kernel<1, 2>(ssa::BwdArgs, ssa::Geometry)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=header)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+@pytest.mark.parametrize("name,cls", [
+    (SPARSE, "sparse_attn"),
+    ("ssa::(anonymous namespace)::attn_sparse_kernel<true>(ssa::AttnArgs, ssa::Geometry)", "sparse_attn_biased"),
+    (FULL, "full_attn"),
+    ("void ssa::(anonymous namespace)::attn_group_kernel<4, false, false>(ssa::AttnArgs)", "sparse_attn_shared"),
+    ("void ssa::(anonymous namespace)::attn_group_kernel<4, false, true>(ssa::AttnArgs)", "sparse_attn_biased"),
+    ("_ZN3ssa12_GLOBAL__N_117attn_group_kernelILi4ELb1ELb0EEEvNS_8AttnArgsENS_8GeometryE", "full_attn"),
+    ("_ZN3ssa12_GLOBAL__N_117attn_group_kernelILi4ELb0ELb0EEEvNS_8AttnArgsENS_8GeometryE", "sparse_attn_shared"),
+    ("ssa::(anonymous namespace)::attn_sparse_early_stop_kernel(ssa::AttnArgs)", "sparse_attn_early_stop"),
+    ("void ssa::(anonymous namespace)::attn_decode_partial_kernel<1>(ssa::AttnArgs, float*)", "decode_attn"),
+    (DKV, "bwd_dkv"),
+    (COPY, "copy"),
+    ("void at::native::vectorized_elementwise_kernel<4>", None),
+])
+def test_classify(name, cls):
+    assert P.classify(name) == cls
+
+
+def test_stats_and_shapes(tmp_path):
+    d = str(tmp_path / "trace")
+    _write_csv(os.path.join(d, "run_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+               [{"Name": FULL, "Calls": 2, "TotalDurationNs": 600000, "AverageNs": 300000, "Percentage": 75.0,
+                 "MinNs": 290000, "MaxNs": 310000},
+                {"Name": DKV, "Calls": 3, "TotalDurationNs": 200000, "AverageNs": 66666.7, "Percentage": 25.0,
+                 "MinNs": 10000, "MaxNs": 120000}])
+    trace_rows = []
+    for k, (name, grid, wg, dur) in enumerate([(FULL, 1024 * 256, 256, 290000), (FULL, 1024 * 256, 256, 310000),
+                                               (DKV, 100 * 128, 128, 10000), (DKV, 100 * 128, 128, 70000),
+                                               (DKV, 50 * 256, 256, 120000)]):
+        trace_rows.append({"Kernel_Name": name, "Start_Timestamp": 1000 * k, "End_Timestamp": 1000 * k + dur,
+                           "Workgroup_Size_X": wg, "Grid_Size_X": grid})
+    _write_csv(os.path.join(d, "run_kernel_trace.csv"),
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Grid_Size_X"], trace_rows)
+    md = P.stats_markdown(d, title="t", command="rocprofv3 ...")
+    assert "| full_attn | 2 | 300.00 | 290.00 | 310.00 | 75.00 |" in md
+    # one row per launch shape; durations averaged per shape
+    assert "| bwd_dkv | 100 x 128 | 2 | 40.00 | 10.00 | 70.00 |" in md
+    assert "| bwd_dkv | 50 x 256 | 1 | 120.00 | 120.00 | 120.00 |" in md
+    assert "| full_attn | 1024 x 256 | 2 | 300.00 | 290.00 | 310.00 |" in md
+
+
+def _counter_rows(counter, values):
+    """values: [(kernel name, dispatch id, value)], each split over two
+    per-dimension rows as rocprofv3 may report them."""
+    rows = []
+    for name, disp, v in values:
+        for half in (0.25, 0.75):
+            rows.append({"Kernel_Name": name, "Dispatch_Id": disp, "Counter_Name": counter,
+                         "Counter_Value": v * half, "Start_Timestamp": 0, "End_Timestamp": 1000})
+    return rows
+
+
+def test_traffic_calibration(tmp_path):
+    hdr = ["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    # the copy moves COPY_BYTES/2 each way; its counters read half of that on
+    # fetch (factor 2) and exactly it on write (factor 1)
+    copy_kib = P.COPY_BYTES / 2 / 1024
+    fd, wd = str(tmp_path / "f"), str(tmp_path / "w")
+    _write_csv(os.path.join(fd, "x_counter_collection.csv"), hdr,
+               _counter_rows("FETCH_SIZE", [(COPY, 1, copy_kib / 2), (SPARSE, 2, 1000.0), (SPARSE, 3, 3000.0)]))
+    _write_csv(os.path.join(wd, "x_counter_collection.csv"), hdr,
+               _counter_rows("WRITE_SIZE", [(COPY, 1, copy_kib), (SPARSE, 2, 10.0), (SPARSE, 3, 30.0)]))
+    out = str(tmp_path / "traffic.json")
+    res = P.traffic(fd, wd, out, command="c")
+    assert res["_f_scale"] == pytest.approx(2.0)
+    assert res["_w_scale"] == pytest.approx(1.0)
+    e = res["sparse_attn"]
+    assert e["dispatches"] == 2
+    assert e["fetch_kib_per_dispatch"] == pytest.approx(2000.0)
+    assert e["bytes_per_launch"] == round(2000.0 * 1024 * 2 + 20.0 * 1024)
+    assert e["source_sha256_16"] == P.source_hash("sparse_attn")
+    with open(out) as f:
+        assert json.load(f)["sparse_attn"]["bytes_per_launch"] == e["bytes_per_launch"]
+
+
+def test_traffic_needs_calibration(tmp_path):
+    hdr = ["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    fd, wd = str(tmp_path / "f"), str(tmp_path / "w")
+    _write_csv(os.path.join(fd, "x_counter_collection.csv"), hdr, _counter_rows("FETCH_SIZE", [(SPARSE, 2, 1.0)]))
+    _write_csv(os.path.join(wd, "x_counter_collection.csv"), hdr, _counter_rows("WRITE_SIZE", [(SPARSE, 2, 1.0)]))
+    with pytest.raises(SystemExit):
+        P.traffic(fd, wd, str(tmp_path / "t.json"))
+
+
+def test_mfma_busy_fraction(tmp_path):
+    hdr = ["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    # 2000 active cycles on each of the 8 dies over a 1000 ns dispatch (2 GHz);
+    # the matrix cores of all SIMDs busy for a quarter of them
+    gui = 2000.0 * P.XCD_NUM
+    busy = 0.25 * 2000.0 * P.SIMD_NUM
+    rows = []
+    for ctr, v in (("GRBM_GUI_ACTIVE", gui), ("SQ_VALU_MFMA_BUSY_CYCLES", busy),
+                   ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e6), ("SQ_INSTS_MFMA", 2e6), ("SQ_INSTS_VALU", 2.2e7)):
+        rows += _counter_rows(ctr, [(FULL, 7, v)])
+    d = str(tmp_path / "m")
+    _write_csv(os.path.join(d, "x_counter_collection.csv"), hdr, rows)
+    md = P.mfma_markdown(d)
+    assert "| full_attn | 1 | 25.0 | 2.00 | 0.51 | 2.000 | 11.00 |" in md
