@@ -142,26 +142,30 @@ __device__ __forceinline__ void map_unit_bwd(int w, int n_groups, int per_group,
 
 // R: K/V tile buffers in the ring (3: the tile after next is requested while a
 // tile is computed; 2: the next one, for less LDS and more workgroups per CU).
-template <int R>
-__global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry geo) {
+// NH: query heads of one KV group per workgroup (two waves each); with NH = 2
+// (full backward) each K/V tile serves both heads.
+template <int R, int NH>
+__global__ __launch_bounds__(128 * NH, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry geo) {
+  constexpr int kTileReq = 8 / NH;  // requests per wave per tile (its K and V slices)
   __shared__ __attribute__((aligned(1024))) uint8_t sK[R][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[R][kTileBytes];
-  __shared__ int sList[2][kMaxTopk];
+  __shared__ int sList[2 * NH][kMaxTopk];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = geo.group;
   int gi, u;
-  map_unit_bwd(blockIdx.x, geo.batch * geo.hkv, G * a.qb_count, gi, u);
-  const int i = a.qb_begin + a.qb_count - 1 - u / G;  // longest rows first
+  const int GU = G / NH;  // workgroups per (KV group, query block)
+  map_unit_bwd(blockIdx.x, geo.batch * geo.hkv, GU * a.qb_count, gi, u);
+  const int i = a.qb_begin + a.qb_count - 1 - u / GU;  // longest rows first
   const int b = gi / geo.hkv, g = gi - b * geo.hkv;
-  const int h = g * G + (u - (u / G) * G);
+  const int h = g * G + (u - (u / GU) * GU) * NH + (wave >> 1);
   const int bh = b * geo.hq + h;
   const int jd = (geo.q_offset + i * kBlock) / kBlock;
   const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
   const uint16_t* kbase = a.k + kvoff;
   const uint16_t* vbase = a.v + kvoff;
 
-  const int row = i * kBlock + 32 * wave + l32;  // this lane's query row
+  const int row = i * kBlock + 32 * (wave & 1) + l32;  // this lane's query row
   const bool vrow = row < geo.seq_q;
   const int orow = row - a.qb_begin * kBlock;    // its row in the slice-shaped tensors
   int nt = jd + 1;
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
   load_row_op(a.o + srow * kHeadDim, vrow, hl, oop);
   const float lse = vrow ? a.lse[srow] : 0.f;
   auto tile_block = [&](int t) { return a.full ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
-  TileOffsets<2, 0> toff;
+  TileOffsets<2 * NH, 0> toff;
   toff.init(lane, wave);
   // requests of tile t into ring buffer BUF (a compile-time index, so that
   // every LDS address below is a fixed per-lane offset plus an immediate)
@@ -214,10 +218,10 @@ __global__ __launch_bounds__(128, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry
   auto step = [&](auto BUF, int t) {
     constexpr int buf = decltype(BUF)::value;
     const int j = tile_block(t);
-    // this wave's share of tile t landed (with three buffers tile t+1's 8
+    // this wave's share of tile t landed (with three buffers tile t+1's
     // requests may still be in flight)
     if (R == 3 && t + 1 < nt)
-      wait_vmem<8>();
+      wait_vmem<kTileReq>();
     else
       wait_vmem<0>();
     __syncthreads();  // every wave's share; every wave is done with tile t-1
@@ -689,7 +693,10 @@ hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t
     hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)(ngroups * g.nkb)), dim3(64), 0, stream, a, g);
   }
   hipLaunchKernelGGL(bwd_items_kernel, dim3((unsigned)ngroups), dim3(256), 0, stream, a, g);
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing>), dim3((unsigned)units), dim3(128), 0, stream, a, g);
+  if (a.full && g.group % 2 == 0)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing, 2>), dim3((unsigned)(units / 2)), dim3(256), 0, stream, a, g);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing, 1>), dim3((unsigned)units), dim3(128), 0, stream, a, g);
   // enough workgroups to fill the chip a few times over; each walks its
   // group's items with a stride
   const size_t slots = std::max<size_t>(1, std::min<size_t>((size_t)a.plan.max_items, 2048 / ngroups));
