@@ -143,7 +143,7 @@ __device__ __forceinline__ void map_unit_bwd(int w, int n_groups, int per_group,
 // R: K/V tile buffers in the ring (3: the tile after next is requested while a
 // tile is computed; 2: the next one, for less LDS and more workgroups per CU).
 // NH: query heads of one KV group per workgroup (two waves each); with NH = 2
-// (full backward) each K/V tile serves both heads.
+// (full backward, or one list per KV group) each K/V tile serves both heads.
 template <int R, int NH>
 __global__ __launch_bounds__(128 * NH, 2) void attn_bwd_dq_kernel(BwdArgs a, Geometry geo) {
   constexpr int kTileReq = 8 / NH;  // requests per wave per tile (its K and V slices)
@@ -693,7 +693,8 @@ hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t
     hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)(ngroups * g.nkb)), dim3(64), 0, stream, a, g);
   }
   hipLaunchKernelGGL(bwd_items_kernel, dim3((unsigned)ngroups), dim3(256), 0, stream, a, g);
-  if (a.full && g.group % 2 == 0)
+  // heads that walk the same tiles (full, or one list per KV group) pair up
+  if ((a.full || a.idx_shared) && g.group % 2 == 0)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing, 2>), dim3((unsigned)(units / 2)), dim3(256), 0, stream, a, g);
   else
     hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing, 1>), dim3((unsigned)units), dim3(128), 0, stream, a, g);
