@@ -258,12 +258,24 @@ def _row_attention(qrow, keys, vals, scale):
     return (w @ vals) / z, m + math.log(z), logits
 
 
+def _listed_blocks(sel_row):
+    """(position, block) of each block an index row names: its non-negative
+    entries, a block listed twice taken at its first listing.  The selection
+    is a set of blocks ([SSA-guide] "Block-sparse attention e Receptive
+    Field": the chosen blocks), so order and repetition carry no meaning."""
+    seen, out = set(), []
+    for e, j in enumerate(sel_row):
+        j = int(j)
+        if j >= 0 and j not in seen:
+            seen.add(j)
+            out.append((e, j))
+    return out
+
+
 def _allowed_keys(sel_row, pos: int, block: int, seq_kv: int) -> np.ndarray:
-    """Key positions c <= pos whose block is in the selected list."""
+    """Key positions c <= pos whose block is in the selected set."""
     cols = []
-    for j in sel_row:
-        if j < 0:
-            continue
+    for _, j in _listed_blocks(sel_row):
         lo, hi = j * block, min((j + 1) * block, seq_kv, pos + 1)
         if lo < hi:
             cols.append(np.arange(lo, hi))
@@ -544,9 +556,7 @@ def prior_attention(q, k, v, sel, bias, block: int, scale: Optional[float] = Non
                 r0, r1 = i * block, min((i + 1) * block, seq_q)
                 last = q_offset + r1 - 1
                 cols, shift = [], []
-                for e, j in enumerate(sel[bi, g, i]):
-                    if j < 0:
-                        continue
+                for e, j in _listed_blocks(sel[bi, g, i]):
                     c = _allowed_keys([j], last, block, seq_kv)
                     cols.append(c)
                     shift.append(np.full(len(c), bias[bi, g, i, e]))
@@ -652,7 +662,7 @@ def early_stop_order(sel_row, score_row, jd: int):
     [S2O] "Regla de Parada Temprana" (candidate blocks processed in descending
     order of estimated importance) and "Implementacion del Kernel" (a dense
     pass over the query's own segment initialises the softmax state first)."""
-    listed = [int(j) for j in sel_row if j >= 0]
+    listed = [j for _, j in _listed_blocks(sel_row)]
     others = sorted((j for j in listed if j != jd), key=lambda j: _rank_key(float(score_row[j]), j))
     return ([jd] if jd in listed else []) + others
 

@@ -718,6 +718,130 @@ def check_prior_attention(O):
     del rng
 
 
+# ----------------------------------------------------------------------------- per-row branches, list reading
+
+def _masked_lse(q, kk, mask, sc):
+    """Natural log-sum-exp over the allowed keys of each row (torch, float64;
+    -inf where a row allows none)."""
+    qt, kt = tr.t64(q), tr.t64(kk)
+    group = qt.shape[1] // kt.shape[1]
+    logits = torch.matmul(qt, kt.repeat_interleave(group, dim=1).transpose(-1, -2)) * sc
+    return torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1).numpy()
+
+
+def check_full_rows_branch(O):
+    """The per-row evaluation of the full counterpart (rows=...) against torch:
+    SDPA for O, logsumexp for LSE, and the log-sum-exp over the dropped keys for
+    delta; a prefill with a ragged tail and a decode-shaped call."""
+    rng = np.random.default_rng(31)
+    for (b, hq, hkv, n, d, B, k, qo) in [(1, 4, 2, 200, 16, 32, 3, 0),   # 200 rows = 6 blocks + 8
+                                         (2, 4, 1, 1, 8, 32, 4, 299)]:  # one row at position 299
+        seq_kv = qo + n
+        q = bf16_values((b, hq, n, d), rng)
+        kk, v = bf16_values((b, hkv, seq_kv, d), rng), bf16_values((b, hkv, seq_kv, d), rng)
+        sc = float(np.float32(1.0 / math.sqrt(d)))
+        idx = O.select_blocks(O.block_scores(q, kk, B, q_offset=qo), k, B, q_offset=qo)
+        rows = sorted({(bi, h, r) for bi in range(b) for h in (0, hq - 1) for r in (0, n // 2, n - 1)})
+        o_r, l_r, d_r = O.full_attention_dropped_mass(q, kk, v, idx, B, q_offset=qo, rows=rows)
+        causal = tr.causal_mask(n, seq_kv, qo)
+        o_ref, l_ref = tr.sdpa(q, kk, v, causal, sc)
+        drop = causal & ~tr.block_mask_from_idx(idx, n, seq_kv, B, qo)
+        l_drop = _masked_lse(q, kk, drop, sc)
+        for t, (bi, h, r) in enumerate(rows):
+            np.testing.assert_allclose(o_r[t], o_ref[bi, h, r], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(l_r[t], l_ref[bi, h, r], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(d_r[t], math.exp(l_drop[bi, h, r] - l_ref[bi, h, r]), rtol=1e-10, atol=1e-15)
+        if n > B:   # some row of the prefill case must drop keys, or delta is not exercised
+            assert max(d_r) > 0.05
+
+
+def check_early_stop_used_branch(O):
+    """An imposed block count (used=...) attends over the first `used` blocks
+    of the visiting order -- the diagonal, then by coarse score -- which is
+    block-sparse attention over those blocks (SDPA with their mask)."""
+    rng = np.random.default_rng(37)
+    q, k, v = rand_qkv(1, 2, 1, 256, 16, rng)
+    B = 32
+    s = O.block_scores(q, k, B)
+    sel = O.select_blocks(s, 4, B)
+    nqb = 256 // B
+    listed = (sel >= 0).sum(-1)
+    used = np.array([[[rng.integers(1, listed[0, h, i] + 1) for i in range(nqb)] for h in range(2)]])
+    o, lse, u, _ = O.early_stop_attention(q, k, v, s, sel, 0.1, B, used=used)
+    assert np.array_equal(u, used)
+    first = np.full_like(sel, -1)
+    for h in range(2):
+        for i in range(nqb):
+            others = sorted((int(j) for j in sel[0, h, i] if 0 <= j < i), key=lambda j: (-s[0, h, i, j], j))
+            keep = ([i] + others)[: used[0, h, i]]
+            first[0, h, i, : len(keep)] = keep
+    sc = float(np.float32(1.0 / 4.0))
+    o_ref, l_ref = tr.sdpa(q, k, v, tr.block_mask_from_idx(first, 256, 256, B, 0), sc)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref, rtol=1e-12, atol=1e-12)
+
+
+def _scramble_rows(idx, rng):
+    """Each index row shuffled, a -1 put in its middle and its first entry
+    listed once more at the end (width topk + 2): the same set of blocks."""
+    b, h, nqb, k = idx.shape
+    out = np.full((b, h, nqb, k + 2), -1, dtype=idx.dtype)
+    for bi in range(b):
+        for hh in range(h):
+            for i in range(nqb):
+                lst = list(rng.permutation([int(j) for j in idx[bi, hh, i] if j >= 0]))
+                mid = len(lst) // 2
+                row = lst[:mid] + [-1] + lst[mid:] + lst[:1]
+                out[bi, hh, i, : len(row)] = row
+    return out
+
+
+def check_index_row_as_set(O):
+    """An index row names a set of blocks: shuffling it, putting a -1 in its
+    middle and listing a block twice change nothing.  Pinned against SDPA with
+    the mask of the set, and the scrambled rows against the ascending ones in
+    the full counterpart, the prior-biased softmax (a repeated listing's bias
+    is ignored), the early-stopping order and the backward."""
+    rng = np.random.default_rng(41)
+    b, hq, hkv, n, d, B, k = 1, 4, 2, 256, 16, 32, 4
+    q, kk, v = rand_qkv(b, hq, hkv, n, d, rng)
+    sc = float(np.float32(0.25))
+    s = O.block_scores(q, kk, B)
+    idx = O.select_blocks(s, k, B)
+    scr = _scramble_rows(idx, rng)
+    o, lse = O.sparse_attention(q, kk, v, scr, B)
+    o_ref, l_ref = tr.sdpa(q, kk, v, tr.block_mask_from_idx(idx, n, n, B, 0), sc)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref, rtol=1e-12, atol=1e-12)
+    _, _, dm0 = O.full_attention_dropped_mass(q, kk, v, idx, B)
+    _, _, dm1 = O.full_attention_dropped_mass(q, kk, v, scr, B)
+    np.testing.assert_allclose(dm1, dm0, rtol=1e-13, atol=1e-15)
+    for h in range(hq):
+        for i in range(n // B):
+            assert O.early_stop_order(scr[0, h, i], s[0, h, i], i) == O.early_stop_order(idx[0, h, i], s[0, h, i], i)
+    dout = bf16_values((b, hq, n, d), rng)
+    g0 = O.attention_backward(q, kk, v, dout, idx, B)
+    g1 = O.attention_backward(q, kk, v, dout, scr, B)
+    for a0, a1 in zip(g0, g1):
+        np.testing.assert_allclose(a1, a0, rtol=1e-12, atol=1e-13)
+    # prior-biased softmax on group-shared rows: the first listing's bias counts
+    sel_g = idx[:, ::2]
+    bias = rng.standard_normal(sel_g.shape) * (sel_g >= 0)
+    scr_g = np.full(sel_g.shape[:-1] + (k + 2,), -1, dtype=sel_g.dtype)
+    bias_g = np.zeros(scr_g.shape)
+    for g in range(hkv):
+        for i in range(n // B):
+            ent = [(int(j), float(bb)) for j, bb in zip(sel_g[0, g, i], bias[0, g, i]) if j >= 0]
+            order = rng.permutation(len(ent))
+            row = [ent[t] for t in order] + [(ent[order[0]][0], 7.0)]   # repeat with another bias
+            for e, (j, bb) in enumerate(row):
+                scr_g[0, g, i, e], bias_g[0, g, i, e] = j, bb
+    p0 = O.prior_attention(q, kk, v, sel_g, bias, B)
+    p1 = O.prior_attention(q, kk, v, scr_g, bias_g, B)
+    np.testing.assert_allclose(p1[0], p0[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(p1[1], p0[1], rtol=1e-12, atol=1e-13)
+
+
 ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_causal,
               check_select_brute_force, check_select_ties_and_decode, check_sparse_vs_sdpa,
               check_sparse_special_cases, check_sparse_brute_force_loops,
@@ -727,7 +851,8 @@ ALL_CHECKS = [check_block_means, check_scores_token_level, check_scores_gqa_and_
               check_early_stop_loops, check_backward_finite_differences, check_backward_autograd,
               check_backward_identities, check_entmax_hand_example, check_entmax_closed_forms,
               check_learned_summaries, check_entmax_routing, check_routing_support_and_bias,
-              check_prior_attention]
+              check_prior_attention, check_full_rows_branch, check_early_stop_used_branch,
+              check_index_row_as_set]
 
 
 # ----------------------------------------------------------------------------- the pins
@@ -788,6 +913,9 @@ MUTANTS = {
     "routing_includes_diagonal": ("entmax_routing", None),
     "prior_bias_ignores_sigma": ("prior_bias", None),
     "summaries_ignore_learned_query": ("learned_key_summaries", None),
+    "repeated_block_counted_twice": ("_listed_blocks", None),
+    "full_rows_delta_off_by_one_key": ("full_attention_dropped_mass", None),
+    "early_stop_used_ignored": ("early_stop_attention", None),
 }
 
 
@@ -887,6 +1015,33 @@ def _mutant_summaries_mean(k, qbar, block, scale=None):
     return ssa_oracle.key_summaries(k, block)
 
 
+def _mutant_listed_with_repeats(sel_row):
+    return [(e, int(j)) for e, j in enumerate(sel_row) if j >= 0]
+
+
+_orig_full = ssa_oracle.full_attention_dropped_mass
+
+
+def _mutant_full_rows(q, k, v, sel, block, scale=None, q_offset=0, row_range=None, rows=None):
+    """Per-row branch that leaves the row's own key out of delta's complement."""
+    if rows is None:
+        return _orig_full(q, k, v, sel, block, scale=scale, q_offset=q_offset, row_range=row_range)
+    o, lse, delta = _orig_full(q, k, v, sel, block, scale=scale, q_offset=q_offset, rows=rows)
+    q64, k64 = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    sc = float(np.float32(scale if scale is not None else 1.0 / math.sqrt(q64.shape[-1])))
+    g = q64.shape[1] // k64.shape[1]
+    extra = np.array([math.exp(sc * float(q64[bi, h, r] @ k64[bi, h // g, q_offset + r]) - lse[t])
+                      for t, (bi, h, r) in enumerate(rows)])
+    return o, lse, delta + extra
+
+
+_orig_es = ssa_oracle.early_stop_attention
+
+
+def _mutant_es_used(q, k, v, scores, sel, tau, block, scale=None, q_offset=0, used=None):
+    return _orig_es(q, k, v, scores, sel, tau, block, scale=scale, q_offset=q_offset, used=None)
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch, golden_dir):
     attr, fn = MUTANTS[name]
@@ -902,7 +1057,10 @@ def test_mutant_is_caught(name, monkeypatch, golden_dir):
         fn = _mutant_allowed
     fn = {"entmax_linear_for_any_alpha": _mutant_entmax_linear, "routing_includes_diagonal": _mutant_routing_diag,
           "prior_bias_ignores_sigma": _mutant_bias_no_sigma,
-          "summaries_ignore_learned_query": _mutant_summaries_mean}.get(name, fn)
+          "summaries_ignore_learned_query": _mutant_summaries_mean,
+          "repeated_block_counted_twice": _mutant_listed_with_repeats,
+          "full_rows_delta_off_by_one_key": _mutant_full_rows,
+          "early_stop_used_ignored": _mutant_es_used}.get(name, fn)
     if name.startswith("bwd_"):
         fn = _mutant_bwd({"bwd_no_softmax_correction": "no_correction", "bwd_dk_unscaled": "unscaled",
                           "bwd_dv_unnormalised": "unnormalised"}[name])
