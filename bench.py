@@ -147,14 +147,18 @@ def bench_prefill(args, torch, ssa, W, shared=False):
     out_f = torch.empty((w.batch, w.n_q_heads, rows, w.head_dim), dtype=torch.bfloat16, device=dev)
     lse_f = torch.empty((w.batch, w.n_q_heads, rows), dtype=torch.float32, device=dev)
     drop = torch.empty_like(lse_f)
+    # work queues of the persistent attention launches (zeroed once, left zeroed by every call)
+    ws_sp = torch.zeros((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD),), dtype=torch.uint8, device=dev)
+    ws_full = torch.zeros((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_FULL_FWD),), dtype=torch.uint8, device=dev)
     timer = KernelTimer(torch)
 
     def step(t, i=0):
         t.run("scores", ssa.ssa_block_scores, shape, q, k, summary_out=ksum, scores=scores)
         t.run("topk", select, shape, scores, idx)
-        t.run("sparse_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, out=out, lse=lse, shared=shared)
+        t.run("sparse_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, workspace=ws_sp, out=out, lse=lse,
+              shared=shared)
         t.run("full_attn", ssa.ssa_full_attn_fwd_dropped_mass, shape, q, k, v, idx, fb0, fcnt,
-              out=out_f, lse=lse_f, dropped=drop, shared=shared)
+              out=out_f, lse=lse_f, dropped=drop, shared=shared, workspace=ws_full)
 
     plain = PlainRunner()
     for i in range(args.warmup):

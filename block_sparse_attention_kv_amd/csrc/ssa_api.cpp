@@ -222,6 +222,11 @@ ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void
     CHECK_PTR(workspace, 16, fn);
     e = ssa::launch_attn_decode(a, (float*)workspace, g, stream);
   } else {
+    // an optional zeroed workspace of kQueueBytes makes the launch persistent
+    if (workspace && workspace_bytes >= ssa::kQueueBytes) {
+      CHECK_PTR(workspace, 16, fn);
+      a.queue = (int32_t*)workspace;
+    }
     e = ssa::launch_attn_prefill(a, false, g, stream);
   }
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
@@ -229,7 +234,8 @@ ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void
 
 ssa_status_t full_impl(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
                        const int32_t* block_idx, bool shared, int32_t q_block_begin, int32_t q_block_count,
-                       void* out_full, float* lse_full, float* dropped_mass, hipStream_t stream, const char* fn) {
+                       void* out_full, float* lse_full, float* dropped_mass, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, const char* fn) {
   ssa::Geometry g;
   bool empty;
   ssa_status_t st = make_geometry(shape, &g, &empty, fn);
@@ -258,6 +264,10 @@ ssa_status_t full_impl(const ssa_shape_t* shape, const void* q, const void* k, c
   a.qb_count = q_block_count;
   const int64_t end_row = (int64_t)(q_block_begin + q_block_count) * ssa::kBlock;
   a.rows_out = (int)((end_row < g.seq_q ? end_row : g.seq_q) - (int64_t)q_block_begin * ssa::kBlock);
+  if (workspace && workspace_bytes >= ssa::kQueueBytes) {
+    CHECK_PTR(workspace, 16, fn);
+    a.queue = (int32_t*)workspace;
+  }
   hipError_t e = ssa::launch_attn_prefill(a, true, g, stream);
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
@@ -394,10 +404,8 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void
                                             int32_t q_block_count, void* out_full, float* lse_full,
                                             float* dropped_mass, void* workspace, size_t workspace_bytes,
                                             hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return full_impl(shape, q, k, v, block_idx, false, q_block_begin, q_block_count, out_full, lse_full,
-                   dropped_mass, stream, "ssa_full_attn_fwd_dropped_mass");
+                   dropped_mass, workspace, workspace_bytes, stream, "ssa_full_attn_fwd_dropped_mass");
 }
 
 ssa_status_t ssa_full_attn_fwd_dropped_mass_shared(const ssa_shape_t* shape, const void* q, const void* k,
@@ -405,10 +413,8 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass_shared(const ssa_shape_t* shape, con
                                                    int32_t q_block_begin, int32_t q_block_count, void* out_full,
                                                    float* lse_full, float* dropped_mass, void* workspace,
                                                    size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   return full_impl(shape, q, k, v, block_idx, true, q_block_begin, q_block_count, out_full, lse_full,
-                   dropped_mass, stream, "ssa_full_attn_fwd_dropped_mass_shared");
+                   dropped_mass, workspace, workspace_bytes, stream, "ssa_full_attn_fwd_dropped_mass_shared");
 }
 
 ssa_status_t ssa_block_sparse_attn_fwd_early_stop(const ssa_shape_t* shape, const void* q, const void* k,
@@ -452,6 +458,7 @@ size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {
   if (make_geometry(shape, &g, &empty, "ssa_workspace_bytes") != SSA_OK) return SIZE_MAX;
   if (empty) return 0;
   if (op == SSA_OP_SPARSE_FWD && g.seq_q == 1) return ssa::decode_workspace_bytes(g.batch, g.hq, g.hkv);
+  if (op == SSA_OP_SPARSE_FWD || op == SSA_OP_FULL_FWD) return ssa::kQueueBytes;
   if (op == SSA_OP_SPARSE_BWD || op == SSA_OP_FULL_BWD) {
     ssa::BwdPlan plan;
     size_t off[7], need;

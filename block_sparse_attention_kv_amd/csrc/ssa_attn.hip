@@ -237,6 +237,27 @@ __device__ __forceinline__ void map_unit(int w, int n_groups, int per_group, int
   }
 }
 
+// Persistent launches: workgroup b first takes unit b of the static order,
+// then further units from share x = b % nx of a work queue in the caller's
+// workspace: units G + x, G + x + nx, ... (G workgroups), which keeps a
+// share's units on the KV groups map_unit gives XCD x when the workgroups are
+// dealt to the XCDs round-robin.  Each share has its own counter; a
+// workgroup's first ticket past the share's units ends it, and the share's
+// last such ticket (the counter has then seen every workgroup of the share
+// for the last time) returns the counter to zero.
+__device__ __forceinline__ int queue_next(int32_t* q, int nx, int n_units, int lane) {
+  const int G = (int)gridDim.x, b = (int)blockIdx.x, x = b % nx;
+  const int share = G + x < n_units ? (n_units - G - x + nx - 1) / nx : 0;  // dynamic units of share x
+  const int members = (G - x + nx - 1) / nx;                               // workgroups of share x
+  int t = 0;
+  if (lane == 0) {
+    t = __hip_atomic_fetch_add(q + x * kQueueStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == share + members - 1) __hip_atomic_store(q + x * kQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  t = __builtin_amdgcn_readfirstlane(t);
+  return t < share ? G + x + nx * t : -1;
+}
+
 // Tile loop of the block-sparse forward.  The LDS buffers arrive as distinct
 // restrict pointers so that, once inlined, the compiler can tell a K read from
 // an in-flight V load (and the tile list from both) and waits only for the
@@ -272,84 +293,85 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
   }
 }
 
-// Block-sparse forward: one wavefront per unit, private K and V buffers.
+// Block-sparse forward: a wavefront per unit, private K and V buffers.  With
+// a work queue the launch is persistent: each wavefront takes units until the
+// queue is drained; otherwise unit = workgroup.
 // BIAS: each listed block's logits are shifted by its entry of a.bias.
 template <bool BIAS>
 __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry geo) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[kTileBytes];
   __shared__ int sList[kMaxTopk];
+  __shared__ int sTmp[kMaxTopk];
   __shared__ float sBias[BIAS ? kMaxTopk : 1];
   const int lane = threadIdx.x, hl = lane >> 5, l32 = lane & 31;
   const int G = geo.group;
-  int gi, u;
-  map_unit(blockIdx.x, geo.batch * geo.hkv, G * a.qb_count, gi, u);
-  const int i = a.qb_begin + a.qb_count - 1 - u / G;  // longest rows first
-  const int b = gi / geo.hkv, g = gi - b * geo.hkv;
-  const int h = g * G + (u - (u / G) * G);
-  const int bh = b * geo.hq + h;
-  const int jd = (geo.q_offset + i * kBlock) / kBlock;
-  const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
-
-  // index row (per query head, or per KV group when shared) and Q requested
-  // together, so their latencies overlap
-  // The diagonal block ends every valid (ascending) list, so its tile is
-  // requested before the list is read, and visited first.
+  const int n_groups = geo.batch * geo.hkv, per_group = G * a.qb_count;
+  int w = (int)blockIdx.x;
   TileOffsets<1, 0> toff;
   toff.init(lane, 0);
-  tile_load(a.k + kvoff + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sK, lane, toff);
-  tile_load(a.v + kvoff + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sV, lane, toff);
-  const int irow = a.idx_shared ? gi : bh;
-  int iv[4];
-  load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
-  float bv[4];
-  if (BIAS) load_value_row(a.bias + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, bv);
-  bf16x8 qop[2][4];
-  load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
-  int nt = BIAS ? compact_index_row(iv, bv, geo.topk, jd, sList, sBias, lane)
-                : compact_index_row(iv, geo.topk, jd, sList, lane);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const bool has_diag = nt > 0 && __builtin_amdgcn_readfirstlane(sList[nt - 1]) == jd;
-  if (has_diag) {
-    // rotate: diagonal first, then the others in list order
-    int jv[kMaxTopk / 64];
-    float bw[kMaxTopk / 64];
+  while (w >= 0) {
+    int gi, u;
+    map_unit(w, n_groups, per_group, gi, u);
+    const int i = a.qb_begin + a.qb_count - 1 - u / G;  // longest rows first
+    const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+    const int h = g * G + (u - (u / G) * G);
+    const int bh = b * geo.hq + h;
+    const int jd = (geo.q_offset + i * kBlock) / kBlock;
+    const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
+
+    // The diagonal block comes first on every valid list, so its tile is
+    // requested before the list is read; the index row (per query head, or
+    // per KV group when shared) and Q are requested together.
+    tile_load(a.k + kvoff + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sK, lane, toff);
+    tile_load(a.v + kvoff + (size_t)jd * kBlock * kHeadDim, geo.seq_kv - jd * kBlock, sV, lane, toff);
+    const int irow = a.idx_shared ? gi : bh;
+    int iv[4];
+    load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (BIAS) load_value_row(a.bias + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, bv);
+    bf16x8 qop[2][4];
+    load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
+    const int nt = canonical_index_row<BIAS>(iv, bv, geo.topk, jd, sList, sBias, sTmp, lane);
+    const bool has_diag = nt > 0 && __builtin_amdgcn_readfirstlane(sList[nt - 1]) == jd;
+    if (has_diag) {
+      // rotate: diagonal first, then the others in ascending order
+      int jv[kMaxTopk / 64];
+      float bw[kMaxTopk / 64];
 #pragma unroll
-    for (int cc = 0; cc < kMaxTopk / 64; ++cc) {
-      const int e = lane + 64 * cc;
-      jv[cc] = e < nt ? sList[(e + nt - 1) % nt] : 0;
-      if (BIAS) bw[cc] = e < nt ? sBias[(e + nt - 1) % nt] : 0.f;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int cc = 0; cc < kMaxTopk / 64; ++cc) {
+        const int e = lane + 64 * cc;
+        jv[cc] = e < nt ? sList[(e + nt - 1) % nt] : 0;
+        if (BIAS) bw[cc] = e < nt ? sBias[(e + nt - 1) % nt] : 0.f;
+      }
+      wave_lds_sync();
 #pragma unroll
-    for (int cc = 0; cc < kMaxTopk / 64; ++cc) {
-      const int e = lane + 64 * cc;
-      if (e < nt) {
-        sList[e] = jv[cc];
-        if (BIAS) sBias[e] = bw[cc];
+      for (int cc = 0; cc < kMaxTopk / 64; ++cc) {
+        const int e = lane + 64 * cc;
+        if (e < nt) {
+          sList[e] = jv[cc];
+          if (BIAS) sBias[e] = bw[cc];
+        }
       }
     }
+    UnitState st;
+    init_state(st);
+    wait_vmem<0>();  // Q, the list, and the diagonal tile
+    wave_lds_sync();
+    if (!has_diag && nt > 0) {  // a list without its diagonal: the prefetched tile is not used
+      const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
+      tile_load(a.k + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK, lane, toff);
+      tile_load(a.v + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV, lane, toff);
+      wait_vmem<0>();
+      __builtin_amdgcn_wave_barrier();
+    }
+    sparse_tiles<BIAS>(sK, sV, sList, sBias, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd,
+                       geo.q_offset + i * kBlock, geo.scale_log2, qop, st, lane, l32, hl);
+    unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
+    if (!a.queue) break;
+    wait_lds_reads();  // the next unit's tile requests overwrite sK and sV
+    w = queue_next(a.queue, a.n_xcc, n_groups * per_group, lane);
   }
-  UnitState st;
-  init_state(st);
-  wait_vmem<0>();  // Q, the list, and the diagonal tile
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (!has_diag && nt > 0) {  // a list without its diagonal: the prefetched tile is not used
-    const int j0 = __builtin_amdgcn_readfirstlane(sList[0]);
-    tile_load(a.k + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK, lane, toff);
-    tile_load(a.v + kvoff + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV, lane, toff);
-    wait_vmem<0>();
-    __builtin_amdgcn_wave_barrier();
-  }
-  sparse_tiles<BIAS>(sK, sV, sList, sBias, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd,
-                     geo.q_offset + i * kBlock, geo.scale_log2, qop, st, lane, l32, hl);
-  unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
 }
 
 // Block-sparse forward with early stopping.  One wavefront per unit, as
@@ -391,7 +413,7 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
   load_index_row(a.idx + ((size_t)bh * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
   bf16x8 qop[2][4];
   load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
-  const int n = compact_index_row(iv, geo.topk, jd, sList, lane);
+  const int n = canonical_index_row<false>(iv, nullptr, geo.topk, jd, sList, nullptr, sOrder, lane);
   // visiting order: the diagonal block, then the rest by (score desc, index asc)
   const float* srow = scores + ((size_t)bh * geo.nqb + i) * geo.nkb;
   int has_diag = 0;
@@ -489,77 +511,96 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
   __shared__ __attribute__((aligned(1024))) uint8_t sK[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[2][kTileBytes];
   __shared__ int sList[NW][kMaxTopk];
+  __shared__ int sTmp[NW][kMaxTopk];
   __shared__ float sBias[BIAS ? NW : 1][BIAS ? kMaxTopk : 1];
+  __shared__ int sUnit;
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = geo.group, GS = G / NW;
-  int gi, u;
-  map_unit(blockIdx.x, geo.batch * geo.hkv, GS * a.qb_count, gi, u);
-  const int i = a.qb_begin + a.qb_count - 1 - u / GS;
-  const int b = gi / geo.hkv, g = gi - b * geo.hkv;
-  const int h = g * G + (u - (u / GS) * GS) * NW + wave;
-  const int bh = b * geo.hq + h;
-  const int jd = (geo.q_offset + i * kBlock) / kBlock;
-  const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
-  const uint16_t* kbase = a.k + kvoff;
-  const uint16_t* vbase = a.v + kvoff;
-
-  // index row (per query head, or per KV group when shared) and Q requested
-  // together, so their latencies overlap
-  const int irow = a.idx_shared ? gi : bh;
-  int iv[4];
-  load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
-  float bv[4];
-  if (BIAS) load_value_row(a.bias + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, bv);
-  bf16x8 qop[2][4];
-  load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
-  const int nsel = BIAS ? compact_index_row(iv, bv, geo.topk, jd, sList[wave], sBias[BIAS ? wave : 0], lane)
-                        : compact_index_row(iv, geo.topk, jd, sList[wave], lane);
-  // tiles walked: 0..jd (full), or the shared list (identical in every wave)
-  const int nt = FULL ? jd + 1 : nsel;
-  auto tile_block = [&](int t) { return FULL ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
+  const int n_groups = geo.batch * geo.hkv, per_group = GS * a.qb_count;
+  // next unit of the workgroup: wave 0 takes it from the queue, the others read it from LDS
+  auto next_unit = [&]() -> int {
+    if (wave == 0) {
+      const int t = queue_next(a.queue, a.n_xcc, n_groups * per_group, lane);
+      if (lane == 0) sUnit = t;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(sUnit);
+  };
+  int w = (int)blockIdx.x;
   TileOffsets<NW, 0> toff;
   toff.init(lane, wave);
-  if (nt > 0) {  // first tile requested before waiting for Q, so the two latencies overlap
-    const int j0 = tile_block(0);
-    tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK[0], lane, toff);
-    tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV[0], lane, toff);
-  }
-  UnitState st;
-  init_state(st);
-  wait_vmem<0>();
-  __builtin_amdgcn_wave_barrier();
-  const float c = geo.scale_log2;
-  const int pos0 = geo.q_offset + i * kBlock;
-  int sel_ptr = 0;
-  int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
-  for (int t = 0; t < nt; ++t) {
-    const int j = tile_block(t);
-    wait_vmem<0>();   // this wave's share of tile t landed
-    __syncthreads();  // ... every wave's share; and every wave is done with tile t-1
-    if (t + 1 < nt) {
-      const int jn = tile_block(t + 1);
-      const size_t off = (size_t)jn * kBlock * kHeadDim;
-      const int nv = geo.seq_kv - jn * kBlock;
-      tile_load(kbase + off, nv, sK[(t + 1) & 1], lane, toff);
-      tile_load(vbase + off, nv, sV[(t + 1) & 1], lane, toff);
+  while (w >= 0) {
+    int gi, u;
+    map_unit(w, n_groups, per_group, gi, u);
+    const int i = a.qb_begin + a.qb_count - 1 - u / GS;
+    const int b = gi / geo.hkv, g = gi - b * geo.hkv;
+    const int h = g * G + (u - (u / GS) * GS) * NW + wave;
+    const int bh = b * geo.hq + h;
+    const int jd = (geo.q_offset + i * kBlock) / kBlock;
+    const size_t kvoff = (size_t)gi * geo.seq_kv * kHeadDim;
+    const uint16_t* kbase = a.k + kvoff;
+    const uint16_t* vbase = a.v + kvoff;
+
+    // index row (per query head, or per KV group when shared) and Q requested
+    // together, so their latencies overlap
+    const int irow = a.idx_shared ? gi : bh;
+    int iv[4];
+    load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (BIAS) load_value_row(a.bias + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, bv);
+    bf16x8 qop[2][4];
+    load_q(a.q + (size_t)bh * geo.seq_q * kHeadDim, i, geo.seq_q, l32, hl, qop);
+    const int nsel =
+        canonical_index_row<BIAS>(iv, bv, geo.topk, jd, sList[wave], sBias[BIAS ? wave : 0], sTmp[wave], lane);
+    // tiles walked: 0..jd (full), or the shared list (identical in every wave)
+    const int nt = FULL ? jd + 1 : nsel;
+    auto tile_block = [&](int t) { return FULL ? t : __builtin_amdgcn_readfirstlane(sList[wave][t]); };
+    if (nt > 0) {  // first tile requested before waiting for Q, so the two latencies overlap
+      const int j0 = tile_block(0);
+      tile_load(kbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sK[0], lane, toff);
+      tile_load(vbase + (size_t)j0 * kBlock * kHeadDim, geo.seq_kv - j0 * kBlock, sV[0], lane, toff);
     }
-    bool selected = true;
-    if (FULL) {
-      selected = (nxt == t);
-      if (selected) {
-        ++sel_ptr;
-        nxt = sel_ptr < nsel ? __builtin_amdgcn_readfirstlane(sList[wave][sel_ptr]) : -1;
+    UnitState st;
+    init_state(st);
+    wait_vmem<0>();
+    __builtin_amdgcn_wave_barrier();
+    const float c = geo.scale_log2;
+    const int pos0 = geo.q_offset + i * kBlock;
+    int sel_ptr = 0;
+    int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
+    for (int t = 0; t < nt; ++t) {
+      const int j = tile_block(t);
+      wait_vmem<0>();   // this wave's share of tile t landed
+      __syncthreads();  // ... every wave's share; and every wave is done with tile t-1
+      if (t + 1 < nt) {
+        const int jn = tile_block(t + 1);
+        const size_t off = (size_t)jn * kBlock * kHeadDim;
+        const int nv = geo.seq_kv - jn * kBlock;
+        tile_load(kbase + off, nv, sK[(t + 1) & 1], lane, toff);
+        tile_load(vbase + off, nv, sV[(t + 1) & 1], lane, toff);
       }
+      bool selected = true;
+      if (FULL) {
+        selected = (nxt == t);
+        if (selected) {
+          ++sel_ptr;
+          nxt = sel_ptr < nsel ? __builtin_amdgcn_readfirstlane(sList[wave][sel_ptr]) : -1;
+        }
+      }
+      f32x16 s[2][2];
+      tile_scores(sK[t & 1], qop, l32, hl, s);
+      u32x4 pk[2][2][2];
+      const float b2 = BIAS ? sBias[BIAS ? wave : 0][BIAS ? t : 0] * kLog2eF : 0.f;
+      tile_softmax<FULL, BIAS>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c, nullptr, b2);
+      tile_pv(sV[t & 1], pk, st, lane);
     }
-    f32x16 s[2][2];
-    tile_scores(sK[t & 1], qop, l32, hl, s);
-    u32x4 pk[2][2][2];
-    const float b2 = BIAS ? sBias[BIAS ? wave : 0][BIAS ? t : 0] * kLog2eF : 0.f;
-    tile_softmax<FULL, BIAS>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c, nullptr, b2);
-    tile_pv(sV[t & 1], pk, st, lane);
+    unit_epilogue<FULL>(st, a, geo, bh, i, l32, hl);
+    if (!a.queue) break;
+    wait_lds_reads();
+    __syncthreads();  // every wave is done with the tiles, the lists and the unit slot
+    w = next_unit();
   }
-  unit_epilogue<FULL>(st, a, geo, bh, i, l32, hl);
 }
 
 }  // namespace
@@ -573,29 +614,55 @@ hipError_t launch_attn_early_stop(const AttnArgs& a, const float* scores, float 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream) {
-  const size_t units = (size_t)g.batch * g.hq * a.qb_count;
+// Compute units of the current device (cached per device id).
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  }
+  return n;
+}
+
+// Grid of a launch: one workgroup per unit, or with a work queue as many
+// workgroups as fit on the device at once (`per_cu` per compute unit).
+static unsigned prefill_grid(AttnArgs& a, size_t units_per_group, int per_cu) {
+  if (!a.queue) return (unsigned)units_per_group;
+  const int cus = device_cus();
+  const size_t resident = (size_t)cus * per_cu;
+  const unsigned grid = (unsigned)(units_per_group < resident ? units_per_group : resident);
+  a.n_xcc = grid < (unsigned)kMaxXcc ? (int)grid : kMaxXcc;
+  return grid;
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& args, bool full, const Geometry& g, hipStream_t stream) {
+  const size_t units = (size_t)g.batch * g.hq * args.qb_count;
   if (units == 0) return hipSuccess;
+  AttnArgs a = args;
   const bool bias = !full && a.bias != nullptr;
   if (!full && !(a.idx_shared && g.group % 4 == 0)) {
-    // per-head lists (or groups too small to share): one wavefront per unit
+    // per-head lists (or groups too small to share): a wavefront per unit, 8 per compute unit
+    const unsigned grid = prefill_grid(a, units, 8);
     if (bias)
-      hipLaunchKernelGGL(attn_sparse_kernel<true>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+      hipLaunchKernelGGL(attn_sparse_kernel<true>, dim3(grid), dim3(64), 0, stream, a, g);
     else
-      hipLaunchKernelGGL(attn_sparse_kernel<false>, dim3((unsigned)units), dim3(64), 0, stream, a, g);
+      hipLaunchKernelGGL(attn_sparse_kernel<false>, dim3(grid), dim3(64), 0, stream, a, g);
   } else if (!full) {
     // group-shared lists: four heads of a group share every tile
+    const unsigned grid = prefill_grid(a, units / 4, 2);
     if (bias)
-      hipLaunchKernelGGL((attn_group_kernel<4, false, true>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a,
-                         g);
+      hipLaunchKernelGGL((attn_group_kernel<4, false, true>), dim3(grid), dim3(256), 0, stream, a, g);
     else
-      hipLaunchKernelGGL((attn_group_kernel<4, false>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
+      hipLaunchKernelGGL((attn_group_kernel<4, false>), dim3(grid), dim3(256), 0, stream, a, g);
   } else if (g.group % 4 == 0) {
-    hipLaunchKernelGGL((attn_group_kernel<4, true>), dim3((unsigned)(units / 4)), dim3(256), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_group_kernel<4, true>), dim3(prefill_grid(a, units / 4, 2)), dim3(256), 0, stream, a, g);
   } else if (g.group % 2 == 0) {
-    hipLaunchKernelGGL((attn_group_kernel<2, true>), dim3((unsigned)(units / 2)), dim3(128), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_group_kernel<2, true>), dim3(prefill_grid(a, units / 2, 4)), dim3(128), 0, stream, a, g);
   } else {
-    hipLaunchKernelGGL((attn_group_kernel<1, true>), dim3((unsigned)units), dim3(64), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_group_kernel<1, true>), dim3(prefill_grid(a, units, 8)), dim3(64), 0, stream, a, g);
   }
   return hipGetLastError();
 }

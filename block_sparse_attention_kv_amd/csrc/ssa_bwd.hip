@@ -83,18 +83,13 @@ __global__ __launch_bounds__(64) void bwd_mask_kernel(const int32_t* __restrict_
   const int jd = (geo.q_offset + i * kBlock) / kBlock;
   int iv[kMaxTopk / 64];
   load_index_row(idx + (size_t)row * geo.topk, geo.topk, lane, iv);
-  int first_neg = geo.topk;
-#pragma unroll
-  for (int c = 0; c < kMaxTopk / 64; ++c) {
-    const int e = lane + 64 * c;
-    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < geo.topk && iv[c] < 0);
-    if (neg != 0ull && first_neg == geo.topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
-  }
+  // the row is read as the set it names: a -1 or out-of-range entry is
+  // skipped wherever it stands, and a repeated block sets the same bit
 #pragma unroll
   for (int c = 0; c < kMaxTopk / 64; ++c) {
     const int e = lane + 64 * c;
     const int j = iv[c];
-    if (e < first_neg && j >= 0 && j <= jd)
+    if (e < geo.topk && j >= 0 && j <= jd)
       atomicOr(mask + ((size_t)gi * geo.nkb + j) * geo.nqb + i, (uint32_t)bits);
   }
 }
@@ -150,6 +145,7 @@ __global__ __launch_bounds__(128 * NH, 2) void attn_bwd_dq_kernel(BwdArgs a, Geo
   __shared__ __attribute__((aligned(1024))) uint8_t sK[R][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[R][kTileBytes];
   __shared__ int sList[2 * NH][kMaxTopk];
+  __shared__ int sTmp[2 * NH][kMaxTopk];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = geo.group;
@@ -173,7 +169,7 @@ __global__ __launch_bounds__(128 * NH, 2) void attn_bwd_dq_kernel(BwdArgs a, Geo
     const int irow = a.idx_shared ? gi : bh;
     int iv[kMaxTopk / 64];
     load_index_row(a.idx + ((size_t)irow * geo.nqb + i) * geo.topk, geo.topk, lane, iv);
-    nt = compact_index_row(iv, geo.topk, jd, sList[wave], lane);
+    nt = canonical_index_row<false>(iv, nullptr, geo.topk, jd, sList[wave], nullptr, sTmp[wave], lane);
   }
   bf16x8 qop[4], dop[4], oop[4];
   load_row_op(a.q + ((size_t)bh * geo.seq_q + (vrow ? row : 0)) * kHeadDim, vrow, hl, qop);

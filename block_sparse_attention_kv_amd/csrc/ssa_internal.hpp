@@ -33,7 +33,16 @@ struct AttnArgs {
   int qb_begin;      // first query block handled
   int qb_count;      // number of query blocks handled
   int rows_out;      // rows per (b, h) in the output tensors
+  int32_t* queue;    // prefill: work queue of a persistent launch (kQueueBytes, zero between calls), or null
+  int n_xcc;         // shares the queue is split into (1..kMaxXcc), one per XCD
 };
+
+// Work queue of the persistent prefill launches, in the caller's workspace:
+// one counter per share of the launch, each on its own 128-byte line (all
+// zero before and after every call).
+constexpr int kMaxXcc = 8;
+constexpr int kQueueStride = 32;  // int32 words between counters
+constexpr size_t kQueueBytes = (size_t)kMaxXcc * kQueueStride * sizeof(int32_t);
 
 // Decode split: the union of the key blocks that the query heads of one
 // (batch, KV head) group selected is cut into `decode_pieces` equal slices, one

@@ -86,57 +86,74 @@ __device__ __forceinline__ void load_value_row(const float* __restrict__ vrow, i
   }
 }
 
-// Compact an index row (as loaded by load_index_row) into LDS: the entries
-// before the first -1 that name a causal block (j <= jd), in list order.
-// Returns their count.  Whole-wave operation; `lst` has room for kMaxTopk
-// entries.
-__device__ __forceinline__ int compact_index_row(const int iv[4], int topk, int jd, int* lst, int lane) {
-  int first_neg = topk;
-#pragma unroll
-  for (int c = 0; c < kMaxTopk / 64; ++c) {
-    const int e = lane + 64 * c;
-    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < topk && iv[c] < 0);
-    if (neg != 0ull && first_neg == topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
-  }
-  int n = 0;
-#pragma unroll
-  for (int c = 0; c < kMaxTopk / 64; ++c) {
-    const int e = lane + 64 * c;
-    const int j = iv[c];
-    const bool keep = e < first_neg && j >= 0 && j <= jd;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
-    if (keep) lst[n + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = j;
-    n += (int)__builtin_popcountll(m);
-  }
-  return n;
+// LDS writes of this wave are visible to its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// compact_index_row that also carries a per-entry value (bv, loaded like iv)
-// into vlst at the same positions.
-__device__ __forceinline__ int compact_index_row(const int iv[4], const float bv[4], int topk, int jd, int* lst,
-                                                 float* vlst, int lane) {
-  int first_neg = topk;
-#pragma unroll
-  for (int c = 0; c < kMaxTopk / 64; ++c) {
-    const int e = lane + 64 * c;
-    const uint64_t neg = __builtin_amdgcn_ballot_w64(e < topk && iv[c] < 0);
-    if (neg != 0ull && first_neg == topk) first_neg = 64 * c + (int)__builtin_ctzll(neg);
-  }
+// Canonical form of an index row (as loaded by load_index_row) in LDS: the
+// distinct blocks j with 0 <= j <= jd, ascending.  A -1 or any other entry
+// outside [0, jd] is skipped wherever it stands, and a block listed twice is
+// kept once, so the row is read as the set it names.  With VAL each kept block
+// carries the value (bv, loaded like iv) of its first listing into vlst.  A row
+// that is already strictly ascending is only compacted; any other row is
+// ranked entry by entry against a copy in tmp (n^2/64 LDS broadcast reads per
+// lane).  Returns the count.  Whole-wave operation; lst, vlst and tmp have
+// room for kMaxTopk entries (vlst only with VAL).
+template <bool VAL>
+__device__ __forceinline__ int canonical_index_row(const int iv[4], const float bv[4], int topk, int jd, int* lst,
+                                                   float* vlst, int* tmp, int lane) {
   int n = 0;
 #pragma unroll
   for (int c = 0; c < kMaxTopk / 64; ++c) {
     const int e = lane + 64 * c;
     const int j = iv[c];
-    const bool keep = e < first_neg && j >= 0 && j <= jd;
+    const bool keep = e < topk && j >= 0 && j <= jd;
     const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
     if (keep) {
       const int pos = n + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
       lst[pos] = j;
-      vlst[pos] = bv[c];
+      if (VAL) vlst[pos] = bv[c];
     }
     n += (int)__builtin_popcountll(m);
   }
-  return n;
+  wave_lds_sync();
+  bool unordered = false;
+  for (int e = lane + 1; e < n; e += 64) unordered |= lst[e] <= lst[e - 1];
+  if (__builtin_amdgcn_ballot_w64(unordered) == 0ull) return n;
+
+  // General row.  tmp: the listing with later listings of a block replaced
+  // by a sentinel; each first listing then goes to its rank among the
+  // distinct blocks (the values are read before lst and vlst are rewritten).
+  for (int e = lane; e < n; e += 64) {
+    const int j = lst[e];
+    bool first = true;
+    for (int f = 0; f < e; ++f) first = first && lst[f] != j;
+    tmp[e] = first ? j : 0x7fffffff;
+  }
+  float vv[kMaxTopk / 64];
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) vv[c] = (VAL && lane + 64 * c < n) ? vlst[lane + 64 * c] : 0.f;
+  wave_lds_sync();
+  int cnt = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxTopk / 64; ++c) {
+    const int e = lane + 64 * c;
+    if (64 * c >= n) break;
+    const int j = e < n ? tmp[e] : 0x7fffffff;
+    int rank = 0;
+    for (int f = 0; f < n; ++f) rank += tmp[f] < j ? 1 : 0;
+    const bool first = j != 0x7fffffff;
+    cnt += (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(first));
+    if (first) {
+      lst[rank] = j;
+      if (VAL) vlst[rank] = vv[c];
+    }
+  }
+  wave_lds_sync();
+  return cnt;
 }
 
 // One direct-to-LDS load: every lane fetches the 16 bytes at gtile + voff and

@@ -123,6 +123,45 @@ def _require_gpu(*tensors):
             raise ValueError("libssa expects contiguous tensors")
 
 
+BF16, F32, I32, U8 = torch.bfloat16, torch.float32, torch.int32, torch.uint8
+
+
+def _validate(fn: str, **spec):
+    """Check every given tensor's dtype, exact shape and device against what the
+    entry point reads or writes for this Shape (spec: name -> (tensor or None,
+    dtype, shape or None for any)), then that they are contiguous GPU tensors.
+    A mismatch raises ValueError before anything reaches the library."""
+    dev = None
+    for name, (t, dtype, shp) in spec.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{fn}: {name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected {dtype}")
+        if shp is not None and tuple(t.shape) != tuple(int(x) for x in shp):
+            raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shp)}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{fn}: {name} is on {t.device}, the other tensors on {dev}")
+    _require_gpu(*(t for t, _, _ in spec.values()))
+
+
+def _dims(shape: "Shape"):
+    """(b, Hq, Hkv, seq_q, seq_kv, d, nqb, nkb, topk) of a Shape."""
+    return (shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.seq_q, shape.seq_kv, shape.head_dim,
+            n_blocks(shape.seq_q, shape.block), n_blocks(shape.seq_kv, shape.block), shape.topk)
+
+
+def _full_rows(shape: "Shape", q_block_begin: int, q_block_count: Optional[int]):
+    nqb = n_blocks(shape.seq_q, shape.block)
+    if q_block_count is None:
+        q_block_count = nqb - q_block_begin
+    rows = max(0, min(shape.seq_q, (q_block_begin + q_block_count) * shape.block) - q_block_begin * shape.block)
+    return q_block_count, rows
+
+
 def make_shape(q: torch.Tensor, kv_heads: int, seq_kv: int, *, block: int = 64, topk: int = 16,
                scale: float = 0.0, causal: int = 1) -> Shape:
     """Shape for Q [b, Hq, seq_q, d] against a K/V of ``seq_kv`` rows; the query
@@ -143,7 +182,9 @@ def ssa_workspace_bytes(shape: Shape, op: int) -> int:
 
 def ssa_block_summaries(k: torch.Tensor, *, block: int = 64) -> torch.Tensor:
     """Key-block summaries fp32 [b, Hkv, nkb, d] of bf16 K [b, Hkv, seq_kv, d]."""
-    _require_gpu(k)
+    _validate("ssa_block_summaries", k=(k, BF16, None))
+    if k.dim() != 4:
+        raise ValueError(f"ssa_block_summaries: k must be [b, Hkv, seq_kv, d], got shape {tuple(k.shape)}")
     b, hkv, n, d = k.shape
     shape = Shape(batch=b, n_q_heads=hkv, n_kv_heads=hkv, seq_q=n, seq_kv=n, q_offset=0,
                   head_dim=d, block=block, topk=1, causal=1, scale=0.0)
@@ -157,8 +198,11 @@ def ssa_block_summaries_learned(k: torch.Tensor, qbar: torch.Tensor, *, block: i
                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Chunk summaries fp32 [b, Hkv, nkb, d] from a learned query qbar fp32
     [Hkv, d] (softmax-weighted key average per block; scale 0 = 1/sqrt(d))."""
-    _require_gpu(k, qbar, out)
+    if k.dim() != 4:
+        raise ValueError(f"ssa_block_summaries_learned: k must be [b, Hkv, seq_kv, d], got shape {tuple(k.shape)}")
     b, hkv, n, d = k.shape
+    _validate("ssa_block_summaries_learned", k=(k, BF16, None), qbar=(qbar, F32, (hkv, d)),
+              out=(out, F32, (b, hkv, n_blocks(n, block), d)))
     shape = Shape(batch=b, n_q_heads=hkv, n_kv_heads=hkv, seq_q=n, seq_kv=n, q_offset=0,
                   head_dim=d, block=block, topk=1, causal=1, scale=float(scale))
     if out is None:
@@ -173,7 +217,9 @@ def ssa_entmax_route(shape: Shape, scores: torch.Tensor, alpha: float, gamma: fl
     """(block_idx int32 [b, Hkv, nqb, topk], block_bias fp32 [b, Hkv, nqb, topk],
     weights fp32 [b, Hkv, nqb, nkb] or None): alpha-entmax routing averaged over
     each KV group."""
-    _require_gpu(scores, idx, bias, weights)
+    b_, hq_, hkv_, _, _, _, nqb_, nkb_, k_ = _dims(shape)
+    _validate("ssa_entmax_route", scores=(scores, F32, (b_, hq_, nqb_, nkb_)), idx=(idx, I32, (b_, hkv_, nqb_, k_)),
+              bias=(bias, F32, (b_, hkv_, nqb_, k_)), weights=(weights, F32, (b_, hkv_, nqb_, nkb_)))
     b, hkv = shape.batch, shape.n_kv_heads
     nqb, nkb = n_blocks(shape.seq_q, shape.block), n_blocks(shape.seq_kv, shape.block)
     if idx is None:
@@ -193,14 +239,18 @@ def ssa_block_sparse_attn_fwd_biased(shape: Shape, q, k, v, block_idx, block_bia
     """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q]) of the block-sparse
     forward over group-shared lists with a per-block logit bias (decode uses a
     workspace, allocated here when not given)."""
-    _require_gpu(q, k, v, block_idx, block_bias, out, lse, workspace)
+    b_, hq_, hkv_, sq_, skv_, d_, nqb_, _, k_ = _dims(shape)
+    _validate("ssa_block_sparse_attn_fwd_biased", q=(q, BF16, (b_, hq_, sq_, d_)), k=(k, BF16, (b_, hkv_, skv_, d_)),
+              v=(v, BF16, (b_, hkv_, skv_, d_)), block_idx=(block_idx, I32, (b_, hkv_, nqb_, k_)),
+              block_bias=(block_bias, F32, (b_, hkv_, nqb_, k_)), out=(out, BF16, (b_, hq_, sq_, d_)),
+              lse=(lse, F32, (b_, hq_, sq_)), workspace=(workspace, U8, None))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     need = ssa_workspace_bytes(shape, SSA_OP_SPARSE_FWD)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ssa_block_sparse_attn_fwd_biased", load_library().ssa_block_sparse_attn_fwd_biased(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(block_bias), _ptr(out), _ptr(lse),
@@ -214,7 +264,12 @@ def ssa_block_scores(shape: Shape, q: torch.Tensor, k: Optional[torch.Tensor] = 
     """(scores [b, Hq, nqb, nkb] fp32, k_summary).  With ``k_summary`` given the
     cached summaries are used (K may be None); otherwise they are computed from K
     (into ``summary_out`` when given)."""
-    _require_gpu(q, k, k_summary, summary_out, scores)
+    b_, hq_, hkv_, sq_, skv_, d_, nqb_, nkb_, _ = _dims(shape)
+    _validate("ssa_block_scores", q=(q, BF16, (b_, hq_, sq_, d_)), k=(k, BF16, (b_, hkv_, skv_, d_)),
+              k_summary=(k_summary, F32, (b_, hkv_, nkb_, d_)), summary_out=(summary_out, F32, (b_, hkv_, nkb_, d_)),
+              scores=(scores, F32, (b_, hq_, nqb_, nkb_)))
+    if k is None and k_summary is None:
+        raise ValueError("ssa_block_scores: give k or k_summary")
     summary_is_input = k_summary is not None
     if not summary_is_input:
         k_summary = summary_out if summary_out is not None else torch.empty(
@@ -231,7 +286,8 @@ def ssa_block_scores(shape: Shape, q: torch.Tensor, k: Optional[torch.Tensor] = 
 
 def ssa_select_topk(shape: Shape, scores: torch.Tensor, idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Selected key blocks int32 [b, Hq, nqb, topk], ascending, -1 padded."""
-    _require_gpu(scores, idx)
+    b_, hq_, _, _, _, _, nqb_, nkb_, k_ = _dims(shape)
+    _validate("ssa_select_topk", scores=(scores, F32, (b_, hq_, nqb_, nkb_)), idx=(idx, I32, (b_, hq_, nqb_, k_)))
     if idx is None:
         idx = torch.empty((shape.batch, shape.n_q_heads, n_blocks(shape.seq_q, shape.block), shape.topk),
                           dtype=torch.int32, device=scores.device)
@@ -243,7 +299,9 @@ def ssa_select_topk(shape: Shape, scores: torch.Tensor, idx: Optional[torch.Tens
 def ssa_select_topk_shared(shape: Shape, scores: torch.Tensor, idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Group-shared selection int32 [b, Hkv, nqb, topk] from the mean of each
     KV group's per-head scores."""
-    _require_gpu(scores, idx)
+    b_, hq_, hkv_, _, _, _, nqb_, nkb_, k_ = _dims(shape)
+    _validate("ssa_select_topk_shared", scores=(scores, F32, (b_, hq_, nqb_, nkb_)),
+              idx=(idx, I32, (b_, hkv_, nqb_, k_)))
     if idx is None:
         idx = torch.empty((shape.batch, shape.n_kv_heads, n_blocks(shape.seq_q, shape.block), shape.topk),
                           dtype=torch.int32, device=scores.device)
@@ -256,15 +314,20 @@ def ssa_block_sparse_attn_fwd(shape: Shape, q, k, v, block_idx, workspace: Optio
                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                               shared: bool = False):
     """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q]).  ``shared``: block_idx
-    is a group-shared selection [b, Hkv, nqb, topk] (ssa_block_sparse_attn_fwd_shared)."""
-    _require_gpu(q, k, v, block_idx, workspace, out, lse)
+    is a group-shared selection [b, Hkv, nqb, topk] (ssa_block_sparse_attn_fwd_shared).  ``workspace``
+    (zero-filled before first use; every call leaves its work queue zero) is
+    allocated when not given."""
+    b_, hq_, hkv_, sq_, skv_, d_, nqb_, _, k_ = _dims(shape)
+    _validate("ssa_block_sparse_attn_fwd", q=(q, BF16, (b_, hq_, sq_, d_)), k=(k, BF16, (b_, hkv_, skv_, d_)),
+              v=(v, BF16, (b_, hkv_, skv_, d_)), block_idx=(block_idx, I32, (b_, hkv_ if shared else hq_, nqb_, k_)),
+              workspace=(workspace, U8, None), out=(out, BF16, (b_, hq_, sq_, d_)), lse=(lse, F32, (b_, hq_, sq_)))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     need = ssa_workspace_bytes(shape, SSA_OP_SPARSE_FWD)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     name = "ssa_block_sparse_attn_fwd_shared" if shared else "ssa_block_sparse_attn_fwd"
     _check(name, getattr(load_library(), name)(
@@ -275,15 +338,18 @@ def ssa_block_sparse_attn_fwd(shape: Shape, q, k, v, block_idx, workspace: Optio
 
 def ssa_full_attn_fwd_dropped_mass(shape: Shape, q, k, v, block_idx, q_block_begin: int = 0,
                                    q_block_count: Optional[int] = None, out=None, lse=None, dropped=None,
-                                   shared: bool = False):
+                                   shared: bool = False, workspace: Optional[torch.Tensor] = None):
     """(out_full bf16, lse_full fp32, dropped_mass fp32) over query blocks
     [q_block_begin, q_block_begin + q_block_count).  ``shared``: block_idx is a
-    group-shared selection (ssa_full_attn_fwd_dropped_mass_shared)."""
-    _require_gpu(q, k, v, block_idx, out, lse, dropped)
-    nqb = n_blocks(shape.seq_q, shape.block)
-    if q_block_count is None:
-        q_block_count = nqb - q_block_begin
-    rows = max(0, min(shape.seq_q, (q_block_begin + q_block_count) * shape.block) - q_block_begin * shape.block)
+    group-shared selection (ssa_full_attn_fwd_dropped_mass_shared).  ``workspace``
+    (zero-filled before first use; every call leaves it zero) holds the work
+    queue; one is allocated when not given."""
+    q_block_count, rows = _full_rows(shape, q_block_begin, q_block_count)
+    b_, hq_, hkv_, sq_, skv_, d_, nqb_, _, k_ = _dims(shape)
+    _validate("ssa_full_attn_fwd_dropped_mass", q=(q, BF16, (b_, hq_, sq_, d_)), k=(k, BF16, (b_, hkv_, skv_, d_)),
+              v=(v, BF16, (b_, hkv_, skv_, d_)), block_idx=(block_idx, I32, (b_, hkv_ if shared else hq_, nqb_, k_)),
+              out=(out, BF16, (b_, hq_, rows, d_)), lse=(lse, F32, (b_, hq_, rows)),
+              dropped=(dropped, F32, (b_, hq_, rows)), workspace=(workspace, U8, None))
     b, hq, d = shape.batch, shape.n_q_heads, shape.head_dim
     if out is None:
         out = torch.empty((b, hq, rows, d), dtype=torch.bfloat16, device=q.device)
@@ -291,17 +357,26 @@ def ssa_full_attn_fwd_dropped_mass(shape: Shape, q, k, v, block_idx, q_block_beg
         lse = torch.empty((b, hq, rows), dtype=torch.float32, device=q.device)
     if dropped is None:
         dropped = torch.empty((b, hq, rows), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros((max(1, ssa_workspace_bytes(shape, SSA_OP_FULL_FWD)),), dtype=torch.uint8,
+                                device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     name = "ssa_full_attn_fwd_dropped_mass_shared" if shared else "ssa_full_attn_fwd_dropped_mass"
     _check(name, getattr(load_library(), name)(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), int(q_block_begin),
-        int(q_block_count), _ptr(out), _ptr(lse), _ptr(dropped), None, 0, _stream(q.device)))
+        int(q_block_count), _ptr(out), _ptr(lse), _ptr(dropped), _ptr(workspace), ws_bytes, _stream(q.device)))
     return out, lse, dropped
 
 
 def ssa_block_sparse_attn_fwd_early_stop(shape: Shape, q, k, v, scores, block_idx, tau: float, out=None, lse=None,
                                          blocks_used=None):
     """(out bf16 [b, Hq, seq_q, d], lse fp32 [b, Hq, seq_q], blocks_used int32 [b, Hq, nqb])."""
-    _require_gpu(q, k, v, scores, block_idx, out, lse, blocks_used)
+    b_, hq_, hkv_, sq_, skv_, d_, nqb_, nkb_, k_ = _dims(shape)
+    _validate("ssa_block_sparse_attn_fwd_early_stop", q=(q, BF16, (b_, hq_, sq_, d_)),
+              k=(k, BF16, (b_, hkv_, skv_, d_)), v=(v, BF16, (b_, hkv_, skv_, d_)),
+              scores=(scores, F32, (b_, hq_, nqb_, nkb_)), block_idx=(block_idx, I32, (b_, hq_, nqb_, k_)),
+              out=(out, BF16, (b_, hq_, sq_, d_)), lse=(lse, F32, (b_, hq_, sq_)),
+              blocks_used=(blocks_used, I32, (b_, hq_, nqb_)))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -333,7 +408,12 @@ def ssa_block_sparse_attn_bwd(shape: Shape, q, k, v, block_idx, out, lse, dout, 
     """(dq bf16 [b, Hq, seq_q, d], dk, dv bf16 [b, Hkv, seq_kv, d]): gradients of
     sum(dout * out) for the block-sparse forward that produced out and lse.
     ``shared``: block_idx is a group-shared selection (ssa_block_sparse_attn_bwd_shared)."""
-    _require_gpu(q, k, v, block_idx, out, lse, dout, dq, dk, dv, workspace)
+    b_, hq_, hkv_, sq_, skv_, d_, nqb_, _, k_ = _dims(shape)
+    _validate("ssa_block_sparse_attn_bwd", q=(q, BF16, (b_, hq_, sq_, d_)), k=(k, BF16, (b_, hkv_, skv_, d_)),
+              v=(v, BF16, (b_, hkv_, skv_, d_)), block_idx=(block_idx, I32, (b_, hkv_ if shared else hq_, nqb_, k_)),
+              out=(out, BF16, (b_, hq_, sq_, d_)), lse=(lse, F32, (b_, hq_, sq_)), dout=(dout, BF16, (b_, hq_, sq_, d_)),
+              dq=(dq, BF16, (b_, hq_, sq_, d_)), dk=(dk, BF16, (b_, hkv_, skv_, d_)), dv=(dv, BF16, (b_, hkv_, skv_, d_)),
+              workspace=(workspace, U8, None))
     dq, dk, dv, workspace, ws_bytes = _bwd_outputs(shape, q, shape.seq_q, dq, dk, dv, workspace, SSA_OP_SPARSE_BWD)
     name = "ssa_block_sparse_attn_bwd_shared" if shared else "ssa_block_sparse_attn_bwd"
     _check(name, getattr(load_library(), name)(
@@ -348,11 +428,13 @@ def ssa_full_attn_bwd(shape: Shape, q, k, v, out_full, lse_full, dout_full, q_bl
     """(dq bf16 [b, Hq, rows, d], dk, dv bf16 [b, Hkv, seq_kv, d]): gradients of
     sum(dout_full * out_full) for the full causal forward over query blocks
     [q_block_begin, q_block_begin + q_block_count)."""
-    _require_gpu(q, k, v, out_full, lse_full, dout_full, dq, dk, dv, workspace)
-    nqb = n_blocks(shape.seq_q, shape.block)
-    if q_block_count is None:
-        q_block_count = nqb - q_block_begin
-    rows = max(0, min(shape.seq_q, (q_block_begin + q_block_count) * shape.block) - q_block_begin * shape.block)
+    q_block_count, rows = _full_rows(shape, q_block_begin, q_block_count)
+    b_, hq_, hkv_, sq_, skv_, d_, _, _, _ = _dims(shape)
+    _validate("ssa_full_attn_bwd", q=(q, BF16, (b_, hq_, sq_, d_)), k=(k, BF16, (b_, hkv_, skv_, d_)),
+              v=(v, BF16, (b_, hkv_, skv_, d_)), out_full=(out_full, BF16, (b_, hq_, rows, d_)),
+              lse_full=(lse_full, F32, (b_, hq_, rows)), dout_full=(dout_full, BF16, (b_, hq_, rows, d_)),
+              dq=(dq, BF16, (b_, hq_, rows, d_)), dk=(dk, BF16, (b_, hkv_, skv_, d_)),
+              dv=(dv, BF16, (b_, hkv_, skv_, d_)), workspace=(workspace, U8, None))
     dq, dk, dv, workspace, ws_bytes = _bwd_outputs(shape, q, rows, dq, dk, dv, workspace, SSA_OP_FULL_BWD)
     _check("ssa_full_attn_bwd", load_library().ssa_full_attn_bwd(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), int(q_block_begin), int(q_block_count), _ptr(out_full),

@@ -125,8 +125,9 @@ def test_decode_workspace(lib):
     sh = good_shape(batch=64, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=32768, q_offset=32767, topk=17)
     need = lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_SPARSE_FWD)
     assert need == 64 * 32 * 8 * 66 * 4        # 8 slices per KV group, (max, sum, o[64]) per head each
-    assert lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_FULL_FWD) == 0
-    assert lib.ssa_workspace_bytes(ctypes.byref(good_shape()), ssa.SSA_OP_SPARSE_FWD) == 0
+    # prefill: the optional work queue of the persistent launches (8 counters, one 128-byte line each)
+    assert lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_FULL_FWD) == 1024
+    assert lib.ssa_workspace_bytes(ctypes.byref(good_shape()), ssa.SSA_OP_SPARSE_FWD) == 1024
     assert lib.ssa_workspace_bytes(ctypes.byref(good_shape(head_dim=8)), ssa.SSA_OP_SPARSE_FWD) == 2**64 - 1
     # too small a workspace is refused before launch
     assert lib.ssa_block_sparse_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4,

@@ -434,3 +434,75 @@ def test_early_stop_parity(dev, case):
 
 def test_early_stop_prefill_8k(dev):
     check_early_stop(W.PREFILL_8K, [0.05, 1.0], dev, heads=[0, 17])
+
+
+def test_work_queue_reuse_and_static_grid(dev):
+    """The persistent prefill launches take units from a work queue in the
+    caller's workspace and leave it zeroed: one workspace serves call after
+    call, and the results equal those of the one-workgroup-per-unit grid
+    (used when no workspace is given) bit for bit.  prefill_8k has more units
+    than resident workgroups, so waves take several units each."""
+    w = W.BY_NAME["prefill_8k"]
+    say(f"work queue reuse on {w.name}")
+    q, k, v = (t.to(dev) for t in W.make_inputs(w))
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    scores, _ = ssa.ssa_block_scores(shape, q, k)
+    idx = ssa.ssa_select_topk(shape, scores)
+    none = torch.zeros((0,), dtype=torch.uint8, device=dev)  # too small: static grid
+    o0, l0 = ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx, workspace=none)
+    of0, lf0, d0 = ssa.ssa_full_attn_fwd_dropped_mass(shape, q, k, v, idx, workspace=none)
+    ws = torch.zeros((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD),), dtype=torch.uint8, device=dev)
+    wsf = torch.zeros((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_FULL_FWD),), dtype=torch.uint8, device=dev)
+    for rep in range(3):
+        o, l = ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx, workspace=ws)
+        of, lf, d = ssa.ssa_full_attn_fwd_dropped_mass(shape, q, k, v, idx, workspace=wsf)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0 and int(wsf.count_nonzero()) == 0, f"queue not zeroed after call {rep}"
+        assert torch.equal(o, o0) and torch.equal(l, l0), f"sparse forward differs from the static grid (call {rep})"
+        assert torch.equal(of, of0) and torch.equal(lf, lf0) and torch.equal(d, d0), \
+            f"full counterpart differs from the static grid (call {rep})"
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["per_head", "shared"])
+def test_index_rows_read_as_sets(dev, shared):
+    """An index row names a set of blocks: rows shuffled, with a -1 in the
+    middle and a block listed twice, give the results of the ascending rows
+    bit for bit in the block-sparse forward, the full counterpart's dropped
+    mass and the backward (the kernels put every row in ascending order
+    first); and both match the oracle."""
+    w = W.TINY_512.scaled(n_q_heads=8, n_kv_heads=2, seq_q=1000, seq_kv=1000, topk=5)
+    say(f"scrambled index rows, {w.seq_q} rows, topk {w.topk}, shared={shared}")
+    q, k, v = W.make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    shape = ssa.make_shape(qd, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    scores, _ = ssa.ssa_block_scores(shape, qd, kd)
+    idx = (ssa.ssa_select_topk_shared if shared else ssa.ssa_select_topk)(shape, scores)
+    rng = np.random.default_rng(77)
+    src = idx.cpu().numpy()
+    scr = np.full(src.shape[:-1] + (w.topk + 2,), -1, dtype=np.int32)
+    for pos in np.ndindex(*src.shape[:-1]):
+        lst = list(rng.permutation([int(j) for j in src[pos] if j >= 0]))
+        row = lst[: len(lst) // 2] + [-1] + lst[len(lst) // 2:] + lst[:1]
+        scr[pos][: len(row)] = row
+    shape2 = ssa.make_shape(qd, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk + 2)
+    scr_d = torch.from_numpy(scr).to(dev)
+    o0, l0 = ssa.ssa_block_sparse_attn_fwd(shape, qd, kd, vd, idx, shared=shared)
+    o1, l1 = ssa.ssa_block_sparse_attn_fwd(shape2, qd, kd, vd, scr_d, shared=shared)
+    _, _, d0 = ssa.ssa_full_attn_fwd_dropped_mass(shape, qd, kd, vd, idx, shared=shared)
+    _, _, d1 = ssa.ssa_full_attn_fwd_dropped_mass(shape2, qd, kd, vd, scr_d, shared=shared)
+    dout = W.make_output_grad(w, device=dev)
+    g0 = ssa.ssa_block_sparse_attn_bwd(shape, qd, kd, vd, idx, o0, l0, dout, shared=shared)
+    g1 = ssa.ssa_block_sparse_attn_bwd(shape2, qd, kd, vd, scr_d, o0, l0, dout, shared=shared)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0) and torch.equal(l1, l0), "sparse forward depends on the order of the index row"
+    assert torch.equal(d1, d0), "dropped mass depends on the order of the index row"
+    for a0, a1, name in zip(g0, g1, ("dq", "dk", "dv")):
+        assert torch.equal(a1, a0), f"{name} depends on the order of the index row"
+    # and the scrambled rows against the oracle (which reads rows as sets too)
+    per_head = scr if not shared else np.repeat(scr, w.n_q_heads // w.n_kv_heads, axis=1)
+    qn, kn, vn = np_inputs(q, k, v)
+    o_ref, l_ref = O.sparse_attention(qn, kn, vn, per_head, w.block)
+    P.check_close_outputs(o1, o_ref, "O_sparse (scrambled rows)")
+    P.check_abs(l1, l_ref, P.LSE_ABS, "LSE_sparse (scrambled rows)")
+    _, _, d_ref = O.full_attention_dropped_mass(qn, kn, vn, per_head, w.block)
+    P.check_abs(d1, d_ref, P.DROP_ABS, "dropped mass (scrambled rows)")
