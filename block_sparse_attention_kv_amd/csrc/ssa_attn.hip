@@ -145,7 +145,8 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float nm = BIAS ? b2 - st.m[qb] : -st.m[qb];
+    // a block whose bias is -inf (prior weight 0) adds nothing, whatever the reference max
+    const float nm = BIAS ? (b2 == -__builtin_inff() ? -__builtin_inff() : b2 - st.m[qb]) : -st.m[qb];
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)

@@ -266,8 +266,9 @@ __global__ __launch_bounds__(64, 1) void attn_decode_partial_kernel(AttnArgs a, 
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[hb][db][r] *= alpha;
       }
-      // unselected head: p = exp2(-inf) = 0; selected head: exponent relative to its reference max
-      const float nm = !sel ? -__builtin_inff() : b2 - m[hb];
+      // unselected head, or a block whose bias is -inf (prior weight 0): p = exp2(-inf) = 0;
+      // otherwise the exponent is relative to the head's reference max
+      const float nm = (!sel || b2 == -__builtin_inff()) ? -__builtin_inff() : b2 - m[hb];
       float rs = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {

@@ -176,7 +176,11 @@ __global__ __launch_bounds__(64 * kRouteWaves) void entmax_route_kernel(const fl
       if (kept) {
         const int e = outp + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
         irow[e] = j;
-        brow[e] = sigma * (__builtin_amdgcn_logf(wbar[j]) * kLn2);
+        // the hardware log takes no subnormal input: those weights are scaled by 2^64 first
+        const float wj = wbar[j];
+        const bool tiny = wj < 1.17549435e-38f;
+        const float lg2 = __builtin_amdgcn_logf(tiny ? wj * 18446744073709551616.f : wj) - (tiny ? 64.f : 0.f);
+        brow[e] = sigma * (lg2 * kLn2);
       }
       outp += (int)__builtin_popcountll(m);
     }

@@ -129,18 +129,26 @@ ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int3
                              hipStream_t stream);
 
 /* Block-sparse attention forward: query row r of block i attends to the keys
- * c <= q_offset + r whose block is listed in block_idx[b,h,i,:] (-1 entries
- * ignored; entries must be ascending, distinct and <= diag(i), and the list
- * must contain diag(i)):
+ * c <= q_offset + r whose block is listed in block_idx[b,h,i,:].  A row is
+ * read as the set of blocks it names: entries in any order, -1 anywhere
+ * skipped, entries outside [0, diag(i)] skipped, a block listed twice
+ * attended once (ssa_select_topk writes them ascending and -1 padded):
  *   out[b,h,r,:] = sum_c softmax_c(scale * q_r . k_c) v_c   (bf16, fp32 accumulation)
  *   lse[b,h,r]   = natural log of sum_c exp(scale * q_r . k_c)  (fp32)
  * [SSA-summary] 2 "Mecanismo Central" (the sparse attention stream);
  * [SSA-guide] "Block-sparse attention e Receptive Field" (attention over the
  * tokens of the selected blocks only); [S2O] "Permutacion en Linea" (tiles
  * gathered by index from an unchanged HBM layout).
- * With seq_q == 1 (decode) the work is split over the key blocks of each
- * KV-head group and merged; that needs ssa_workspace_bytes(shape,
- * SSA_OP_SPARSE_FWD) bytes of workspace (0 for prefill, workspace may be NULL).
+ * Workspace: ssa_workspace_bytes(shape, SSA_OP_SPARSE_FWD) bytes, 16-byte
+ * aligned.
+ *   decode (seq_q == 1): required (else SSA_ERR_WORKSPACE); the work is split
+ *     over the key blocks of each KV-head group and the slices' partial
+ *     results are merged through it.
+ *   prefill: optional work queue.  With at least that many bytes, zero-filled
+ *     before the first call, the launch is persistent (workgroups take further
+ *     query blocks from the queue); every call leaves the queue zero again, so
+ *     one buffer serves every later call, but calls sharing it must not
+ *     overlap in time.  NULL or fewer bytes: one workgroup per query block.
  *   q, k, v    bf16 as above;  block_idx int32 [b,Hq,nqb,topk]
  *   out        bf16 [b,Hq,seq_q,d] (output);  lse fp32 [b,Hq,seq_q] (output) */
 ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, const void* k,
@@ -159,7 +167,11 @@ ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, 
  * opposite mode, used only for alignment) and 1 "Planteamiento del Problema"
  * (approximation error linear in the attention weight on unselected tokens).
  * Outputs hold rows_out = min(seq_q, (begin+count)*B) - begin*B rows per (b,h).
- * No workspace is needed (workspace may be NULL). */
+ * block_idx rows are read as sets, as in ssa_block_sparse_attn_fwd.
+ * Workspace: optional work queue of ssa_workspace_bytes(shape,
+ * SSA_OP_FULL_FWD) bytes, as for a prefill ssa_block_sparse_attn_fwd
+ * (zero-filled before the first call, left zero by every call; NULL: one
+ * workgroup per group of query heads and query block). */
 ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void* q, const void* k,
                                             const void* v, const int32_t* block_idx,
                                             int32_t q_block_begin, int32_t q_block_count,
@@ -291,8 +303,8 @@ ssa_status_t ssa_block_summaries_learned(const ssa_shape_t* shape, const void* k
  * query block i) and each query head h of the group,
  *   w_h = alpha-entmax(gamma * scores[b,h,i,j]) over j < diag(i),
  *   alpha-entmax(z)_j = max(0, (alpha-1) z_j - tau)^(1/(alpha-1)), tau such that sum_j = 1,
- * and the group's weights are wbar = mean_h w_h (fp32; tau by bisection in
- * fp32).  block_idx lists diag(i) plus every j with wbar_j > 0 -- past topk
+ * and the group's weights are wbar = mean_h w_h (fp32; tau by Newton
+ * iterations from below in fp32).  block_idx lists diag(i) plus every j with wbar_j > 0 -- past topk
  * blocks, the topk-1 largest wbar (lower index on ties) -- ascending, -1
  * padded; block_bias holds sigma * ln(wbar_j) for each listed j != diag(i)
  * and 0 for diag(i) and padding.  Non-finite scores take no weight.
@@ -316,7 +328,10 @@ ssa_status_t ssa_entmax_route(const ssa_shape_t* shape, const float* scores, flo
  * logits scale * q_r . k_c + block_bias[b, h/G, i, e] for c in the e-th listed
  * block (out, lse as ssa_block_sparse_attn_fwd; lse includes the bias).  With
  * the output of ssa_entmax_route this is the softmax taken relative to the
- * prior g proportional to wbar^sigma.
+ * prior g proportional to wbar^sigma.  A block whose bias is -inf (prior
+ * weight 0) contributes nothing; a row whose every listed block has bias -inf
+ * has an empty support and gets NaN in out and lse.  A block listed twice
+ * takes the bias of its first listing.
  * [DashAttn] "Etapa 2" (prior-induced sparse softmax: a FlashAttention-style
  * loop over the active chunks adding the routing bias to the logits).
  *   block_idx   int32 [b,Hkv,nqb,topk];  block_bias fp32 [b,Hkv,nqb,topk]

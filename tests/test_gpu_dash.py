@@ -21,7 +21,7 @@ from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 B = 64
-W_ABS = 1e-5          # routing weights: fp32 bisection (2^-30 of the bracket) and fp32 sums
+W_ABS = 1e-5          # routing weights: fp32 Newton iterations from below and fp32 sums
 SUMMARY_ULPS = 2      # learned summaries: fp64 on both sides, one fp32 rounding
 
 
@@ -198,3 +198,41 @@ def test_dash_prefill_8k(dev):
                 bias[:, h // 16:h // 16 + 1, :i + 1], B)
             P.check_close_outputs(g["o"][:, h:h + 1, rows], o_ref[:, :, i * B:], f"O_prior h{h} i{i}")
             P.check_abs(g["lse"][:, h:h + 1, rows], lse_ref[:, :, i * B:], P.LSE_ABS, f"LSE_prior h{h} i{i}")
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[8]], ids=lambda c: c[0].name)
+def test_minus_inf_bias(dev, case):
+    """A listed block whose bias is -inf (a prior weight of 0) contributes
+    nothing, also when it is the first block a row visits (the diagonal, or the
+    first of a decode slice): the biased forward stays finite and matches the
+    oracle.  Every other row's diagonal bias is set to -inf, and the first
+    other listed block of every third row; each row keeps a finite block."""
+    w, alpha, gamma, sigma = case
+    say(f"{w.name}: -inf biases on listed blocks")
+    q, k, v = W.make_inputs(w)
+    qbar = W.make_learned_query(w)
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ks = ssa.ssa_block_summaries_learned(kd, qbar.to(dev))
+    scores, _ = ssa.ssa_block_scores(shape, qd, None, ks)
+    idx, bias, _ = ssa.ssa_entmax_route(shape, scores, alpha, gamma, sigma, with_weights=False)
+    idx_n, bias_n = idx.cpu().numpy(), bias.cpu().numpy().astype(np.float32)
+    nrow = 0
+    for pos in np.ndindex(*idx_n.shape[:-1]):
+        listed = [e for e in range(idx_n.shape[-1]) if idx_n[pos][e] >= 0]
+        if len(listed) < 2:
+            continue
+        if nrow % 2 == 0:
+            bias_n[pos][listed[-1]] = -np.inf          # the diagonal (listed last, visited first)
+        if nrow % 3 == 0 and (len(listed) > 2 or nrow % 2 == 1):
+            bias_n[pos][listed[0]] = -np.inf           # the first other block (one listed block stays finite)
+        nrow += 1
+    assert nrow > 0
+    assert np.all(np.any(np.isfinite(bias_n) & (idx_n >= 0), axis=-1) | (idx_n < 0).all(-1))
+    o, lse = ssa.ssa_block_sparse_attn_fwd_biased(shape, qd, kd, vd, idx, torch.from_numpy(bias_n).to(dev))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), "-inf bias produced non-finite outputs"
+    o_ref, lse_ref = O.prior_attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), idx_n,
+                                       bias_n.astype(np.float64), B, q_offset=w.q_offset)
+    P.check_close_outputs(o, o_ref, "O_prior with -inf biases")
+    P.check_abs(lse, lse_ref, P.LSE_ABS, "LSE_prior with -inf biases")
