@@ -1,7 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
 same seeded inputs.  Small problems are compared element by element; the
-full-size workloads are compared on every block index and on sampled rows,
-plus properties that hold at any size."""
+full-size workloads on every block index and element by element over every
+row of: prefill_8k (all heads, both selections), batch row 0 of structured_8k
+in both variants, eight heads spanning both KV groups of extrap_32k (every
+sparse row and the full slice), and all 64 decode_32k sequences; plus
+properties that hold at any size."""
 from __future__ import annotations
 
 import math
@@ -259,14 +262,50 @@ def check_full_size(w: W.Workload, dev, nrows=96, seq_subset=None, shared=False)
     return g
 
 
+def check_every_row(w: W.Workload, g, q, k, v, batches, heads, shared=False):
+    """Element-wise parity over every row of the given batch rows and query
+    heads: O, LSE of the block-sparse forward and O, LSE, dropped mass of the
+    full counterpart (over its query-block range), against the oracle run
+    with the GPU's own indices, one KV group at a time."""
+    G = w.n_q_heads // w.n_kv_heads
+    gidx = per_head(g["idx"].numpy(), w, shared)
+    lo = (0 if w.full_rows is None else w.full_rows[0] // B * B)
+    hi = lo + g["of"].shape[2]
+    for bi in batches:
+        for kvh in range(w.n_kv_heads):
+            hs = [h for h in heads if h // G == kvh]
+            if not hs:
+                continue
+            qn = q[bi:bi + 1, hs].double().numpy()
+            kn = k[bi:bi + 1, kvh:kvh + 1].double().numpy()
+            vn = v[bi:bi + 1, kvh:kvh + 1].double().numpy()
+            sel = gidx[bi:bi + 1, hs]
+            tag = f"{w.name} b{bi} heads {hs[0]}..{hs[-1]}"
+            o_ref, l_ref = O.sparse_attention(qn, kn, vn, sel, B, q_offset=w.q_offset)
+            P.check_close_outputs(g["o"][bi:bi + 1, hs], o_ref, f"O_sparse every row, {tag}")
+            P.check_abs(g["lse"][bi:bi + 1, hs], l_ref, P.LSE_ABS, f"LSE_sparse every row, {tag}")
+            of_ref, lf_ref, dm_ref = O.full_attention_dropped_mass(qn, kn, vn, sel, B, q_offset=w.q_offset,
+                                                                   row_range=(lo, hi))
+            P.check_close_outputs(g["of"][bi:bi + 1, hs], of_ref, f"O_full every row, {tag}")
+            P.check_abs(g["lf"][bi:bi + 1, hs], lf_ref, P.LSE_ABS, f"LSE_full every row, {tag}")
+            P.check_abs(g["dm"][bi:bi + 1, hs], dm_ref, P.DROP_ABS, f"dropped mass every row, {tag}")
+
+
 def test_prefill_8k_full_size(dev):
-    g = check_full_size(W.PREFILL_8K, dev)
+    w = W.PREFILL_8K
+    g = check_full_size(w, dev)
     # rows of the first k blocks keep every causal key
-    assert torch.all(g["dm"][:, :, : W.PREFILL_8K.topk * B] == 0)
+    assert torch.all(g["dm"][:, :, : w.topk * B] == 0)
+    # every row of every head
+    q, k, v = W.make_inputs(w)
+    check_every_row(w, g, q, k, v, batches=[0], heads=list(range(w.n_q_heads)))
 
 
 def test_structured_8k_planted_full_size(dev):
-    check_full_size(W.STRUCTURED_8K, dev, nrows=64)
+    w = W.STRUCTURED_8K
+    g = check_full_size(w, dev, nrows=64)
+    q, k, v = W.make_inputs(w)
+    check_every_row(w, g, q, k, v, batches=[0], heads=list(range(w.n_q_heads)))
 
 
 def test_structured_8k_tie_full_size(dev):
@@ -301,10 +340,16 @@ def test_structured_8k_tie_full_size(dev):
     num = torch.where(torch.from_numpy(blk < k_)[None, None, :, None], csum, pre[:, :, None, :] + csum - before)
     mean_sp = num / torch.from_numpy(kept.astype(np.float64))[:, None]
     P.check_close_outputs(g["o"], mean_sp.repeat_interleave(w.n_q_heads // w.n_kv_heads, dim=1), "O_sparse closed form")
+    # and every row of batch row 0 against the oracle
+    check_every_row(w, g, q, k, v, batches=[0], heads=list(range(w.n_q_heads)))
 
 
 def test_extrap_32k_full_size(dev):
-    check_full_size(W.EXTRAP_32K, dev, nrows=64)
+    w = W.EXTRAP_32K
+    g = check_full_size(w, dev, nrows=64)
+    # every sparse row and every row of the full slice, four heads of each KV group
+    q, k, v = W.make_inputs(w)
+    check_every_row(w, g, q, k, v, batches=[0], heads=[0, 5, 10, 15, 16, 21, 26, 31])
 
 
 def test_decode_32k_full_size(dev):
@@ -312,16 +357,19 @@ def test_decode_32k_full_size(dev):
     say(w)
     q, k, v = W.make_inputs(w)
     g = gpu_path(w, q, k, v, dev, with_full=False)
-    sub = [0, 17, 63]
-    qn, kn, vn = q[sub].double().numpy(), k[sub].double().numpy(), v[sub].double().numpy()
-    ks_ref = O.key_summaries(kn, B)
-    assert np.array_equal(P.np64(g["k_summary"][sub]), ks_ref)
-    s_ref = O.block_scores(qn, None, B, q_offset=w.q_offset, k_summary=ks_ref)
-    idx_ref = O.select_blocks(s_ref, w.topk, B, q_offset=w.q_offset)
-    P.check_indices(g["idx"][sub], s_ref, idx_ref, w.topk, B, w.q_offset)
-    o_ref, lse_ref = O.sparse_attention(qn, kn, vn, g["idx"][sub].numpy(), B, q_offset=w.q_offset)
-    P.check_close_outputs(g["o"][sub], o_ref, "O_decode")
-    P.check_abs(g["lse"][sub], lse_ref, P.LSE_ABS, "LSE_decode")
+    # every sequence, eight at a time (the fp64 copies of one chunk's cache are 0.5 GB)
+    for s0 in range(0, w.batch, 8):
+        sub = list(range(s0, min(s0 + 8, w.batch)))
+        qn, kn, vn = q[sub].double().numpy(), k[sub].double().numpy(), v[sub].double().numpy()
+        ks_ref = O.key_summaries(kn, B)
+        assert np.array_equal(P.np64(g["k_summary"][sub]), ks_ref)
+        s_ref = O.block_scores(qn, None, B, q_offset=w.q_offset, k_summary=ks_ref)
+        idx_ref = O.select_blocks(s_ref, w.topk, B, q_offset=w.q_offset)
+        P.check_indices(g["idx"][sub], s_ref, idx_ref, w.topk, B, w.q_offset)
+        o_ref, lse_ref = O.sparse_attention(qn, kn, vn, g["idx"][sub].numpy(), B, q_offset=w.q_offset)
+        P.check_close_outputs(g["o"][sub], o_ref, f"O_decode sequences {sub[0]}..{sub[-1]}")
+        P.check_abs(g["lse"][sub], lse_ref, P.LSE_ABS, f"LSE_decode sequences {sub[0]}..{sub[-1]}")
+        del qn, kn, vn
     # every sequence: the forced block is the most recent one
     assert torch.all(g["idx"][..., -1] == (w.seq_kv - 1) // B)
 
@@ -354,8 +402,11 @@ def test_shared_one_head_per_group_matches_per_head(dev):
 
 
 def test_prefill_8k_shared_full_size(dev):
-    g = check_full_size(W.PREFILL_8K, dev, nrows=64, shared=True)
-    assert torch.all(g["dm"][:, :, : W.PREFILL_8K.topk * B] == 0)
+    w = W.PREFILL_8K
+    g = check_full_size(w, dev, nrows=64, shared=True)
+    assert torch.all(g["dm"][:, :, : w.topk * B] == 0)
+    q, k, v = W.make_inputs(w)
+    check_every_row(w, g, q, k, v, batches=[0], heads=list(range(w.n_q_heads)), shared=True)
 
 
 def test_decode_32k_shared_full_size(dev):
