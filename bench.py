@@ -11,7 +11,10 @@ and reported under "decode".
 Prints ONE JSON line.  ``value`` is tokens/s of the whole step (inputs already
 resident in HBM), from the timed steps, which run with no event between their
 kernels; per-kernel timings come from HIP events recorded around each call on
-the stream the kernels run on, averaged over as many further steps.
+the stream the kernels run on, over as many further steps (medians reported).
+The 8k prefill step is also timed on the planted and tie 8k workloads (batch
+4) and on the 32k extrapolation workload, and a peaks leg measures what the
+matrix cores, HBM and the shader clock deliver on this GPU.
 """
 from __future__ import annotations
 
@@ -61,13 +64,12 @@ def full_useful_pairs(lo: int, hi: int) -> int:
 
 
 class KernelTimer:
-    """Accumulates HIP-event durations of named calls on the current stream."""
+    """Collects HIP-event durations of named calls on the current stream."""
 
     def __init__(self, torch):
         self.torch = torch
         self.pending = []
-        self.total = {}
-        self.count = {}
+        self.times = {}
 
     def run(self, name, fn, *args, **kw):
         e0 = self.torch.cuda.Event(enable_timing=True)
@@ -80,12 +82,16 @@ class KernelTimer:
 
     def collect(self):
         for name, e0, e1 in self.pending:
-            self.total[name] = self.total.get(name, 0.0) + e0.elapsed_time(e1)
-            self.count[name] = self.count.get(name, 0) + 1
+            self.times.setdefault(name, []).append(e0.elapsed_time(e1))
         self.pending.clear()
 
+    def median_ms(self, name):
+        t = sorted(self.times[name])
+        n = len(t)
+        return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+
     def avg_ms(self, name):
-        return self.total[name] / self.count[name]
+        return sum(self.times[name]) / len(self.times[name])
 
 
 class PlainRunner:
@@ -123,10 +129,11 @@ def kernel_pass(torch, timer, step, n):
     timer.collect()
 
 
-def bench_prefill(args, torch, ssa, W, shared=False):
+def bench_prefill(args, torch, ssa, W, shared=False, workload=None, steps=None):
     """One step = summaries+scores, top-k, block-sparse forward, full forward
     with dropped mass; ``shared`` uses the group-shared selection."""
-    w = W.BY_NAME[args.workload]
+    w = W.BY_NAME[workload or args.workload]
+    n_steps = steps or args.steps
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in W.make_inputs(w))
     shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
@@ -163,8 +170,8 @@ def bench_prefill(args, torch, ssa, W, shared=False):
     plain = PlainRunner()
     for i in range(args.warmup):
         step(plain, i)
-    ms_step, wall = timed_steps(torch, step, args.steps)
-    kernel_pass(torch, timer, step, args.steps)
+    ms_step, wall = timed_steps(torch, step, n_steps)
+    kernel_pass(torch, timer, step, n_steps)
 
     pairs_sp = w.batch * w.n_q_heads * sparse_useful_pairs(nqb, w.topk, w.block)
     pairs_full = w.batch * w.n_q_heads * full_useful_pairs(fb0 * w.block, fb0 * w.block + rows)
@@ -176,8 +183,8 @@ def bench_prefill(args, torch, ssa, W, shared=False):
     }
     kernels = {}
     for name in ("scores", "topk", "sparse_attn", "full_attn"):
-        ms = timer.avg_ms(name)
-        e = {"avg_ms": round(ms, 5)}
+        ms = timer.median_ms(name)
+        e = {"median_ms": round(ms, 5), "mean_ms": round(timer.avg_ms(name), 5)}
         if name in flops:
             tf = flops[name] / (ms * 1e-3) / 1e12
             e.update(bound="mfma", gflop_per_launch=round(flops[name] / 1e9, 3),
@@ -187,16 +194,19 @@ def bench_prefill(args, torch, ssa, W, shared=False):
             e.update(bound="hbm", mbytes_per_launch=round(bytes_alg[name] / 1e6, 3),
                      gbs=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
         kernels[name] = e
-    dominant = max(kernels, key=lambda n: kernels[n]["avg_ms"])
-    roof = roofline_entry(dominant, kernels[dominant], flops, bytes_alg, shared)
-    return dict(w=w, ms_step=ms_step, wall=wall, kernels=kernels, roofline=roof, dominant=dominant,
+    # the metric's kernel: the block-sparse forward on selected-block flops
+    counted = not shared and w.name == "prefill_8k"
+    roof = roofline_entry("sparse_attn", kernels["sparse_attn"], flops, bytes_alg, counted)
+    roof_full = roofline_entry("full_attn", kernels["full_attn"], flops, bytes_alg, counted)
+    del q, k, v, scores, ksum, idx, out, lse, out_f, lse_f, drop, ws_sp, ws_full
+    return dict(w=w, ms_step=ms_step, wall=wall, kernels=kernels, roofline=roof, roofline_full=roof_full,
                 tokens_per_s=w.batch * w.seq_q / (ms_step * 1e-3))
 
 
-def roofline_entry(name, e, flops, bytes_alg, shared=False):
-    """Roofline object of one kernel.  The committed counter summary was taken
-    on the per-head selection: the group-shared sparse forward is another
-    kernel, so it gets no traffic figure."""
+def roofline_entry(name, e, flops, bytes_alg, counted=True):
+    """Roofline object of one kernel.  The committed counter summary covers the
+    per-head selection on the 8k prefill workload only: other launches get no
+    traffic figure."""
     if e["bound"] == "mfma":
         ach = e["tflops"]
         r = {"kernel": name, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -205,9 +215,132 @@ def roofline_entry(name, e, flops, bytes_alg, shared=False):
         ach = e["gbs"]
         r = {"kernel": name, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_per_launch": bytes_alg[name]}
-    counted = name == "full_attn" or (name == "sparse_attn" and not shared)
     r["traffic"] = measured_traffic(name) if counted else None
     return r
+
+
+def prefill_leg(res):
+    """Bench-line entry of a prefill run on another workload."""
+    w = res["w"]
+    return {"workload": w.name, "batch": w.batch, "seq_len": w.seq_q, "variant": w.variant,
+            "full_rows": list(w.full_rows) if w.full_rows else None,
+            "ms_per_step": round(res["ms_step"], 5), "tokens_per_s": round(res["tokens_per_s"], 1),
+            "kernels": res["kernels"], "roofline": res["roofline"], "roofline_full": res["roofline_full"]}
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def _event_ms(torch, fn, reps):
+    """Median HIP-event time of ``reps`` single calls of ``fn``."""
+    out = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return _median(out)
+
+
+def _u32(t):
+    """int32 tensor holding uint32 bit patterns -> int64 values on the CPU."""
+    return t.long().cpu() & 0xFFFFFFFF
+
+
+def bench_peaks(args, torch, ssa, W):
+    """Measured peaks beside the nominal ones: a matrix-instruction loop with no
+    memory traffic (bf16 32x32x16, 2 waves per SIMD), a streaming read and a
+    streaming copy of 1 GiB, and the shader clock seen by one wavefront when
+    the GPU is idle and while the block-sparse forward runs on another stream."""
+    from block_sparse_attention_kv_amd import peaks as P
+    P.load_library()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {"compute_units": cus}
+    i32 = torch.int32
+
+    def clock_ghz(out):
+        c = _u32(out)
+        return float(c[0]) / float(c[1]) * P.REALTIME_HZ / 1e9
+
+    clk = torch.zeros(2, dtype=i32, device=dev)
+    P.clock(20000, clk)
+    torch.cuda.synchronize()
+    res["clock_idle_ghz"] = round(clock_ghz(clk), 3)
+
+    # matrix-instruction loop: 2 waves per SIMD, about 2 ms
+    iters, nb = 4000, 2 * cus
+    mo = torch.zeros(16 * nb, dtype=i32, device=dev)
+    P.mfma(iters, nb, mo)
+    torch.cuda.synchronize()
+    ms = _event_ms(torch, lambda: P.mfma(iters, nb, mo), 5)
+    per_wave = _u32(mo).view(-1, 4)
+    ghz = float((per_wave[:, 1].double() / per_wave[:, 2].double()).median()) * P.REALTIME_HZ / 1e9
+    fl = 4 * nb * iters * P.MFMA_PER_ITER * P.FLOP_PER_MFMA
+    tf = fl / (ms * 1e-3) / 1e12
+    res["mfma_bf16"] = {"tflops": round(tf, 1), "frac_of_nominal": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "clock_ghz": round(ghz, 3), "ms": round(ms, 4), "waves": 4 * nb,
+                        "note": "v_mfma_f32_32x32x16_bf16 back to back on registers; the nominal peak assumes 2.4 GHz"}
+
+    # streaming read and copy of 1 GiB (well above the 256 MB last-level cache)
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=i32, device=dev)
+    best_r, best_c = None, None
+    for per_cu in (4, 8, 16):
+        nbr = per_cu * cus
+        ro = torch.zeros(nbr, dtype=i32, device=dev)
+        P.read(src, ro, nbr)
+        ms = _event_ms(torch, lambda: P.read(src, ro, nbr), 7)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if best_r is None or gbs > best_r["gbs"]:
+            best_r = {"gbs": round(gbs, 1), "frac_of_nominal": round(gbs / PEAK_HBM_GBS, 4), "blocks": nbr,
+                      "ms": round(ms, 4)}
+    half = nbytes // 2
+    a, b = src[: half // 4], src[half // 4:]
+    for per_cu in (4, 8, 16):
+        nbr = per_cu * cus
+        P.copy(a, b, nbr)
+        ms = _event_ms(torch, lambda: P.copy(a, b, nbr), 7)
+        gbs = 2 * half / (ms * 1e-3) / 1e9
+        if best_c is None or gbs > best_c["gbs"]:
+            best_c = {"gbs": round(gbs, 1), "frac_of_nominal": round(gbs / PEAK_HBM_GBS, 4), "blocks": nbr,
+                      "ms": round(ms, 4), "bytes_counted": "read + write"}
+    res["hbm_read"] = best_r
+    res["hbm_copy"] = best_c
+    del src, a, b
+
+    # shader clock while the block-sparse forward of the bench workload runs
+    w = W.BY_NAME[args.workload]
+    q, k, v = (t.to(dev) for t in W.make_inputs(w))
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    scores, _ = ssa.ssa_block_scores(shape, q, k)
+    idx = ssa.ssa_select_topk(shape, scores)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.zeros((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD),), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx, workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)     # default priority
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(40):                      # about 4 ms of back-to-back launches
+        ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx, workspace=ws, out=out, lse=lse)
+    ev[1].record()
+    with torch.cuda.stream(side):
+        P.clock(100000, clk, stream=side)    # a 1 ms window inside them
+        ev[2].record(side)
+    torch.cuda.synchronize()
+    res["clock_under_sparse_fwd"] = {"ghz": round(clock_ghz(clk), 3),
+                                     # the window ended before the last launch did
+                                     "overlapped": bool(ev[0].elapsed_time(ev[2]) < ev[0].elapsed_time(ev[1]))}
+    return res
 
 
 def bench_decode(args, torch, ssa, W, shared=False):
@@ -257,9 +390,10 @@ def bench_decode(args, torch, ssa, W, shared=False):
     topk_bytes = scores.numel() * 4 + idx.numel() * 4
     kern = {}
     for name, b in (("decode_scores", score_bytes), ("decode_topk", topk_bytes), ("decode_attn", attn_bytes)):
-        ms = timer.avg_ms(name)
+        ms = timer.median_ms(name)
         gbs = b / (ms * 1e-3) / 1e9
-        kern[name] = {"avg_ms": round(ms, 5), "bound": "hbm", "mbytes_per_launch": round(b / 1e6, 3),
+        kern[name] = {"median_ms": round(ms, 5), "mean_ms": round(timer.avg_ms(name), 5), "bound": "hbm",
+                      "mbytes_per_launch": round(b / 1e6, 3),
                       "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
     step_bytes = attn_bytes + score_bytes + topk_bytes
     return {
@@ -403,13 +537,44 @@ def bench_dash(args, torch, ssa, W, alpha=1.5, gamma=800.0, sigma=1.0, cap=64):
     # useful pairs: every listed block whole, the diagonal block's causal half
     listed = (idx >= 0).sum(-1).double()                       # [b, Hkv, nqb]
     pairs = float(((listed - 1) * w.block * w.block + w.block * (w.block + 1) / 2).sum()) * (w.n_q_heads // w.n_kv_heads)
-    attn_ms = timer.avg_ms("attn")
+    attn_ms = timer.median_ms("attn")
     tf = 4.0 * w.head_dim * pairs / (attn_ms * 1e-3) / 1e12
     return {"workload": w.name, "alpha": alpha, "gamma": gamma, "sigma": sigma, "list_cap": cap,
             "blocks_listed_per_query_block": round(float(listed.mean()), 3), "ms_per_step": round(ms, 5),
             "tokens_per_s": round(w.batch * w.seq_q / (ms * 1e-3), 1),
-            "kernels_ms": {kk: round(timer.avg_ms(kk), 5) for kk in ("summaries", "scores", "route", "attn")},
+            "kernels_median_ms": {kk: round(timer.median_ms(kk), 5) for kk in ("summaries", "scores", "route", "attn")},
             "attn_tflops": round(tf, 2), "attn_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_decode_baseline(args, W, seconds):
+    """The fp64 oracle on whole sequences of the decode workload (scores, top-k
+    and attention, cached summaries computed outside the timing), until about
+    ``seconds`` elapse."""
+    from oracle import ssa_oracle as O
+    w = W.DECODE_32K
+    q, k, v = W.make_inputs(w)
+    seqs, spent = 0, 0.0
+    while seqs < w.batch and spent < seconds:
+        qs, ks, vs = (t[seqs:seqs + 1].double().numpy() for t in (q, k, v))
+        ksum = O.key_summaries(ks, w.block)
+        t0 = time.perf_counter()
+        O.hot_path(qs, ks, vs, w.block, w.topk, q_offset=w.q_offset, k_summary=ksum, with_full=False)
+        spent += time.perf_counter() - t0
+        seqs += 1
+    return {"value": round(seqs / spent, 3), "unit": "tokens/s", "kind": "oracle",
+            "sample": f"{seqs} of {w.batch} sequences of {w.name} (1 token each against {w.seq_kv} keys): "
+                      f"scores+top-k+sparse attention in fp64 NumPy ({spent:.1f} s)"}
 
 
 def cpu_baseline(args, W):
@@ -422,6 +587,7 @@ def cpu_baseline(args, W):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
+    affinity = len(os.sched_getaffinity(0))
     w = W.BY_NAME[args.workload]
     q, k, v = W.make_inputs(w)
     G = w.n_q_heads // w.n_kv_heads
@@ -439,11 +605,13 @@ def cpu_baseline(args, W):
             break
     dt = time.perf_counter() - t0
     tokens = w.seq_q * heads / w.n_q_heads   # fraction of one batch row's work
-    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": affinity, "kind": "oracle",
+            "cpu_model": _cpu_model(), "affinity_cpus": affinity, "blas_threads": blas_threads,
             "sample": f"{heads} of {w.n_q_heads} query heads of batch row 0 of {w.name}, all {w.seq_q} rows, "
                       f"summaries+scores+top-k+sparse+full+dropped mass in fp64 NumPy ({dt:.1f} s; "
-                      f"BLAS threads {blas_threads}, elementwise ops single-threaded); "
-                      f"tokens/s scaled by the head fraction"}
+                      f"matrix products on {blas_threads} BLAS threads, elementwise ops on one); "
+                      f"tokens/s scaled by the head fraction",
+            "decode": None if args.no_decode else cpu_decode_baseline(args, W, args.cpu_seconds / 2)}
 
 
 def counter_pass(args, torch, ssa, W):
@@ -477,6 +645,10 @@ def main():
                     help="skip the extra legs (group-shared selection, early stopping, DashAttention stages)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the other prefill workloads (structured_8k, structured_8k_tie, extrap_32k)")
+    ap.add_argument("--leg-steps", type=int, default=10)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peaks leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--counter-pass", action="store_true",
                     help="only issue the dispatches a rocprofv3 --pmc run needs (no JSON line)")
@@ -509,6 +681,12 @@ def main():
             sd = bench_decode(args, torch, ssa, W, shared=True)
             shared["decode"] = {k2: sd[k2] for k2 in ("workload", "tokens_per_s", "ms_per_step",
                                                        "union_blocks_per_group", "kernels", "roofline")}
+    legs = None
+    if not args.no_legs:
+        legs = {}
+        for name in ("structured_8k", "structured_8k_tie", "extrap_32k"):
+            legs[name] = prefill_leg(bench_prefill(args, torch, ssa, W, workload=name, steps=args.leg_steps))
+    peaks = None if args.no_peaks else bench_peaks(args, torch, ssa, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, W)
     w = pre["w"]
     line = {
@@ -528,12 +706,17 @@ def main():
                    "seq_len": w.seq_q, "head_dim": w.head_dim, "block": w.block, "topk": w.topk,
                    "step": "summaries+scores, top-k, block-sparse fwd, full fwd + dropped mass"},
         "roofline": pre["roofline"],
+        "roofline_full": pre["roofline_full"],
         "kernels": pre["kernels"],
-        "sparse_fwd": {"tokens_per_s": round(w.batch * w.seq_q / (pre["kernels"]["sparse_attn"]["avg_ms"] * 1e-3), 1),
+        "sparse_fwd": {"tokens_per_s": round(w.batch * w.seq_q / (pre["kernels"]["sparse_attn"]["median_ms"] * 1e-3), 1),
                        "tflops": pre["kernels"]["sparse_attn"]["tflops"],
                        "frac_of_bf16_peak": pre["kernels"]["sparse_attn"]["frac_of_peak"],
                        "traffic": measured_traffic("sparse_attn")},
+        "targets": {"sparse_fwd_frac_of_bf16_peak": pre["kernels"]["sparse_attn"]["frac_of_peak"],
+                    "decode_step_frac_of_hbm_peak": None if dec is None else dec["step_frac_of_hbm_peak"]},
         "decode": dec,
+        "workload_legs": legs,
+        "peaks": peaks,
         "shared_selection": shared,
         "early_stop": None if args.no_shared else bench_early_stop(args, torch, ssa, W),
         "backward": None if args.no_backward else bench_backward(args, torch, ssa, W),

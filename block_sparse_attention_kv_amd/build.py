@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssa.so")
 SOURCES = ["ssa_api.cpp", "ssa_scores.hip", "ssa_topk.hip", "ssa_attn.hip", "ssa_decode.hip", "ssa_bwd.hip", "ssa_route.hip"]
+# measurement aid (include/ssa_peaks.h), a library of its own beside libssa
+PEAKS_LIB = os.path.join(PKG, "libssa_peaks.so")
+PEAKS_SOURCES = ["ssa_peaks.hip"]
 ARCH = os.environ.get("SSA_OFFLOAD_ARCH", "gfx950")
 
 CXXFLAGS = [
@@ -50,14 +53,7 @@ def _compile(src: str, verbose: bool, build_dir: str = BUILD, defines=()) -> str
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None, out: str = LIB, build_dir: str = BUILD,
-          defines=()) -> str:
-    """Compile every source and link the library (default: in-tree libssa.so);
-    ``defines`` are extra NAME=VALUE preprocessor definitions (tuning knobs)."""
-    os.makedirs(build_dir, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2) // 2))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+def _link(objs, out: str, verbose: bool) -> str:
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
@@ -66,6 +62,22 @@ def build(verbose: bool = False, jobs: int | None = None, out: str = LIB, build_
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, jobs: int | None = None, out: str = LIB, build_dir: str = BUILD,
+          defines=(), peaks: bool = True) -> str:
+    """Compile every source and link the library (default: in-tree libssa.so),
+    and the measurement library libssa_peaks.so beside it (``peaks``);
+    ``defines`` are extra NAME=VALUE preprocessor definitions (tuning knobs)."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = SOURCES + (PEAKS_SOURCES if peaks else [])
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2) // 2))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), srcs))
+    _link(objs[:len(SOURCES)], out, verbose)
+    if peaks:
+        _link(objs[len(SOURCES):], PEAKS_LIB, verbose)
     return out
 
 

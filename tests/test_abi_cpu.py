@@ -12,13 +12,14 @@ from block_sparse_attention_kv_amd import ssa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssa.h")
+PEAKS_HEADER = os.path.join(ROOT, "include", "ssa_peaks.h")
 
 FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
 MISALIGNED = ctypes.c_void_p(0x10002)
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
 
@@ -43,6 +44,23 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(declared) == set(ssa.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_peaks_library_exports_its_header():
+    from block_sparse_attention_kv_amd import peaks
+    if not os.path.exists(peaks.LIB_PATH):
+        from block_sparse_attention_kv_amd import build
+        build.build()
+    plib = peaks.load_library()
+    declared = header_functions(PEAKS_HEADER)
+    assert set(declared) == set(peaks.EXPORTS)
+    for name in declared:
+        assert hasattr(plib, name), name
+    # argument checks return before any launch
+    assert plib.ssa_peak_mfma(0, 1, FAKE, None) == 1
+    assert plib.ssa_peak_read(FAKE, 24, FAKE, 1, None) == 1
+    assert plib.ssa_peak_copy(FAKE, MISALIGNED, 32, 1, None) == 1
+    assert plib.ssa_peak_clock(0, FAKE, None) == 1
 
 
 def test_version_and_status_strings(lib):
