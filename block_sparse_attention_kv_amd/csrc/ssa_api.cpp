@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/ssa.h"
 #include "ssa_internal.hpp"
 
@@ -83,6 +85,57 @@ ssa_status_t make_geometry(const ssa_shape_t* s, ssa::Geometry* g, bool* empty, 
     if (!(p)) return fail(SSA_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);                    \
     if (!aligned((p), (align))) return fail(SSA_ERR_INVALID_ARG, "%s: %s is not %d-byte aligned", fn, #p, (int)(align)); \
   } while (0)
+
+// Scratch of ssa_block_sparse_attn_fwd_noalloc: one static array per GPU, held
+// until the process ends.  The first kScratchQueueBytes are the prefill work
+// queue (zero between calls: every completed launch leaves its counters zero);
+// the rest holds the decode partials (written before they are read).
+constexpr size_t kScratchQueueBytes = 1024;
+constexpr size_t kScratchPartialBytes = (size_t)8 << 20;
+constexpr size_t kScratchBytes = kScratchQueueBytes + kScratchPartialBytes;
+static_assert(kScratchQueueBytes >= ssa::kQueueBytes, "queue region too small");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_zeroed[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of the current device's scratch array (looked up once per
+// device).  Until one clearing of the queue region has run outside stream
+// capture, every call enqueues it first (inside a capture it becomes part of
+// the graph).
+ssa_status_t scratch_base(hipStream_t stream, uint8_t** base, const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(SSA_ERR_UNSUPPORTED, "%s: device %d (at most %d)", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    const int words = (int)(kScratchQueueBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       (uint32_t*)g_scratch_ptr[dev], words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (cs == hipStreamCaptureStatusNone) g_scratch_zeroed[dev] = true;
+  }
+  *base = g_scratch_ptr[dev];
+  return SSA_OK;
+}
 
 }  // namespace
 
@@ -184,7 +237,7 @@ ssa_status_t select_topk_impl(const ssa_shape_t* shape, const float* scores, int
 ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
                              const int32_t* block_idx, bool shared, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, hipStream_t stream, const char* fn,
-                             const float* block_bias = nullptr, bool biased = false) {
+                             const float* block_bias = nullptr, bool biased = false, bool use_scratch = false) {
   ssa::Geometry g;
   bool empty;
   ssa_status_t st = make_geometry(shape, &g, &empty, fn);
@@ -217,11 +270,28 @@ ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void
       return fail(SSA_ERR_UNSUPPORTED, "%s: decode needs (query heads per KV head) x topk <= %d and <= %d key blocks",
                   fn, ssa::kDecodeMaxList, ssa::kDecodeMaxBlocks);
     const size_t need = ssa::decode_workspace_bytes(g.batch, g.hq, g.hkv);
+    if (use_scratch) {
+      if (need > kScratchPartialBytes)
+        return fail(SSA_ERR_WORKSPACE, "%s: %zu bytes of scratch needed, the static array holds %zu", fn, need,
+                    kScratchPartialBytes);
+      uint8_t* base = nullptr;
+      st = scratch_base(stream, &base, fn);
+      if (st != SSA_OK) return st;
+      workspace = base + kScratchQueueBytes;
+      workspace_bytes = kScratchPartialBytes;
+    }
     if (workspace_bytes < need)
       return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
     CHECK_PTR(workspace, 16, fn);
     e = ssa::launch_attn_decode(a, (float*)workspace, g, stream);
   } else {
+    if (use_scratch) {
+      uint8_t* base = nullptr;
+      st = scratch_base(stream, &base, fn);
+      if (st != SSA_OK) return st;
+      workspace = base;
+      workspace_bytes = kScratchQueueBytes;
+    }
     // an optional zeroed workspace of kQueueBytes makes the launch persistent
     if (workspace && workspace_bytes >= ssa::kQueueBytes) {
       CHECK_PTR(workspace, 16, fn);
@@ -382,6 +452,13 @@ ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, 
                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return sparse_fwd_impl(shape, q, k, v, block_idx, false, out, lse, workspace, workspace_bytes, stream,
                          "ssa_block_sparse_attn_fwd");
+}
+
+ssa_status_t ssa_block_sparse_attn_fwd_noalloc(const ssa_shape_t* shape, const void* q, const void* k,
+                                               const void* v, const int32_t* block_idx, void* out, float* lse,
+                                               hipStream_t stream) {
+  return sparse_fwd_impl(shape, q, k, v, block_idx, false, out, lse, nullptr, 0, stream,
+                         "ssa_block_sparse_attn_fwd_noalloc", nullptr, false, true);
 }
 
 ssa_status_t ssa_block_sparse_attn_fwd_shared(const ssa_shape_t* shape, const void* q, const void* k,

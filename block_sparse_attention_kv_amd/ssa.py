@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared", "ssa_block_sparse_attn_fwd_shared",
     "ssa_full_attn_fwd_dropped_mass_shared", "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
     "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_block_summaries_learned", "ssa_entmax_route",
-    "ssa_block_sparse_attn_fwd_biased", "ssa_workspace_bytes",
+    "ssa_block_sparse_attn_fwd_biased", "ssa_block_sparse_attn_fwd_noalloc", "ssa_workspace_bytes",
     "ssa_status_string",
     "ssa_last_error", "ssa_version",
 )
@@ -82,12 +82,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssa_block_summaries_learned.argtypes = [sp, vp, vp, vp, vp]
     lib.ssa_entmax_route.argtypes = [sp, vp, f32, f32, f32, vp, vp, vp, vp]
     lib.ssa_block_sparse_attn_fwd_biased.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssa_block_sparse_attn_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
     for fn in ("ssa_block_summaries", "ssa_block_scores", "ssa_select_topk",
                "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared",
                "ssa_block_sparse_attn_fwd_shared", "ssa_full_attn_fwd_dropped_mass_shared",
                "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
                "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_block_summaries_learned",
-               "ssa_entmax_route", "ssa_block_sparse_attn_fwd_biased"):
+               "ssa_entmax_route", "ssa_block_sparse_attn_fwd_biased", "ssa_block_sparse_attn_fwd_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ssa_workspace_bytes.argtypes = [sp, ctypes.c_int]
     lib.ssa_workspace_bytes.restype = ctypes.c_size_t
@@ -333,6 +334,21 @@ def ssa_block_sparse_attn_fwd(shape: Shape, q, k, v, block_idx, workspace: Optio
     _check(name, getattr(load_library(), name)(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(q.device)))
+    return out, lse
+
+
+def ssa_block_sparse_attn_fwd_noalloc(shape: Shape, q, k, v, block_idx, out: torch.Tensor, lse: torch.Tensor):
+    """ssa_block_sparse_attn_fwd with the library's static scratch array as
+    workspace: the caller passes the outputs and nothing is allocated."""
+    if out is None or lse is None:
+        raise ValueError("ssa_block_sparse_attn_fwd_noalloc: out and lse are required")
+    b_, hq_, hkv_, sq_, skv_, d_, nqb_, _, k_ = _dims(shape)
+    _validate("ssa_block_sparse_attn_fwd_noalloc", q=(q, BF16, (b_, hq_, sq_, d_)),
+              k=(k, BF16, (b_, hkv_, skv_, d_)), v=(v, BF16, (b_, hkv_, skv_, d_)),
+              block_idx=(block_idx, I32, (b_, hq_, nqb_, k_)), out=(out, BF16, (b_, hq_, sq_, d_)),
+              lse=(lse, F32, (b_, hq_, sq_)))
+    _check("ssa_block_sparse_attn_fwd_noalloc", load_library().ssa_block_sparse_attn_fwd_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse), _stream(q.device)))
     return out, lse
 
 

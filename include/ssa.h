@@ -236,6 +236,25 @@ ssa_status_t ssa_block_sparse_attn_fwd_early_stop(const ssa_shape_t* shape, cons
                                                   float tau, void* out, float* lse, int32_t* blocks_used,
                                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, kernels and results as ssa_block_sparse_attn_fwd, with the
+ * workspace taken from a static array of the library instead of an argument.
+ * The call allocates nothing.  The array holds 8 MiB + 1 KiB per GPU, from
+ * the first call on that GPU until the process ends:
+ *   decode (seq_q == 1): batch * n_q_heads * slices * 264 bytes of partials,
+ *     at most 8 MiB (64 sequences x 32 query heads on 2 KV heads use 4.3 MB);
+ *     a larger shape fails with SSA_ERR_WORKSPACE and launches nothing.
+ *   prefill: the 1 KiB work queue of the persistent launch.
+ * The first call on a GPU looks the array up and enqueues one clearing of
+ * the queue on `stream` (repeated on later calls while it has only been
+ * captured into a graph).  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU, from any stream or graph, race and
+ * give wrong results; calls ordered one after another are safe. */
+ssa_status_t ssa_block_sparse_attn_fwd_noalloc(const ssa_shape_t* shape, const void* q, const void* k,
+                                               const void* v, const int32_t* block_idx, void* out, float* lse,
+                                               hipStream_t stream);
+
 /* Backward of the block-sparse forward: for the scalar L = sum(dout * out),
  * with P = exp(scale * q_r . k_c - lse_r) on the keys c that row r attends to
  * in ssa_block_sparse_attn_fwd (block_idx as there) and D_r = dout_r . out_r,

@@ -139,6 +139,22 @@ def test_early_stop_threshold_validation(lib):
     assert b"scores is NULL" in lib.ssa_last_error()
 
 
+def test_noalloc_validation(lib):
+    """The allocation-free forward validates like the workspace entry point and
+    refuses a decode whose partials exceed its static array, all before any
+    HIP call."""
+    assert lib.ssa_block_sparse_attn_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                 None) == ssa.SSA_ERR_INVALID_ARG
+    p = ctypes.byref(good_shape())
+    assert lib.ssa_block_sparse_attn_fwd_noalloc(p, FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE,
+                                                 None) == ssa.SSA_ERR_INVALID_ARG
+    # 1024 sequences x 32 heads x 1 slice x 264 B = 8.65 MB > 8 MiB
+    big = good_shape(batch=1024, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=128, q_offset=127, topk=2)
+    assert lib.ssa_block_sparse_attn_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                 None) == ssa.SSA_ERR_WORKSPACE
+    assert b"scratch" in lib.ssa_last_error()
+
+
 def test_decode_workspace(lib):
     sh = good_shape(batch=64, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=32768, q_offset=32767, topk=17)
     need = lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_SPARSE_FWD)
