@@ -90,6 +90,10 @@ __device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(ka[kb][ks], qop[qb][ks], s[kb][qb]);
   }
+  // keep the reads ahead of the products: the compiler otherwise reuses one
+  // operand register set and waits for each read in turn
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 }
 
 // Online-softmax update for one tile; leaves packed bf16 probabilities in pk.
@@ -120,12 +124,12 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
   bool grow = false;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float mx = fmaxf(s[0][qb][0], s[0][qb][1]);
+    float mx = max_nan(s[0][qb][0], s[0][qb][1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[0][qb][r]), s[0][qb][r + 1]);
+    for (int r = 2; r < 16; r += 2) mx = max_nan(max_nan(mx, s[0][qb][r]), s[0][qb][r + 1]);
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[1][qb][r]), s[1][qb][r + 1]);
-    mx = max_xor32(mx);
+    for (int r = 0; r < 16; r += 2) mx = max_nan(max_nan(mx, s[1][qb][r]), s[1][qb][r + 1]);
+    mx = max_nan_xor32(mx);
     mt[qb] = BIAS ? fmaf(mx, c, b2) : mx * c;
     grow |= !(mt[qb] <= st.m[qb] + kRescaleSlack);
   }

@@ -259,10 +259,15 @@ __device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, con
     for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k)
       dma_1k(gtile, off.v[k], __builtin_amdgcn_readfirstlane(base + (off.first + k * STEP) * 1024));
   } else {
+    // The lane index passes through an opaque copy here, so that the partial
+    // path's offsets are computed on that (rare) path instead of being hoisted
+    // out of the tile loop into registers the full path needs.
+    int l = lane;
+    asm volatile("" : "+v"(l));
 #pragma unroll
     for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k) {
       const int c = off.first + k * STEP;
-      dma_1k_ragged(gtile, slice_offset<S>(c, lane, nvalid), __builtin_amdgcn_readfirstlane(base + c * 1024));
+      dma_1k_ragged(gtile, slice_offset<S>(c, l, nvalid), __builtin_amdgcn_readfirstlane(base + c * 1024));
     }
   }
 }
