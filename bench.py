@@ -546,6 +546,53 @@ def bench_dash(args, torch, ssa, W, alpha=1.5, gamma=800.0, sigma=1.0, cap=64):
             "attn_tflops": round(tf, 2), "attn_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
+def bench_trace(args, torch, ssa, W, workloads=("prefill_8k", "structured_8k")):
+    """One launch each of the block-sparse and the full forward with per-workgroup
+    timing records (workspace past the work queue): the shader clock each
+    workgroup ran at, how evenly the persistent workgroups finished, and the
+    rate against the matrix peak at the measured clock."""
+    from block_sparse_attention_kv_amd.profiling import TRACE_WORDS, trace_summary
+    dev = torch.device("cuda:0")
+    res = {}
+    for name in workloads:
+        w = W.BY_NAME[name]
+        q, k, v = (t.to(dev) for t in W.make_inputs(w))
+        shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+        nqb = ssa.n_blocks(w.seq_q, w.block)
+        fb0 = 0 if w.full_rows is None else w.full_rows[0] // w.block
+        fcnt = nqb - fb0
+        scores, _ = ssa.ssa_block_scores(shape, q, k)
+        idx = ssa.ssa_select_topk(shape, scores)
+        qbytes = ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD)
+        cap = 8192
+        ws = torch.zeros((qbytes + cap * TRACE_WORDS * 4,), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        rows = fcnt * w.block
+        of = torch.empty((w.batch, w.n_q_heads, rows, w.head_dim), dtype=torch.bfloat16, device=dev)
+        lf = torch.empty((w.batch, w.n_q_heads, rows), dtype=torch.float32, device=dev)
+        dm = torch.empty_like(lf)
+        pairs_sp = w.batch * w.n_q_heads * sparse_useful_pairs(nqb, w.topk, w.block)
+        pairs_full = w.batch * w.n_q_heads * full_useful_pairs(fb0 * w.block, fb0 * w.block + rows)
+        calls = {
+            "sparse_attn": (lambda: ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx, workspace=ws, out=out, lse=lse),
+                            4.0 * w.head_dim * pairs_sp),
+            "full_attn": (lambda: ssa.ssa_full_attn_fwd_dropped_mass(shape, q, k, v, idx, fb0, fcnt, out=of, lse=lf,
+                                                                     dropped=dm, workspace=ws),
+                          4.0 * w.head_dim * pairs_full),
+        }
+        res[name] = {}
+        for kname, (fn, fl) in calls.items():
+            for _ in range(4):          # the last launch's records are kept
+                fn()
+            torch.cuda.synchronize()
+            recs = ws[qbytes:].view(torch.int32).cpu().numpy().view("uint32")
+            res[name][kname] = trace_summary(recs, fl, PEAK_BF16_TFLOPS)
+            ws[qbytes:].zero_()
+        del q, k, v, scores, idx, ws, out, lse, of, lf, dm
+    return res
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -687,6 +734,7 @@ def main():
         for name in ("structured_8k", "structured_8k_tie", "extrap_32k"):
             legs[name] = prefill_leg(bench_prefill(args, torch, ssa, W, workload=name, steps=args.leg_steps))
     peaks = None if args.no_peaks else bench_peaks(args, torch, ssa, W)
+    trace = None if args.no_peaks else bench_trace(args, torch, ssa, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, W)
     w = pre["w"]
     line = {
@@ -717,6 +765,7 @@ def main():
         "decode": dec,
         "workload_legs": legs,
         "peaks": peaks,
+        "workgroup_trace": trace,
         "shared_selection": shared,
         "early_stop": None if args.no_shared else bench_early_stop(args, torch, ssa, W),
         "backward": None if args.no_backward else bench_backward(args, torch, ssa, W),

@@ -86,6 +86,14 @@ ssa_status_t make_geometry(const ssa_shape_t* s, ssa::Geometry* g, bool* empty, 
     if (!aligned((p), (align))) return fail(SSA_ERR_INVALID_ARG, "%s: %s is not %d-byte aligned", fn, #p, (int)(align)); \
   } while (0)
 
+// Workspace bytes past the work queue hold per-workgroup timing records.
+void set_trace(ssa::AttnArgs* a, void* workspace, size_t workspace_bytes) {
+  const size_t rec = (workspace_bytes - ssa::kQueueBytes) / (ssa::kTraceWords * sizeof(uint32_t));
+  if (rec == 0) return;
+  a->trace = (uint32_t*)((uint8_t*)workspace + ssa::kQueueBytes);
+  a->trace_cap = rec > (size_t)INT32_MAX ? INT32_MAX : (int)rec;
+}
+
 // Scratch of ssa_block_sparse_attn_fwd_noalloc: one static array per GPU, held
 // until the process ends.  The first kScratchQueueBytes are the prefill work
 // queue (zero between calls: every completed launch leaves its counters zero);
@@ -296,6 +304,7 @@ ssa_status_t sparse_fwd_impl(const ssa_shape_t* shape, const void* q, const void
     if (workspace && workspace_bytes >= ssa::kQueueBytes) {
       CHECK_PTR(workspace, 16, fn);
       a.queue = (int32_t*)workspace;
+      set_trace(&a, workspace, workspace_bytes);
     }
     e = ssa::launch_attn_prefill(a, false, g, stream);
   }
@@ -337,6 +346,7 @@ ssa_status_t full_impl(const ssa_shape_t* shape, const void* q, const void* k, c
   if (workspace && workspace_bytes >= ssa::kQueueBytes) {
     CHECK_PTR(workspace, 16, fn);
     a.queue = (int32_t*)workspace;
+    set_trace(&a, workspace, workspace_bytes);
   }
   hipError_t e = ssa::launch_attn_prefill(a, true, g, stream);
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);

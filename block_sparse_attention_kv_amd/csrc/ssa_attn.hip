@@ -223,6 +223,43 @@ __device__ __forceinline__ void unit_epilogue(const UnitState& st, const AttnArg
   }
 }
 
+// Optional timing record of a persistent workgroup (AttnArgs::trace): a few
+// scalar counter reads per unit; written by lane 0 at the end.
+struct WgTrace {
+  uint64_t rt0, t0, l0;
+  uint32_t loop, units, tiles;
+  __device__ __forceinline__ void begin() {
+    rt0 = __builtin_amdgcn_s_memrealtime();
+    t0 = __builtin_amdgcn_s_memtime();
+    loop = units = tiles = 0u;
+  }
+  __device__ __forceinline__ void loop_begin() { l0 = __builtin_amdgcn_s_memtime(); }
+  __device__ __forceinline__ void loop_end(int nt) {
+    loop += (uint32_t)(__builtin_amdgcn_s_memtime() - l0);
+    units += 1u;
+    tiles += (uint32_t)nt;
+  }
+  __device__ __forceinline__ void end(const AttnArgs& a, int lane) {
+    if (!a.trace || (int)blockIdx.x >= a.trace_cap) return;
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t rt1 = __builtin_amdgcn_s_memrealtime();
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if (lane == 0) {
+      uint32_t* d = a.trace + (size_t)kTraceWords * blockIdx.x;
+      d[0] = (uint32_t)rt0;
+      d[1] = (uint32_t)rt1;
+      d[2] = (uint32_t)(t1 - t0);
+      d[3] = loop;
+      d[4] = units;
+      d[5] = tiles;
+      d[6] = hw;
+      d[7] = xcc;
+    }
+  }
+};
+
 // Workgroup id -> (KV group gi = b*Hkv + g, unit index within the group, 0 = heaviest).
 // Workgroups are dealt to the 8 XCDs round-robin; when the counts allow, each
 // KV group's units stay on a fixed subset of XCDs so its K/V stay in that L2.
@@ -315,6 +352,8 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
   int w = (int)blockIdx.x;
   TileOffsets<1, 0> toff;
   toff.init(lane, 0);
+  WgTrace tr;
+  tr.begin();
   while (w >= 0) {
     int gi, u;
     map_unit(w, n_groups, per_group, gi, u);
@@ -370,13 +409,16 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
       wait_vmem<0>();
       __builtin_amdgcn_wave_barrier();
     }
+    tr.loop_begin();
     sparse_tiles<BIAS>(sK, sV, sList, sBias, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd,
                        geo.q_offset + i * kBlock, geo.scale_log2, qop, st, lane, l32, hl);
+    tr.loop_end(nt);
     unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
     if (!a.queue) break;
     wait_lds_reads();  // the next unit's tile requests overwrite sK and sV
     w = queue_next(a.queue, a.n_xcc, n_groups * per_group, lane);
   }
+  tr.end(a, lane);
 }
 
 // Block-sparse forward with early stopping.  One wavefront per unit, as
@@ -535,6 +577,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
   int w = (int)blockIdx.x;
   TileOffsets<NW, 0> toff;
   toff.init(lane, wave);
+  WgTrace tr;
+  tr.begin();
   while (w >= 0) {
     int gi, u;
     map_unit(w, n_groups, per_group, gi, u);
@@ -574,6 +618,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
     const int pos0 = geo.q_offset + i * kBlock;
     int sel_ptr = 0;
     int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
+    tr.loop_begin();
     for (int t = 0; t < nt; ++t) {
       const int j = tile_block(t);
       wait_vmem<0>();   // this wave's share of tile t landed
@@ -600,12 +645,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
       tile_softmax<FULL, BIAS>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c, nullptr, b2);
       tile_pv(sV[t & 1], pk, st, lane);
     }
+    tr.loop_end(nt);
     unit_epilogue<FULL>(st, a, geo, bh, i, l32, hl);
     if (!a.queue) break;
     wait_lds_reads();
     __syncthreads();  // every wave is done with the tiles, the lists and the unit slot
     w = next_unit();
   }
+  if (wave == 0) tr.end(a, lane);
 }
 
 }  // namespace

@@ -35,7 +35,15 @@ struct AttnArgs {
   int rows_out;      // rows per (b, h) in the output tensors
   int32_t* queue;    // prefill: work queue of a persistent launch (kQueueBytes, zero between calls), or null
   int n_xcc;         // shares the queue is split into (1..kMaxXcc), one per XCD
+  uint32_t* trace;   // optional per-workgroup timing records (kTraceWords each), or null
+  int trace_cap;     // records the trace buffer holds
 };
+
+// Timing record of one workgroup of a persistent prefill launch: 100 MHz
+// real-time counter at start and end (low 32 bits), shader cycles from start
+// to end, shader cycles inside the tile loops, units and tiles processed, the
+// hardware id and the XCC id of the wavefront that wrote it.
+constexpr int kTraceWords = 8;
 
 // Work queue of the persistent prefill launches, in the caller's workspace:
 // one counter per share of the launch, each on its own 128-byte line (all

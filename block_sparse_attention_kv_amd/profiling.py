@@ -257,18 +257,20 @@ def _counters_per_dispatch(d: str):
 def mfma_markdown(d: str, title: str = "", command: str = "") -> str:
     """Per kernel, averaged over its dispatches: matrix-core busy fraction
     (busy cycles summed over the SIMDs / (active cycles of one die x SIMDs)),
-    the clock the dispatch ran at (active cycles of one die / duration),
     executed bf16 matrix flops (MOPS x 512), matrix instructions, and vector
-    instructions issued per matrix instruction."""
+    instructions issued per matrix instruction.  GRBM_GUI_ACTIVE spans the
+    counting window, which adds some 20-30 thousand cycles to every dispatch,
+    so the busy fraction of a short dispatch reads low; no clock is derived
+    from it (the attention launches' own timing records give the clock)."""
     per = _counters_per_dispatch(d)
     out = [f"# {title}".rstrip(), ""]
     if command:
         out += ["Command:", "", "```", command, "```", ""]
-    out += ["| kernel | dispatches | matrix-core busy % | clock GHz | executed bf16 GFLOP | MFMA instr (M) | "
+    out += ["| kernel | dispatches | matrix-core busy % | executed bf16 GFLOP | MFMA instr (M) | "
             "VALU instr per MFMA instr |",
-            "|---|---|---|---|---|---|---|"]
+            "|---|---|---|---|---|---|"]
     for cls in sorted(per):
-        util, clk, gflop, nmf, ratio = [], [], [], [], []
+        util, gflop, nmf, ratio = [], [], [], []
         for ctr, dur in per[cls].values():
             if not all(c in ctr for c in MFMA_COUNTERS) or ctr["SQ_INSTS_MFMA"] <= 0:
                 continue
@@ -276,14 +278,13 @@ def mfma_markdown(d: str, title: str = "", command: str = "") -> str:
             if gui <= 0 or dur <= 0:
                 continue
             util.append(100.0 * ctr["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM))
-            clk.append(gui / dur)
             gflop.append(ctr["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9)
             nmf.append(ctr["SQ_INSTS_MFMA"] / 1e6)
             ratio.append(ctr["SQ_INSTS_VALU"] / ctr["SQ_INSTS_MFMA"])
         if not util:
             continue
         avg = lambda v: sum(v) / len(v)
-        out.append(f"| {cls} | {len(util)} | {avg(util):.1f} | {avg(clk):.2f} | {avg(gflop):.2f} | {avg(nmf):.3f} | "
+        out.append(f"| {cls} | {len(util)} | {avg(util):.1f} | {avg(gflop):.2f} | {avg(nmf):.3f} | "
                    f"{avg(ratio):.2f} |")
     return "\n".join(out) + "\n"
 
@@ -317,6 +318,51 @@ def waits_markdown(d: str, title: str = "", command: str = "") -> str:
         out.append(f"| {cls} | {len(fr['SQ_WAIT_ANY'])} | " +
                    " | ".join(f"{avg(fr[c]):.3f}" for c in WAIT_COUNTERS[1:]) + " |")
     return "\n".join(out) + "\n"
+
+
+TRACE_WORDS = 8  # words per workgroup timing record of a persistent attention launch
+
+
+def trace_summary(records, flops: float = 0.0, peak_tflops: float = 2516.6, nominal_ghz: float = 2.4) -> dict:
+    """Summary of the per-workgroup timing records of one persistent launch
+    (uint32 [n, 8]: real-time start/end in 10 ns ticks, shader cycles, cycles
+    in the tile loops, units, tiles, hardware id, XCC id; unused rows zero).
+    The shader clock of a workgroup is its cycles over its real time; with
+    ``flops`` the launch's rate is also given against the matrix peak scaled
+    to the median measured clock."""
+    import numpy as np
+    r = np.asarray(records, dtype=np.uint64).reshape(-1, TRACE_WORDS).astype(np.int64)
+    r = r[r[:, 4] > 0]
+    if len(r) == 0:
+        return {}
+    rt0, rt1 = r[:, 0], r[:, 1]
+    rt1 = np.where(rt1 < rt0, rt1 + (1 << 32), rt1)
+    base = rt0.min()
+    start_us, end_us = (rt0 - base) * 1e-2, (rt1 - base) * 1e-2
+    busy_us = end_us - start_us
+    ghz = r[:, 2] / np.maximum(rt1 - rt0, 1) * 0.1
+    span = float(end_us.max())
+    q = lambda x: [round(float(np.percentile(x, p)), 3) for p in (0, 10, 50, 90, 100)]
+    out = {
+        "workgroups": int(len(r)),
+        "span_us": round(span, 2),
+        "start_us_p0_10_50_90_100": q(start_us),
+        "end_us_p0_10_50_90_100": q(end_us),
+        "clock_ghz_p0_10_50_90_100": q(ghz),
+        "busy_fraction": round(float(busy_us.sum() / (len(r) * span)), 4) if span > 0 else None,
+        "loop_fraction_of_cycles": round(float(r[:, 3].sum() / max(r[:, 2].sum(), 1)), 4),
+        "tiles_per_workgroup_p0_50_100": [int(r[:, 5].min()), int(np.median(r[:, 5])), int(r[:, 5].max())],
+        "units": int(r[:, 4].sum()),
+        "tiles": int(r[:, 5].sum()),
+        "loop_cycles_per_tile_p10_50_90": [round(float(np.percentile(r[:, 3] / np.maximum(r[:, 5], 1), p)), 1)
+                                           for p in (10, 50, 90)],
+    }
+    if flops and span > 0:
+        clk = float(np.median(ghz))
+        tf = flops / (span * 1e-6) / 1e12
+        out["tflops_over_span"] = round(tf, 2)
+        out["frac_of_peak_at_measured_clock"] = round(tf / (peak_tflops * clk / nominal_ghz), 4)
+    return out
 
 
 def main(argv=None):

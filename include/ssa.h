@@ -149,6 +149,10 @@ ssa_status_t ssa_select_topk(const ssa_shape_t* shape, const float* scores, int3
  *     query blocks from the queue); every call leaves the queue zero again, so
  *     one buffer serves every later call, but calls sharing it must not
  *     overlap in time.  NULL or fewer bytes: one workgroup per query block.
+ *     Bytes past the queue, if any, receive one timing record of 8 uint32 per
+ *     workgroup of the launch (as many as fit): 100 MHz real-time counter at
+ *     start and end (low 32 bits), shader cycles start to end, shader cycles
+ *     in the tile loops, query blocks and tiles processed, hardware id, XCC id.
  *   q, k, v    bf16 as above;  block_idx int32 [b,Hq,nqb,topk]
  *   out        bf16 [b,Hq,seq_q,d] (output);  lse fp32 [b,Hq,seq_q] (output) */
 ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, const void* k,
@@ -171,7 +175,8 @@ ssa_status_t ssa_block_sparse_attn_fwd(const ssa_shape_t* shape, const void* q, 
  * Workspace: optional work queue of ssa_workspace_bytes(shape,
  * SSA_OP_FULL_FWD) bytes, as for a prefill ssa_block_sparse_attn_fwd
  * (zero-filled before the first call, left zero by every call; NULL: one
- * workgroup per group of query heads and query block). */
+ * workgroup per group of query heads and query block); bytes past the queue
+ * receive the same per-workgroup timing records. */
 ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void* q, const void* k,
                                             const void* v, const int32_t* block_idx,
                                             int32_t q_block_begin, int32_t q_block_count,

@@ -122,4 +122,35 @@ def test_mfma_busy_fraction(tmp_path):
     d = str(tmp_path / "m")
     _write_csv(os.path.join(d, "x_counter_collection.csv"), hdr, rows)
     md = P.mfma_markdown(d)
-    assert "| full_attn | 1 | 25.0 | 2.00 | 0.51 | 2.000 | 11.00 |" in md
+    assert "| full_attn | 1 | 25.0 | 0.51 | 2.000 | 11.00 |" in md
+
+
+def test_trace_summary_hand_case():
+    """Two workgroup records (third row unused): clock = cycles / ticks x 0.1 GHz,
+    span from the earliest start to the latest end, busy fraction = summed
+    busy time / (workgroups x span)."""
+    import numpy as np
+    from block_sparse_attention_kv_amd.profiling import trace_summary
+    r = np.zeros((3, 8), dtype=np.uint32)
+    # ticks of 10 ns: wg0 runs 0..1000 (10 us), wg1 runs 500..1500 (10 us)
+    r[0, :6] = [5000, 6000, 20000, 15000, 2, 32]   # 20000 cycles / 10 us = 2.0 GHz
+    r[1, :6] = [5500, 6500, 15000, 9000, 1, 16]    # 15000 cycles / 10 us = 1.5 GHz
+    s = trace_summary(r, flops=1e9, peak_tflops=1000.0, nominal_ghz=2.0)
+    assert s["workgroups"] == 2 and s["units"] == 3 and s["tiles"] == 48
+    assert s["span_us"] == 15.0
+    assert s["clock_ghz_p0_10_50_90_100"][0] == 1.5 and s["clock_ghz_p0_10_50_90_100"][-1] == 2.0
+    assert abs(s["busy_fraction"] - 20.0 / 30.0) < 1e-4
+    assert abs(s["loop_fraction_of_cycles"] - 24000 / 35000) < 1e-4
+    # 1e9 flop over 15 us = 66.67 TFLOP/s; peak at the median clock 1.75 GHz = 875 TFLOP/s
+    assert abs(s["tflops_over_span"] - 66.67) < 0.01
+    assert abs(s["frac_of_peak_at_measured_clock"] - 66.6667 / 875.0) < 1e-4
+
+
+def test_trace_summary_wraps_the_tick_counter():
+    import numpy as np
+    from block_sparse_attention_kv_amd.profiling import trace_summary
+    r = np.zeros((1, 8), dtype=np.uint32)
+    r[0, :6] = [0xFFFFFF00, 0x00000100, 1024 * 16, 0, 1, 1]   # 512 ticks across the wrap
+    s = trace_summary(r)
+    assert s["span_us"] == 5.12
+    assert abs(s["clock_ghz_p0_10_50_90_100"][2] - 3.2) < 1e-6
