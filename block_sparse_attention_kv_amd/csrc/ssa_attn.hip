@@ -314,6 +314,14 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
   TileOffsets<1, 0> toff;
   toff.init(lane, 0);
   for (int t = 0; t < nt; ++t) {
+    // Two wavefronts share each SIMD; left to the oldest-first arbiter one of
+    // them runs close to its solo speed and the other at about half, so the
+    // pair finishes its units far apart.  Alternating the issue priority every
+    // tile keeps the two at similar speed.
+    if (t & 1)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
     const int j = __builtin_amdgcn_readfirstlane(sList[t]);
     const bool more = t + 1 < nt;
     const int jn = more ? __builtin_amdgcn_readfirstlane(sList[t + 1]) : 0;
@@ -333,6 +341,7 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     wait_lds_reads();
     if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sV, lane, toff);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Block-sparse forward: a wavefront per unit, private K and V buffers.  With
@@ -620,6 +629,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
     int nxt = nsel > 0 ? __builtin_amdgcn_readfirstlane(sList[wave][0]) : -1;
     tr.loop_begin();
     for (int t = 0; t < nt; ++t) {
+      // issue priority alternates every tile, as in the block-sparse loop
+      if (t & 1)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
       const int j = tile_block(t);
       wait_vmem<0>();   // this wave's share of tile t landed
       __syncthreads();  // ... every wave's share; and every wave is done with tile t-1
@@ -645,6 +659,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
       tile_softmax<FULL, BIAS>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c, nullptr, b2);
       tile_pv(sV[t & 1], pk, st, lane);
     }
+    __builtin_amdgcn_s_setprio(0);
     tr.loop_end(nt);
     unit_epilogue<FULL>(st, a, geo, bh, i, l32, hl);
     if (!a.queue) break;
