@@ -345,7 +345,8 @@ def bench_peaks(args, torch, ssa, W):
 
 def bench_decode(args, torch, ssa, W, shared=False):
     """One decode step = scores, top-k, attention over the selected blocks;
-    ``shared`` uses the group-shared selection."""
+    ``shared`` uses the group-shared selection (then scores and top-k are one
+    fused launch)."""
     w = W.DECODE_32K
     dev = torch.device("cuda:0")
     q0, k0, v0 = W.make_inputs(w)
@@ -359,7 +360,6 @@ def bench_decode(args, torch, ssa, W, shared=False):
     nkb = ssa.n_blocks(w.seq_kv, w.block)
     scores = torch.empty((w.batch, w.n_q_heads, 1, nkb), dtype=torch.float32, device=dev)
     idx = torch.empty((w.batch, w.n_kv_heads if shared else w.n_q_heads, 1, w.topk), dtype=torch.int32, device=dev)
-    select = ssa.ssa_select_topk_shared if shared else ssa.ssa_select_topk
     out = torch.empty_like(copies[0][0])
     lse = torch.empty((w.batch, w.n_q_heads, 1), dtype=torch.float32, device=dev)
     ws = torch.empty((ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD),), dtype=torch.uint8, device=dev)
@@ -367,8 +367,16 @@ def bench_decode(args, torch, ssa, W, shared=False):
 
     def step(t, c):
         q, k, v, ks = copies[c % len(copies)]
-        t.run("decode_scores", ssa.ssa_block_scores, shape, q, None, ks, scores=scores)
-        t.run("decode_topk", select, shape, scores, idx)
+        if shared:
+            # one ranked row per KV group: scores and selection in one launch
+            # (the scores are still written out)
+            t.run("decode_scores_select", ssa.ssa_decode_scores_select, shape, q, ks, scores=scores, idx=idx,
+                  shared=True)
+        else:
+            # per-head rows: the separate launches spread the fp64 scoring and
+            # the 2048 selections over every compute unit
+            t.run("decode_scores", ssa.ssa_block_scores, shape, q, None, ks, scores=scores)
+            t.run("decode_topk", ssa.ssa_select_topk, shape, scores, idx)
         t.run("decode_attn", ssa.ssa_block_sparse_attn_fwd, shape, q, k, v, idx, workspace=ws, out=out, lse=lse,
               shared=shared)
 
@@ -386,16 +394,20 @@ def bench_decode(args, torch, ssa, W, shared=False):
     union_blocks = int(sel[..., :nkb].sum())
     kv_bytes = union_blocks * w.block * w.head_dim * 2 * 2
     attn_bytes = kv_bytes + copies[0][0].numel() * 2 * 2 + idx.numel() * 4 + lse.numel() * 4
+    # summaries and queries read, scores written; the selection reads the scores and writes the indices
     score_bytes = copies[0][3].numel() * 4 + copies[0][0].numel() * 2 + scores.numel() * 4
     topk_bytes = scores.numel() * 4 + idx.numel() * 4
+    select_bytes = score_bytes + idx.numel() * 4
+    legs = ((("decode_scores_select", select_bytes),) if shared else
+            (("decode_scores", score_bytes), ("decode_topk", topk_bytes)))
     kern = {}
-    for name, b in (("decode_scores", score_bytes), ("decode_topk", topk_bytes), ("decode_attn", attn_bytes)):
+    for name, b in legs + (("decode_attn", attn_bytes),):
         ms = timer.median_ms(name)
         gbs = b / (ms * 1e-3) / 1e9
         kern[name] = {"median_ms": round(ms, 5), "mean_ms": round(timer.avg_ms(name), 5), "bound": "hbm",
                       "mbytes_per_launch": round(b / 1e6, 3),
                       "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    step_bytes = attn_bytes + score_bytes + topk_bytes
+    step_bytes = attn_bytes + (select_bytes if shared else score_bytes + topk_bytes)
     return {
         "workload": w.name, "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5),
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssa.so")
-SOURCES = ["ssa_api.cpp", "ssa_scores.hip", "ssa_topk.hip", "ssa_attn.hip", "ssa_decode.hip", "ssa_bwd.hip", "ssa_route.hip"]
+SOURCES = ["ssa_api.cpp", "ssa_scores.hip", "ssa_topk.hip", "ssa_decode_select.hip", "ssa_attn.hip", "ssa_decode.hip",
+           "ssa_bwd.hip", "ssa_route.hip"]
 # measurement aid (include/ssa_peaks.h), a library of its own beside libssa
 PEAKS_LIB = os.path.join(PKG, "libssa_peaks.so")
 PEAKS_SOURCES = ["ssa_peaks.hip"]

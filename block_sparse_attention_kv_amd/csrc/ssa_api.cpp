@@ -225,6 +225,28 @@ ssa_status_t ssa_block_scores(const ssa_shape_t* shape, const void* q, const voi
   return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
 }
 
+ssa_status_t ssa_decode_scores_select(const ssa_shape_t* shape, const void* q, const float* k_summary, float* scores,
+                                      int32_t* block_idx, int32_t shared, hipStream_t stream) {
+  const char* fn = "ssa_decode_scores_select";
+  ssa::Geometry g;
+  bool empty;
+  ssa_status_t st = make_geometry(shape, &g, &empty, fn);
+  if (st != SSA_OK) return st;
+  if (g.seq_q != 1) return fail(SSA_ERR_INVALID_ARG, "%s: decode only (seq_q == 1), got seq_q %d", fn, g.seq_q);
+  if (empty) return SSA_OK;
+  CHECK_PTR(q, 16, fn);
+  CHECK_PTR(k_summary, 16, fn);
+  CHECK_PTR(block_idx, 4, fn);
+  if (scores) CHECK_PTR(scores, 4, fn);
+  if (!ssa::decode_select_fits(g, shared != 0))
+    return fail(SSA_ERR_UNSUPPORTED,
+                "%s: %d query heads per KV head x %d key blocks do not fit one workgroup; "
+                "use ssa_block_scores and ssa_select_topk",
+                fn, g.group, g.nkb);
+  hipError_t e = ssa::launch_decode_select((const uint16_t*)q, k_summary, scores, block_idx, g, shared != 0, stream);
+  return e == hipSuccess ? SSA_OK : hip_fail(e, fn);
+}
+
 }  // extern "C"
 
 namespace {

@@ -138,6 +138,11 @@ hipError_t launch_prefill_scores(const uint16_t* q, const float* k_summary, floa
                                  const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_scores(const uint16_t* q, const float* k_summary, float* scores,
                                 const Geometry& g, hipStream_t stream);
+// Fused decode scoring + selection: whether a shape fits (scores of a KV
+// group held in LDS) and the launch.
+bool decode_select_fits(const Geometry& g, bool shared);
+hipError_t launch_decode_select(const uint16_t* q, const float* ksum, float* scores, int32_t* idx, const Geometry& g,
+                                bool shared, hipStream_t stream);
 hipError_t launch_select_topk(const float* scores, int32_t* idx, const Geometry& g, bool shared,
                               hipStream_t stream);
 hipError_t launch_attn_prefill(const AttnArgs& a, bool full, const Geometry& g, hipStream_t stream);

@@ -88,6 +88,8 @@ def classify(name: str):
         return "decode_combine"
     if "prefill_scores_kernel" in name:
         return "prefill_scores"
+    if "decode_select_kernel" in name:
+        return "decode_scores_select"
     if "decode_scores_kernel" in name:
         return "decode_scores"
     if "block_summaries_kernel" in name:

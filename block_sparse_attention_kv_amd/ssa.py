@@ -25,7 +25,8 @@ EXPORTED_SYMBOLS = (
     "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared", "ssa_block_sparse_attn_fwd_shared",
     "ssa_full_attn_fwd_dropped_mass_shared", "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
     "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_block_summaries_learned", "ssa_entmax_route",
-    "ssa_block_sparse_attn_fwd_biased", "ssa_block_sparse_attn_fwd_noalloc", "ssa_workspace_bytes",
+    "ssa_block_sparse_attn_fwd_biased", "ssa_block_sparse_attn_fwd_noalloc", "ssa_decode_scores_select",
+    "ssa_workspace_bytes",
     "ssa_status_string",
     "ssa_last_error", "ssa_version",
 )
@@ -83,12 +84,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssa_entmax_route.argtypes = [sp, vp, f32, f32, f32, vp, vp, vp, vp]
     lib.ssa_block_sparse_attn_fwd_biased.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssa_block_sparse_attn_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssa_decode_scores_select.argtypes = [sp, vp, vp, vp, vp, i32, vp]
     for fn in ("ssa_block_summaries", "ssa_block_scores", "ssa_select_topk",
                "ssa_block_sparse_attn_fwd", "ssa_full_attn_fwd_dropped_mass", "ssa_select_topk_shared",
                "ssa_block_sparse_attn_fwd_shared", "ssa_full_attn_fwd_dropped_mass_shared",
                "ssa_block_sparse_attn_fwd_early_stop", "ssa_block_sparse_attn_bwd",
                "ssa_block_sparse_attn_bwd_shared", "ssa_full_attn_bwd", "ssa_block_summaries_learned",
-               "ssa_entmax_route", "ssa_block_sparse_attn_fwd_biased", "ssa_block_sparse_attn_fwd_noalloc"):
+               "ssa_entmax_route", "ssa_block_sparse_attn_fwd_biased", "ssa_block_sparse_attn_fwd_noalloc",
+               "ssa_decode_scores_select"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.ssa_workspace_bytes.argtypes = [sp, ctypes.c_int]
     lib.ssa_workspace_bytes.restype = ctypes.c_size_t
@@ -309,6 +312,24 @@ def ssa_select_topk_shared(shape: Shape, scores: torch.Tensor, idx: Optional[tor
     _check("ssa_select_topk_shared", load_library().ssa_select_topk_shared(
         ctypes.byref(shape), _ptr(scores), _ptr(idx), _stream(scores.device)))
     return idx
+
+
+def ssa_decode_scores_select(shape: Shape, q, k_summary, scores: Optional[torch.Tensor] = None,
+                             idx: Optional[torch.Tensor] = None, shared: bool = False, with_scores: bool = True):
+    """Decode scores and top-k selection in one launch: (scores fp32 [b, Hq, 1, nkb]
+    or None, idx int32 [b, Hq or Hkv, 1, topk]).  ``with_scores=False`` skips
+    writing the scores."""
+    b_, hq_, hkv_, sq_, _, d_, nqb_, nkb_, k_ = _dims(shape)
+    _validate("ssa_decode_scores_select", q=(q, BF16, (b_, hq_, sq_, d_)), k_summary=(k_summary, F32, (b_, hkv_, nkb_, d_)),
+              scores=(scores, F32, (b_, hq_, nqb_, nkb_)), idx=(idx, I32, (b_, hkv_ if shared else hq_, nqb_, k_)))
+    if scores is None and with_scores:
+        scores = torch.empty((b_, hq_, nqb_, nkb_), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((b_, hkv_ if shared else hq_, nqb_, k_), dtype=torch.int32, device=q.device)
+    _check("ssa_decode_scores_select", load_library().ssa_decode_scores_select(
+        ctypes.byref(shape), _ptr(q), _ptr(k_summary), _ptr(scores), _ptr(idx), 1 if shared else 0,
+        _stream(q.device)))
+    return scores, idx
 
 
 def ssa_block_sparse_attn_fwd(shape: Shape, q, k, v, block_idx, workspace: Optional[torch.Tensor] = None,

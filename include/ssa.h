@@ -197,6 +197,25 @@ ssa_status_t ssa_full_attn_fwd_dropped_mass(const ssa_shape_t* shape, const void
 ssa_status_t ssa_select_topk_shared(const ssa_shape_t* shape, const float* scores, int32_t* block_idx,
                                     hipStream_t stream);
 
+/* Decode (seq_q == 1) scoring and selection in one launch: the block scores
+ * of every query head against the cached key summaries, exactly as
+ * ssa_block_scores with summary_is_input = 1, and the top-k selection with the
+ * most recent block kept, exactly as ssa_select_topk (shared == 0) or
+ * ssa_select_topk_shared (shared != 0).  Results are identical to those two
+ * calls; the scores stay on chip and the second launch is saved.
+ * [SSA-guide] "Block-sparse attention e Receptive Field"; [DashAttn] "Etapa 0"
+ * (cached chunk summaries), "Etapa 1" (routing logits, averaged over the
+ * query heads of a KV head when shared) and "Etapa 2" (most recent chunk kept).
+ *   q          bf16 [b,Hq,1,d];  k_summary fp32 [b,Hkv,nkb,d] (input)
+ *   scores     fp32 [b,Hq,1,nkb] (output, may be NULL)
+ *   block_idx  int32 [b,Hq,1,topk], or [b,Hkv,1,topk] when shared (output)
+ * The scores of one KV group are held in 64 KB of LDS: (Hq/Hkv) * nkb (plus
+ * nkb when shared) fp32 values, with at most 32 query heads per KV head;
+ * larger shapes return SSA_ERR_UNSUPPORTED (the two calls cover them).
+ * seq_q != 1 returns SSA_ERR_INVALID_ARG. */
+ssa_status_t ssa_decode_scores_select(const ssa_shape_t* shape, const void* q, const float* k_summary,
+                                      float* scores, int32_t* block_idx, int32_t shared, hipStream_t stream);
+
 /* ssa_block_sparse_attn_fwd with a group-shared selection: query head h
  * attends over the list block_idx[b, h/G, i, :] (int32 [b,Hkv,nqb,topk], as
  * written by ssa_select_topk_shared); same outputs, workspace and errors. */

@@ -155,6 +155,20 @@ def test_noalloc_validation(lib):
     assert b"scratch" in lib.ssa_last_error()
 
 
+def test_decode_scores_select_validation(lib):
+    """The fused decode scoring + selection is decode only and refuses groups
+    whose scores do not fit one workgroup, before any HIP call."""
+    pre = good_shape()   # seq_q 256
+    assert lib.ssa_decode_scores_select(ctypes.byref(pre), FAKE, FAKE, None, FAKE, 0, None) == ssa.SSA_ERR_INVALID_ARG
+    big = good_shape(n_q_heads=64, n_kv_heads=1, seq_q=1, seq_kv=4096, q_offset=4095, topk=4)
+    assert lib.ssa_decode_scores_select(ctypes.byref(big), FAKE, FAKE, None, FAKE, 0, None) == ssa.SSA_ERR_UNSUPPORTED
+    long_ = good_shape(n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=64 * 1024, q_offset=64 * 1024 - 1, topk=4)
+    assert lib.ssa_decode_scores_select(ctypes.byref(long_), FAKE, FAKE, None, FAKE, 1, None) == ssa.SSA_ERR_UNSUPPORTED
+    ok = good_shape(n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=4096, q_offset=4095, topk=4)
+    assert lib.ssa_decode_scores_select(ctypes.byref(ok), FAKE, FAKE, None, None, 0, None) == ssa.SSA_ERR_INVALID_ARG
+    assert b"block_idx is NULL" in lib.ssa_last_error()
+
+
 def test_decode_workspace(lib):
     sh = good_shape(batch=64, n_q_heads=32, n_kv_heads=2, seq_q=1, seq_kv=32768, q_offset=32767, topk=17)
     need = lib.ssa_workspace_bytes(ctypes.byref(sh), ssa.SSA_OP_SPARSE_FWD)
