@@ -82,12 +82,59 @@ def build(verbose: bool = False, jobs: int | None = None, out: str = LIB, build_
     return out
 
 
+ASAN_BUILD = os.path.join(PKG, "_build_asan")
+ASAN_LIB = os.path.join(ASAN_BUILD, "libssa_asan.so")
+
+
+def asan_runtime() -> str | None:
+    """The compiler's AddressSanitizer runtime, preloaded into the (not
+    instrumented) Python process that loads the instrumented library."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "..",
+                                         "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    hits += sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return os.path.realpath(hits[0]) if hits else None
+
+
+def build_asan(verbose: bool = False, jobs: int | None = None) -> str:
+    """libssa with its host code built under AddressSanitizer (device code as
+    usual), for running the host-layer tests under ASan on a CPU machine."""
+    os.makedirs(ASAN_BUILD, exist_ok=True)
+    flags = ("-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer")
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2) // 2))
+
+    def comp(src):
+        obj = os.path.join(ASAN_BUILD, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *CXXFLAGS, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-fsanitize=address", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--asan", action="store_true", help="also build the host-ASan library (_build_asan/)")
     args = ap.parse_args(argv)
     print(build(verbose=args.verbose, jobs=args.jobs))
+    if args.asan:
+        print(build_asan(verbose=args.verbose, jobs=args.jobs))
 
 
 if __name__ == "__main__":

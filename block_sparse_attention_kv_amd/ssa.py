@@ -15,7 +15,8 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libssa.so")
+# SSA_LIBRARY overrides the in-tree build (e.g. the host-ASan build of the same sources)
+LIB_PATH = os.environ.get("SSA_LIBRARY") or os.path.join(_PKG, "libssa.so")
 
 SSA_OK, SSA_ERR_INVALID_ARG, SSA_ERR_UNSUPPORTED, SSA_ERR_HIP, SSA_ERR_WORKSPACE = range(5)
 SSA_OP_BLOCK_SCORES, SSA_OP_SELECT_TOPK, SSA_OP_SPARSE_FWD, SSA_OP_FULL_FWD, SSA_OP_SPARSE_BWD, SSA_OP_FULL_BWD = range(6)
