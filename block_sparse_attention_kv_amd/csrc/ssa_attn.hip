@@ -96,6 +96,32 @@ __device__ __forceinline__ void tile_scores(const uint8_t* sK, const bf16x8 qop[
   __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 }
 
+// p = 2^(c s + b2 - m) of a tile against the reference max m, packed to bf16
+// pairs in pk, and this lane's fp32 sum per query block in rs.
+template <bool BIAS>
+__device__ __forceinline__ void tile_probs(const f32x16 s[2][2], const UnitState& st, u32x4 pk[2][2][2], float c,
+                                           float b2, float rs[2]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    // a block whose bias is -inf (prior weight 0) adds nothing, whatever the reference max
+    const float nm = BIAS ? (b2 == -__builtin_inff() ? -__builtin_inff() : b2 - st.m[qb]) : -st.m[qb];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[kb][qb][8 * ap + 2 * e], c, nm));
+          const float p1 = fast_exp2(fmaf(s[kb][qb][8 * ap + 2 * e + 1], c, nm));
+          pk[kb][ap][qb][e] = pack_bf16x2(p0, p1);
+          rs0 += p0;
+          rs1 += p1;
+        }
+    rs[qb] = rs0 + rs1;
+  }
+}
+
 // Online-softmax update for one tile; leaves packed bf16 probabilities in pk.
 // tile_rs (optional) receives this lane's fp32 sum of the tile's
 // probabilities per query block (relative to the updated reference max).
@@ -120,54 +146,51 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
           s[kb][qb][r] += __uint_as_float(neg_inf_if_future);
         }
   }
-  float mt[2];
-  bool grow = false;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float mx = max_nan(s[0][qb][0], s[0][qb][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = max_nan(max_nan(mx, s[0][qb][r]), s[0][qb][r + 1]);
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = max_nan(max_nan(mx, s[1][qb][r]), s[1][qb][r + 1]);
-    mx = max_nan_xor32(mx);
-    mt[qb] = BIAS ? fmaf(mx, c, b2) : mx * c;
-    grow |= !(mt[qb] <= st.m[qb] + kRescaleSlack);
-  }
-  if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+  // Probabilities against the running reference max, without this tile's
+  // own max: kept while no row's sum over this lane's 32 values exceeds
+  // 32 * 2^kRescaleSlack, so no probability is more than 2^13 times the
+  // reference (ample headroom for the fp32 sums).  Otherwise -- a first tile
+  // (reference -inf), values far above the reference, a NaN -- the tile
+  // takes the exact step: its row max, the rescale of the state, the
+  // probabilities again.
+  float rs[2];
+  tile_probs<BIAS>(s, st, pk, c, b2, rs);
+  constexpr float kFastSumLimit = 32.f * (1 << (int)kRescaleSlack);
+  if (__builtin_amdgcn_ballot_w64(!(rs[0] <= kFastSumLimit) || !(rs[1] <= kFastSumLimit)) != 0ull) {
+    float mt[2];
+    bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mn = fmaxf(st.m[qb], mt[qb]);
-      const float alpha = fast_exp2(st.m[qb] - mn);
-      st.m[qb] = mn;
-      st.l[qb] *= alpha;
-      if (FULL) st.ld[qb] *= alpha;
+      float mx = max_nan(s[0][qb][0], s[0][qb][1]);
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int r = 2; r < 16; r += 2) mx = max_nan(max_nan(mx, s[0][qb][r]), s[0][qb][r + 1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[db][qb][r] *= alpha;
+      for (int r = 0; r < 16; r += 2) mx = max_nan(max_nan(mx, s[1][qb][r]), s[1][qb][r + 1]);
+      mx = max_nan_xor32(mx);
+      mt[qb] = BIAS ? fmaf(mx, c, b2) : mx * c;
+      grow |= !(mt[qb] <= st.m[qb] + kRescaleSlack);
     }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mn = fmaxf(st.m[qb], mt[qb]);
+        const float alpha = fast_exp2(st.m[qb] - mn);
+        st.m[qb] = mn;
+        st.l[qb] *= alpha;
+        if (FULL) st.ld[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st.o[db][qb][r] *= alpha;
+      }
+    }
+    tile_probs<BIAS>(s, st, pk, c, b2, rs);
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    // a block whose bias is -inf (prior weight 0) adds nothing, whatever the reference max
-    const float nm = BIAS ? (b2 == -__builtin_inff() ? -__builtin_inff() : b2 - st.m[qb]) : -st.m[qb];
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ap = 0; ap < 2; ++ap)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[kb][qb][8 * ap + 2 * e], c, nm));
-          const float p1 = fast_exp2(fmaf(s[kb][qb][8 * ap + 2 * e + 1], c, nm));
-          pk[kb][ap][qb][e] = pack_bf16x2(p0, p1);
-          rs0 += p0;
-          rs1 += p1;
-        }
-    const float rs = rs0 + rs1;
-    if (tile_rs) tile_rs[qb] = rs;
-    st.l[qb] += rs;
-    if (FULL && !selected) st.ld[qb] += rs;
+    if (tile_rs) tile_rs[qb] = rs[qb];
+    st.l[qb] += rs[qb];
+    if (FULL && !selected) st.ld[qb] += rs[qb];
   }
 }
 
