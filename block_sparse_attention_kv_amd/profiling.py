@@ -126,20 +126,21 @@ def _bench_line(path: str):
 
 
 def bench_comparison(path: str) -> str:
-    """Markdown rows: the same run's HIP-event averages from bench.py for the
-    kernels the trace also times."""
+    """Markdown rows: the same run's HIP-event medians and means from bench.py
+    for the kernels the trace also times."""
     b = _bench_line(path)
     if not b:
         return ""
-    rows = [("sparse_attn", b["kernels"]["sparse_attn"]["avg_ms"]), ("full_attn", b["kernels"]["full_attn"]["avg_ms"])]
+    k = b["kernels"]
+    rows = [("sparse_attn", k["sparse_attn"]), ("full_attn", k["full_attn"])]
     if b.get("decode"):
-        rows.append(("decode_attn (decode_attn + decode_combine)", b["decode"]["kernels"]["decode_attn"]["avg_ms"]))
-    out = ["", "The same run's bench.py HIP-event averages (prefill_8k, decode_32k; each event pair brackets one",
-           "call). Unless the run skipped the extra legs (--no-shared --no-backward), the trace rows",
-           "above also count the group-shared legs' calls of the same kernels, which run at the same",
-           "launch shapes.", "",
-           "| call | avg us |", "|---|---|"]
-    out += [f"| {n} | {ms * 1e3:.2f} |" for n, ms in rows]
+        rows.append(("decode_attn (decode_attn + decode_combine)", b["decode"]["kernels"]["decode_attn"]))
+    out = ["", "The same run's bench.py HIP-event timings (prefill_8k, decode_32k): each event pair brackets",
+           "one call of the event-timed pass, the last of the run's three passes (warm-up, back-to-back",
+           "timed steps, event-timed calls).  The trace above covers the dispatches of all three, whose",
+           "shader clocks differ by a few percent, so the medians agree to within that.", "",
+           "| call | event median us | event mean us |", "|---|---|---|"]
+    out += [f"| {n} | {e['median_ms'] * 1e3:.2f} | {e['mean_ms'] * 1e3:.2f} |" for n, e in rows]
     return "\n".join(out) + "\n"
 
 
@@ -165,9 +166,13 @@ def shape_markdown(d: str) -> str:
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             per[(cls, grid // max(wg, 1), wg)].append(dur)
     out = ["", "Per launch shape (workgroups x threads per workgroup):", "",
-           "| kernel | workgroups x threads | calls | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+           "| kernel | workgroups x threads | calls | avg us | median us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
     for (cls, nwg, wg), v in sorted(per.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
-        out.append(f"| {cls} | {nwg} x {wg} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+        v = sorted(v)
+        med = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+        out.append(f"| {cls} | {nwg} x {wg} | {len(v)} | {sum(v) / len(v):.2f} | {med:.2f} | {min(v):.2f} | "
+                   f"{max(v):.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -291,6 +296,56 @@ def mfma_markdown(d: str, title: str = "", command: str = "") -> str:
     return "\n".join(out) + "\n"
 
 
+VALU_MIX_COUNTERS = ("SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_ADD_F32",
+                     "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_CVT", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA")
+
+
+def valu_mix_markdown(d: str, title: str = "", command: str = "") -> str:
+    """Per kernel, averaged over its dispatches: instructions of each class
+    (summed over all waves) per matrix instruction -- transcendental (exp,
+    log), fp32 fma, add and mul, conversions, scalar, LDS."""
+    per = _counters_per_dispatch(d)
+    out = [f"# {title}".rstrip(), ""]
+    if command:
+        out += ["Command:", "", "```", command, "```", ""]
+    cols = VALU_MIX_COUNTERS[:-1]
+    out += ["Instructions per v_mfma instruction (wave-level instruction counts):", "",
+            "| kernel | dispatches | MFMA instr (M) | " + " | ".join(c.replace("SQ_INSTS_", "") for c in cols) + " |",
+            "|---|---|---|" + "---|" * len(cols)]
+    for cls in sorted(per):
+        rows = [ctr for ctr, _ in per[cls].values()
+                if all(c in ctr for c in VALU_MIX_COUNTERS) and ctr["SQ_INSTS_MFMA"] > 0]
+        if not rows:
+            continue
+        avg = lambda f: sum(f(r) for r in rows) / len(rows)
+        out.append(f"| {cls} | {len(rows)} | {avg(lambda r: r['SQ_INSTS_MFMA']) / 1e6:.3f} | " +
+                   " | ".join(f"{avg(lambda r, c=c: r[c] / r['SQ_INSTS_MFMA']):.2f}" for c in cols) + " |")
+    return "\n".join(out) + "\n"
+
+
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS")
+
+
+def lds_markdown(d: str, title: str = "", command: str = "") -> str:
+    """Per kernel, averaged over its dispatches: LDS bank-conflict cycles as a
+    fraction of the cycles the LDS was indexing, and LDS instructions."""
+    per = _counters_per_dispatch(d)
+    out = [f"# {title}".rstrip(), ""]
+    if command:
+        out += ["Command:", "", "```", command, "```", ""]
+    out += ["| kernel | dispatches | bank-conflict cycles | LDS active cycles | conflict / active | LDS instr (M) |",
+            "|---|---|---|---|---|---|"]
+    for cls in sorted(per):
+        rows = [ctr for ctr, _ in per[cls].values() if all(c in ctr for c in LDS_COUNTERS)]
+        if not rows:
+            continue
+        avg = lambda c: sum(r[c] for r in rows) / len(rows)
+        act = avg("SQ_LDS_IDX_ACTIVE")
+        out.append(f"| {cls} | {len(rows)} | {avg('SQ_LDS_BANK_CONFLICT'):.0f} | {act:.0f} | "
+                   f"{(avg('SQ_LDS_BANK_CONFLICT') / act if act else 0.0):.4f} | {avg('SQ_INSTS_LDS') / 1e6:.3f} |")
+    return "\n".join(out) + "\n"
+
+
 WAIT_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
                  "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY")
 
@@ -367,6 +422,46 @@ def trace_summary(records, flops: float = 0.0, peak_tflops: float = 2516.6, nomi
     return out
 
 
+def workgroup_trace_markdown(bench_log: str, title: str = "", command: str = "") -> str:
+    """The bench line's measured peaks and per-workgroup timing summaries of
+    the persistent attention launches, as tables."""
+    b = _bench_line(bench_log)
+    if not b:
+        raise SystemExit(f"no bench line in {bench_log}")
+    out = [f"# {title}".rstrip(), ""]
+    if command:
+        out += ["Command:", "", "```", command, "```", ""]
+    pk = b.get("peaks") or {}
+    if pk:
+        m, r, c = pk["mfma_bf16"], pk["hbm_read"], pk["hbm_copy"]
+        out += ["Measured peaks (libssa_peaks):", "",
+                "| quantity | measured | nominal | fraction |", "|---|---|---|---|",
+                f"| bf16 32x32x16 matrix loop | {m['tflops']} TFLOP/s at {m['clock_ghz']} GHz | 2516.6 TFLOP/s at 2.4 GHz "
+                f"| {m['frac_of_nominal']} |",
+                f"| streaming read, 1 GiB | {r['gbs']} GB/s | 8000 GB/s | {r['frac_of_nominal']} |",
+                f"| streaming copy, 2 x 512 MiB | {c['gbs']} GB/s | 8000 GB/s | {c['frac_of_nominal']} |",
+                f"| shader clock, idle | {pk['clock_idle_ghz']} GHz | 2.4 GHz | |", ""]
+    tr = b.get("workgroup_trace") or {}
+    if tr:
+        out += ["One traced launch per kernel (records in the workspace past the work queue).  Clock = a",
+                "workgroup's shader cycles over its real time; busy = summed workgroup time over",
+                "(workgroups x span); the last column is the launch's useful rate against the bf16 peak",
+                "scaled to the median measured clock.", "",
+                "| workload | kernel | workgroups | span us | clock GHz p10 / p50 / p90 | busy | end us p50 / max | "
+                "tiles per workgroup min / med / max | loop cycles per tile p10 / p50 / p90 | TFLOP/s over span | "
+                "fraction of peak at measured clock |",
+                "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for wl, ks in tr.items():
+            for kn, x in ks.items():
+                cg, en = x["clock_ghz_p0_10_50_90_100"], x["end_us_p0_10_50_90_100"]
+                out.append(f"| {wl} | {kn} | {x['workgroups']} | {x['span_us']} | {cg[1]} / {cg[2]} / {cg[3]} | "
+                           f"{x['busy_fraction']} | {en[2]} / {en[4]} | "
+                           f"{' / '.join(str(t) for t in x['tiles_per_workgroup_p0_50_100'])} | "
+                           f"{' / '.join(str(t) for t in x['loop_cycles_per_tile_p10_50_90'])} | "
+                           f"{x.get('tflops_over_span')} | {x.get('frac_of_peak_at_measured_clock')} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -388,6 +483,18 @@ def main(argv=None):
     m.add_argument("dir")
     m.add_argument("--title", default="")
     m.add_argument("--command", default="")
+    vm = sub.add_parser("valu")
+    vm.add_argument("dir")
+    vm.add_argument("--title", default="")
+    vm.add_argument("--command", default="")
+    wt = sub.add_parser("wgtrace")
+    wt.add_argument("bench_log")
+    wt.add_argument("--title", default="")
+    wt.add_argument("--command", default="")
+    ld = sub.add_parser("lds")
+    ld.add_argument("dir")
+    ld.add_argument("--title", default="")
+    ld.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.dir, a.title, a.command))
@@ -397,6 +504,12 @@ def main(argv=None):
         sys.stdout.write(mfma_markdown(a.dir, a.title, a.command))
     elif a.cmd == "waits":
         sys.stdout.write(waits_markdown(a.dir, a.title, a.command))
+    elif a.cmd == "valu":
+        sys.stdout.write(valu_mix_markdown(a.dir, a.title, a.command))
+    elif a.cmd == "wgtrace":
+        sys.stdout.write(workgroup_trace_markdown(a.bench_log, a.title, a.command))
+    elif a.cmd == "lds":
+        sys.stdout.write(lds_markdown(a.dir, a.title, a.command))
     else:
         print(json.dumps(traffic(a.fetch_dir, a.write_dir, a.out, a.command), indent=1))
 

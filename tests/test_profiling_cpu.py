@@ -61,9 +61,9 @@ def test_stats_and_shapes(tmp_path):
     md = P.stats_markdown(d, title="t", command="rocprofv3 ...")
     assert "| full_attn | 2 | 300.00 | 290.00 | 310.00 | 75.00 |" in md
     # one row per launch shape; durations averaged per shape
-    assert "| bwd_dkv | 100 x 128 | 2 | 40.00 | 10.00 | 70.00 |" in md
-    assert "| bwd_dkv | 50 x 256 | 1 | 120.00 | 120.00 | 120.00 |" in md
-    assert "| full_attn | 1024 x 256 | 2 | 300.00 | 290.00 | 310.00 |" in md
+    assert "| bwd_dkv | 100 x 128 | 2 | 40.00 | 40.00 | 10.00 | 70.00 |" in md
+    assert "| bwd_dkv | 50 x 256 | 1 | 120.00 | 120.00 | 120.00 | 120.00 |" in md
+    assert "| full_attn | 1024 x 256 | 2 | 300.00 | 300.00 | 290.00 | 310.00 |" in md
 
 
 def _counter_rows(counter, values):
@@ -154,3 +154,23 @@ def test_trace_summary_wraps_the_tick_counter():
     s = trace_summary(r)
     assert s["span_us"] == 5.12
     assert abs(s["clock_ghz_p0_10_50_90_100"][2] - 3.2) < 1e-6
+
+
+def test_valu_mix_and_lds_summaries(tmp_path):
+    hdr = ["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    vals = {"SQ_INSTS_VALU_TRANS_F32": 4e6, "SQ_INSTS_VALU_FMA_F32": 4e6, "SQ_INSTS_VALU_ADD_F32": 3e6,
+            "SQ_INSTS_VALU_MUL_F32": 1e6, "SQ_INSTS_VALU_CVT": 2e6, "SQ_INSTS_SALU": 5e5, "SQ_INSTS_LDS": 1e6,
+            "SQ_INSTS_MFMA": 2e6}
+    rows = []
+    for ctr, v in vals.items():
+        rows += _counter_rows(ctr, [(FULL, 7, v)])
+    d = str(tmp_path / "v")
+    _write_csv(os.path.join(d, "x_counter_collection.csv"), hdr, rows)
+    md = P.valu_mix_markdown(d)
+    assert "| full_attn | 1 | 2.000 | 2.00 | 2.00 | 1.50 | 0.50 | 1.00 | 0.25 | 0.50 |" in md
+    rows = []
+    for ctr, v in (("SQ_LDS_BANK_CONFLICT", 50.0), ("SQ_LDS_IDX_ACTIVE", 1000.0), ("SQ_INSTS_LDS", 2e6)):
+        rows += _counter_rows(ctr, [(FULL, 7, v)])
+    d2 = str(tmp_path / "l")
+    _write_csv(os.path.join(d2, "x_counter_collection.csv"), hdr, rows)
+    assert "| full_attn | 1 | 50 | 1000 | 0.0500 | 2.000 |" in P.lds_markdown(d2)
