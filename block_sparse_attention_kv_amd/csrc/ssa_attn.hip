@@ -129,7 +129,7 @@ __device__ __forceinline__ void tile_probs(const f32x16 s[2][2], const UnitState
 template <bool FULL, bool BIAS = false>
 __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x4 pk[2][2][2], bool diag,
                                              bool selected, int key0, int pos0, int l32, int hl, float c,
-                                             float* tile_rs = nullptr, float b2 = 0.f) {
+                                             float* tile_rs = nullptr, float b2 = 0.f, bool first = false) {
   if (diag) {
     // Causal mask of the tile holding the query rows' own positions: key > pos
     // becomes -inf.  Branch-free sign arithmetic (no compare masks to keep live).
@@ -153,10 +153,11 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
   // (reference -inf), values far above the reference, a NaN -- the tile
   // takes the exact step: its row max, the rescale of the state, the
   // probabilities again.
-  float rs[2];
-  tile_probs<BIAS>(s, st, pk, c, b2, rs);
+  // A unit's first tile (reference -inf) goes to the exact step directly.
+  float rs[2] = {0.f, 0.f};
+  if (!first) tile_probs<BIAS>(s, st, pk, c, b2, rs);
   constexpr float kFastSumLimit = 32.f * (1 << (int)kRescaleSlack);
-  if (__builtin_amdgcn_ballot_w64(!(rs[0] <= kFastSumLimit) || !(rs[1] <= kFastSumLimit)) != 0ull) {
+  if (first || __builtin_amdgcn_ballot_w64(!(rs[0] <= kFastSumLimit) || !(rs[1] <= kFastSumLimit)) != 0ull) {
     float mt[2];
     bool grow = false;
 #pragma unroll
@@ -355,7 +356,7 @@ __device__ __attribute__((always_inline)) inline void sparse_tiles(
     if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, seq_kv - jn * kBlock, sK, lane, toff);
     u32x4 pk[2][2][2];
     const float b2 = BIAS ? sBias[t] * kLog2eF : 0.f;
-    tile_softmax<false, BIAS>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c, nullptr, b2);
+    tile_softmax<false, BIAS>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c, nullptr, b2, t == 0);
     if (more)
       wait_vmem<8>();  // V_t landed (K_{t+1} may still be in flight)
     else
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
     if (more) tile_load(kbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sK, lane, toff);
     u32x4 pk[2][2][2];
     float trs[2];
-    tile_softmax<false>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c, trs);
+    tile_softmax<false>(s, st, pk, j == jd, true, j * kBlock, pos0, l32, hl, c, trs, 0.f, t == 0);
     // stop after this tile if every valid row gained less than tau times its earlier mass
     bool stop = false;
     if (t > 0) {

@@ -557,3 +557,40 @@ def test_index_rows_read_as_sets(dev, shared):
     P.check_abs(l1, l_ref, P.LSE_ABS, "LSE_sparse (scrambled rows)")
     _, _, d_ref = O.full_attention_dropped_mass(qn, kn, vn, per_head, w.block)
     P.check_abs(d1, d_ref, P.DROP_ABS, "dropped mass (scrambled rows)")
+
+
+def test_workgroup_timing_records(dev):
+    """The timing records a persistent launch writes past its work queue are
+    consistent with the launch: one per workgroup, every unit and every tile
+    of the selection counted once, end after start, and the outputs equal
+    those of a launch without records."""
+    from block_sparse_attention_kv_amd.profiling import TRACE_WORDS, trace_summary
+    w = W.Workload("trace_2k", 2, 8, 2, 2048, 2048, 64, 64, 6, seed=61)
+    say(f"{w.name}: timing records of the sparse and full forward")
+    q, k, v = (t.to(dev) for t in W.make_inputs(w))
+    shape = ssa.make_shape(q, w.n_kv_heads, w.seq_kv, block=w.block, topk=w.topk)
+    scores, _ = ssa.ssa_block_scores(shape, q, k)
+    idx = ssa.ssa_select_topk(shape, scores)
+    qbytes = ssa.ssa_workspace_bytes(shape, ssa.SSA_OP_SPARSE_FWD)
+    ws = torch.zeros((qbytes + 4096 * TRACE_WORDS * 4,), dtype=torch.uint8, device=dev)
+    o1, l1 = ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx, workspace=ws)
+    o2, l2 = ssa.ssa_block_sparse_attn_fwd(shape, q, k, v, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    rec = ws[qbytes:].view(torch.int32).cpu().numpy().view(np.uint32).reshape(-1, TRACE_WORDS)
+    used = rec[rec[:, 4] > 0]
+    nqb = ssa.n_blocks(w.seq_q, B)
+    assert int(used[:, 4].sum()) == w.batch * w.n_q_heads * nqb           # every unit once
+    listed = int((idx >= 0).sum())                                       # the kernels visit every listed block
+    assert int(used[:, 5].sum()) == listed
+    s = trace_summary(rec)
+    assert s["workgroups"] == len(used) and s["span_us"] > 0 and s["busy_fraction"] <= 1.0
+    assert 0.5 < s["clock_ghz_p0_10_50_90_100"][2] < 3.0
+    # full counterpart: tiles = every causal block of every query block, per group of 4 heads
+    wsf = torch.zeros_like(ws)
+    ssa.ssa_full_attn_fwd_dropped_mass(shape, q, k, v, idx, workspace=wsf)
+    torch.cuda.synchronize()
+    recf = wsf[qbytes:].view(torch.int32).cpu().numpy().view(np.uint32).reshape(-1, TRACE_WORDS)
+    usedf = recf[recf[:, 4] > 0]
+    assert int(usedf[:, 4].sum()) == w.batch * w.n_q_heads * nqb // 4
+    assert int(usedf[:, 5].sum()) == w.batch * w.n_q_heads // 4 * sum(i + 1 for i in range(nqb))
