@@ -49,11 +49,11 @@ ssa_status_t make_geometry(const ssa_shape_t* s, ssa::Geometry* g, bool* empty, 
   if (s->scale < 0.f) return fail(SSA_ERR_UNSUPPORTED, "%s: negative scale", fn);
   if (s->causal != 1) return fail(SSA_ERR_UNSUPPORTED, "%s: only causal attention is implemented", fn);
   if (s->head_dim != ssa::kHeadDim)
-    return fail(SSA_ERR_UNSUPPORTED, "%s: head_dim %d (this build: %d)", fn, s->head_dim, ssa::kHeadDim);
+    return fail(SSA_ERR_UNSUPPORTED, "%s: head_dim %d (supported: %d)", fn, s->head_dim, ssa::kHeadDim);
   if (s->block != ssa::kBlock)
-    return fail(SSA_ERR_UNSUPPORTED, "%s: block %d (this build: %d)", fn, s->block, ssa::kBlock);
+    return fail(SSA_ERR_UNSUPPORTED, "%s: block %d (supported: %d)", fn, s->block, ssa::kBlock);
   if (s->topk > ssa::kMaxTopk)
-    return fail(SSA_ERR_UNSUPPORTED, "%s: topk %d (this build: <= %d)", fn, s->topk, ssa::kMaxTopk);
+    return fail(SSA_ERR_UNSUPPORTED, "%s: topk %d (supported: <= %d)", fn, s->topk, ssa::kMaxTopk);
   const int64_t rows_q = (int64_t)s->batch * s->n_q_heads * s->seq_q * s->head_dim;
   const int64_t rows_kv = (int64_t)s->batch * s->n_kv_heads * s->seq_kv * s->head_dim;
   const int64_t nkb = (s->seq_kv + s->block - 1) / s->block;

@@ -7,8 +7,8 @@
 
 namespace ssa {
 
-constexpr int kHeadDim = 64;  // d supported by this build
-constexpr int kBlock = 64;    // B supported by this build (one 64-key tile per block)
+constexpr int kHeadDim = 64;  // the head dimension d the kernels implement
+constexpr int kBlock = 64;    // the block size B the kernels implement (one 64-key tile per block)
 constexpr int kMaxTopk = 256;
 
 struct Geometry {

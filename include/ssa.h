@@ -31,7 +31,7 @@
  *   valid once the stream reaches that point.
  * Errors.  Arguments are validated on the host before anything is launched:
  *   SSA_ERR_INVALID_ARG (bad pointer, alignment, or inconsistent shape) or
- *   SSA_ERR_UNSUPPORTED (a valid shape this build does not implement: d != 64,
+ *   SSA_ERR_UNSUPPORTED (a valid shape the library does not implement: d != 64,
  *   B != 64, causal == 0, topk > 256, a negative scale).  A failed launch
  *   returns SSA_ERR_HIP.
  *   On error nothing is written.  ssa_last_error() gives a message for the
@@ -67,8 +67,8 @@ typedef struct ssa_shape {
   int32_t seq_q;      /* query rows per (b, h): N for prefill, 1 for decode */
   int32_t seq_kv;     /* key/value rows per (b, kv head); == q_offset + seq_q */
   int32_t q_offset;   /* absolute position of query row 0 */
-  int32_t head_dim;   /* d; this build: 64 */
-  int32_t block;      /* B; this build: 64 */
+  int32_t head_dim;   /* d; the library implements 64 */
+  int32_t block;      /* B; the library implements 64 */
   int32_t topk;       /* k: blocks kept per query block, counting the forced diagonal
                          (most recent) block; 1 <= k <= 256 */
   int32_t causal;     /* must be 1 */
