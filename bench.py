@@ -255,9 +255,10 @@ def _u32(t):
 
 def bench_peaks(args, torch, ssa, W):
     """Measured peaks beside the nominal ones: a matrix-instruction loop with no
-    memory traffic (bf16 32x32x16, 2 waves per SIMD), a streaming read and a
-    streaming copy of 1 GiB, and the shader clock of an idle GPU (the clock
-    under the attention kernels comes from their own timing records)."""
+    memory traffic (bf16 32x32x16, 2 waves per SIMD), a compute-only replica
+    of the attention tile, a streaming read and a streaming copy of 1 GiB, and
+    the shader clock of an idle GPU (the clock under the attention kernels
+    comes from their own timing records)."""
     from block_sparse_attention_kv_amd import peaks as P
     P.load_library()
     dev = torch.device("cuda:0")
@@ -287,6 +288,25 @@ def bench_peaks(args, torch, ssa, W):
     res["mfma_bf16"] = {"tflops": round(tf, 1), "frac_of_nominal": round(tf / PEAK_BF16_TFLOPS, 4),
                         "clock_ghz": round(ghz, 3), "ms": round(ms, 4), "waves": 4 * nb,
                         "note": "v_mfma_f32_32x32x16_bf16 back to back on registers; the nominal peak assumes 2.4 GHz"}
+
+    # compute-only replica of the attention tile, 2 waves per SIMD as the
+    # attention kernels run: the cycles a tile's arithmetic needs with no LDS,
+    # memory traffic or masking
+    tiles = 500
+    to = torch.zeros(16 * nb, dtype=i32, device=dev)
+    P.tile(tiles, nb, to)
+    torch.cuda.synchronize()
+    ms = _event_ms(torch, lambda: P.tile(tiles, nb, to), 5)
+    per_wave = _u32(to).view(-1, 4)
+    cyc = per_wave[:, 1].double() / tiles
+    ghz = float((per_wave[:, 1].double() / per_wave[:, 2].double()).median()) * P.REALTIME_HZ / 1e9
+    fl = 4 * nb * tiles * P.MFMA_PER_TILE * P.FLOP_PER_MFMA
+    tf = fl / (ms * 1e-3) / 1e12
+    res["attention_tile_replica"] = {
+        "cycles_per_tile_p10_50_90": [round(float(cyc.quantile(x)), 1) for x in (0.1, 0.5, 0.9)],
+        "tflops": round(tf, 1), "frac_of_nominal": round(tf / PEAK_BF16_TFLOPS, 4), "clock_ghz": round(ghz, 3),
+        "ms": round(ms, 4), "waves": 4 * nb,
+        "note": "32 MFMAs + the fast-path softmax of one 64x64 tile per wave, operands in registers"}
 
     # streaming read and copy of 1 GiB (well above the 256 MB last-level cache)
     nbytes = 1 << 30
@@ -687,8 +707,8 @@ def main():
                     help="only issue the dispatches a rocprofv3 --pmc run needs (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the path shards with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard over sequences and KV heads with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -721,6 +741,12 @@ def main():
             legs[name] = prefill_leg(bench_prefill(args, torch, ssa, W, workload=name, steps=args.leg_steps))
     peaks = None if args.no_peaks else bench_peaks(args, torch, ssa, W)
     trace = None if args.no_peaks else bench_trace(args, torch, ssa, W)
+    if peaks is not None and trace is not None:
+        # each kernel's median tile-loop cycles against the compute-only replica's
+        rep = peaks["attention_tile_replica"]["cycles_per_tile_p10_50_90"][1]
+        for per_kernel in trace.values():
+            for tr in per_kernel.values():
+                tr["replica_over_loop_cycles_per_tile"] = round(rep / tr["loop_cycles_per_tile_p10_50_90"][1], 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, W)
     w = pre["w"]
     line = {

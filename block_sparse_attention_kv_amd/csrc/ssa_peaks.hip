@@ -1,6 +1,7 @@
 // Measured peaks of one MI355X (gfx950), beside which the attention kernels'
 // rates are read: a loop of bf16 matrix instructions with no memory traffic,
-// a streaming read and a streaming copy of device memory, and the shader
+// a compute-only replica of the attention tile, a streaming read and a
+// streaming copy of device memory, and the shader
 // clock (shader cycles over the 100 MHz real-time counter) seen by one
 // wavefront while other work runs.  C ABI, caller-owned buffers, stream order.
 #include <hip/hip_runtime.h>
@@ -44,6 +45,92 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, uint32_t* __r
     for (int r = 0; r < 16; ++r) s += acc[c][r];
   if (lane == 0) {
     out[4 * wave + 0] = __float_as_uint(s);
+    out[4 * wave + 1] = (uint32_t)(t1 - t0);
+    out[4 * wave + 2] = (uint32_t)(r1 - r0);
+    out[4 * wave + 3] = 0u;
+  }
+}
+
+// Compute-only replica of one block-sparse attention tile (64 query rows x 64
+// keys, d = 64, one wavefront): the score products (16 MFMAs), the softmax
+// arithmetic of the tile's fast path (per score: one fma, one exp2, one add to
+// the row sum; per pair: one bf16 pack) and the P.V products (16 MFMAs) that
+// consume the packed probabilities, with the same register layout and the same
+// dependencies as the attention kernels' tile, but with the K, V and Q operands
+// in registers: no LDS, no memory traffic, no masking.  Each wave runs `tiles`
+// such tiles; out[4 * wave + 0..2] = checksum bits, shader cycles, real-time
+// ticks of the loop.
+__global__ __launch_bounds__(256, 2) void peak_tile_kernel(int tiles, uint32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  bf16x8 qop[2][4], kop[2][4], vop[2][2];
+  for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < 4; ++y)
+      for (int r = 0; r < 8; ++r) {
+        qop[x][y][r] = (__bf16)(0.01f * ((lane + r + x + y) & 7));
+        kop[x][y][r] = (__bf16)(0.01f * ((lane + 2 * r + x + 3 * y) & 7));
+        if (y < 2) vop[x][y][r] = (__bf16)(0.001f * ((lane + r + 5 * x + y) & 15));
+      }
+  f32x16 o[2][2];
+  for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < 2; ++y)
+      for (int r = 0; r < 16; ++r) o[x][y][r] = 0.f;
+  float rs[2] = {0.f, 0.f};
+  const float c = 0.18033688f, nm = -1.f;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int t = 0; t < tiles; ++t) {
+    f32x16 s[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 acc;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][ks], qop[qb][ks], acc, 0, 0, 0);
+        s[kb][qb] = acc;
+      }
+    u32x4 pk[2][2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * ap + 2 * e], c, nm));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * ap + 2 * e + 1], c, nm));
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const f32x2 v = {p0, p1};
+            pk[kb][ap][qb][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+            rs0 += p0;
+            rs1 += p1;
+          }
+      rs[qb] += rs0 + rs1;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[ap][db], __builtin_bit_cast(bf16x8, pk[kb][ap][qb]),
+                                                                o[db][qb], 0, 0, 0);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = rs[0] + rs[1];
+  for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < 2; ++y)
+      for (int r = 0; r < 16; ++r) sum += o[x][y][r];
+  if (lane == 0) {
+    out[4 * wave + 0] = __float_as_uint(sum);
     out[4 * wave + 1] = (uint32_t)(t1 - t0);
     out[4 * wave + 2] = (uint32_t)(r1 - r0);
     out[4 * wave + 3] = 0u;
@@ -114,6 +201,12 @@ extern "C" {
 int ssa_peak_mfma(int32_t iters, int32_t n_blocks, uint32_t* out, hipStream_t stream) {
   if (iters < 1 || n_blocks < 1 || !out) return 1;
   hipLaunchKernelGGL(peak_mfma_kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, (int)iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+int ssa_peak_tile(int32_t tiles, int32_t n_blocks, uint32_t* out, hipStream_t stream) {
+  if (tiles < 1 || n_blocks < 1 || !out) return 1;
+  hipLaunchKernelGGL(peak_tile_kernel, dim3((unsigned)n_blocks), dim3(256), 0, stream, (int)tiles, out);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

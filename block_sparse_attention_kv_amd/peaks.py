@@ -9,9 +9,10 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssa_peaks.so")
-EXPORTS = ("ssa_peak_mfma", "ssa_peak_read", "ssa_peak_copy", "ssa_peak_clock")
+EXPORTS = ("ssa_peak_mfma", "ssa_peak_tile", "ssa_peak_read", "ssa_peak_copy", "ssa_peak_clock")
 FLOP_PER_MFMA = 2 * 32 * 32 * 16     # v_mfma_f32_32x32x16_bf16
 MFMA_PER_ITER = 16
+MFMA_PER_TILE = 32                   # 16 score products + 16 P.V products
 REALTIME_HZ = 100e6
 
 _lib = None
@@ -27,6 +28,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, sz, i32, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_uint32
     lib.ssa_peak_mfma.argtypes = [i32, i32, vp, vp]
+    lib.ssa_peak_tile.argtypes = [i32, i32, vp, vp]
     lib.ssa_peak_read.argtypes = [vp, sz, vp, i32, vp]
     lib.ssa_peak_copy.argtypes = [vp, vp, sz, i32, vp]
     lib.ssa_peak_clock.argtypes = [u32, vp, vp]
@@ -50,6 +52,13 @@ def mfma(iters: int, n_blocks: int, out: torch.Tensor, stream=None):
     """Matrix-instruction loop; ``out`` is uint32-sized int32 [n_blocks * 16]."""
     assert out.is_cuda and out.dtype == torch.int32 and out.numel() >= 16 * n_blocks
     _check("ssa_peak_mfma", load_library().ssa_peak_mfma(iters, n_blocks, ctypes.c_void_p(out.data_ptr()),
+                                                         _stream(stream)))
+
+
+def tile(tiles: int, n_blocks: int, out: torch.Tensor, stream=None):
+    """Compute-only attention-tile replica; ``out`` is uint32-sized int32 [n_blocks * 16]."""
+    assert out.is_cuda and out.dtype == torch.int32 and out.numel() >= 16 * n_blocks
+    _check("ssa_peak_tile", load_library().ssa_peak_tile(tiles, n_blocks, ctypes.c_void_p(out.data_ptr()),
                                                          _stream(stream)))
 
 

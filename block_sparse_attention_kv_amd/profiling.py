@@ -441,6 +441,13 @@ def workgroup_trace_markdown(bench_log: str, title: str = "", command: str = "")
                 f"| streaming read, 1 GiB | {r['gbs']} GB/s | 8000 GB/s | {r['frac_of_nominal']} |",
                 f"| streaming copy, 2 x 512 MiB | {c['gbs']} GB/s | 8000 GB/s | {c['frac_of_nominal']} |",
                 f"| shader clock, idle | {pk['clock_idle_ghz']} GHz | 2.4 GHz | |", ""]
+        rp = pk.get("attention_tile_replica")
+        if rp:
+            cy = rp["cycles_per_tile_p10_50_90"]
+            out += ["Compute-only replica of the attention tile (32 matrix instructions and the fast-path softmax",
+                    "of one 64 x 64 tile per wave, operands in registers, 2 waves per SIMD): "
+                    f"{cy[0]} / {cy[1]} / {cy[2]} cycles per tile (p10 / p50 / p90), {rp['tflops']} TFLOP/s at "
+                    f"{rp['clock_ghz']} GHz ({rp['frac_of_nominal']} of the nominal peak).", ""]
     tr = b.get("workgroup_trace") or {}
     if tr:
         out += ["One traced launch per kernel (records in the workspace past the work queue).  Clock = a",
@@ -449,8 +456,8 @@ def workgroup_trace_markdown(bench_log: str, title: str = "", command: str = "")
                 "scaled to the median measured clock.", "",
                 "| workload | kernel | workgroups | span us | clock GHz p10 / p50 / p90 | busy | end us p50 / max | "
                 "tiles per workgroup min / med / max | loop cycles per tile p10 / p50 / p90 | TFLOP/s over span | "
-                "fraction of peak at measured clock |",
-                "|---|---|---|---|---|---|---|---|---|---|---|"]
+                "fraction of peak at measured clock | replica / loop cycles per tile |",
+                "|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for wl, ks in tr.items():
             for kn, x in ks.items():
                 cg, en = x["clock_ghz_p0_10_50_90_100"], x["end_us_p0_10_50_90_100"]
@@ -458,7 +465,8 @@ def workgroup_trace_markdown(bench_log: str, title: str = "", command: str = "")
                            f"{x['busy_fraction']} | {en[2]} / {en[4]} | "
                            f"{' / '.join(str(t) for t in x['tiles_per_workgroup_p0_50_100'])} | "
                            f"{' / '.join(str(t) for t in x['loop_cycles_per_tile_p10_50_90'])} | "
-                           f"{x.get('tflops_over_span')} | {x.get('frac_of_peak_at_measured_clock')} |")
+                           f"{x.get('tflops_over_span')} | {x.get('frac_of_peak_at_measured_clock')} | "
+                           f"{x.get('replica_over_loop_cycles_per_tile', '')} |")
     return "\n".join(out) + "\n"
 
 

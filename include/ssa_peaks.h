@@ -23,6 +23,18 @@ extern "C" {
  *        cycles and the 100 MHz real-time ticks of its loop. */
 int ssa_peak_mfma(int32_t iters, int32_t n_blocks, uint32_t* out, hipStream_t stream);
 
+/* n_blocks workgroups of 4 wavefronts (2 * compute units of them gives two
+ * wavefronts per SIMD, as the attention kernels run); each wavefront runs
+ * `tiles` compute-only replicas of one block-sparse attention tile: 16
+ * v_mfma_f32_32x32x16_bf16 score products, the fast-path softmax arithmetic
+ * of the 4096 scores (fma, exp2 and a row-sum add per score, a bf16 pack per
+ * pair) and 16 P.V products on the packed probabilities, with the attention
+ * tile's register layout and dependencies but with operands in registers (no
+ * LDS or memory traffic).  1 048 576 matrix flop per tile.
+ *   out  uint32 [4 * 4 * n_blocks]: per wavefront a checksum, the shader
+ *        cycles and the 100 MHz real-time ticks of its loop. */
+int ssa_peak_tile(int32_t tiles, int32_t n_blocks, uint32_t* out, hipStream_t stream);
+
 /* Streaming read of `bytes` (a multiple of 16, 16-byte aligned) by n_blocks
  * workgroups of 256 threads.
  *   out  uint32 [n_blocks]: each workgroup's XOR of the words it read. */

@@ -58,6 +58,8 @@ def test_peaks_library_exports_its_header():
         assert hasattr(plib, name), name
     # argument checks return before any launch
     assert plib.ssa_peak_mfma(0, 1, FAKE, None) == 1
+    assert plib.ssa_peak_tile(0, 1, FAKE, None) == 1
+    assert plib.ssa_peak_tile(1, 0, FAKE, None) == 1
     assert plib.ssa_peak_read(FAKE, 24, FAKE, 1, None) == 1
     assert plib.ssa_peak_copy(FAKE, MISALIGNED, 32, 1, None) == 1
     assert plib.ssa_peak_clock(0, FAKE, None) == 1

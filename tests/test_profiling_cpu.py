@@ -174,3 +174,27 @@ def test_valu_mix_and_lds_summaries(tmp_path):
     d2 = str(tmp_path / "l")
     _write_csv(os.path.join(d2, "x_counter_collection.csv"), hdr, rows)
     assert "| full_attn | 1 | 50 | 1000 | 0.0500 | 2.000 |" in P.lds_markdown(d2)
+
+
+def test_workgroup_trace_markdown_with_replica(tmp_path):
+    """The summary of a bench line carries the measured peaks, the attention-tile
+    replica and each traced kernel's replica-to-loop cycle ratio."""
+    trace = {"workgroups": 2, "span_us": 15.0, "clock_ghz_p0_10_50_90_100": [1.5, 1.5, 1.75, 2.0, 2.0],
+             "busy_fraction": 0.6667, "end_us_p0_10_50_90_100": [10.0, 10.0, 12.5, 15.0, 15.0],
+             "tiles_per_workgroup_p0_50_100": [16, 24, 32], "loop_cycles_per_tile_p10_50_90": [1500.0, 2000.0, 2500.0],
+             "tflops_over_span": 66.67, "frac_of_peak_at_measured_clock": 0.0762,
+             "replica_over_loop_cycles_per_tile": 0.75}
+    line = {"metric": "m", "value": 1.0,
+            "peaks": {"clock_idle_ghz": 2.4,
+                      "mfma_bf16": {"tflops": 1858.0, "clock_ghz": 1.93, "frac_of_nominal": 0.738},
+                      "attention_tile_replica": {"cycles_per_tile_p10_50_90": [1400.0, 1500.0, 3000.0],
+                                                 "tflops": 900.0, "clock_ghz": 2.1, "frac_of_nominal": 0.3576},
+                      "hbm_read": {"gbs": 5830.0, "frac_of_nominal": 0.7288},
+                      "hbm_copy": {"gbs": 5160.0, "frac_of_nominal": 0.645}},
+            "workgroup_trace": {"prefill_8k": {"sparse_attn": trace}}}
+    log = tmp_path / "bench.log"
+    log.write_text("noise\n" + json.dumps(line) + "\n")
+    md = P.workgroup_trace_markdown(str(log), title="t", command="c")
+    assert "1400.0 / 1500.0 / 3000.0 cycles per tile" in md
+    assert "| prefill_8k | sparse_attn | 2 |" in md
+    assert md.rstrip().endswith("| 0.0762 | 0.75 |")
