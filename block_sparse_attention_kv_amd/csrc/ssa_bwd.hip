@@ -50,8 +50,11 @@ namespace ssa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSparsePairs = 64;   // pairs per work item, block-sparse backward
-constexpr int kFullPairs = 128;    // pairs per work item, full backward
+constexpr int kSparsePairs = 32;   // pairs per work item, block-sparse backward (32 against 64: 4% faster)
+// pairs per work item, full backward: smaller items end the launch with a
+// shorter tail (48 against 128: the full backward 8% faster on prefill_8k)
+// at the cost of more partial sums to reduce
+constexpr int kFullPairs = 48;
 constexpr int kRing = 3;           // tile buffers per loop (full dK/dV)
 constexpr int kDqRing = 2;         // K/V tile buffers of the dQ loop
 
