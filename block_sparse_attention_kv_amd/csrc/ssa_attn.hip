@@ -247,6 +247,60 @@ __device__ __forceinline__ void unit_epilogue(const UnitState& st, const AttnArg
   }
 }
 
+// Epilogue of the block-sparse forward with the output block staged in LDS
+// (`stage`: 8 KB this wave may overwrite): the lane pairs that hold a row in
+// the matrix-instruction layout write it there, then each lane stores 16
+// contiguous bytes, so one store instruction writes eight whole 128-byte
+// rows instead of sixteen bytes of each of 32 rows.  16-byte chunks are
+// placed at chunk ^ (row % 8) so that neither side conflicts on LDS banks.
+template <bool FULL>
+__device__ __forceinline__ void unit_epilogue_staged(const UnitState& st, const AttnArgs& a, const Geometry& geo,
+                                                     int bh, int i, int lane, uint8_t* stage) {
+  // the lane index passes through an opaque copy, so that the staging
+  // addresses are formed here rather than hoisted out of the unit loop into
+  // registers the tile loop needs
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int lr = ln & 31, lh = ln >> 5;
+  float inv[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = sum_xor32(st.l[qb]);
+    const float dt = FULL ? sum_xor32(st.ld[qb]) : 0.f;
+    inv[qb] = 1.f / lt;
+    const int row = i * kBlock + 32 * qb + lr;
+    if (lh == 0 && row < geo.seq_q) {
+      const size_t orow = (size_t)bh * a.rows_out + row - a.qb_begin * kBlock;
+      a.lse[orow] = (st.m[qb] + fast_log2(lt)) * kLn2;
+      if (FULL) a.dropped[orow] = dt * inv[qb];
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = 32 * qb + lr;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        // columns 32 db + 8 rg + 4 hl .. + 3: half of 16-byte chunk 4 db + rg
+        u32x2 w;
+        w[0] = pack_bf16x2(st.o[db][qb][4 * rg] * inv[qb], st.o[db][qb][4 * rg + 1] * inv[qb]);
+        w[1] = pack_bf16x2(st.o[db][qb][4 * rg + 2] * inv[qb], st.o[db][qb][4 * rg + 3] * inv[qb]);
+        const int chunk = (4 * db + rg) ^ (r & 7);
+        *reinterpret_cast<u32x2*>(stage + r * 128 + chunk * 16 + 8 * lh) = w;
+      }
+  }
+  wave_lds_sync();
+  const int c = ln & 7;
+  const size_t obase = (size_t)bh * a.rows_out + (size_t)(i - a.qb_begin) * kBlock;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = (ln >> 3) + 8 * k;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 128 + ((c ^ (r & 7)) * 16));
+    if (i * kBlock + r < geo.seq_q) *reinterpret_cast<u32x4*>(a.out + (obase + r) * kHeadDim + 8 * c) = v;
+  }
+}
+
 // Optional timing record of a persistent workgroup (AttnArgs::trace): a few
 // scalar counter reads per unit; written by lane 0 at the end.
 struct WgTrace {
@@ -446,7 +500,8 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_kernel(AttnArgs a, Geometry
     sparse_tiles<BIAS>(sK, sV, sList, sBias, nt, a.k + kvoff, a.v + kvoff, geo.seq_kv, jd,
                        geo.q_offset + i * kBlock, geo.scale_log2, qop, st, lane, l32, hl);
     tr.loop_end(nt);
-    unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
+    wait_lds_reads();  // the tiles' last reads are done: sK is the staging area
+    unit_epilogue_staged<false>(st, a, geo, bh, i, lane, sK);
     if (!a.queue) break;
     wait_lds_reads();  // the next unit's tile requests overwrite sK and sV
     w = queue_next(a.queue, a.n_xcc, n_groups * per_group, lane);
@@ -685,7 +740,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
     }
     __builtin_amdgcn_s_setprio(0);
     tr.loop_end(nt);
-    unit_epilogue<FULL>(st, a, geo, bh, i, l32, hl);
+    wait_lds_reads();
+    __syncthreads();  // every wave is done with the tiles: each stages its outputs in a quarter of them
+    unit_epilogue_staged<FULL>(st, a, geo, bh, i, lane, wave < 2 ? sK[wave] : sV[wave - 2]);
     if (!a.queue) break;
     wait_lds_reads();
     __syncthreads();  // every wave is done with the tiles, the lists and the unit slot
