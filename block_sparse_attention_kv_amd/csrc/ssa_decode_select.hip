@@ -28,7 +28,7 @@ constexpr size_t kFsMaxLds = 64 * 1024;
 // Ranks one row of candidates 0 .. jd-1 (jd = the most recent block, always kept).
 template <int NPER>
 __device__ __forceinline__ void select_one_row(const float* srow_base, int32_t* __restrict__ orow, int jd, int k,
-                                               int lane) {
+                                               int lane, uint32_t* cbuf) {
   if (jd + 1 <= k) {
     for (int e = lane; e < k; e += 64) orow[e] = e <= jd ? e : -1;
     return;
@@ -38,7 +38,7 @@ __device__ __forceinline__ void select_one_row(const float* srow_base, int32_t* 
   srow.hstride = 0;
   srow.heads = 1;
   if (NPER > 0)
-    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane);
+    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane, cbuf);
   else
     select_rows_long(srow, orow, jd, k - 1, lane);
   if (lane == 0) orow[k - 1] = jd;
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(64 * kFsWaves) void decode_select_kernel(const uint
                                                                     float* __restrict__ scores,
                                                                     int32_t* __restrict__ idx, Geometry geo) {
   extern __shared__ float sS[];  // [G][nkb] scores; with SHARED then [nkb] group mean
+  __shared__ uint32_t sCb[kFsWaves][64];  // per-wave gather buffers of the narrowed search
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, ks = lane >> 4;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(64 * kFsWaves) void decode_select_kernel(const uint
   const int k = geo.topk;
   if (!SHARED) {
     for (int hh = wave; hh < G; hh += kFsWaves)
-      select_one_row<NPER>(sS + hh * nkb, idx + (size_t)(b * geo.hq + g * G + hh) * k, jd, k, lane);
+      select_one_row<NPER>(sS + hh * nkb, idx + (size_t)(b * geo.hq + g * G + hh) * k, jd, k, lane, sCb[wave]);
   } else {
     // mean of the group's scores: fp64 sum in head order, divided by the group
     // size, rounded once to fp32
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(64 * kFsWaves) void decode_select_kernel(const uint
       smean[j] = (float)(acc / G);
     }
     __syncthreads();
-    if (wave == 0) select_one_row<NPER>(smean, idx + (size_t)bg * k, jd, k, lane);
+    if (wave == 0) select_one_row<NPER>(smean, idx + (size_t)bg * k, jd, k, lane, sCb[0]);
   }
 }
 

@@ -41,9 +41,15 @@ struct RowScores {
 };
 
 // Keys of candidates j = lane + 64*c, c < NPER, held in registers.
+// With NPER >= 4 and a 64-word LDS buffer `cbuf` for this wavefront, the
+// search narrows after its first 12 bits: the keys that share those bits with
+// the threshold (at most 64 of them, else the search simply goes on) are
+// gathered one per lane, so the remaining 20 steps compare one register
+// instead of NPER (the keys above that prefix are counted once).  The result
+// is the same threshold.
 template <int NPER>
 __device__ __forceinline__ void select_rows(const RowScores& srow, int32_t* __restrict__ orow, int jd,
-                                            int need, int lane) {
+                                            int need, int lane, uint32_t* cbuf = nullptr) {
   // every score is requested before the first is used (rows past the
   // candidates read candidate 0 and are dropped)
   float sv[NPER];
@@ -56,7 +62,46 @@ __device__ __forceinline__ void select_rows(const RowScores& srow, int32_t* __re
 #pragma unroll
   for (int c = 0; c < NPER; ++c) key[c] = lane + 64 * c < jd ? cand_key(sv[c]) : 0u;
   uint32_t t = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
+  int bit = 31;
+  if (NPER >= 4 && cbuf) {
+    constexpr int kHi = 12;
+    for (; bit >= 32 - kHi; --bit) {
+      const uint32_t trial = t | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int c = 0; c < NPER; ++c) cnt += wave_count(key[c] >= trial);
+      if (cnt >= need) t = trial;
+    }
+    constexpr uint32_t kLow = (1u << (32 - kHi)) - 1u;
+    const uint32_t hi_next = t + (kLow + 1u);  // 0 when the prefix is all ones
+    int above = 0, live = 0;
+#pragma unroll
+    for (int c = 0; c < NPER; ++c) {
+      if (hi_next != 0u) above += wave_count(key[c] >= hi_next);
+      live += wave_count((key[c] & ~kLow) == t);
+    }
+    if (live <= 64) {
+      int base = 0;
+#pragma unroll
+      for (int c = 0; c < NPER; ++c) {
+        const bool lv = (key[c] & ~kLow) == t;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(lv);
+        if (lv) cbuf[base + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = key[c];
+        base += (int)__builtin_popcountll(m);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint32_t lk = lane < live ? cbuf[lane] : 0u;
+      const int need2 = need - above;
+      for (; bit >= 0; --bit) {
+        const uint32_t trial = t | (1u << bit);
+        if (wave_count(lk >= trial) >= need2) t = trial;
+      }
+      __builtin_amdgcn_wave_barrier();  // the buffer's reads are done before it is written again
+    }
+  }
+  for (; bit >= 0; --bit) {
     const uint32_t trial = t | (1u << bit);
     int cnt = 0;
 #pragma unroll

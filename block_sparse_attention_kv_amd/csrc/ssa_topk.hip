@@ -29,6 +29,7 @@ constexpr int kRowsPerWg = 4;
 template <int NPER, bool SHARED>
 __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restrict__ scores,
                                                           int32_t* __restrict__ idx, Geometry geo, int nrows) {
+  __shared__ uint32_t sCb[kRowsPerWg][64];  // per-wave gather buffer of the narrowed search
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerWg + wave;
   if (row >= nrows) return;  // whole wavefront leaves together; no block barriers below
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(const float* __restric
     return;
   }
   if (NPER > 0)
-    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane);
+    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane, sCb[wave]);
   else
     select_rows_long(srow, orow, jd, k - 1, lane);
   if (lane == 0) orow[k - 1] = jd;
@@ -67,6 +68,7 @@ template <int NPER>
 __global__ __launch_bounds__(256) void select_topk_shared_kernel(const float* __restrict__ scores,
                                                                  int32_t* __restrict__ idx, Geometry geo) {
   extern __shared__ float smean[];  // [jd]: averaged scores of the candidates
+  __shared__ uint32_t sCb[64];       // gather buffer of the narrowed search
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int row = blockIdx.x;
   const int i = row % geo.nqb;
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void select_topk_shared_kernel(const float* __
   srow.hstride = 0;
   srow.heads = 1;
   if (NPER > 0)
-    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane);
+    select_rows<(NPER > 0 ? NPER : 1)>(srow, orow, jd, k - 1, lane, sCb);
   else
     select_rows_long(srow, orow, jd, k - 1, lane);
   if (lane == 0) orow[k - 1] = jd;
