@@ -194,6 +194,44 @@ def test_select_topk_nan_inf_ties(dev):
     assert np.array_equal(idx, ref)
 
 
+def _long_row_scores(nkb: int, nqb: int, rng) -> np.ndarray:
+    """Scores for rows of many candidates, one pattern per head: continuous
+    values; coarse exact ties; one constant; and rows where exactly 64 or 65
+    candidates tie at the threshold (the narrowed search gathers at most 64
+    keys and falls back to the full search beyond), with NaN, -inf and +-0."""
+    s = rng.standard_normal((2, 4, nqb, nkb)).astype(np.float32)
+    s[:, 1] = np.round(s[:, 1])
+    s[:, 2] = 1.0
+    h3 = s[:, 3]
+    h3[...] = np.float32(-1.0) - np.abs(h3)
+    for bi in range(2):
+        for i in range(nqb):
+            n_tied = 64 if (i + bi) % 2 == 0 else 65
+            cols = rng.choice(nkb - nqb, size=n_tied + 3, replace=False)
+            h3[bi, i, cols[:n_tied]] = 2.0
+            h3[bi, i, cols[n_tied:n_tied + 3]] = (np.nan, -np.inf, -0.0)
+    s[0, 0, 0, :5] = (np.nan, np.inf, -np.inf, 0.0, -0.0)
+    return s
+
+
+@pytest.mark.parametrize("nkb", [300, 600])
+def test_select_topk_long_rows(dev, nkb):
+    say(f"select_topk, per head and group-shared, {nkb} key blocks (ties, NaN, 64/65 tied at the threshold)")
+    rng = np.random.default_rng(nkb)
+    nqb, k = 12, 16
+    q_offset = (nkb - nqb) * B
+    s = _long_row_scores(nkb, nqb, rng)
+    for i in range(nqb):
+        s[..., i, nkb - nqb + i + 1:] = -np.inf
+    shape = ssa.Shape(batch=2, n_q_heads=4, n_kv_heads=2, seq_q=nqb * B, seq_kv=nkb * B, q_offset=q_offset,
+                      head_dim=64, block=64, topk=k, causal=1, scale=0.0)
+    sd = torch.from_numpy(s).to(dev)
+    idx = ssa.ssa_select_topk(shape, sd).cpu().numpy()
+    assert np.array_equal(idx, O.select_blocks(s.astype(np.float64), k, B, q_offset))
+    idx_s = ssa.ssa_select_topk_shared(shape, sd).cpu().numpy()
+    assert np.array_equal(idx_s, O.select_blocks_shared(s.astype(np.float64), 2, k, B, q_offset))
+
+
 def test_empty_problem_writes_nothing(dev):
     say("empty problems")
     import ctypes
