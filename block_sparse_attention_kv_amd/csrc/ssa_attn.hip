@@ -217,38 +217,9 @@ __device__ __forceinline__ void tile_pv(const uint8_t* sV, const u32x4 pk[2][2][
   }
 }
 
-template <bool FULL>
-__device__ __forceinline__ void unit_epilogue(const UnitState& st, const AttnArgs& a, const Geometry& geo, int bh,
-                                              int i, int l32, int hl) {
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = sum_xor32(st.l[qb]);
-    const float dt = FULL ? sum_xor32(st.ld[qb]) : 0.f;
-    const float inv = 1.f / lt;
-    const int row = i * kBlock + 32 * qb + l32;
-    if (row < geo.seq_q) {
-      const int orow = row - a.qb_begin * kBlock;
-      uint16_t* op = a.out + ((size_t)bh * a.rows_out + orow) * kHeadDim;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          u32x2 w;
-          w[0] = pack_bf16x2(st.o[db][qb][4 * rg] * inv, st.o[db][qb][4 * rg + 1] * inv);
-          w[1] = pack_bf16x2(st.o[db][qb][4 * rg + 2] * inv, st.o[db][qb][4 * rg + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + 32 * db + 8 * rg + 4 * hl) = w;
-        }
-      }
-      if (hl == 0) {
-        a.lse[(size_t)bh * a.rows_out + orow] = (st.m[qb] + fast_log2(lt)) * kLn2;
-        if (FULL) a.dropped[(size_t)bh * a.rows_out + orow] = dt * inv;
-      }
-    }
-  }
-}
-
-// Epilogue of the block-sparse forward with the output block staged in LDS
-// (`stage`: 8 KB this wave may overwrite): the lane pairs that hold a row in
+// Epilogue of a unit: the row sums and maxima give the normalised output
+// block, its LSE and (FULL) the dropped mass.  The output block is staged in
+// LDS (`stage`: 8 KB this wave may overwrite): the lane pairs that hold a row in
 // the matrix-instruction layout write it there, then each lane stores 16
 // contiguous bytes, so one store instruction writes eight whole 128-byte
 // rows instead of sixteen bytes of each of 32 rows.  16-byte chunks are
@@ -629,7 +600,8 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
     if (stop) break;
     if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sV, lane, toff);
   }
-  unit_epilogue<false>(st, a, geo, bh, i, l32, hl);
+  // the last K reads are done and no tile request is in flight: sK is free
+  unit_epilogue_staged<false>(st, a, geo, bh, i, lane, sK);
   if (lane == 0) blocks_used[(size_t)bh * geo.nqb + i] = used;
 }
 
