@@ -403,10 +403,10 @@ ssa_status_t bwd_impl(const ssa_shape_t* shape, const void* q, const void* k, co
   CHECK_PTR(dk, 16, fn);
   CHECK_PTR(dv, 16, fn);
   ssa::BwdPlan plan;
-  size_t off[7], need;
+  size_t off[6], need;
   ssa::bwd_plan(g, full, q_block_begin, q_block_count, &plan, off, &need);
-  const uint64_t grid = (uint64_t)g.batch * g.hkv * (uint64_t)plan.max_items;
-  if (grid > 0x7fffffffull || plan.max_items == 0x7fffffff)
+  const uint64_t grid = (uint64_t)g.batch * g.hkv * (uint64_t)plan.slots;
+  if (grid > 0x7fffffffull || plan.max_pairs > 0x7fffffffll)
     return fail(SSA_ERR_UNSUPPORTED, "%s: problem too large", fn);
   if (workspace_bytes < need)
     return fail(SSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
@@ -429,9 +429,8 @@ ssa_status_t bwd_impl(const ssa_shape_t* shape, const void* q, const void* k, co
   a.delta = (float*)(ws + off[1]);
   a.mask = full ? nullptr : (uint32_t*)(ws + off[2]);
   a.pairs = full ? nullptr : (int*)(ws + off[3]);
-  a.item_base = (int*)(ws + off[4]);
-  a.item_key = (int*)(ws + off[5]);
-  a.part = (float*)(ws + off[6]);
+  a.pair_base = (int*)(ws + off[4]);
+  a.part = (float*)(ws + off[5]);
   a.qb_begin = q_block_begin;
   a.qb_count = q_block_count;
   const int64_t end_row = (int64_t)(q_block_begin + q_block_count) * ssa::kBlock;
@@ -570,7 +569,7 @@ size_t ssa_workspace_bytes(const ssa_shape_t* shape, ssa_op_t op) {
   if (op == SSA_OP_SPARSE_FWD || op == SSA_OP_FULL_FWD) return ssa::kQueueBytes;
   if (op == SSA_OP_SPARSE_BWD || op == SSA_OP_FULL_BWD) {
     ssa::BwdPlan plan;
-    size_t off[7], need;
+    size_t off[6], need;
     ssa::bwd_plan(g, op == SSA_OP_FULL_BWD, 0, g.nqb, &plan, off, &need);
     return need;
   }

@@ -20,17 +20,19 @@
 //     key-side kernel reads.  Per tile, transposed as in the forward (a lane
 //     owns one query column):  S^T = K Q^T,  dP^T = V dO^T  (Q, dO in
 //     registers), then dQ^T += K^T dS^T with K^T read transposed from LDS.
-//   * dK/dV kernel: workgroups walk the work items of their (batch, KV head)
-//     group with a stride; an item is at most P consecutive (query head,
-//     query block) pairs, in (query block, head) order, of the pairs whose
-//     list holds key block j (block-sparse: 2 waves of 32 keys on block j), or
-//     of every pair of key block j (full: 4 waves on blocks j and j+1, which
-//     share each pair's tiles; block j+1 skips the pairs wholly in its
-//     future).  Per pair, untransposed (a lane owns one key column):
-//     S = Q K^T,  dP = dO V^T (K, V in registers), then dV += P^T dO and
-//     dK += dS^T Q with dO, Q read transposed from LDS.  Each item writes an
-//     fp32 partial per key block; a reduce kernel sums the items of a key
-//     block in item order and rounds to bf16.
+//   * dK/dV kernel: the (query head, query block) pairs of each (batch, KV
+//     head) group, numbered key block by key block and in (query block,
+//     head) order within one -- the pairs whose list holds key block j
+//     (block-sparse: 2 waves of 32 keys on block j), or every pair of key
+//     block j (full: 4 waves on blocks j and j+1, which share each pair's
+//     tiles; block j+1 skips the pairs wholly in its future) -- are cut into
+//     equal contiguous ranges, one per workgroup, so that every workgroup
+//     does the same number of pairs whatever the selection.  Per pair,
+//     untransposed (a lane owns one key column): S = Q K^T,  dP = dO V^T
+//     (K, V in registers), then dV += P^T dO and dK += dS^T Q with dO, Q read
+//     transposed from LDS.  A range writes one fp32 partial per key block it
+//     touches; a reduce kernel sums the partials of a key block in range
+//     order and rounds to bf16.
 // The tile loops stream through rings of LDS buffers.  The dQ loop and the
 // block-sparse dK/dV loop use two: the next step's tiles are requested while
 // a step is computed, and the smaller LDS footprint lets more workgroups
@@ -38,7 +40,7 @@
 // The pairs of a key block come from a bitmask mask[b, g, j, i] (bit hh: head
 // g*G+hh lists j for query block i) built from the index rows with atomic
 // ORs (order-independent); the pairs of each key block are then counted from
-// the bits, so the item boundaries do not depend on timing.
+// the bits, so the range boundaries do not depend on timing.
 #include <algorithm>
 #include <type_traits>
 
@@ -50,11 +52,13 @@ namespace ssa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSparsePairs = 32;   // pairs per work item, block-sparse backward (32 against 64: 4% faster)
-// pairs per work item, full backward: smaller items end the launch with a
-// shorter tail (48 against 128: the full backward 8% faster on prefill_8k)
-// at the cost of more partial sums to reduce
-constexpr int kFullPairs = 48;
+constexpr int kSparsePairs = 64;   // pair-list entries per step of a block-sparse range
+constexpr int kFullPairs = 1 << 30;  // full ranges need no list: one step per key unit
+// dK/dV workgroups in flight at once on a 256-CU device (per CU: four of the
+// block-sparse kernel, two of the full one); a launch of this many, split
+// over the groups, runs in one round
+constexpr int kSparseDkvWorkgroups = 1024;
+constexpr int kFullDkvWorkgroups = 512;
 constexpr int kRing = 3;           // tile buffers per loop (full dK/dV)
 constexpr int kDqRing = 2;         // K/V tile buffers of the dQ loop
 
@@ -65,8 +69,8 @@ __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(uint32_t* __restrict
 }
 
 // One wavefront per index row (b, query head or KV group, query block i): the
-// row's entries before its first -1 that name a causal block j <= diag(i) set
-// the bits of their query heads in mask[b, g, j, i].
+// row's entries that name a causal block 0 <= j <= diag(i) set the bits of
+// their query heads in mask[b, g, j, i].
 __global__ __launch_bounds__(64) void bwd_mask_kernel(const int32_t* __restrict__ idx, uint32_t* __restrict__ mask,
                                                       Geometry geo, int shared) {
   const int lane = threadIdx.x;
@@ -327,40 +331,49 @@ __global__ __launch_bounds__(64) void bwd_count_kernel(BwdArgs a, Geometry geo) 
   if (lane == 0) a.pairs[blockIdx.x] = cnt;
 }
 
-// Exclusive scan over key units of each group's item counts:
-// item_base[gi, u] = first item of key unit u, item_base[gi, nku] = total;
-// item_key[gi, e] = key unit of item e.
-__global__ __launch_bounds__(256) void bwd_items_kernel(BwdArgs a, Geometry geo) {
+// Exclusive scan over key units of each group's pair counts:
+// pair_base[gi, u] = first pair of key unit u, pair_base[gi, nku] = the
+// group's pairs.
+__global__ __launch_bounds__(256) void bwd_pair_scan_kernel(BwdArgs a, Geometry geo) {
   __shared__ int sTot[256];
   const int gi = blockIdx.x, tid = threadIdx.x;
   const BwdPlan pl = a.plan;
-  const int nku = (geo.nkb + pl.kpb - 1) / pl.kpb;
+  const int nku = pl.n_units(geo.nkb);
   const int per = (nku + 255) / 256;
   const int u0 = min(nku, tid * per), u1 = min(nku, u0 + per);
-  auto items = [&](int u) {
-    const int j = u * pl.kpb;  // the unit's first key block
-    const int np = a.full ? geo.group * pl.n_blocks(j) : a.pairs[(size_t)gi * geo.nkb + j];
-    return (np + pl.P - 1) / pl.P;
+  auto pairs = [&](int u) {
+    const int j = u * pl.kpb;  // the unit's first key block: its pairs are the unit's
+    return a.full ? geo.group * pl.n_blocks(j) : a.pairs[(size_t)gi * geo.nkb + j];
   };
   int tot = 0;
-  for (int u = u0; u < u1; ++u) tot += items(u);
+  for (int u = u0; u < u1; ++u) tot += pairs(u);
   sTot[tid] = tot;
   __syncthreads();
   int base = 0;
   for (int t = 0; t < tid; ++t) base += sTot[t];
-  int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
-  int* ik = a.item_key + (size_t)gi * pl.max_items;
+  int* pb = a.pair_base + (size_t)gi * (geo.nkb + 1);
   for (int u = u0; u < u1; ++u) {
-    ib[u] = base;
-    const int n = items(u);
-    for (int e = 0; e < n && base + e < pl.max_items; ++e) ik[base + e] = u;  // never exceeds the bound
-    base += n;
+    pb[u] = base;
+    base += pairs(u);
   }
-  if (tid == 255) ib[nku] = base;
+  if (tid == 255) pb[nku] = base;
 }
 
-// KPB key blocks per work item (1: block-sparse, 2: full), two waves of 32
-// keys per block; the waves share every pair's Q and dO tiles.
+// Workgroups a group's pairs are cut into (at most one pair each), and the
+// first pair of range s: floor(s * n / slots).
+__device__ __forceinline__ int range_slots(const BwdPlan& pl, int n) { return min(pl.slots, n); }
+__device__ __forceinline__ int range_begin(int s, int n, int slots) {
+  return (int)(((long long)s * n) / slots);
+}
+// The range that holds pair x (ranges are non-empty as slots <= n).
+__device__ __forceinline__ int range_of(int x, int n, int slots) {
+  return (int)((((long long)x + 1) * slots - 1) / n);
+}
+
+// KPB key blocks per key unit (1: block-sparse, 2: full), two waves of 32
+// keys per block; the waves share every pair's Q and dO tiles.  Workgroup
+// (s, group) walks range s of the group's pairs, key unit by key unit, P
+// pairs per step.
 // R: pair buffers in the ring (3: the pair after next is requested while a
 // pair is computed; 2: the next one, for less LDS and more workgroups per CU).
 template <int KPB, int R = kRing>
@@ -378,31 +391,62 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
   const BwdPlan pl = a.plan;
   const int ngroups = geo.batch * geo.hkv;
   const int gi = blockIdx.x % ngroups;
-  const int nslots = gridDim.x / ngroups;
-  const int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
-  const int* item_key = a.item_key + (size_t)gi * pl.max_items;
-  const int nku = (geo.nkb + KPB - 1) / KPB;
-  const int total = __builtin_amdgcn_readfirstlane(min(ib[nku], pl.max_items));
+  const int rs = blockIdx.x / ngroups;  // this workgroup's range
+  const int* pb = a.pair_base + (size_t)gi * (geo.nkb + 1);
+  const int nku = pl.n_units(geo.nkb);
+  const int npg = __builtin_amdgcn_readfirstlane(pb[nku]);  // the group's pairs
+  const int nrs = range_slots(pl, npg);
+  if (rs >= nrs) return;  // the whole workgroup: no barrier is passed before this
+  const int x_end = range_begin(rs + 1, npg, nrs);
   const int b = gi / geo.hkv, g = gi - b * geo.hkv;
   const int kblk = wave >> 1, kw = wave & 1;  // this wave's key block within the unit, and 32-key half
   TileOffsets<NW, 0> toff;
   toff.init(lane, wave);
   const size_t rows_pad = (size_t)a.qb_count * kBlock;
   const float c = geo.scale_log2;
-  // items in key-unit order, dealt round-robin to this group's workgroups
-  for (int li = blockIdx.x / ngroups; li < total; li += nslots) {
-  const int ku = __builtin_amdgcn_readfirstlane(item_key[li]);
-  const int j0 = ku * KPB;        // the unit's first key block: its pairs are the item's
+  // the key unit that holds the range's first pair: the last u with pb[u] <= x
+  int x = range_begin(rs, npg, nrs);
+  int ku = 0;
+  for (int lo = 0, hi = nku; lo < hi;) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(pb[mid]) <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+    ku = lo;
+  }
+  for (; x < x_end; ++ku) {
+  const int ub = __builtin_amdgcn_readfirstlane(pb[ku]);
+  const int ue = __builtin_amdgcn_readfirstlane(pb[ku + 1]);
+  if (ue <= x) continue;  // a key unit with no pairs
+  const int j0 = ku * KPB;        // the unit's first key block: its pairs are the unit's
   const int j = j0 + kblk;        // this wave's key block
   const bool kvalid = j < geo.nkb;
-  const int p_lo = (li - ib[ku]) * pl.P;
-  const int pairs_j = a.full ? G * pl.n_blocks(j0) : a.pairs[(size_t)gi * geo.nkb + j0];
-  const int npairs = __builtin_amdgcn_readfirstlane(min(pl.P, pairs_j - p_lo));
   const int ifirst = pl.first_block(j0);
-  __syncthreads();  // every wave is done with the previous item's buffers and pair list
+  const int p_end = min(x_end, ue) - ub;  // the range's pairs of this unit: x - ub .. p_end - 1
+
+  // this wave's 32 keys as MFMA B operands (rows past seq_kv re-read a valid
+  // row; such keys lie in the future of every query and are masked)
+  const int key = j * kBlock + 32 * kw + l32;
+  const int krow = min(key, geo.seq_kv - 1);
+  bf16x8 kop[4], vop[4];
+  load_row_op(a.k + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, kop);
+  load_row_op(a.v + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, vop);
+  f32x16 dk[2], dv[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.f;
+      dv[db][r] = 0.f;
+    }
+
+  for (int p_lo = x - ub, npairs; p_lo < p_end; p_lo += npairs) {
+  npairs = __builtin_amdgcn_readfirstlane(min(pl.P, p_end - p_lo));
+  __syncthreads();  // every wave is done with the previous step's buffers and pair list
 
   if (!a.full) {
-    // this item's pairs: numbers p_lo .. p_lo + npairs - 1 of key block j, in
+    // this step's pairs: numbers p_lo .. p_lo + npairs - 1 of key block j, in
     // (query block, head) order, from the head bits of query blocks ifirst..
     if (wave == 0) {
       int before = 0;  // pairs of the query blocks already passed
@@ -441,14 +485,6 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
     }
   };
 
-  // this wave's 32 keys as MFMA B operands (rows past seq_kv re-read a valid
-  // row; such keys lie in the future of every query and are masked)
-  const int key = j * kBlock + 32 * kw + l32;
-  const int krow = min(key, geo.seq_kv - 1);
-  bf16x8 kop[4], vop[4];
-  load_row_op(a.k + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, kop);
-  load_row_op(a.v + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, vop);
-
   // requests of pair p into ring buffer BUF (a compile-time index, so that
   // every LDS address below is a fixed per-lane offset plus an immediate)
   auto issue = [&](auto BUF, int p) {
@@ -474,14 +510,6 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
   if (npairs > 0) issue(B0{}, 0);
   if (R == 3 && npairs > 1) issue(B1{}, 1);
 
-  f32x16 dk[2], dv[2];
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.f;
-      dv[db][r] = 0.f;
-    }
   auto step = [&](auto BUF, int p) {
     constexpr int buf = decltype(BUF)::value;
     int ii, hh;
@@ -569,12 +597,15 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
     if (p0 + 1 < npairs) step(B1{}, p0 + 1);
     if (R == 3 && p0 + 2 < npairs) step(std::integral_constant<int, 2 % R>{}, p0 + 2);
   }
-  // partial sums of this item's block kblk: [2][64 keys][64 d] fp32 (dK unscaled)
+  }  // steps
+  x = ub + p_end;
+  // partial sums of block kblk over this range's pairs of the unit (piece
+  // rs + ku of the group): [2][64 keys][64 d] fp32 (dK unscaled)
   if (!kvalid) continue;
-  float* pk = a.part + (((size_t)gi * pl.max_items + li) * KPB + kblk) * (2 * kBlock * kHeadDim);
+  float* pk = a.part + (((size_t)gi * pl.n_pieces(geo.nkb) + rs + ku) * KPB + kblk) * (2 * kBlock * kHeadDim);
   if constexpr (KPB == 1) {
     // this lane's offset, opaque so that the 32 per-register offsets are
-    // formed here rather than hoisted out of the item loop, where they are
+    // formed here rather than hoisted out of the unit loop, where they are
     // spilled (measured: 4% faster for this kernel, 3% slower for KPB = 2)
     pk = const_cast<float*>(uniform_ptr(pk));
     int lo = 4 * hl * kHeadDim + l32;
@@ -601,8 +632,9 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
   }
 }
 
-// Sum the item partials of each key block in item order: dK = scale * sum,
-// dV = sum, rounded to bf16.  One thread per 4 columns of a key row.
+// Sum the partials of each key block in range order: dK = scale * sum,
+// dV = sum, rounded to bf16 (zero for a block no pair attends to).  One
+// thread per 4 columns of a key row.
 __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometry geo) {
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t per_group = (size_t)geo.seq_kv * (kHeadDim / 4);
@@ -612,18 +644,25 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometr
   const int key = rem / (kHeadDim / 4);
   const int c4 = rem - key * (kHeadDim / 4);
   const int j = key / kBlock, kr = key - j * kBlock;
-  const int kpb = a.plan.kpb;
+  const BwdPlan pl = a.plan;
+  const int kpb = pl.kpb;
   const int ku = j / kpb, kblk = j - ku * kpb;  // key unit of block j, and j's place in it
-  const int* ib = a.item_base + (size_t)gi * (geo.nkb + 1);
-  const int n = min(ib[ku + 1], a.plan.max_items) - ib[ku];
-  const size_t item_floats = (size_t)kpb * 2 * kBlock * kHeadDim;
-  const float* base = a.part + ((size_t)gi * a.plan.max_items + ib[ku]) * item_floats +
-                      (size_t)kblk * 2 * kBlock * kHeadDim + kr * kHeadDim + 4 * c4;
+  const int* pb = a.pair_base + (size_t)gi * (geo.nkb + 1);
+  const int npg = pb[pl.n_units(geo.nkb)];
+  const int ub = pb[ku], ue = pb[ku + 1];
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-  for (int e = 0; e < n; ++e) {
-    const float* pe = base + (size_t)e * item_floats;
-    sk += *reinterpret_cast<const f32x4*>(pe);
-    sv += *reinterpret_cast<const f32x4*>(pe + kBlock * kHeadDim);
+  if (ue > ub) {
+    // the ranges that hold the unit's first and last pairs, and every one between
+    const int nrs = range_slots(pl, npg);
+    const int s0 = range_of(ub, npg, nrs), s1 = range_of(ue - 1, npg, nrs);
+    const size_t piece_floats = (size_t)kpb * 2 * kBlock * kHeadDim;
+    const float* base = a.part + ((size_t)gi * pl.n_pieces(geo.nkb) + s0 + ku) * piece_floats +
+                        (size_t)kblk * 2 * kBlock * kHeadDim + kr * kHeadDim + 4 * c4;
+    for (int e = 0; e <= s1 - s0; ++e) {
+      const float* pe = base + (size_t)e * piece_floats;
+      sk += *reinterpret_cast<const f32x4*>(pe);
+      sv += *reinterpret_cast<const f32x4*>(pe + kBlock * kHeadDim);
+    }
   }
   const size_t o = ((size_t)gi * geo.seq_kv + key) * kHeadDim + 4 * c4;
   u32x2 wk, wv;
@@ -637,7 +676,7 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(BwdArgs a, Geometr
 
 }  // namespace
 
-void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan* plan, size_t off[7],
+void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan* plan, size_t off[6],
               size_t* total) {
   BwdPlan p;
   p.lo = qb_begin;
@@ -645,37 +684,37 @@ void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan*
   p.qoffb = g.q_offset / kBlock;
   p.P = full ? kFullPairs : kSparsePairs;
   p.kpb = full ? 2 : 1;
-  long long items = 0;  // every (head, query block) pair present
-  for (int j = 0; j < g.nkb; j += p.kpb) items += ((long long)g.group * p.n_blocks(j) + p.P - 1) / p.P;
+  const long long ngroups = (long long)g.batch * g.hkv;
+  const long long wgs = full ? kFullDkvWorkgroups : kSparseDkvWorkgroups;
+  p.slots = (int)std::max<long long>(1, ngroups > 0 ? wgs / ngroups : 1);
+  long long pairs = 0;  // every (head, query block) pair present
+  for (int j = 0; j < g.nkb; j += p.kpb) pairs += (long long)g.group * p.n_blocks(j);
   if (!full) {
-    // a list names at most min(topk, diag + 1) distinct blocks, so a group has
-    // at most G * sum_i min(topk, diag(i) + 1) pairs; cutting each key block's
-    // pairs into items of P adds at most one partial item per key block
-    long long pairs = 0;
-    for (int i = p.lo; i < p.hi; ++i) pairs += std::min<long long>(g.topk, (long long)p.qoffb + i + 1);
-    items = std::min(items, (g.group * pairs + p.P - 1) / p.P + g.nkb);
+    // a list names at most min(topk, diag + 1) distinct blocks
+    long long listed = 0;
+    for (int i = p.lo; i < p.hi; ++i) listed += std::min<long long>(g.topk, (long long)p.qoffb + i + 1);
+    pairs = std::min(pairs, (long long)g.group * listed);
   }
-  p.max_items = (int)std::min<long long>(items, 0x7fffffff);
+  p.max_pairs = pairs;
+  // no more ranges than pairs (a range holds one pair at least)
+  p.slots = (int)std::max<long long>(1, std::min<long long>(p.slots, pairs));
   *plan = p;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)g.batch * g.hq * qb_count * kBlock;
-  const size_t ngroups = (size_t)g.batch * g.hkv;
   size_t o = 0;
   off[0] = o;
   o += up(rows * sizeof(float));
   off[1] = o;
   o += up(rows * sizeof(float));
   off[2] = o;
-  if (!full) o += ngroups * g.nkb * g.nqb * sizeof(uint32_t);
+  if (!full) o += (size_t)ngroups * g.nkb * g.nqb * sizeof(uint32_t);
   off[3] = o;
-  if (!full) o += ngroups * g.nkb * sizeof(int);
+  if (!full) o += (size_t)ngroups * g.nkb * sizeof(int);
   o = up(o);
   off[4] = o;
-  o += up(ngroups * (g.nkb + 1) * sizeof(int));
+  o += up((size_t)ngroups * (g.nkb + 1) * sizeof(int));
   off[5] = o;
-  o += up(ngroups * (size_t)p.max_items * sizeof(int));
-  off[6] = o;
-  o += up(ngroups * (size_t)p.max_items * p.kpb * 2 * kBlock * kHeadDim * sizeof(float));
+  o += up((size_t)ngroups * p.n_pieces(g.nkb) * p.kpb * 2 * kBlock * kHeadDim * sizeof(float));
   *total = o;
 }
 
@@ -691,19 +730,19 @@ hipError_t launch_attn_backward(const BwdArgs& a, const Geometry& g, hipStream_t
     hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)rows), dim3(64), 0, stream, a.idx, a.mask, g, a.idx_shared);
     hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)(ngroups * g.nkb)), dim3(64), 0, stream, a, g);
   }
-  hipLaunchKernelGGL(bwd_items_kernel, dim3((unsigned)ngroups), dim3(256), 0, stream, a, g);
+  hipLaunchKernelGGL(bwd_pair_scan_kernel, dim3((unsigned)ngroups), dim3(256), 0, stream, a, g);
   // heads that walk the same tiles (full, or one list per KV group) pair up
   if ((a.full || a.idx_shared) && g.group % 2 == 0)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing, 2>), dim3((unsigned)(units / 2)), dim3(256), 0, stream, a, g);
   else
     hipLaunchKernelGGL((attn_bwd_dq_kernel<kDqRing, 1>), dim3((unsigned)units), dim3(128), 0, stream, a, g);
-  // enough workgroups to fill the chip a few times over; each walks its
-  // group's items with a stride
-  const size_t slots = std::max<size_t>(1, std::min<size_t>((size_t)a.plan.max_items, 2048 / ngroups));
+  // one workgroup per range of each group's pairs (ranges past a group's
+  // pair count leave at once)
+  const size_t grid = ngroups * (size_t)a.plan.slots;
   if (a.plan.kpb == 2)
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)(ngroups * slots)), dim3(256), 0, stream, a, g);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a, g);
   else
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<1, 2>), dim3((unsigned)(ngroups * slots)), dim3(128), 0, stream, a, g);
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<1, 2>), dim3((unsigned)grid), dim3(128), 0, stream, a, g);
   const size_t threads = ngroups * g.seq_kv * (kHeadDim / 4);
   if (threads > 0)
     hipLaunchKernelGGL(attn_bwd_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a, g);

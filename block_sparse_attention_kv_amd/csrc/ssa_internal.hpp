@@ -79,24 +79,32 @@ inline size_t decode_workspace_bytes(int batch, int hq, int hkv) {
   return (size_t)batch * hq * decode_pieces(batch, hkv) * kPartialFloats * sizeof(float);
 }
 
-// Backward work items: key blocks are taken kpb at a time (a key unit); the
-// (query head, query block) pairs that attend to the unit's first block j --
-// query blocks i in [lo, hi) with diagonal block qoffb + i >= j, in (query
-// block, head) order -- are cut into items of at most P pairs; items are
-// numbered per (batch, KV head) group in key-unit order.  The unit's later
-// blocks see a subset of those pairs (the rest lie wholly in their future).
+// Backward work split of the key side: key blocks are taken kpb at a time (a
+// key unit); the (query head, query block) pairs that attend to the unit's
+// first block j -- query blocks i in [lo, hi) with diagonal block qoffb + i >=
+// j, in (query block, head) order -- are numbered per (batch, KV head) group
+// in key-unit order, and the group's pairs are cut into `slots` contiguous
+// ranges of equal length (floor(s * n / slots) .. floor((s+1) * n / slots) for
+// n pairs), one per workgroup.  A range is walked P pairs at a time and gives
+// one partial sum per key unit it touches (piece s + u of the group).  The
+// unit's later blocks see a subset of its pairs (the rest lie wholly in their
+// future).
 struct BwdPlan {
   int lo, hi;     // query blocks handled
   int qoffb;      // q_offset / B (floor): query block i's diagonal key block is qoffb + i
-  int P;          // pairs per item
+  int P;          // pairs per step of the pair list
   int kpb;        // key blocks per key unit (1: block-sparse, 2: full)
-  int max_items;  // items of one group when every pair is present (bound)
+  int slots;      // dK/dV workgroups per group (fewer when the group has fewer pairs)
+  long long max_pairs;  // pairs of one group when every listed pair is present (bound)
 
   __host__ __device__ int first_block(int j) const { return j - qoffb > lo ? j - qoffb : lo; }
   __host__ __device__ int n_blocks(int j) const {
     const int n = hi - first_block(j);
     return n > 0 ? n : 0;
   }
+  __host__ __device__ int n_units(int nkb) const { return (nkb + kpb - 1) / kpb; }
+  // partial sums per group: one per (workgroup, key unit) piece, s + u < slots + units
+  __host__ __device__ int n_pieces(int nkb) const { return slots + n_units(nkb); }
 };
 
 struct BwdArgs {
@@ -116,16 +124,15 @@ struct BwdArgs {
   float* delta;       // workspace: per-row dO . O, same layout
   uint32_t* mask;     // workspace (sparse): [b*Hkv, nkb, nqb] head bits
   int* pairs;         // workspace (sparse): [b*Hkv, nkb] pairs per key block
-  int* item_base;     // workspace: [b*Hkv, nkb + 1] first item of each key unit
-  int* item_key;      // workspace: [b*Hkv, max_items] key unit of each item
-  float* part;        // workspace: [b*Hkv, max_items][kpb][2][B][d] fp32 partial dK, dV
+  int* pair_base;     // workspace: [b*Hkv, nkb + 1] first pair of each key unit; [nku] = the group's pairs
+  float* part;        // workspace: [b*Hkv, n_pieces][kpb][2][B][d] fp32 partial dK, dV
   int qb_begin, qb_count, rows_out;
   BwdPlan plan;
 };
 
-// Work-item plan and workspace layout of a backward call (byte offsets of
-// lse2, delta, mask, pairs, item_base, item_key, part; total bytes).
-void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan* plan, size_t off[7],
+// Work plan and workspace layout of a backward call (byte offsets of lse2,
+// delta, mask, pairs, pair_base, part; total bytes).
+void bwd_plan(const Geometry& g, bool full, int qb_begin, int qb_count, BwdPlan* plan, size_t off[6],
               size_t* total);
 
 hipError_t launch_block_summaries(const uint16_t* k, float* k_summary, const Geometry& g,

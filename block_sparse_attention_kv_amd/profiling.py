@@ -74,8 +74,8 @@ def classify(name: str):
         return "bwd_mask"
     if "bwd_count_kernel" in name:
         return "bwd_count"
-    if "bwd_items_kernel" in name:
-        return "bwd_items"
+    if "bwd_pair_scan_kernel" in name:
+        return "bwd_pair_scan"
     if "bwd_fill_zero_kernel" in name:
         return "bwd_clear"
     if "attn_sparse_early_stop_kernel" in name:

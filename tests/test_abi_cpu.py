@@ -196,11 +196,17 @@ def test_backward_workspace_and_validation(lib):
     sh = good_shape()            # b=1, Hq=4, Hkv=2, 256 rows: 4 query / key blocks
     p = ctypes.byref(sh)
     rows = 4 * 4 * 64 * 4        # per-row LSE / D arrays: 4 heads x 4 query blocks x 64 rows, fp32
-    parts = 2 * 4 * 2 * 64 * 64 * 4   # 2 KV heads x 4 items (one per key block) x (dK, dV) 64 x 64 fp32
+    piece = 2 * 64 * 64 * 4           # (dK, dV) partial of one key block: 2 x 64 x 64 fp32
+    # block-sparse: a group (2 query heads) lists at most 2 * (1 + 2 + 2 + 2) = 14 pairs, so
+    # 14 ranges; a partial per (range, key block) piece: 14 + 4 pieces per group
+    parts = 2 * (14 + 4) * piece
     need = lib.ssa_workspace_bytes(p, ssa.SSA_OP_SPARSE_BWD)
-    # + head bits and pair counts, item starts, item key blocks: each under 256 bytes, padded to 256
-    assert need == 2 * rows + 3 * 256 + parts
-    assert lib.ssa_workspace_bytes(p, ssa.SSA_OP_FULL_BWD) == 2 * rows + 2 * 256 + parts
+    # + head bits and pair counts, pair starts: each under 256 bytes, padded to 256
+    assert need == 2 * rows + 2 * 256 + parts
+    # full: 2 * (4 + 2) = 12 pairs over the key units (blocks 0-1, 2-3) of a group, so 12
+    # ranges and 12 + 2 pieces, each holding two key blocks
+    need_full = lib.ssa_workspace_bytes(p, ssa.SSA_OP_FULL_BWD)
+    assert need_full == 2 * rows + 256 + 2 * (12 + 2) * 2 * piece
     args = (FAKE,) * 10
     assert lib.ssa_block_sparse_attn_bwd(p, *args, FAKE, need - 1, None) == ssa.SSA_ERR_WORKSPACE
     assert lib.ssa_block_sparse_attn_bwd(p, *args, ctypes.c_void_p(0x10080), need, None) == ssa.SSA_ERR_INVALID_ARG
@@ -210,12 +216,13 @@ def test_backward_workspace_and_validation(lib):
     assert b"dout is NULL" in lib.ssa_last_error()
     assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 3, 2, *((FAKE,) * 7), need, None) == ssa.SSA_ERR_INVALID_ARG
     # a slice never needs more workspace than the whole range
-    assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 2, 2, *((FAKE,) * 6), None, need, None) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_full_attn_bwd(p, FAKE, FAKE, FAKE, 2, 2, *((FAKE,) * 6), None, need_full,
+                                 None) == ssa.SSA_ERR_INVALID_ARG
     assert b"workspace is NULL" in lib.ssa_last_error()
     # group-shared / per-head masks hold 32 heads per KV head at most
     wide = good_shape(n_q_heads=64, n_kv_heads=1)
     assert lib.ssa_block_sparse_attn_bwd(ctypes.byref(wide), *args, FAKE, 1 << 40, None) == ssa.SSA_ERR_UNSUPPORTED
-    # the long-sequence chunking stays within 64 query blocks per work item
+    # the partials of a long sequence stay bounded by the ranges and key blocks
     long = good_shape(n_q_heads=32, n_kv_heads=2, seq_q=32768, seq_kv=32768, topk=16)
     assert lib.ssa_workspace_bytes(ctypes.byref(long), ssa.SSA_OP_SPARSE_BWD) < 1 << 30
 
