@@ -296,8 +296,10 @@ ssa_status_t ssa_block_sparse_attn_fwd_noalloc(const ssa_shape_t* shape, const v
  *           no row attends to)
  *   workspace  >= ssa_workspace_bytes(shape, SSA_OP_SPARSE_BWD) bytes,
  *              256-byte aligned (else SSA_ERR_WORKSPACE / SSA_ERR_INVALID_ARG)
- * More than 32 query heads per KV head: SSA_ERR_UNSUPPORTED.  Results are
- * bitwise reproducible (no atomics on gradients). */
+ * More than 32 query heads per KV head, or more than 2^31 - 1 listed
+ * (query head, query block, key block) pairs in one KV group:
+ * SSA_ERR_UNSUPPORTED.  Results are bitwise reproducible (no atomics on
+ * gradients; the work split depends only on the listed pairs). */
 ssa_status_t ssa_block_sparse_attn_bwd(const ssa_shape_t* shape, const void* q, const void* k, const void* v,
                                        const int32_t* block_idx, const void* out, const float* lse,
                                        const void* dout, void* dq, void* dk, void* dv, void* workspace,

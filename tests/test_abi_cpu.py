@@ -222,6 +222,11 @@ def test_backward_workspace_and_validation(lib):
     # group-shared / per-head masks hold 32 heads per KV head at most
     wide = good_shape(n_q_heads=64, n_kv_heads=1)
     assert lib.ssa_block_sparse_attn_bwd(ctypes.byref(wide), *args, FAKE, 1 << 40, None) == ssa.SSA_ERR_UNSUPPORTED
+    # a KV group with more than 2^31 - 1 (query head, query block, key block) pairs
+    huge = good_shape(n_q_heads=32, n_kv_heads=1, seq_q=1 << 20, seq_kv=1 << 20)
+    assert lib.ssa_full_attn_bwd(ctypes.byref(huge), FAKE, FAKE, FAKE, 0, (1 << 20) // 64, *((FAKE,) * 7), 1 << 40,
+                                 None) == ssa.SSA_ERR_UNSUPPORTED
+    assert b"too large" in lib.ssa_last_error()
     # the partials of a long sequence stay bounded by the ranges and key blocks
     long = good_shape(n_q_heads=32, n_kv_heads=2, seq_q=32768, seq_kv=32768, topk=16)
     assert lib.ssa_workspace_bytes(ctypes.byref(long), ssa.SSA_OP_SPARSE_BWD) < 1 << 30
