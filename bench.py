@@ -312,7 +312,7 @@ def bench_peaks(args, torch, ssa, W):
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=i32, device=dev)
     best_r, best_c = None, None
-    for per_cu in (4, 8, 16):
+    for per_cu in (4, 8, 16, 64):
         nbr = per_cu * cus
         ro = torch.zeros(nbr, dtype=i32, device=dev)
         P.read(src, ro, nbr)
@@ -323,7 +323,7 @@ def bench_peaks(args, torch, ssa, W):
                       "ms": round(ms, 4)}
     half = nbytes // 2
     a, b = src[: half // 4], src[half // 4:]
-    for per_cu in (4, 8, 16):
+    for per_cu in (4, 8, 16, 64):
         nbr = per_cu * cus
         P.copy(a, b, nbr)
         ms = _event_ms(torch, lambda: P.copy(a, b, nbr), 7)

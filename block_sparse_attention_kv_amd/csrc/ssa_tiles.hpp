@@ -161,25 +161,45 @@ __device__ __forceinline__ int canonical_index_row(const int iv[4], const float 
 // inline asm so the compiler does not track it; each use is ordered by the
 // explicit waits of the pipeline (it has no register outputs: the address
 // registers are read at issue).
+// NT: the non-temporal cache policy, for data read once (streamed past the
+// caches rather than kept in them).
+template <bool NT = false>
 __device__ __forceinline__ void dma_1k(const uint16_t* gtile, uint32_t voff, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(gtile), "s"(lds_base)
-      : "memory", "m0");
+  if (NT)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(gtile), "s"(lds_base)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(gtile), "s"(lds_base)
+        : "memory", "m0");
 }
 
 // Same load for the partial last tile of a sequence.  The asm text differs so
 // the compiler keeps it on its own (rare) path instead of merging the two
 // paths into per-load selects.
+template <bool NT = false>
 __device__ __forceinline__ void dma_1k_ragged(const uint16_t* gtile, uint32_t voff, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1 ; partial tile"
-      :
-      : "v"(voff), "s"(gtile), "s"(lds_base)
-      : "memory", "m0");
+  if (NT)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt ; partial tile"
+        :
+        : "v"(voff), "s"(gtile), "s"(lds_base)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1 ; partial tile"
+        :
+        : "v"(voff), "s"(gtile), "s"(lds_base)
+        : "memory", "m0");
 }
 
 // A wave-uniform global pointer, placed in scalar registers (the DMA
@@ -249,15 +269,16 @@ struct TileOffsets {
 };
 
 // Request this wavefront's slices of one tile into LDS at `lds`.  Full tiles
-// use the precomputed offsets; a partial last tile clamps rows.
-template <int STEP, int S>
+// use the precomputed offsets; a partial last tile clamps rows.  NT: tiles
+// read once (the non-temporal policy).
+template <bool NT = false, int STEP, int S>
 __device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, const uint8_t* lds, int lane,
                                           const TileOffsets<STEP, S>& off) {
   const uint32_t base = lds_addr(lds);
   if (nvalid >= kBlock) {
 #pragma unroll
     for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k)
-      dma_1k(gtile, off.v[k], __builtin_amdgcn_readfirstlane(base + (off.first + k * STEP) * 1024));
+      dma_1k<NT>(gtile, off.v[k], __builtin_amdgcn_readfirstlane(base + (off.first + k * STEP) * 1024));
   } else {
     // The lane index passes through an opaque copy here, so that the partial
     // path's offsets are computed on that (rare) path instead of being hoisted
@@ -267,7 +288,7 @@ __device__ __forceinline__ void tile_load(const uint16_t* gtile, int nvalid, con
 #pragma unroll
     for (int k = 0; k < TileOffsets<STEP, S>::kN; ++k) {
       const int c = off.first + k * STEP;
-      dma_1k_ragged(gtile, slice_offset<S>(c, l, nvalid), __builtin_amdgcn_readfirstlane(base + c * 1024));
+      dma_1k_ragged<NT>(gtile, slice_offset<S>(c, l, nvalid), __builtin_amdgcn_readfirstlane(base + c * 1024));
     }
   }
 }

@@ -36,12 +36,13 @@ int ssa_peak_mfma(int32_t iters, int32_t n_blocks, uint32_t* out, hipStream_t st
 int ssa_peak_tile(int32_t tiles, int32_t n_blocks, uint32_t* out, hipStream_t stream);
 
 /* Streaming read of `bytes` (a multiple of 16, 16-byte aligned) by n_blocks
- * workgroups of 256 threads.
+ * workgroups of 256 threads, one contiguous chunk each, non-temporal loads.
  *   out  uint32 [n_blocks]: each workgroup's XOR of the words it read. */
 int ssa_peak_read(const void* src, size_t bytes, uint32_t* out, int32_t n_blocks, hipStream_t stream);
 
 /* Streaming copy of `bytes` (a multiple of 16; both pointers 16-byte aligned;
- * the ranges must not overlap) by n_blocks workgroups of 256 threads. */
+ * the ranges must not overlap) by n_blocks workgroups of 256 threads, one
+ * contiguous chunk each, non-temporal loads and stores. */
 int ssa_peak_copy(const void* src, void* dst, size_t bytes, int32_t n_blocks, hipStream_t stream);
 
 /* One wavefront waits `ticks` (1 .. 1e8) ticks of the 100 MHz real-time
