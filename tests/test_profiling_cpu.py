@@ -35,6 +35,7 @@ def _write_csv(path, header, rows):
     ("ssa::(anonymous namespace)::attn_sparse_early_stop_kernel(ssa::AttnArgs)", "sparse_attn_early_stop"),
     ("void ssa::(anonymous namespace)::attn_decode_partial_kernel<1>(ssa::AttnArgs, float*)", "decode_attn"),
     (DKV, "bwd_dkv"),
+    ("ssa::(anonymous namespace)::bwd_pair_scan_kernel(ssa::BwdArgs, ssa::Geometry)", "bwd_pair_scan"),
     (COPY, "copy"),
     ("void at::native::vectorized_elementwise_kernel<4>", None),
 ])
@@ -198,3 +199,19 @@ def test_workgroup_trace_markdown_with_replica(tmp_path):
     assert "1400.0 / 1500.0 / 3000.0 cycles per tile" in md
     assert "| prefill_8k | sparse_attn | 2 |" in md
     assert md.rstrip().endswith("| 0.0762 | 0.75 |")
+
+
+def test_bench_comparison_with_default_run(tmp_path):
+    def line(sp, fu, de):
+        k = lambda ms: {"median_ms": ms, "mean_ms": ms * 1.05}
+        return json.dumps({"kernels": {"sparse_attn": k(sp), "full_attn": k(fu)},
+                           "decode": {"kernels": {"decode_attn": k(de)}}})
+    prof, ref = tmp_path / "prof.log", tmp_path / "ref.log"
+    prof.write_text("noise\n" + line(0.0979, 0.3187, 0.0954) + "\n")
+    ref.write_text(line(0.0897, 0.2982, 0.0749) + "\n")
+    md = P.bench_comparison(str(prof), str(ref))
+    assert "| sparse_attn | 97.90 | 102.80 | 89.70 |" in md
+    assert "| decode_attn (decode_attn + decode_combine) | 95.40 | 100.17 | 74.90 |" in md
+    # without a default run: three columns only
+    md2 = P.bench_comparison(str(prof))
+    assert "| full_attn | 318.70 | 334.63 |" in md2 and "default run |" not in md2
