@@ -83,6 +83,8 @@ SMALL = [
     W.Workload("bwd_gqa16_2k", 1, 32, 2, 2048, 2048, 64, 64, 16, seed=27),
     W.Workload("bwd_mha_topk256", 1, 2, 2, 4096, 4096, 64, 64, 256, seed=32),   # every block selected
     W.Workload("bwd_g32", 1, 32, 1, 1024, 1024, 64, 64, 8, seed=33),            # 32 heads on one KV head
+    # 1088 KV groups: more groups than dK/dV workgroups, so one pair range per group
+    W.Workload("bwd_many_groups", 17, 64, 64, 192, 192, 64, 64, 2, seed=34),
 ]
 
 
@@ -110,6 +112,7 @@ FULL_CASES = [
     (W.Workload("bwd_full_slice", 1, 4, 2, 1000, 1000, 64, 64, 5, seed=29), (9, 5)),   # last 5 blocks, ragged
     (W.Workload("bwd_full_slice_mid", 2, 4, 1, 640, 640, 64, 64, 2, seed=30), (3, 4)),
     (W.Workload("bwd_full_chunked", 1, 4, 2, 192, 320, 64, 64, 3, seed=31), (0, 3)),
+    (W.Workload("bwd_full_many_groups", 17, 64, 64, 192, 192, 64, 64, 2, seed=35), (0, 3)),
 ]
 
 
