@@ -38,7 +38,6 @@ struct UnitState {
   f32x16 o[2][2];  // O^T accumulators [d block][query block]
   float m[2];      // reference max (log2 units) per owned query column
   float l[2];      // running sum (this lane's keys)
-  float ld[2];     // running sum over unselected tiles (full kernel)
 };
 
 __device__ __forceinline__ void load_q(const uint16_t* qbase, int i, int seq_q, int l32, int hl, bf16x8 qop[2][4]) {
@@ -65,7 +64,6 @@ __device__ __forceinline__ void init_state(UnitState& st) {
   for (int qb = 0; qb < 2; ++qb) {
     st.m[qb] = -__builtin_inff();
     st.l[qb] = 0.f;
-    st.ld[qb] = 0.f;
   }
 }
 
@@ -126,10 +124,15 @@ __device__ __forceinline__ void tile_probs(const f32x16 s[2][2], const UnitState
 // tile_rs (optional) receives this lane's fp32 sum of the tile's
 // probabilities per query block (relative to the updated reference max).
 // With BIAS, b2 (log2 units) is added to every logit of the tile.
+// FULL: the running sum over unselected tiles is kept in LDS at ld[0] and
+// ld[64] (one slot per lane and query block).  In registers the compiler
+// spills it, and the spill's reload waits for every vector memory operation
+// in flight, the next tile's K/V requests included.
 template <bool FULL, bool BIAS = false>
 __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x4 pk[2][2][2], bool diag,
                                              bool selected, int key0, int pos0, int l32, int hl, float c,
-                                             float* tile_rs = nullptr, float b2 = 0.f, bool first = false) {
+                                             float* tile_rs = nullptr, float b2 = 0.f, bool first = false,
+                                             float* ld = nullptr) {
   if (diag) {
     // Causal mask of the tile holding the query rows' own positions: key > pos
     // becomes -inf.  Branch-free sign arithmetic (no compare masks to keep live).
@@ -178,7 +181,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
         const float alpha = fast_exp2(st.m[qb] - mn);
         st.m[qb] = mn;
         st.l[qb] *= alpha;
-        if (FULL) st.ld[qb] *= alpha;
+        if (FULL) ld[64 * qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -191,7 +194,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 s[2][2], UnitState& st, u32x
   for (int qb = 0; qb < 2; ++qb) {
     if (tile_rs) tile_rs[qb] = rs[qb];
     st.l[qb] += rs[qb];
-    if (FULL && !selected) st.ld[qb] += rs[qb];
+    if (FULL && !selected) ld[64 * qb] += rs[qb];
   }
 }
 
@@ -226,7 +229,8 @@ __device__ __forceinline__ void tile_pv(const uint8_t* sV, const u32x4 pk[2][2][
 // placed at chunk ^ (row % 8) so that neither side conflicts on LDS banks.
 template <bool FULL>
 __device__ __forceinline__ void unit_epilogue_staged(const UnitState& st, const AttnArgs& a, const Geometry& geo,
-                                                     int bh, int i, int lane, uint8_t* stage) {
+                                                     int bh, int i, int lane, uint8_t* stage,
+                                                     const float* ld = nullptr) {
   // the lane index passes through an opaque copy, so that the staging
   // addresses are formed here rather than hoisted out of the unit loop into
   // registers the tile loop needs
@@ -237,7 +241,7 @@ __device__ __forceinline__ void unit_epilogue_staged(const UnitState& st, const 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = sum_xor32(st.l[qb]);
-    const float dt = FULL ? sum_xor32(st.ld[qb]) : 0.f;
+    const float dt = FULL ? sum_xor32(ld[64 * qb]) : 0.f;
     inv[qb] = 1.f / lt;
     const int row = i * kBlock + 32 * qb + lr;
     if (lh == 0 && row < geo.seq_q) {
@@ -620,6 +624,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
   __shared__ int sList[NW][kMaxTopk];
   __shared__ int sTmp[NW][kMaxTopk];
   __shared__ float sBias[BIAS ? NW : 1][BIAS ? kMaxTopk : 1];
+  __shared__ float sLd[FULL ? NW : 1][2][64];  // dropped-mass sums (FULL), one slot per lane and query block
   __shared__ int sUnit;
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -672,6 +677,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
     }
     UnitState st;
     init_state(st);
+    float* ld = FULL ? &sLd[FULL ? wave : 0][0][lane] : nullptr;
+    if (FULL) ld[0] = ld[64] = 0.f;  // this lane's own slots: read back by this lane only
     wait_vmem<0>();
     __builtin_amdgcn_wave_barrier();
     const float c = geo.scale_log2;
@@ -707,14 +714,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_group_kernel(AttnArgs a, Geom
       tile_scores(sK[t & 1], qop, l32, hl, s);
       u32x4 pk[2][2][2];
       const float b2 = BIAS ? sBias[BIAS ? wave : 0][BIAS ? t : 0] * kLog2eF : 0.f;
-      tile_softmax<FULL, BIAS>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c, nullptr, b2);
+      tile_softmax<FULL, BIAS>(s, st, pk, j == jd, selected, j * kBlock, pos0, l32, hl, c, nullptr, b2, false, ld);
       tile_pv(sV[t & 1], pk, st, lane);
     }
     __builtin_amdgcn_s_setprio(0);
     tr.loop_end(nt);
     wait_lds_reads();
     __syncthreads();  // every wave is done with the tiles: each stages its outputs in a quarter of them
-    unit_epilogue_staged<FULL>(st, a, geo, bh, i, lane, wave < 2 ? sK[wave] : sV[wave - 2]);
+    unit_epilogue_staged<FULL>(st, a, geo, bh, i, lane, wave < 2 ? sK[wave] : sV[wave - 2], ld);
     if (!a.queue) break;
     wait_lds_reads();
     __syncthreads();  // every wave is done with the tiles, the lists and the unit slot
