@@ -437,6 +437,13 @@ __global__ __launch_bounds__(128 * KPB, 2) void attn_bwd_dkv_kernel(BwdArgs a, G
   bf16x8 kop[4], vop[4];
   load_row_op(a.k + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, kop);
   load_row_op(a.v + ((size_t)gi * geo.seq_kv + krow) * kHeadDim, true, hl, vop);
+  // The operands are consumed here, so the compiler waits for them once,
+  // before the pair loop.  Left to the first MFMA that reads them, its waits
+  // stay inside the loop, where the vector-memory counter also holds the next
+  // pairs' tile requests (issued by inline asm, which it does not track), and
+  // each step would wait for those to land.
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(kop[ks]), "+v"(vop[ks]));
   f32x16 dk[2], dv[2];
 #pragma unroll
   for (int db = 0; db < 2; ++db)
