@@ -570,6 +570,11 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
   const int pos0 = geo.q_offset + i * kBlock;
   int used = 0;
   for (int t = 0; t < nt; ++t) {
+    // issue priority alternates every tile, as in the block-sparse loop
+    if (t & 1)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
     const int j = __builtin_amdgcn_readfirstlane(sOrder[t]);
     const bool more = t + 1 < nt;
     const int jn = more ? __builtin_amdgcn_readfirstlane(sOrder[t + 1]) : 0;
@@ -604,6 +609,7 @@ __global__ __launch_bounds__(64, 2) void attn_sparse_early_stop_kernel(AttnArgs 
     if (stop) break;
     if (more) tile_load(vbase + (size_t)jn * kBlock * kHeadDim, geo.seq_kv - jn * kBlock, sV, lane, toff);
   }
+  __builtin_amdgcn_s_setprio(0);
   // the last K reads are done and no tile request is in flight: sK is free
   unit_epilogue_staged<false>(st, a, geo, bh, i, lane, sK);
   if (lane == 0) blocks_used[(size_t)bh * geo.nqb + i] = used;
